@@ -1,0 +1,146 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each test swaps one oracle step for a plausible wrong version (on the CPU) and
+checks that at least one pin test fails.
+"""
+import numpy as np
+import pytest
+
+import test_oracle_attention as TA
+import test_oracle_builder as TB
+from oracle import attention as A
+from oracle import builder as Bd
+
+
+def fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+ATTN_PINS = [
+    (TA.test_all_ones_equals_torch_sdpa, (100, 32)),
+    (TA.test_sparse_equals_torch_sdpa_with_token_mask, (77, 16)),
+    (TA.test_q_zero_closed_form, ()),
+    (TA.test_v_constant, ()),
+    (TA.test_hand_two_token, ()),
+    (TA.test_hand_gpu_sized, ()),
+    (TA.test_rows_sum_to_one_and_lse_bounds, ()),
+    (TA.test_empty_row, ()),
+]
+
+
+def any_attn_pin_fails():
+    return any(fails(f, *a) for f, a in ATTN_PINS)
+
+
+def test_unmodified_oracle_passes():
+    assert not any_attn_pin_fails()
+
+
+def test_mutant_skipped_block_as_zero_score(monkeypatch):
+    """BSA-DiT §4.3's pitfall: skipped blocks treated as score 0 instead of -inf."""
+    monkeypatch.setattr(A, "apply_mask", lambda s, allowed: np.where(allowed, s, 0.0))
+    assert any_attn_pin_fails()
+
+
+def test_mutant_missing_denominator(monkeypatch):
+    orig = A.softmax_stats
+
+    def bad(s):
+        p, lse = orig(s)
+        m = np.where(np.isfinite(s.max(1)), s.max(1), 0.0)
+        return np.exp(s - m[:, None]), lse
+    monkeypatch.setattr(A, "softmax_stats", bad)
+    assert any_attn_pin_fails()
+
+
+def test_mutant_scale_dropped(monkeypatch):
+    monkeypatch.setattr(A, "scores", lambda q, k, scale: q @ k.T)
+    assert any_attn_pin_fails()
+
+
+def test_mutant_transposed_scores(monkeypatch):
+    monkeypatch.setattr(A, "scores", lambda q, k, scale: scale * (k @ q.T) if q.shape == k.shape else scale * (q @ k.T))
+    assert any_attn_pin_fails()
+
+
+def test_mutant_lse_base2(monkeypatch):
+    orig = A.softmax_stats
+    monkeypatch.setattr(A, "softmax_stats", lambda s: (orig(s)[0], orig(s)[1] / np.log(2)))
+    assert any_attn_pin_fails()
+
+
+def test_mutant_off_by_one_block(monkeypatch):
+    orig = A.active_blocks
+    monkeypatch.setattr(A, "active_blocks", lambda rp, ci, r: np.clip(orig(rp, ci, r) + 1, 0, 10 ** 6))
+    assert any_attn_pin_fails()
+
+
+BUILDER_PINS = [
+    (TB.test_hand_block_constant, (8,)),
+    (TB.test_hand_block_constant, (7,)),
+    (TB.test_partial_block_mean_uses_valid_tokens, ()),
+    (TB.test_bruteforce_subsets, (0,)),
+    (TB.test_bruteforce_ties_prefer_lower_index, ()),
+    (TB.test_density_table, ()),
+    (TB.test_invariants, (0,)),
+]
+
+
+def any_builder_pin_fails():
+    return any(fails(f, *a) for f, a in BUILDER_PINS)
+
+
+def test_unmodified_builder_passes():
+    assert not any_builder_pin_fails()
+
+
+def test_mutant_mean_over_full_block(monkeypatch):
+    def bad(x, block):
+        x = Bd._as64(x)
+        B, H, N, D = x.shape
+        nb = -(-N // block)
+        pad = np.zeros((B, H, nb * block, D)); pad[:, :, :N] = x
+        return pad.reshape(B, H, nb, block, D).sum(3) / block
+    monkeypatch.setattr(Bd, "mean_pool", bad)
+    assert any_builder_pin_fails()
+
+
+def test_mutant_ties_to_higher_index(monkeypatch):
+    orig = Bd.select_row
+
+    def bad(score_row, sel, k_i):
+        nb = score_row.shape[0]
+        cols, gap = orig(score_row[::-1].copy(), sel[::-1].copy(), k_i)
+        return np.sort(nb - 1 - cols), gap
+    monkeypatch.setattr(Bd, "select_row", bad)
+    assert any_builder_pin_fails()
+
+
+def test_mutant_ascending_scores(monkeypatch):
+    orig = Bd.select_row
+    monkeypatch.setattr(Bd, "select_row", lambda s, sel, k: orig(-s, sel, k))
+    assert any_builder_pin_fails()
+
+
+def test_mutant_diagonal_outside_budget(monkeypatch):
+    orig = Bd.select_row
+    monkeypatch.setattr(Bd, "select_row", lambda s, sel, k: orig(s, sel, k + 1))
+    assert any_builder_pin_fails()
+
+
+def test_mutant_budget_ceil(monkeypatch):
+    import math
+    monkeypatch.setattr(Bd, "budget", lambda nb, d: 0 if d <= 0 else min(nb, max(1, math.ceil(d * nb))))
+    assert any_builder_pin_fails()
+
+
+def test_mutant_scaled_scores_are_harmless_for_ranking(monkeypatch):
+    """A positive scale on the block scores does not change any selection."""
+    orig = Bd.block_scores
+    monkeypatch.setattr(Bd, "block_scores", lambda pq, pk: 0.125 * orig(pq, pk))
+    assert fails(TB.test_hand_block_constant, 8)      # the hand scores are exact integers
+    assert not fails(TB.test_bruteforce_subsets, 0)   # but selections are unchanged
