@@ -1,0 +1,302 @@
+"""Block-sparse FlashAttention forward and mean-pool top-k mask builder for MI355X.
+
+A thin ctypes binding over libbsa.so (C ABI declared in include/bsa.h).  Every
+step of the computation runs in the library's HIP kernels; this module only
+checks tensor arguments, allocates outputs and workspaces with torch, and
+passes raw pointers plus torch's current HIP stream.  There is no fallback:
+if libbsa.so is missing or a call fails, an exception is raised.
+
+Typical use::
+
+    import block_sparse_attention_flashattn_amd as bsa
+    row_ptr, col_idx = bsa.build_mask(q, k, block=64, density=0.1)
+    o, lse = bsa.forward(q, k, v, row_ptr, col_idx, block=64)
+
+For a fixed shape and static prior, `Plan` precomputes the data-independent
+parts once (row_ptr, launch order, device copies of prior and budgets,
+workspace) so a step only launches kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "BsaError", "lib", "LIB_PATH", "status_string", "abi_version", "budget_from_density",
+    "mask_plan", "schedule_host", "validate_csr_host", "build_mask_workspace_bytes",
+    "build_mask", "build_mask_status", "schedule", "forward", "Plan", "n_blocks",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+_i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "bsa_status_string": (ctypes.c_char_p, [_i32]),
+    "bsa_abi_version": (_i32, []),
+    "bsa_budget_from_density": (_i32, [_i32, _f64]),
+    "bsa_mask_plan": (_i32, [_i32, _i32, _i32, _f64, _vp, _i32, _vp, _i32, _vp, _vp]),
+    "bsa_schedule_host": (_i32, [_vp, _i32, _vp]),
+    "bsa_validate_csr_host": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
+    "bsa_build_mask_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "bsa_build_mask": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp, _i32,
+                              _i32, _vp, _vp, _vp, _sz, _vp]),
+    "bsa_build_mask_status": (_i32, [_vp, _vp, _vp]),
+    "bsa_schedule_workspace_bytes": (_sz, [_i32]),
+    "bsa_schedule": (_i32, [_vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "bsa_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _f32,
+                           _vp, _vp, _vp]),
+}
+
+
+class BsaError(RuntimeError):
+    """A libbsa entry point returned a non-zero status."""
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m block_sparse_attention_flashattn_amd.build`")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.bsa_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise BsaError(f"{what} failed: {status_string(code)} ({code})")
+
+
+def abi_version() -> int:
+    return lib.bsa_abi_version()
+
+
+def n_blocks(N: int, block: int) -> int:
+    return (N + block - 1) // block
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _t_ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def budget_from_density(nb: int, density: float) -> int:
+    k = lib.bsa_budget_from_density(nb, density)
+    if k < 0:
+        raise BsaError("bsa_budget_from_density: invalid arguments")
+    return k
+
+
+def _prior_host(prior, B: int, H: int, nb: int):
+    if prior is None:
+        return None, 0
+    p = prior.detach().cpu().numpy() if isinstance(prior, torch.Tensor) else np.asarray(prior)
+    p = np.ascontiguousarray(p != 0, dtype=np.uint8)
+    if p.shape == (nb, nb):
+        return p, 0
+    if p.shape == (B, H, nb, nb):
+        return p, 1
+    raise ValueError(f"prior must be [nb,nb] or [B,H,nb,nb] with nb={nb}, got {p.shape}")
+
+
+def _budgets_host(budgets, nb: int):
+    if budgets is None:
+        return None
+    b = budgets.detach().cpu().numpy() if isinstance(budgets, torch.Tensor) else np.asarray(budgets)
+    b = np.ascontiguousarray(b, dtype=np.int32)
+    if b.shape != (nb,):
+        raise ValueError(f"budgets must have shape [{nb}], got {b.shape}")
+    return b
+
+
+def mask_plan(B: int, H: int, nb: int, density: float = 0.0, prior=None, budgets=None,
+              force_diag: bool = True):
+    """Host CSR plan: (row_ptr int32 [B*H*nb+1], nnz)."""
+    p, per_head = _prior_host(prior, B, H, nb)
+    b = _budgets_host(budgets, nb)
+    row_ptr = np.empty(B * H * nb + 1, dtype=np.int32)
+    nnz = ctypes.c_int64(0)
+    _check(lib.bsa_mask_plan(B, H, nb, float(density), _np_ptr(p), per_head, _np_ptr(b),
+                             int(bool(force_diag)), _np_ptr(row_ptr), ctypes.byref(nnz)),
+           "bsa_mask_plan")
+    return row_ptr, int(nnz.value)
+
+
+def schedule_host(row_ptr) -> np.ndarray:
+    rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
+    n_rows = rp.shape[0] - 1
+    order = np.empty(n_rows, dtype=np.int32)
+    _check(lib.bsa_schedule_host(_np_ptr(rp), n_rows, _np_ptr(order)), "bsa_schedule_host")
+    return order
+
+
+def validate_csr_host(row_ptr, col_idx, nb: int, strict: bool = True) -> int:
+    """-1 if the CSR is well formed, else the first offending row."""
+    rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
+    ci = np.ascontiguousarray(np.asarray(col_idx), dtype=np.int32)
+    bad = ctypes.c_int64(-1)
+    lib.bsa_validate_csr_host(_np_ptr(rp), _np_ptr(ci) if ci.size else None, rp.shape[0] - 1,
+                              nb, int(bool(strict)), ctypes.byref(bad))
+    return int(bad.value)
+
+
+def build_mask_workspace_bytes(B: int, H: int, N: int, D: int, block: int) -> int:
+    return int(lib.bsa_build_mask_workspace_bytes(B, H, N, D, block))
+
+
+def _check_qkv(*ts):
+    t0 = ts[0]
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("inputs must be CUDA (HIP) tensors")
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("inputs must be contiguous bf16 [B,H,N,D]")
+        if t.shape != t0.shape or t.device != t0.device:
+            raise ValueError("inputs must share shape and device")
+    return tuple(t0.shape)
+
+
+def _dev_i32(x, device) -> torch.Tensor:
+    if isinstance(x, torch.Tensor):
+        if x.dtype != torch.int32 or not x.is_contiguous():
+            x = x.to(torch.int32).contiguous()
+        return x.to(device)
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x), dtype=np.int32)).to(device)
+
+
+@dataclass
+class Plan:
+    """Data-independent CSR plan for one shape, prior and density (host + device copies)."""
+    B: int
+    H: int
+    N: int
+    D: int
+    block: int
+    density: float
+    force_diag: bool
+    row_ptr_host: np.ndarray
+    order_host: np.ndarray
+    nnz: int
+    row_ptr: torch.Tensor
+    order: torch.Tensor
+    prior: Optional[torch.Tensor]
+    prior_per_head: int
+    budgets: Optional[torch.Tensor]
+    workspace: torch.Tensor
+
+    @property
+    def nb(self) -> int:
+        return n_blocks(self.N, self.block)
+
+    @classmethod
+    def create(cls, B, H, N, D, block, density=0.0, prior=None, budgets=None, force_diag=True,
+               device="cuda"):
+        nb = n_blocks(N, block)
+        p, per_head = _prior_host(prior, B, H, nb)
+        b = _budgets_host(budgets, nb)
+        row_ptr_h, nnz = mask_plan(B, H, nb, density, p, b, force_diag)
+        order_h = schedule_host(row_ptr_h)
+        ws = torch.empty(build_mask_workspace_bytes(B, H, N, D, block), dtype=torch.uint8,
+                         device=device)
+        return cls(B, H, N, D, block, float(density), bool(force_diag), row_ptr_h, order_h, nnz,
+                   _dev_i32(row_ptr_h, device), _dev_i32(order_h, device),
+                   None if p is None else torch.from_numpy(p).to(device), per_head,
+                   None if b is None else torch.from_numpy(b).to(device), ws)
+
+
+def build_mask(q: torch.Tensor, k: torch.Tensor, block: int, density: float = 0.0, prior=None,
+               budgets=None, force_diag: bool = True, plan: Optional[Plan] = None,
+               col_idx: Optional[torch.Tensor] = None):
+    """Mean-pool top-k block mask on the GPU -> (row_ptr, col_idx) int32 device tensors.
+
+    Each query block keeps `prior` (+ its diagonal if force_diag) and is filled
+    up to its budget (`budgets[i]`, else round(density * nb)) with the KV blocks
+    of highest mean-pooled score.  Pass a `Plan` to reuse the host plan.
+    """
+    B, H, N, D = _check_qkv(q, k)
+    if plan is None:
+        plan = Plan.create(B, H, N, D, block, density, prior, budgets, force_diag, q.device)
+    if (plan.B, plan.H, plan.N, plan.D, plan.block) != (B, H, N, D, block):
+        raise ValueError("plan does not match the input shape")
+    if col_idx is None:
+        col_idx = torch.empty(max(plan.nnz, 1), dtype=torch.int32, device=q.device)
+    _check(lib.bsa_build_mask(_t_ptr(q), _t_ptr(k), B, H, N, D, block, plan.density,
+                              _t_ptr(plan.budgets), _t_ptr(plan.prior), plan.prior_per_head,
+                              int(plan.force_diag), _t_ptr(plan.row_ptr), _t_ptr(col_idx),
+                              _t_ptr(plan.workspace), plan.workspace.numel(),
+                              _stream_ptr(q.device)), "bsa_build_mask")
+    return plan.row_ptr, col_idx
+
+
+def build_mask_status(plan: Plan) -> int:
+    """Synchronously read how many rows disagreed with the plan in the last build."""
+    v = ctypes.c_int32(0)
+    lib.bsa_build_mask_status(_t_ptr(plan.workspace), _stream_ptr(plan.workspace.device),
+                              ctypes.byref(v))
+    return int(v.value)
+
+
+def schedule(row_ptr: torch.Tensor, max_len: int) -> torch.Tensor:
+    """Longest-first row order computed on the device."""
+    n_rows = row_ptr.numel() - 1
+    order = torch.empty(n_rows, dtype=torch.int32, device=row_ptr.device)
+    _check(lib.bsa_schedule(_t_ptr(row_ptr), n_rows, max_len, _t_ptr(order), None, 0,
+                            _stream_ptr(row_ptr.device)), "bsa_schedule")
+    return order
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx, block: int,
+            scale: Optional[float] = None, order: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+            return_lse: bool = True):
+    """Block-sparse attention forward -> (O bf16 [B,H,N,D], LSE fp32 [B,H,N] or None)."""
+    B, H, N, D = _check_qkv(q, k, v)
+    dev = q.device
+    nb = n_blocks(N, block)
+    row_ptr = _dev_i32(row_ptr, dev)
+    col_idx = _dev_i32(col_idx, dev)
+    if row_ptr.numel() != B * H * nb + 1:
+        raise ValueError(f"row_ptr must have B*H*nb+1 = {B * H * nb + 1} entries")
+    if col_idx.numel() == 0:
+        col_idx = torch.zeros(1, dtype=torch.int32, device=dev)
+    if order is not None:
+        order = _dev_i32(order, dev)
+        if order.numel() != B * H * nb:
+            raise ValueError("order must have B*H*nb entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not s > 0.0:
+        raise ValueError("scale must be positive (or None for 1/sqrt(D))")
+    _check(lib.bsa_forward(_t_ptr(q), _t_ptr(k), _t_ptr(v), B, H, N, D, block, _t_ptr(row_ptr),
+                           _t_ptr(col_idx), _t_ptr(order), s, _t_ptr(out),
+                           _t_ptr(lse) if return_lse else None, _stream_ptr(dev)),
+           "bsa_forward")
+    return out, (lse if return_lse else None)

@@ -1,0 +1,331 @@
+// Block-sparse FlashAttention forward for gfx950 (MI355X).
+//
+// BSA-DiT §4.1: the FlashAttention tile loop keeps its outer loop over query
+// blocks, and its inner loop visits only the KV blocks listed for that query
+// block in a compact index read from global memory (here CSR).  BSA-DiT §4.3:
+// the online softmax is carried over the visited blocks only and divided by
+// their true total at the end, which is exactly the softmax with skipped
+// blocks at -inf.
+//
+// Kernel design (one workgroup per CSR row = one query block of one head):
+//   * BLK/32 wavefronts, each owning 32 query rows; the query fragment stays
+//     in VGPRs for the whole row.
+//   * Per active KV block: K [BLK x D] row-major and V^T [D x BLK] are staged
+//     in LDS, double buffered, from 16-byte coalesced global loads that are
+//     issued one tile ahead (register staging), so one barrier per tile.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator of a lane holds
+//     16 keys of ONE query, so row max / row sum are in-lane plus one
+//     cross-half exchange, and P^T leaves the accumulator already in the
+//     B-operand layout of the next product.
+//   * O^T += V^T P^T on the same MFMA; V^T is stored with bits 2 and 3 of the
+//     key index swapped inside each 16-key group, which puts the 8 keys a lane
+//     needs for one MFMA step in 16 contiguous bytes.
+//   * Softmax in the exp2 domain with scale*log2(e) folded into one FMA;
+//     fp32 state (m, l, acc); the running sum stays lane-partial until the
+//     epilogue; P is rounded to bf16 only as the MFMA operand.
+//   * A partial last block masks keys >= N to -inf and stores no query row
+//     >= N.  Columns outside [0, nb) are treated as empty tiles.
+#include <math.h>
+
+#include <mutex>
+
+#include "common.h"
+
+namespace bsa {
+namespace {
+
+template <int BLK, int HD>
+struct FwdCfg {
+  static constexpr int NW = BLK / 32;             // wavefronts, 32 query rows each
+  static constexpr int NT = 64 * NW;              // threads per workgroup (= 2 * BLK)
+  static constexpr int KS = HD + 8;               // LDS row stride of K (bf16 elements)
+  static constexpr int VS = BLK + 8;              // LDS row stride of V^T (bf16 elements)
+  static constexpr int K_ELEMS = BLK * KS;
+  static constexpr int V_ELEMS = HD * VS;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;  // bf16 elements per pipeline stage
+  static constexpr size_t LDS_BYTES = size_t(2) * STAGE * 2;
+  static constexpr int CPR = HD / 8;               // 16-byte chunks per token row
+  static constexpr int KCH = BLK * CPR / NT;       // K chunks per thread
+  static constexpr int VQ = BLK * CPR / 4 / NT;    // V quads (4 rows x 8 d) per thread
+  static constexpr int NDC = HD / 16;              // k-steps of the QK^T product
+  static constexpr int NKT = BLK / 32;             // 32-key subtiles
+  static constexpr int NDT = HD / 32;              // 32-wide d subtiles of the output
+  static_assert(KCH * NT == BLK * CPR, "K chunks must divide evenly");
+  static_assert(VQ * NT * 4 == BLK * CPR, "V quads must divide evenly");
+};
+
+// Position of key kv inside a V^T row: bits 2 and 3 swapped.
+__device__ __forceinline__ int kv_perm(int kv) {
+  return (kv & ~12) | ((kv & 4) << 1) | ((kv & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
+  const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const uint16_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
+  const uint16_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
+  return uint32_t(lo) | (uint32_t(hi) << 16);
+}
+
+template <int BLK, int HD>
+__global__ __launch_bounds__(2 * BLK) void fwd_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order, int32_t N,
+    int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O, float* __restrict__ LSE) {
+  using C = FwdCfg<BLK, HD>;
+  extern __shared__ __align__(16) uint16_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ql = lane & 31;  // query column of this lane in the MFMA tiles
+  const int hh = lane >> 5;  // which half of the k / row dimension the lane feeds
+
+  const int r = order ? order[blockIdx.x] : static_cast<int>(blockIdx.x);
+  if (r < 0 || r >= n_rows) return;
+  const int bh = r / nb;
+  const int qb = r - bh * nb;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+
+  const int nnz = row_ptr[n_rows];
+  int start = row_ptr[r];
+  int end = row_ptr[r + 1];
+  start = min(max(start, 0), nnz);
+  end = min(max(end, start), nnz);
+  const int cnt = end - start;
+
+  // Query fragment (B operand of S^T = K Q^T): lane holds d = 16c + 8hh .. +7.
+  const int qrow = qb * BLK + wave * 32 + ql;
+  bf16x8 qf[C::NDC];
+  if (qrow < N) {
+    const uint4* src = reinterpret_cast<const uint4*>(Q + head + size_t(qrow) * HD);
+#pragma unroll
+    for (int c = 0; c < C::NDC; ++c) qf[c] = __builtin_bit_cast(bf16x8, src[2 * c + hh]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < C::NDC; ++c) qf[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+
+  uint4 kst[C::KCH];
+  uint4 vst[C::VQ][4];
+
+  auto tile_valid = [&](int j) -> int {
+    return (j >= 0 && j < nb) ? min(BLK, N - j * BLK) : 0;
+  };
+
+  auto load_tile = [&](int j) {
+    const int valid = tile_valid(j);
+    const size_t off = head + size_t(valid > 0 ? j : 0) * BLK * HD;
+    const uint16_t* kb = K + off;
+    const uint16_t* vb = V + off;
+#pragma unroll
+    for (int t = 0; t < C::KCH; ++t) {
+      const int ch = tid + t * C::NT;
+      const int row = ch / C::CPR;
+      const int c8 = ch - row * C::CPR;
+      kst[t] = row < valid ? *reinterpret_cast<const uint4*>(kb + size_t(row) * HD + c8 * 8)
+                           : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < C::VQ; ++t) {
+      const int qd = tid + t * C::NT;
+      const int rq = qd / C::CPR;
+      const int c8 = qd - rq * C::CPR;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * rq + e;
+        vst[t][e] = row < valid
+                        ? *reinterpret_cast<const uint4*>(vb + size_t(row) * HD + c8 * 8)
+                        : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t* ks = smem + buf * C::STAGE;
+    uint16_t* vt = ks + C::K_ELEMS;
+#pragma unroll
+    for (int t = 0; t < C::KCH; ++t) {
+      const int ch = tid + t * C::NT;
+      const int row = ch / C::CPR;
+      const int c8 = ch - row * C::CPR;
+      *reinterpret_cast<uint4*>(ks + row * C::KS + c8 * 8) = kst[t];
+    }
+#pragma unroll
+    for (int t = 0; t < C::VQ; ++t) {
+      const int qd = tid + t * C::NT;
+      const int rq = qd / C::CPR;
+      const int c8 = qd - rq * C::CPR;
+      const int p0 = kv_perm(4 * rq);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = half_of(vst[t][0], e) | (half_of(vst[t][1], e) << 16);
+        const uint32_t hi = half_of(vst[t][2], e) | (half_of(vst[t][3], e) << 16);
+        *reinterpret_cast<uint2*>(vt + (c8 * 8 + e) * C::VS + p0) = make_uint2(lo, hi);
+      }
+    }
+  };
+
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s, shared by both halves
+  float l_run = 0.f;        // lane-partial running sum
+  f32x16 acc[C::NDT];
+#pragma unroll
+  for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+
+  if (cnt > 0) load_tile(col_idx[start]);
+
+  for (int t = 0; t < cnt; ++t) {
+    const int buf = t & 1;
+    const int j = col_idx[start + t];
+    store_tile(buf);
+    __syncthreads();
+    if (t + 1 < cnt) load_tile(col_idx[start + t + 1]);
+
+    const uint16_t* ks = smem + buf * C::STAGE;
+    const uint16_t* vt = ks + C::K_ELEMS;
+    const int valid = tile_valid(j);
+
+    // S^T tile: lane (ql, hh) holds keys 32kt + 8(i/4) + 4hh + (i%4) of query ql.
+    f32x16 s[C::NKT];
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < C::NDC; ++c) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(ks + (32 * kt + ql) * C::KS + 16 * c + 8 * hh);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kt], 0, 0, 0);
+      }
+    }
+    if (valid < BLK) {
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kv = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (kv >= valid) s[kt][i] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+
+    float ls = 0.f;
+    bf16x8 pb[C::NKT][2];
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_use));
+        ls += p;
+        pb[kt][i >> 3][i & 7] = static_cast<__bf16>(p);
+      }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[u][i] *= alpha;
+
+    // O^T += V^T P^T: A = V^T rows d = 32u + ql, keys at permuted positions 8hh..8hh+7.
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int u = 0; u < C::NDT; ++u) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * u + ql) * C::VS +
+                                                            32 * kt + 16 * c2 + 8 * hh);
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c2], acc[u], 0, 0, 0);
+        }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    uint16_t* orow = O + head + size_t(qrow) * HD;
+#pragma unroll
+    for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * u + 8 * g + 4 * hh;
+        const uint32_t w0 = pack_bf16x2(acc[u][4 * g + 0] * inv, acc[u][4 * g + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(acc[u][4 * g + 2] * inv, acc[u][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+      }
+    if (hh == 0 && LSE != nullptr) {
+      LSE[size_t(bh) * N + qrow] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+}
+
+template <int BLK, int HD>
+bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
+                      int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                      const int32_t* order, float sl2, void* o, float* lse, hipStream_t stream) {
+  using C = FwdCfg<BLK, HD>;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<BLK, HD>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(C::LDS_BYTES));
+  });
+  if (attr != hipSuccess) return BSA_ERR_HIP;
+  hipLaunchKernelGGL((fwd_kernel<BLK, HD>), dim3(n_rows), dim3(C::NT), C::LDS_BYTES, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), row_ptr, col_idx, order, N, nb, n_rows,
+                     sl2, static_cast<uint16_t*>(o), lse);
+  BSA_HIP_CHECK_LAUNCH();
+  return BSA_OK;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v,
+                                          int32_t B, int32_t H, int32_t N, int32_t D,
+                                          int32_t block, const int32_t* row_ptr_dev,
+                                          const int32_t* col_idx_dev, const int32_t* order_dev,
+                                          float scale, void* o, float* lse, void* stream) {
+  using namespace bsa;
+  if (!q || !k || !v || !o || !row_ptr_dev || !col_idx_dev) return BSA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return BSA_ERR_INVALID_ARG;
+  if (!supported_shape(D, block)) return BSA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return BSA_ERR_INVALID_ARG;
+  if (!(scale == scale)) return BSA_ERR_INVALID_ARG;
+  const int32_t nb = n_blocks(N, block);
+  const int64_t rows = int64_t(B) * H * nb;
+  if (rows > INT32_MAX - 1) return BSA_ERR_UNSUPPORTED;
+  const int32_t n_rows = static_cast<int32_t>(rows);
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
+  const float sl2 = sc * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (block == 64 && D == 64)
+    return launch_fwd<64, 64>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2, o,
+                              lse, s);
+  if (block == 64 && D == 128)
+    return launch_fwd<64, 128>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2,
+                               o, lse, s);
+  if (block == 128 && D == 64)
+    return launch_fwd<128, 64>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2,
+                               o, lse, s);
+  return launch_fwd<128, 128>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2, o,
+                              lse, s);
+}

@@ -1,0 +1,307 @@
+// Mean-pool top-k block-mask builder for gfx950.
+//
+// MC-Sparse summary, section on mean-pooled block scoring: the naive selector
+// represents each query block and each KV block by the mean of its tokens,
+// scores every pair by the dot product of the two means and keeps the best
+// KV blocks per query block at the target density.  BSA-DiT §2.3 unions that
+// with a static prior; BSA-DiT §5.3 lets each query block have its own count;
+// BSA-DiT §5.3 (last paragraph) asks that the dynamic part run on the GPU so
+// no index crosses PCIe per step.
+//
+// Three launches on one stream:
+//   pool    one workgroup per (head, block, Q|K): 16-byte coalesced loads,
+//           fp32 sums over the valid tokens, LDS reduction, divide by count.
+//   score   32x32 output tiles of Pq Pk^T per head from LDS, fp32 FMA.
+//   select  one wavefront per CSR row: prior/diagonal flags, then `fill`
+//           rounds of a wavefront-wide 64-bit argmax over (score, -column)
+//           keys, then a ballot/mbcnt compaction that writes the row's
+//           columns in ascending order at row_ptr[r].
+#include <math.h>
+
+#include "common.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kStatusBytes = 256;
+
+__global__ void zero_status_kernel(int32_t* status) { *status = 0; }
+
+template <int HD>
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ Q,
+                                                   const uint16_t* __restrict__ K, int32_t N,
+                                                   int32_t nb, int32_t block,
+                                                   float* __restrict__ Pq,
+                                                   float* __restrict__ Pk) {
+  constexpr int CPR = HD / 8;     // 16-byte chunks per token row
+  constexpr int RPP = 256 / CPR;  // token rows per pass
+  __shared__ float red[RPP][HD + 1];
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;  // (bh, i) flattened
+  const int bh = blk / nb;
+  const int i = blk - bh * nb;
+  const int valid = min(block, N - i * block);
+  const uint16_t* X = blockIdx.y == 0 ? Q : K;
+  float* P = blockIdx.y == 0 ? Pq : Pk;
+  const uint16_t* base = X + (size_t(bh) * N + size_t(i) * block) * HD;
+  const int c8 = tid % CPR;
+  const int rl = tid / CPR;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int row = rl; row < valid; row += RPP) {
+    const uint4 u = *reinterpret_cast<const uint4*>(base + size_t(row) * HD + c8 * 8);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += __uint_as_float(w[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rl][c8 * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < HD) {
+    float s = 0.f;
+    for (int rr = 0; rr < RPP; ++rr) s += red[rr][tid];
+    P[size_t(blk) * HD + tid] = s / static_cast<float>(valid);
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ Pq,
+                                                    const float* __restrict__ Pk, int32_t nb,
+                                                    float* __restrict__ S) {
+  __shared__ float sq[32][HD + 1];
+  __shared__ float sk[32][HD + 1];
+  const int tid = threadIdx.x;
+  const int j0 = blockIdx.x * 32;
+  const int i0 = blockIdx.y * 32;
+  const size_t bh = blockIdx.z;
+  for (int x = tid; x < 32 * HD; x += 256) {
+    const int rr = x / HD;
+    const int d = x - rr * HD;
+    sq[rr][d] = (i0 + rr < nb) ? Pq[(bh * nb + i0 + rr) * HD + d] : 0.f;
+    sk[rr][d] = (j0 + rr < nb) ? Pk[(bh * nb + j0 + rr) * HD + d] : 0.f;
+  }
+  __syncthreads();
+  const int ti = tid >> 3;
+  const int tj = tid & 7;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < HD; ++d) {
+    const float a = sq[ti][d];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = fmaf(a, sk[tj + 8 * m][d], acc[m]);
+  }
+  if (i0 + ti < nb) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int j = j0 + tj + 8 * m;
+      if (j < nb) S[(bh * nb + i0 + ti) * nb + j] = acc[m];
+    }
+  }
+}
+
+// Order-preserving map of an fp32 score to uint32 (-0 folded onto +0).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f + 0.f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v & 0xffffffffu), off));
+    const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), off));
+    const uint64_t o = (uint64_t(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int popc_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// One wavefront per CSR row; CM = columns per lane (nb <= 64*CM).
+template <int CM>
+__global__ __launch_bounds__(256) void select_kernel(
+    const float* __restrict__ S, const uint8_t* __restrict__ prior, int32_t prior_per_head,
+    const int32_t* __restrict__ budgets, int32_t k_density, int32_t force_diag, int32_t nb,
+    int32_t n_rows, const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+    int32_t* __restrict__ status) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_rows) return;
+  const int bh = r / nb;
+  const int i = r - bh * nb;
+  const uint8_t* pr =
+      prior ? prior + (prior_per_head ? size_t(bh) * nb * nb : size_t(0)) + size_t(i) * nb
+            : nullptr;
+  const float* srow = S ? S + (size_t(bh) * nb + i) * nb : nullptr;
+  const int ki = budgets ? min(max(budgets[i], 0), nb) : k_density;
+
+  uint64_t key[CM];
+  bool insel[CM];
+  bool chosen[CM];
+  int nsel = 0;
+#pragma unroll
+  for (int c = 0; c < CM; ++c) {
+    const int j = lane + 64 * c;
+    const bool in = j < nb && ((pr && pr[j]) || (force_diag && j == i));
+    insel[c] = in;
+    chosen[c] = false;
+    key[c] = (j < nb && !in && srow)
+                 ? ((uint64_t(ordered_bits(srow[j])) << 32) | (0xffffffffu - uint32_t(j)))
+                 : 0ull;
+    nsel += __popcll(__ballot(in));
+  }
+  const int fill = max(0, ki - nsel);
+  const int nnz = row_ptr[n_rows];
+  const int start = row_ptr[r];
+  const int cnt = row_ptr[r + 1] - start;
+  if (cnt != nsel + fill || start < 0 || start + cnt > nnz) {
+    if (lane == 0) atomicAdd(status, 1);
+    return;
+  }
+  for (int f = 0; f < fill; ++f) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int c = 0; c < CM; ++c) best = key[c] > best ? key[c] : best;
+    best = wave_max_u64(best);
+    if (best == 0) break;
+#pragma unroll
+    for (int c = 0; c < CM; ++c)
+      if (key[c] == best) {
+        key[c] = 0;
+        chosen[c] = true;
+      }
+  }
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < CM; ++c) {
+    const bool flag = insel[c] || chosen[c];
+    const uint64_t m = __ballot(flag);
+    if (flag) col_idx[start + base + popc_below(m)] = lane + 64 * c;
+    base += __popcll(m);
+  }
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct MaskWs {
+  size_t status, pq, pk, s, total;
+};
+
+MaskWs mask_ws_layout(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block) {
+  const size_t nb = static_cast<size_t>(n_blocks(N, block));
+  const size_t bhn = size_t(B) * H * nb;
+  MaskWs w;
+  w.status = 0;
+  w.pq = kStatusBytes;
+  w.pk = w.pq + round_up(bhn * D * 4);
+  w.s = w.pk + round_up(bhn * D * 4);
+  w.total = w.s + round_up(bhn * nb * 4);
+  return w;
+}
+
+template <int CM>
+void launch_select(const float* S, const uint8_t* prior, int32_t per_head, const int32_t* budgets,
+                   int32_t kd, int32_t diag, int32_t nb, int32_t n_rows, const int32_t* row_ptr,
+                   int32_t* col_idx, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(select_kernel<CM>, dim3((n_rows + 3) / 4), dim3(256), 0, s, S, prior,
+                     per_head, budgets, kd, diag, nb, n_rows, row_ptr, col_idx, status);
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" BSA_API size_t bsa_build_mask_workspace_bytes(int32_t B, int32_t H, int32_t N,
+                                                         int32_t D, int32_t block) {
+  if (B < 1 || H < 1 || N < 1 || block < 1 || D < 1) return 0;
+  return bsa::mask_ws_layout(B, H, N, D, block).total;
+}
+
+extern "C" BSA_API bsa_status bsa_build_mask(const void* q, const void* k, int32_t B, int32_t H,
+                                             int32_t N, int32_t D, int32_t block, double density,
+                                             const int32_t* budgets_dev, const uint8_t* prior_dev,
+                                             int32_t prior_per_head, int32_t force_diag,
+                                             const int32_t* row_ptr_dev, int32_t* col_idx_dev,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  using namespace bsa;
+  if (!q || !k || !row_ptr_dev || !col_idx_dev || !workspace) return BSA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || density != density) return BSA_ERR_INVALID_ARG;
+  if (!supported_shape(D, block)) return BSA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return BSA_ERR_INVALID_ARG;
+  const int32_t nb = n_blocks(N, block);
+  if (nb > kMaxBlocks) return BSA_ERR_UNSUPPORTED;
+  const int64_t rows = int64_t(B) * H * nb;
+  if (rows > INT32_MAX - 1) return BSA_ERR_UNSUPPORTED;
+  const int32_t n_rows = static_cast<int32_t>(rows);
+  const MaskWs w = mask_ws_layout(B, H, N, D, block);
+  if (workspace_bytes < w.total) return BSA_ERR_CAPACITY;
+  const int32_t kd = bsa_budget_from_density(nb, density);
+  const bool need_scores = budgets_dev != nullptr || kd > 0;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* status = reinterpret_cast<int32_t*>(ws + w.status);
+  float* pq = reinterpret_cast<float*>(ws + w.pq);
+  float* pk = reinterpret_cast<float*>(ws + w.pk);
+  float* S = reinterpret_cast<float*>(ws + w.s);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipLaunchKernelGGL(zero_status_kernel, dim3(1), dim3(1), 0, s, status);
+  BSA_HIP_CHECK_LAUNCH();
+  if (need_scores) {
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    if (D == 64)
+      hipLaunchKernelGGL(pool_kernel<64>, dim3(n_rows, 2), dim3(256), 0, s, qq, kk, N, nb, block,
+                         pq, pk);
+    else
+      hipLaunchKernelGGL(pool_kernel<128>, dim3(n_rows, 2), dim3(256), 0, s, qq, kk, N, nb,
+                         block, pq, pk);
+    BSA_HIP_CHECK_LAUNCH();
+    const dim3 g((nb + 31) / 32, (nb + 31) / 32, B * H);
+    if (D == 64)
+      hipLaunchKernelGGL(score_kernel<64>, g, dim3(256), 0, s, pq, pk, nb, S);
+    else
+      hipLaunchKernelGGL(score_kernel<128>, g, dim3(256), 0, s, pq, pk, nb, S);
+    BSA_HIP_CHECK_LAUNCH();
+  }
+  const float* Sp = need_scores ? S : nullptr;
+  const int32_t diag = force_diag ? 1 : 0;
+  const int32_t ph = prior_per_head ? 1 : 0;
+  if (nb <= 64)
+    launch_select<1>(Sp, prior_dev, ph, budgets_dev, kd, diag, nb, n_rows, row_ptr_dev,
+                     col_idx_dev, status, s);
+  else if (nb <= 128)
+    launch_select<2>(Sp, prior_dev, ph, budgets_dev, kd, diag, nb, n_rows, row_ptr_dev,
+                     col_idx_dev, status, s);
+  else if (nb <= 256)
+    launch_select<4>(Sp, prior_dev, ph, budgets_dev, kd, diag, nb, n_rows, row_ptr_dev,
+                     col_idx_dev, status, s);
+  else if (nb <= 512)
+    launch_select<8>(Sp, prior_dev, ph, budgets_dev, kd, diag, nb, n_rows, row_ptr_dev,
+                     col_idx_dev, status, s);
+  else
+    launch_select<16>(Sp, prior_dev, ph, budgets_dev, kd, diag, nb, n_rows, row_ptr_dev,
+                      col_idx_dev, status, s);
+  BSA_HIP_CHECK_LAUNCH();
+  return BSA_OK;
+}
+
+extern "C" BSA_API bsa_status bsa_build_mask_status(const void* workspace, void* stream,
+                                                    int32_t* mismatched_rows) {
+  if (!workspace || !mismatched_rows) return BSA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return BSA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return BSA_ERR_HIP;
+  *mismatched_rows = v;
+  return v == 0 ? BSA_OK : BSA_ERR_PLAN_MISMATCH;
+}

@@ -1,0 +1,116 @@
+// Host-side planning: density -> count, CSR row lengths, launch order, CSR check.
+//
+// BSA-DiT §5.3 (last paragraph): static structure is prepared ahead of time and
+// nothing data-dependent is built on the CPU.  Everything here depends only on
+// sizes, the static prior and the budgets, never on Q/K/V, so it runs once per
+// shape and prior and its results can be cached across calls.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "bsa.h"
+
+extern "C" BSA_API const char* bsa_status_string(bsa_status s) {
+  switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARG: return "BSA_ERR_INVALID_ARG";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_HIP: return "BSA_ERR_HIP";
+    case BSA_ERR_CAPACITY: return "BSA_ERR_CAPACITY";
+    case BSA_ERR_PLAN_MISMATCH: return "BSA_ERR_PLAN_MISMATCH";
+    default: return "BSA_ERR_UNKNOWN";
+  }
+}
+
+extern "C" BSA_API int32_t bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+extern "C" BSA_API int32_t bsa_budget_from_density(int32_t nb, double density) {
+  if (nb < 1 || density != density) return -1;
+  if (density <= 0.0) return 0;
+  double k = floor(density * static_cast<double>(nb) + 0.5);
+  if (k < 1.0) k = 1.0;
+  if (k > static_cast<double>(nb)) k = static_cast<double>(nb);
+  return static_cast<int32_t>(k);
+}
+
+extern "C" BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double density,
+                                            const uint8_t* prior_host, int32_t prior_per_head,
+                                            const int32_t* budgets_host, int32_t force_diag,
+                                            int32_t* row_ptr_out, int64_t* nnz_out) {
+  if (B < 1 || H < 1 || nb < 1 || !row_ptr_out || density != density) return BSA_ERR_INVALID_ARG;
+  const int32_t kd = bsa_budget_from_density(nb, density);
+  const int64_t n_rows = int64_t(B) * H * nb;
+  if (n_rows > INT32_MAX - 1) return BSA_ERR_CAPACITY;
+  int64_t acc = 0;
+  row_ptr_out[0] = 0;
+  for (int64_t bh = 0; bh < int64_t(B) * H; ++bh) {
+    for (int32_t i = 0; i < nb; ++i) {
+      int64_t sel = 0;
+      if (prior_host) {
+        const uint8_t* row =
+            prior_host + (prior_per_head ? bh * nb * nb : int64_t(0)) + int64_t(i) * nb;
+        for (int32_t j = 0; j < nb; ++j) sel += row[j] ? 1 : 0;
+        if (force_diag && !row[i]) ++sel;
+      } else if (force_diag) {
+        sel = 1;
+      }
+      int64_t ki = kd;
+      if (budgets_host) {
+        ki = budgets_host[i];
+        if (ki < 0) ki = 0;
+        if (ki > nb) ki = nb;
+      }
+      acc += sel > ki ? sel : ki;
+      if (acc > INT32_MAX) return BSA_ERR_CAPACITY;
+      row_ptr_out[bh * nb + i + 1] = static_cast<int32_t>(acc);
+    }
+  }
+  if (nnz_out) *nnz_out = acc;
+  return BSA_OK;
+}
+
+extern "C" BSA_API bsa_status bsa_schedule_host(const int32_t* row_ptr, int32_t n_rows,
+                                                int32_t* order_out) {
+  if (!row_ptr || !order_out || n_rows < 1) return BSA_ERR_INVALID_ARG;
+  int32_t max_len = 0;
+  for (int32_t r = 0; r < n_rows; ++r) {
+    const int32_t len = row_ptr[r + 1] - row_ptr[r];
+    if (len < 0) return BSA_ERR_INVALID_ARG;
+    if (len > max_len) max_len = len;
+  }
+  // Stable counting sort by descending length.
+  std::vector<int32_t> start(size_t(max_len) + 2, 0);
+  for (int32_t r = 0; r < n_rows; ++r) ++start[size_t(max_len - (row_ptr[r + 1] - row_ptr[r])) + 1];
+  for (size_t b = 1; b < start.size(); ++b) start[b] += start[b - 1];
+  for (int32_t r = 0; r < n_rows; ++r)
+    order_out[start[size_t(max_len - (row_ptr[r + 1] - row_ptr[r]))]++] = r;
+  return BSA_OK;
+}
+
+extern "C" BSA_API bsa_status bsa_validate_csr_host(const int32_t* row_ptr,
+                                                    const int32_t* col_idx, int32_t n_rows,
+                                                    int32_t nb, int32_t strict,
+                                                    int64_t* bad_row) {
+  if (bad_row) *bad_row = -1;
+  if (!row_ptr || n_rows < 1 || nb < 1) return BSA_ERR_INVALID_ARG;
+  if (row_ptr[0] != 0) {
+    if (bad_row) *bad_row = 0;
+    return BSA_ERR_INVALID_ARG;
+  }
+  for (int32_t r = 0; r < n_rows; ++r) {
+    const int32_t a = row_ptr[r], b = row_ptr[r + 1];
+    bool ok = b >= a && (b == a || col_idx != nullptr);
+    for (int32_t t = a; ok && t < b; ++t) {
+      const int32_t c = col_idx[t];
+      if (c < 0 || c >= nb) ok = false;
+      if (strict && t > a && col_idx[t - 1] >= c) ok = false;
+    }
+    if (!ok) {
+      if (bad_row) *bad_row = r;
+      return BSA_ERR_INVALID_ARG;
+    }
+  }
+  return BSA_OK;
+}

@@ -1,0 +1,196 @@
+/*
+ * bsa.h - C ABI of libbsa: block-sparse FlashAttention forward and its
+ * mean-pool top-k block-mask builder, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   BSA-DiT   "多模态DiT中的块稀疏注意力：从原理到工程落地" (block-sparse attention
+ *             in multimodal DiTs, from principle to deployment), m.nlpx.cn.
+ *   MC-Sparse summary  "Can sparse attention close the quality gap in
+ *             diffusion transformers" (wispaper.ai summary of the MC-Sparse paper).
+ *
+ * Conventions shared by every entry point
+ *   - Q, K, V, O: bf16, contiguous [B, H, N, D] (D fastest), 16-byte aligned.
+ *   - block size b is both the query-block and the KV-block size; nb = ceil(N/b).
+ *     The last block may be partial: its missing query rows are neither
+ *     computed nor stored, its missing keys are masked out.
+ *   - CSR row r = (bi*H + h)*nb + i lists the KV blocks that query block i of
+ *     head (bi, h) attends to: row_ptr int32 [B*H*nb + 1], col_idx int32 [nnz],
+ *     nnz = row_ptr[B*H*nb].  Columns of a row are in [0, nb); the mask builder
+ *     writes them strictly ascending (the forward does not need any order).
+ *   - LSE: fp32 [B, H, N], natural log, including the softmax scale.
+ *   - Supported: D in {64, 128}, b in {64, 128}, 1 <= N, nb <= 1024.
+ *   - Ownership: the caller allocates every buffer (device buffers with
+ *     hipMalloc or torch, host buffers anywhere); the library allocates no
+ *     memory and keeps no state.  Device work is enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL = the null stream) and is
+ *     asynchronous: the library never synchronises.
+ *   - Errors: every entry point returns a bsa_status; invalid arguments are
+ *     rejected before anything is enqueued.  No C++ exception crosses the ABI.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_API __attribute__((visibility("default")))
+
+typedef int32_t bsa_status;
+#define BSA_OK 0
+#define BSA_ERR_INVALID_ARG (-1) /* null pointer, bad size, misaligned buffer   */
+#define BSA_ERR_UNSUPPORTED (-2) /* D, block or nb outside the supported set     */
+#define BSA_ERR_HIP (-3)         /* a HIP launch or runtime call failed          */
+#define BSA_ERR_CAPACITY (-4)    /* workspace too small, or nnz beyond int32     */
+#define BSA_ERR_PLAN_MISMATCH (-5) /* CSR rows do not match prior + budget plan */
+
+/* Human-readable name of a status code (static string, never NULL). */
+BSA_API const char* bsa_status_string(bsa_status s);
+
+/* ABI version of this header (incremented on any signature change). */
+#define BSA_ABI_VERSION 1
+BSA_API int32_t bsa_abi_version(void);
+
+/* ---------------------------------------------------------------- host plan */
+
+/*
+ * Blocks per query block for a target density (host, pure).
+ * BSA-DiT §5.1 and the MC-Sparse summary (mean-pooled selection "at a given
+ * attention density") fix a density, not a count; the count is
+ *   K = 0                                   if density <= 0
+ *   K = clamp(floor(density*nb + 0.5), 1, nb) otherwise.
+ * Returns K, or -1 if nb < 1 or density is NaN.
+ */
+BSA_API int32_t bsa_budget_from_density(int32_t nb, double density);
+
+/*
+ * Data-independent CSR plan (host, synchronous).  BSA-DiT §2.3 (static prior
+ * combined with dynamic selection) and §5.3 (a target count per query block):
+ * row r keeps its prior blocks (plus the diagonal when force_diag != 0) and is
+ * filled up to K_i blocks by score, so its length is max(|prior_i ∪ diag|, K_i)
+ * whatever the data.
+ *   prior_host    uint8 [nb*nb] (prior_per_head == 0) or [B*H*nb*nb] (!= 0),
+ *                 nonzero = block kept; may be NULL (empty prior).
+ *   budgets_host  int32 [nb] per-query-block K_i (shared by all heads), or NULL
+ *                 to use K = bsa_budget_from_density(nb, density) for every row.
+ *                 Values are clamped to [0, nb].
+ *   row_ptr_out   int32 [B*H*nb + 1], written.
+ *   nnz_out       total number of (row, column) entries, written (may be NULL).
+ * Errors: INVALID_ARG for bad sizes or a NULL row_ptr_out; CAPACITY if nnz
+ * would not fit in int32.
+ */
+BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double density,
+                                 const uint8_t* prior_host, int32_t prior_per_head,
+                                 const int32_t* budgets_host, int32_t force_diag,
+                                 int32_t* row_ptr_out, int64_t* nnz_out);
+
+/*
+ * Longest-row-first work order (host, synchronous).  BSA-DiT §5.3: uneven
+ * active counts per query block leave some workgroups busy and others idle;
+ * the forward launches rows in this order so long rows start first.
+ *   row_ptr  int32 [n_rows + 1]; order_out int32 [n_rows] (a permutation of
+ *   0..n_rows-1, by descending row length, ties by ascending row index).
+ */
+BSA_API bsa_status bsa_schedule_host(const int32_t* row_ptr, int32_t n_rows,
+                                     int32_t* order_out);
+
+/*
+ * Structural CSR check (host, synchronous): row_ptr[0] == 0, non-decreasing,
+ * every column in [0, nb), and (if strict != 0) strictly ascending per row.
+ * On failure returns INVALID_ARG and writes the first offending row to
+ * *bad_row (if non-NULL); on success *bad_row = -1.
+ */
+BSA_API bsa_status bsa_validate_csr_host(const int32_t* row_ptr, const int32_t* col_idx,
+                                         int32_t n_rows, int32_t nb, int32_t strict,
+                                         int64_t* bad_row);
+
+/* ------------------------------------------------------------- device calls */
+
+/*
+ * Bytes of device workspace bsa_build_mask needs: pooled Q and K (fp32
+ * [B,H,nb,D] each), block scores (fp32 [B,H,nb,nb]) and a status word.
+ */
+BSA_API size_t bsa_build_mask_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D,
+                                              int32_t block);
+
+/*
+ * Mean-pool top-k block mask (device, async on `stream`).
+ * MC-Sparse summary, section on mean-pooled block scoring: every query block
+ * and KV block is represented by the mean of its (valid) tokens, every pair is
+ * scored by the dot product of those means (fp32, no scale), and each query
+ * block keeps its highest-scoring KV blocks; BSA-DiT §2.3: unioned with a
+ * static prior; BSA-DiT §5.3: optional per-row target counts.
+ *   q, k          bf16 [B,H,N,D] device.
+ *   density       target density (used when budgets_dev is NULL).
+ *   budgets_dev   int32 [nb] device, or NULL.
+ *   prior_dev     uint8 [nb*nb] or [B*H*nb*nb] device, or NULL.
+ *   force_diag    nonzero: block i is always kept in row i.
+ *   row_ptr_dev   int32 [B*H*nb+1] device: MUST be the plan of bsa_mask_plan
+ *                 for the same prior, budgets/density and force_diag.
+ *   col_idx_dev   int32 [nnz] device, written: per row the prior (and diagonal)
+ *                 plus the best max(0, K_i - |prior_i|) other blocks by
+ *                 descending score (ties: lower column), in ascending order.
+ *   workspace     device buffer of >= bsa_build_mask_workspace_bytes bytes.
+ * Rows whose planned length disagrees with the prior and budget are left
+ * unwritten and counted in the workspace status word; read it with
+ * bsa_build_mask_status.  Errors: INVALID_ARG, UNSUPPORTED, CAPACITY, HIP.
+ */
+BSA_API bsa_status bsa_build_mask(const void* q, const void* k, int32_t B, int32_t H,
+                                  int32_t N, int32_t D, int32_t block, double density,
+                                  const int32_t* budgets_dev, const uint8_t* prior_dev,
+                                  int32_t prior_per_head, int32_t force_diag,
+                                  const int32_t* row_ptr_dev, int32_t* col_idx_dev,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronously read the status word of the last bsa_build_mask that used
+ * `workspace` (waits for `stream`): *mismatched_rows = number of rows whose
+ * row_ptr length did not match the plan.  Returns PLAN_MISMATCH if nonzero.
+ */
+BSA_API bsa_status bsa_build_mask_status(const void* workspace, void* stream,
+                                         int32_t* mismatched_rows);
+
+/*
+ * Longest-row-first work order on the device (async): a counting sort of the
+ * rows by length, descending (order among equal lengths unspecified).
+ *   row_ptr_dev int32 [n_rows+1]; order_dev int32 [n_rows] written;
+ *   max_len = an upper bound of any row length (nb).
+ *   workspace   >= bsa_schedule_workspace_bytes(max_len) bytes.
+ */
+BSA_API size_t bsa_schedule_workspace_bytes(int32_t max_len);
+BSA_API bsa_status bsa_schedule(const int32_t* row_ptr_dev, int32_t n_rows, int32_t max_len,
+                                int32_t* order_dev, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Block-sparse attention forward (device, async on `stream`).
+ * BSA-DiT §4.1: for every query block, only the KV blocks listed in its CSR
+ * row are loaded and multiplied; BSA-DiT §4.3: the online softmax runs over
+ * those blocks only and divides by their true total, so skipped blocks count
+ * as score -inf.  Output:
+ *   O[bi,h,a,:] = sum_c softmax_c(scale * q_a.k_c) v_c over active keys c,
+ *   LSE[bi,h,a] = log sum_c exp(scale * q_a.k_c)       (natural log)
+ * bf16 inputs, fp32 accumulation, O rounded to bf16 (nearest even).
+ *   q, k, v     bf16 [B,H,N,D] device; o bf16 [B,H,N,D] device (written);
+ *   lse         fp32 [B,H,N] device (written), or NULL to skip it.
+ *   row_ptr_dev, col_idx_dev  the CSR (see conventions); entries outside
+ *               [0, nb) are skipped, row bounds are clamped to [0, nnz].
+ *   order_dev   int32 [B*H*nb] launch order of rows (bsa_schedule or
+ *               bsa_schedule_host), or NULL for natural order.
+ *   scale       softmax scale; <= 0 means 1/sqrt(D).
+ * A row with no active block yields O = 0 and LSE = -inf.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t B,
+                               int32_t H, int32_t N, int32_t D, int32_t block,
+                               const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
+                               const int32_t* order_dev, float scale, void* o, float* lse,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

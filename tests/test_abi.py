@@ -1,0 +1,112 @@
+"""The C ABI loads, exports every declared symbol, and its host entry points agree
+with the oracle's plan.  No GPU needed: device entry points are only called with
+arguments they must reject before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_flashattn_amd as bsa
+from oracle import builder as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    return re.findall(r"BSA_API\s+[\w\s\*]+?\b(bsa_\w+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert len(names) >= 12
+    handle = ctypes.CDLL(bsa.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert set(names) == set(bsa._SIGS), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    assert bsa.status_string(0) == "BSA_OK"
+    assert bsa.status_string(-1) == "BSA_ERR_INVALID_ARG"
+    assert bsa.status_string(-5) == "BSA_ERR_PLAN_MISMATCH"
+    assert bsa.status_string(-99) == "BSA_ERR_UNKNOWN"
+    assert bsa.abi_version() == 1
+
+
+def test_budget_matches_oracle():
+    for nb in (1, 7, 8, 64, 66, 128, 250, 256, 1000):
+        for d in (0.0, -1.0, 1e-9, 0.01, 0.05, 0.1, 0.15, 0.25, 0.5, 0.999, 1.0, 2.0):
+            assert bsa.budget_from_density(nb, d) == Bd.budget(nb, d), (nb, d)
+    assert bsa.lib.bsa_budget_from_density(0, 0.5) == -1
+    assert bsa.lib.bsa_budget_from_density(8, float("nan")) == -1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mask_plan_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    B, H, nb = 2, 3, int(rng.integers(1, 40))
+    density = float(rng.choice([0.0, 0.07, 0.3, 1.0]))
+    prior = None
+    if seed % 2:
+        prior = (rng.random((B, H, nb, nb) if seed == 3 else (nb, nb)) < 0.2).astype(np.uint8)
+    budgets = rng.integers(-2, nb + 3, nb) if seed >= 2 else None
+    for diag in (True, False):
+        rp, nnz = bsa.mask_plan(B, H, nb, density, prior, budgets, diag)
+        counts = Bd.plan_counts(B, H, nb, density, prior, budgets, diag)
+        assert rp[0] == 0 and np.array_equal(np.diff(rp), counts) and nnz == counts.sum()
+
+
+def test_mask_plan_workload_totals():
+    import workloads as W
+    rp, nnz = bsa.mask_plan(2, 24, 66, 0.0, W.t2i_prior())
+    assert nnz == 2 * 24 * 666
+    rp, nnz = bsa.mask_plan(1, 24, 256, 0.10, W.video_prior())
+    assert nnz == 24 * 6728
+    rp, nnz = bsa.mask_plan(1, 16, 128, 0.10)
+    assert nnz == 16 * 1664
+    rp, nnz = bsa.mask_plan(1, 24, 250, 0.0, None, W.ragged_budgets())
+    assert nnz == 24 * 3125
+
+
+def test_schedule_host_is_stable_longest_first():
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 9, 200)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    order = bsa.schedule_host(rp)
+    assert sorted(order.tolist()) == list(range(200))
+    key = [(-lens[r], r) for r in order]
+    assert key == sorted(key)
+
+
+def test_validate_csr_host():
+    rp = np.array([0, 2, 2, 5], np.int32)
+    assert bsa.validate_csr_host(rp, np.array([0, 3, 1, 2, 3]), 4) == -1
+    assert bsa.validate_csr_host(rp, np.array([0, 4, 1, 2, 3]), 4) == 0      # column out of range
+    assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 1, 3]), 4) == 2      # not ascending
+    assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 1, 3]), 4, strict=False) == -1
+    assert bsa.validate_csr_host(np.array([0, 2, 1], np.int32), np.array([0, 1]), 4) == 1
+
+
+def test_device_entry_points_reject_bad_arguments():
+    L = bsa.lib
+    fake = ctypes.c_void_p(4096)      # never dereferenced: every call below fails validation
+    odd = ctypes.c_void_p(4097)
+    args = lambda q=fake, D=64, blk=64, N=128: (q, fake, fake, 1, 1, N, D, blk, fake, fake, None,
+                                                0.125, fake, None, None)
+    assert L.bsa_forward(*args(q=None)) == -1
+    assert L.bsa_forward(*args(D=96)) == -2
+    assert L.bsa_forward(*args(blk=32)) == -2
+    assert L.bsa_forward(*args(q=odd)) == -1
+    assert L.bsa_forward(*args(N=0)) == -1
+    mk = lambda ws_bytes=0, D=64, N=128, ws=fake: L.bsa_build_mask(
+        fake, fake, 1, 1, N, D, 64, 0.1, None, None, 0, 1, fake, fake, ws, ws_bytes, None)
+    assert mk(ws=None) == -1
+    assert mk(D=80) == -2
+    assert mk(N=64 * 1025) == -2                      # more than 1024 blocks
+    assert mk(ws_bytes=16) == -4                      # workspace too small
+    assert L.bsa_schedule(None, 4, 4, fake, None, 0, None) == -1
+    assert L.bsa_schedule(fake, 4, 100000, fake, None, 0, None) == -2
+    assert L.bsa_build_mask_workspace_bytes(1, 1, 128, 64, 64) >= 256 + 2 * 2 * 64 * 4 + 4 * 4

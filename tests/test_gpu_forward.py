@@ -1,0 +1,170 @@
+"""GPU parity of bsa_forward against the fp64 oracle, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as OA
+from parity import compare_attention, need_gpu, token_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def rand_csr(rng, B, H, nb, p, empty_rows=()):
+    rows = []
+    for r in range(B * H * nb):
+        m = rng.random(nb) < p
+        m[r % nb] = True
+        if r in empty_rows:
+            m[:] = False
+        rows.append(np.flatnonzero(m))
+    rp = np.concatenate([[0], np.cumsum([len(x) for x in rows])]).astype(np.int32)
+    ci = np.concatenate(rows).astype(np.int32) if sum(len(x) for x in rows) else np.zeros(0, np.int32)
+    return rp, ci
+
+
+def run_and_compare(bsa, q, k, v, rp, ci, block, scale=None, order=None):
+    B, H, N, D = q.shape
+    dev = "cuda"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = bsa.forward(qd, kd, vd, rp, ci, block, scale=scale, order=order)
+    torch.cuda.synchronize()
+    sc = scale if scale is not None else 1 / math.sqrt(D)
+    O, L = OA.block_sparse_attention(q, k, v, rp, ci, block, sc)
+    nb = -(-N // block)
+    sel = token_rows(range(B * H * nb), nb, block, N, H)
+    return compare_attention(o, lse, O, L, sel), o, lse
+
+
+@pytest.mark.parametrize("block,D,N", [(64, 64, 500), (64, 128, 448), (128, 64, 200),
+                                       (128, 128, 333), (64, 64, 64), (128, 128, 1)])
+def test_small_ragged_all_shapes(block, D, N):
+    """Several tiles, a ragged last block, every (block, D) the library supports."""
+    bsa = need_gpu()
+    print(f"case block={block} D={D} N={N}", flush=True)
+    rng = np.random.default_rng(block + D + N)
+    B, H = 2, 2
+    q, k, v = W.gaussian_qkv(100 + N, B, H, N, D)
+    nb = -(-N // block)
+    rp, ci = rand_csr(rng, B, H, nb, 0.5)
+    stats, _, _ = run_and_compare(bsa, q, k, v, rp, ci, block)
+    print(stats)
+
+
+def test_tiny_config_end_to_end():
+    """Tiny workload: per-head Bernoulli prior + diagonal through the GPU builder, then forward."""
+    bsa = need_gpu()
+    w = W.make("tiny")
+    q, k, v = w.tensors()
+    from oracle import builder as OB
+    rp_ref, ci_ref, _ = OB.build_mask(q, k, w.block, w.density, w.prior(), None, True)
+    rp, ci = bsa.build_mask(q.cuda(), k.cuda(), w.block, w.density, w.prior(), None, True)
+    assert np.array_equal(rp.cpu().numpy(), rp_ref)
+    assert np.array_equal(ci.cpu().numpy()[:ci_ref.size], ci_ref)
+    stats, _, _ = run_and_compare(bsa, q, k, v, rp.cpu().numpy(), ci.cpu().numpy(), w.block)
+    print(stats)
+
+
+def test_hand_case_gpu_sized():
+    """q = e0, keys 0 / e0, values 0 / e0, scale ln 3: O[:,0] = 3/4 and LSE = ln 256 (or ln 64)."""
+    bsa = need_gpu()
+    N, D = 128, 64
+    q = torch.zeros(1, 1, N, D, dtype=torch.bfloat16); q[..., 0] = 1
+    k = torch.zeros_like(q); k[0, 0, 64:, 0] = 1
+    v = torch.zeros_like(q); v[0, 0, 64:, 0] = 1
+    o, lse = bsa.forward(q.cuda(), k.cuda(), v.cuda(), np.array([0, 2, 4]), np.array([0, 1, 0, 1]),
+                         64, scale=math.log(3))
+    o = o.float().cpu()[0, 0]; lse = lse.cpu()[0, 0]
+    assert torch.allclose(o[:, 0], torch.full((N,), 0.75), atol=4e-3)
+    assert o[:, 1:].abs().max() == 0
+    assert torch.allclose(lse, torch.full((N,), math.log(256)), atol=1e-3)
+    o, lse = bsa.forward(q.cuda(), k.cuda(), v.cuda(), np.array([0, 1, 3]), np.array([0, 0, 1]),
+                         64, scale=math.log(3))
+    o = o.float().cpu()[0, 0]; lse = lse.cpu()[0, 0]
+    assert o[:64].abs().max() == 0
+    assert torch.allclose(lse[:64], torch.full((64,), math.log(64)), atol=1e-3)
+
+
+def test_empty_rows_and_explicit_scale():
+    bsa = need_gpu()
+    rng = np.random.default_rng(7)
+    B, H, N, D, block = 1, 2, 300, 64, 64
+    q, k, v = W.gaussian_qkv(7, B, H, N, D)
+    nb = 5
+    rp, ci = rand_csr(rng, B, H, nb, 0.4, empty_rows=(1, 7))
+    stats, o, lse = run_and_compare(bsa, q, k, v, rp, ci, block, scale=0.3)
+    assert (o[0, 0, 64:128].float() == 0).all()
+    assert torch.isneginf(lse[0, 0, 64:128]).all()
+
+
+def test_inactive_kv_perturbation_is_bit_identical():
+    """Rows that do not list block j are bit-identical when block j's K/V change."""
+    bsa = need_gpu()
+    rng = np.random.default_rng(8)
+    B, H, N, D, block = 1, 1, 512, 128, 64
+    q, k, v = W.gaussian_qkv(8, B, H, N, D)
+    nb = 8
+    rp, ci = rand_csr(rng, B, H, nb, 0.4)
+    j = 3
+    o1, l1 = bsa.forward(q.cuda(), k.cuda(), v.cuda(), rp, ci, block)
+    k2, v2 = k.clone(), v.clone()
+    k2[..., j * block:(j + 1) * block, :] *= -3
+    v2[..., j * block:(j + 1) * block, :] += 5
+    o2, l2 = bsa.forward(q.cuda(), k2.cuda(), v2.cuda(), rp, ci, block)
+    n_checked = 0
+    for i in range(nb):
+        if j not in ci[rp[i]:rp[i + 1]]:
+            sl = slice(i * block, (i + 1) * block)
+            assert torch.equal(o1[0, 0, sl], o2[0, 0, sl]) and torch.equal(l1[0, 0, sl], l2[0, 0, sl])
+            n_checked += 1
+    assert n_checked > 0
+
+
+def test_launch_order_and_invalid_columns():
+    """Results do not depend on the launch order; columns outside [0, nb) are skipped."""
+    bsa = need_gpu()
+    rng = np.random.default_rng(9)
+    B, H, N, D, block = 2, 3, 700, 64, 64
+    q, k, v = (t.cuda() for t in W.gaussian_qkv(9, B, H, N, D))
+    nb = 11
+    rp, ci = rand_csr(rng, B, H, nb, 0.3)
+    o0, l0 = bsa.forward(q, k, v, rp, ci, block)
+    order_h = bsa.schedule_host(rp)
+    o1, l1 = bsa.forward(q, k, v, rp, ci, block, order=order_h)
+    order_d = bsa.schedule(torch.from_numpy(rp).cuda(), nb)
+    o2, l2 = bsa.forward(q, k, v, rp, ci, block, order=order_d)
+    assert torch.equal(o0, o1) and torch.equal(o0, o2) and torch.equal(l0, l1) and torch.equal(l0, l2)
+    od = order_d.cpu().numpy()
+    lens = np.diff(rp)
+    assert sorted(od.tolist()) == list(range(B * H * nb)) and (np.diff(lens[od]) <= 0).all()
+    # insert junk columns (-1 and nb) at the front of every row
+    rows = [np.concatenate([[-1, nb], ci[rp[r]:rp[r + 1]]]) for r in range(B * H * nb)]
+    rp2 = np.concatenate([[0], np.cumsum([len(x) for x in rows])]).astype(np.int32)
+    ci2 = np.concatenate(rows).astype(np.int32)
+    o3, l3 = bsa.forward(q, k, v, rp2, ci2, block)
+    assert torch.equal(o0, o3) and torch.equal(l0, l3)
+
+
+def test_no_lse_output():
+    bsa = need_gpu()
+    q, k, v = (t.cuda() for t in W.gaussian_qkv(11, 1, 1, 256, 64))
+    rp = np.array([0, 1, 3, 4, 8], np.int32); ci = np.array([0, 0, 1, 2, 0, 1, 2, 3], np.int32)
+    o1, l1 = bsa.forward(q, k, v, rp, ci, 64)
+    o2, l2 = bsa.forward(q, k, v, rp, ci, 64, return_lse=False)
+    assert l2 is None and torch.equal(o1, o2)
+
+
+def test_all_ones_equals_dense_oracle():
+    """BSA-DiT §4.3: check the block-sparse kernel against dense attention first."""
+    bsa = need_gpu()
+    B, H, N, D, block = 1, 2, 640, 128, 128
+    q, k, v = W.gaussian_qkv(12, B, H, N, D)
+    nb = 5
+    rp = (np.arange(B * H * nb + 1) * nb).astype(np.int32)
+    ci = np.tile(np.arange(nb), B * H * nb).astype(np.int32)
+    o, lse = bsa.forward(q.cuda(), k.cuda(), v.cuda(), rp, ci, block)
+    O, L = OA.dense_attention(q, k, v, 1 / math.sqrt(D))
+    sel = token_rows(range(B * H * nb), nb, block, N, H)
+    print(compare_attention(o, lse, O, L, sel))
