@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 
@@ -59,16 +60,26 @@ __device__ __forceinline__ int kv_perm(int kv) {
   return (kv & ~12) | ((kv & 4) << 1) | ((kv & 8) >> 1);
 }
 
-__device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
-  const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const uint16_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
   const uint16_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
   return uint32_t(lo) | (uint32_t(hi) << 16);
 }
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Largest growth of the running max (log2 units) tolerated before the
+// accumulator is rescaled; probabilities then stay below 2^8 before the final
+// division, well inside fp32 and bf16 range.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int BLK, int HD>
 __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
@@ -90,6 +101,9 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
   const int bh = r / nb;
   const int qb = r - bh * nb;
   const size_t head = size_t(bh) * size_t(N) * HD;
+  const uint32_t head_bytes = static_cast<uint32_t>(size_t(N) * HD * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + head, head_bytes);
 
   const int nnz = row_ptr[n_rows];
   int start = row_ptr[r];
@@ -99,15 +113,15 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
   const int cnt = end - start;
 
   // Query fragment (B operand of S^T = K Q^T): lane holds d = 16c + 8hh .. +7.
+  // Rows past N read as zeros through the buffer bound.
   const int qrow = qb * BLK + wave * 32 + ql;
   bf16x8 qf[C::NDC];
-  if (qrow < N) {
-    const uint4* src = reinterpret_cast<const uint4*>(Q + head + size_t(qrow) * HD);
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + head, head_bytes);
+    const uint32_t qoff = static_cast<uint32_t>(qrow) * HD * 2;
 #pragma unroll
-    for (int c = 0; c < C::NDC; ++c) qf[c] = __builtin_bit_cast(bf16x8, src[2 * c + hh]);
-  } else {
-#pragma unroll
-    for (int c = 0; c < C::NDC; ++c) qf[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    for (int c = 0; c < C::NDC; ++c)
+      qf[c] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qoff + (2 * c + hh) * 16));
   }
 
   uint4 kst[C::KCH];
@@ -117,18 +131,16 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
     return (j >= 0 && j < nb) ? min(BLK, N - j * BLK) : 0;
   };
 
+  // Global -> registers for KV block j.  Keys past N, and every key of a
+  // column outside [0, nb), read as zeros through the buffer bound.
   auto load_tile = [&](int j) {
-    const int valid = tile_valid(j);
-    const size_t off = head + size_t(valid > 0 ? j : 0) * BLK * HD;
-    const uint16_t* kb = K + off;
-    const uint16_t* vb = V + off;
+    const uint32_t tb = (j >= 0 && j < nb) ? static_cast<uint32_t>(j) * BLK * HD * 2 : head_bytes;
 #pragma unroll
     for (int t = 0; t < C::KCH; ++t) {
       const int ch = tid + t * C::NT;
       const int row = ch / C::CPR;
       const int c8 = ch - row * C::CPR;
-      kst[t] = row < valid ? *reinterpret_cast<const uint4*>(kb + size_t(row) * HD + c8 * 8)
-                           : make_uint4(0, 0, 0, 0);
+      kst[t] = buf_load16(krs, tb + row * HD * 2 + c8 * 16);
     }
 #pragma unroll
     for (int t = 0; t < C::VQ; ++t) {
@@ -136,15 +148,11 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
       const int rq = qd / C::CPR;
       const int c8 = qd - rq * C::CPR;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * rq + e;
-        vst[t][e] = row < valid
-                        ? *reinterpret_cast<const uint4*>(vb + size_t(row) * HD + c8 * 8)
-                        : make_uint4(0, 0, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e) vst[t][e] = buf_load16(vrs, tb + (4 * rq + e) * HD * 2 + c8 * 16);
     }
   };
 
+  // Registers -> LDS: K row-major; V transposed, four keys per 8-byte store.
   auto store_tile = [&](int buf) {
     uint16_t* ks = smem + buf * C::STAGE;
     uint16_t* vt = ks + C::K_ELEMS;
@@ -160,17 +168,25 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
       const int qd = tid + t * C::NT;
       const int rq = qd / C::CPR;
       const int c8 = qd - rq * C::CPR;
-      const int p0 = kv_perm(4 * rq);
+      uint16_t* dst = vt + (c8 * 8) * C::VS + kv_perm(4 * rq);
+      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vst[t][0]);
+      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vst[t][1]);
+      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vst[t][2]);
+      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vst[t][3]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = half_of(vst[t][0], e) | (half_of(vst[t][1], e) << 16);
-        const uint32_t hi = half_of(vst[t][2], e) | (half_of(vst[t][3], e) << 16);
-        *reinterpret_cast<uint2*>(vt + (c8 * 8 + e) * C::VS + p0) = make_uint2(lo, hi);
+      for (int w = 0; w < 4; ++w) {
+        // d = 8*c8 + 2w takes the low halves, d + 1 the high halves.
+        const uint2 even = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u),
+                                      __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u));
+        const uint2 odd = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u),
+                                     __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u));
+        *reinterpret_cast<uint2*>(dst + (2 * w) * C::VS) = even;
+        *reinterpret_cast<uint2*>(dst + (2 * w + 1) * C::VS) = odd;
       }
     }
   };
 
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s, shared by both halves
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s (possibly stale by < slack)
   float l_run = 0.f;        // lane-partial running sum
   f32x16 acc[C::NDT];
 #pragma unroll
@@ -178,33 +194,21 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
 
-  if (cnt > 0) load_tile(col_idx[start]);
-
-  for (int t = 0; t < cnt; ++t) {
-    const int buf = t & 1;
-    const int j = col_idx[start + t];
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < cnt) load_tile(col_idx[start + t + 1]);
-
-    const uint16_t* ks = smem + buf * C::STAGE;
-    const uint16_t* vt = ks + C::K_ELEMS;
-    const int valid = tile_valid(j);
-
-    // S^T tile: lane (ql, hh) holds keys 32kt + 8(i/4) + 4hh + (i%4) of query ql.
+  // One KV tile from LDS; keys >= valid (only in a partial last block or an
+  // out-of-range column) are masked to -inf on a rarely taken branch.
+  auto compute_tile = [&](const uint16_t* ks, const uint16_t* vt, int valid) {
+    const f32x16 zero = {};
     f32x16 s[C::NKT];
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-#pragma unroll
       for (int c = 0; c < C::NDC; ++c) {
         const bf16x8 a =
             *reinterpret_cast<const bf16x8*>(ks + (32 * kt + ql) * C::KS + 16 * c + 8 * hh);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? zero : s[kt], 0, 0, 0);
       }
     }
-    if (valid < BLK) {
+    if (__builtin_expect(valid < BLK, 0)) {
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
@@ -213,16 +217,25 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
           if (kv >= valid) s[kt][i] = -INFINITY;
         }
     }
-
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float mt = mx * sl2;
+    // Lazy rescale: only when some row's max grew by more than the slack.
+    const bool need = mt > m_run + kRescaleSlack;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+      m_run = need ? mt : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[u][i] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
     float ls = 0.f;
     bf16x8 pb[C::NKT][2];
@@ -234,12 +247,7 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
         ls += p;
         pb[kt][i >> 3][i & 7] = static_cast<__bf16>(p);
       }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int u = 0; u < C::NDT; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[u][i] *= alpha;
+    l_run += ls;
 
     // O^T += V^T P^T: A = V^T rows d = 32u + ql, keys at permuted positions 8hh..8hh+7.
 #pragma unroll
@@ -252,6 +260,20 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
                                                             32 * kt + 16 * c2 + 8 * hh);
           acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c2], acc[u], 0, 0, 0);
         }
+  };
+
+  if (cnt > 0) load_tile(col_idx[start]);
+
+  for (int t = 0; t < cnt; ++t) {
+    const int buf = t & 1;
+    const int j = col_idx[start + t];
+    store_tile(buf);
+    __syncthreads();
+    // Prefetch the next tile (the last iteration harmlessly reloads its own).
+    load_tile(col_idx[start + min(t + 1, cnt - 1)]);
+    const uint16_t* ks = smem + buf * C::STAGE;
+    const uint16_t* vt = ks + C::K_ELEMS;
+    compute_tile(ks, vt, tile_valid(j));
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -311,6 +333,8 @@ extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const vo
     return BSA_ERR_INVALID_ARG;
   if (!(scale == scale)) return BSA_ERR_INVALID_ARG;
   const int32_t nb = n_blocks(N, block);
+  // Buffer offsets inside one head are 32-bit: keep a head plus one tile below 2^31 bytes.
+  if ((int64_t(nb) + 1) * block * D * 2 >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
   const int64_t rows = int64_t(B) * H * nb;
   if (rows > INT32_MAX - 1) return BSA_ERR_UNSUPPORTED;
   const int32_t n_rows = static_cast<int32_t>(rows);
