@@ -8,11 +8,16 @@
 // blocks at -inf.
 //
 // Kernel design (one workgroup per CSR row = one query block of one head):
-//   * BLK/32 wavefronts, each owning 32 query rows; the query fragment stays
-//     in VGPRs for the whole row.
+//   * 2*BLK/32 wavefronts: BLK/32 query groups of 32 rows times 2 key halves.
+//     Wave (g, h) keeps its own online-softmax state for query rows
+//     32g..32g+31 over keys h*BLK/2 .. (h+1)*BLK/2-1 of every visited tile;
+//     the two halves are merged through LDS once, after the last tile.  This
+//     halves both the serial chain of each wave and the registers it needs.
 //   * Per active KV block: K [BLK x D] row-major and V^T [D x BLK] are staged
-//     in LDS, double buffered, from 16-byte coalesced global loads that are
-//     issued one tile ahead (register staging), so one barrier per tile.
+//     in LDS, double buffered, from 16-byte buffer loads issued one tile ahead
+//     (register staging: half of the waves fetch K, the other half V), so one
+//     barrier per tile.  Buffer bounds turn keys past N and invalid columns
+//     into zeros without branches.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator of a lane holds
 //     16 keys of ONE query, so row max / row sum are in-lane plus one
 //     cross-half exchange, and P^T leaves the accumulator already in the
@@ -22,13 +27,14 @@
 //     needs for one MFMA step in 16 contiguous bytes.
 //   * Softmax in the exp2 domain with scale*log2(e) folded into one FMA;
 //     fp32 state (m, l, acc); the running sum stays lane-partial until the
-//     epilogue; P is rounded to bf16 only as the MFMA operand.
+//     epilogue; the accumulator is rescaled only when a row maximum grows by
+//     more than 2^8 (exact: the final division uses the same stale maximum);
+//     P is rounded to bf16 only as the MFMA operand.
 //   * A partial last block masks keys >= N to -inf and stores no query row
-//     >= N.  Columns outside [0, nb) are treated as empty tiles.
+//     >= N.  Columns outside [0, nb) contribute nothing.
 #include <math.h>
 
 #include <mutex>
-#include <type_traits>
 
 #include "common.h"
 
@@ -37,8 +43,9 @@ namespace {
 
 template <int BLK, int HD>
 struct FwdCfg {
-  static constexpr int NW = BLK / 32;             // wavefronts, 32 query rows each
-  static constexpr int NT = 64 * NW;              // threads per workgroup (= 2 * BLK)
+  static constexpr int NQG = BLK / 32;            // query groups of 32 rows
+  static constexpr int NW = 2 * NQG;              // wavefronts: query group x key half
+  static constexpr int NT = 64 * NW;              // threads per workgroup (= 4 * BLK)
   static constexpr int KS = HD + 8;               // LDS row stride of K (bf16 elements)
   static constexpr int VS = BLK + 8;              // LDS row stride of V^T (bf16 elements)
   static constexpr int K_ELEMS = BLK * KS;
@@ -46,13 +53,16 @@ struct FwdCfg {
   static constexpr int STAGE = K_ELEMS + V_ELEMS;  // bf16 elements per pipeline stage
   static constexpr size_t LDS_BYTES = size_t(2) * STAGE * 2;
   static constexpr int CPR = HD / 8;               // 16-byte chunks per token row
-  static constexpr int KCH = BLK * CPR / NT;       // K chunks per thread
-  static constexpr int VQ = BLK * CPR / 4 / NT;    // V quads (4 rows x 8 d) per thread
+  static constexpr int KCH = BLK * CPR / (NT / 2); // K chunks per K-loading thread
+  static constexpr int VQ = BLK * CPR / 4 / (NT / 2);  // V quads per V-loading thread
   static constexpr int NDC = HD / 16;              // k-steps of the QK^T product
-  static constexpr int NKT = BLK / 32;             // 32-key subtiles
+  static constexpr int NKT = BLK / 64;             // 32-key subtiles per key half
   static constexpr int NDT = HD / 32;              // 32-wide d subtiles of the output
-  static_assert(KCH * NT == BLK * CPR, "K chunks must divide evenly");
-  static_assert(VQ * NT * 4 == BLK * CPR, "V quads must divide evenly");
+  static_assert(KCH * (NT / 2) == BLK * CPR, "K chunks must divide evenly");
+  static_assert(VQ * (NT / 2) * 4 == BLK * CPR, "V quads must divide evenly");
+  // Merge area (reuses the stage buffers): per query group 64 lanes x (acc + m + l).
+  static constexpr size_t MERGE_BYTES = size_t(NQG) * 64 * (NDT * 16 + 4) * 4;
+  static_assert(MERGE_BYTES <= LDS_BYTES, "merge area must fit in the stage buffers");
 };
 
 // Position of key kv inside a V^T row: bits 2 and 3 swapped.
@@ -82,7 +92,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 constexpr float kRescaleSlack = 8.0f;
 
 template <int BLK, int HD>
-__global__ __launch_bounds__(2 * BLK) void fwd_kernel(
+__global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order, int32_t N,
@@ -93,8 +103,10 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int ql = lane & 31;  // query column of this lane in the MFMA tiles
-  const int hh = lane >> 5;  // which half of the k / row dimension the lane feeds
+  const int qg = wave % C::NQG;  // query group
+  const int kh = wave / C::NQG;  // key half
+  const int ql = lane & 31;      // query column of this lane in the MFMA tiles
+  const int hh = lane >> 5;      // which half of the k / row dimension the lane feeds
 
   const int r = order ? order[blockIdx.x] : static_cast<int>(blockIdx.x);
   if (r < 0 || r >= n_rows) return;
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
 
   // Query fragment (B operand of S^T = K Q^T): lane holds d = 16c + 8hh .. +7.
   // Rows past N read as zeros through the buffer bound.
-  const int qrow = qb * BLK + wave * 32 + ql;
+  const int qrow = qb * BLK + qg * 32 + ql;
   bf16x8 qf[C::NDC];
   {
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + head, head_bytes);
@@ -124,8 +136,11 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
       qf[c] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qoff + (2 * c + hh) * 16));
   }
 
-  uint4 kst[C::KCH];
-  uint4 vst[C::VQ][4];
+  // Staging registers: threads [0, NT/2) fetch V quads, threads [NT/2, NT) fetch K.
+  const bool loads_k = tid >= C::NT / 2;
+  const int lt = loads_k ? tid - C::NT / 2 : tid;
+  constexpr int NREG = C::KCH > 4 * C::VQ ? C::KCH : 4 * C::VQ;
+  uint4 st[NREG];
 
   auto tile_valid = [&](int j) -> int {
     return (j >= 0 && j < nb) ? min(BLK, N - j * BLK) : 0;
@@ -135,20 +150,24 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
   // column outside [0, nb), read as zeros through the buffer bound.
   auto load_tile = [&](int j) {
     const uint32_t tb = (j >= 0 && j < nb) ? static_cast<uint32_t>(j) * BLK * HD * 2 : head_bytes;
+    if (loads_k) {
 #pragma unroll
-    for (int t = 0; t < C::KCH; ++t) {
-      const int ch = tid + t * C::NT;
-      const int row = ch / C::CPR;
-      const int c8 = ch - row * C::CPR;
-      kst[t] = buf_load16(krs, tb + row * HD * 2 + c8 * 16);
-    }
+      for (int t = 0; t < C::KCH; ++t) {
+        const int ch = lt + t * (C::NT / 2);
+        const int row = ch / C::CPR;
+        const int c8 = ch - row * C::CPR;
+        st[t] = buf_load16(krs, tb + row * HD * 2 + c8 * 16);
+      }
+    } else {
 #pragma unroll
-    for (int t = 0; t < C::VQ; ++t) {
-      const int qd = tid + t * C::NT;
-      const int rq = qd / C::CPR;
-      const int c8 = qd - rq * C::CPR;
+      for (int t = 0; t < C::VQ; ++t) {
+        const int qd = lt + t * (C::NT / 2);
+        const int rq = qd % (BLK / 4);
+        const int c8 = qd / (BLK / 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vst[t][e] = buf_load16(vrs, tb + (4 * rq + e) * HD * 2 + c8 * 16);
+        for (int e = 0; e < 4; ++e)
+          st[4 * t + e] = buf_load16(vrs, tb + (4 * rq + e) * HD * 2 + c8 * 16);
+      }
     }
   };
 
@@ -156,32 +175,37 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
   auto store_tile = [&](int buf) {
     uint16_t* ks = smem + buf * C::STAGE;
     uint16_t* vt = ks + C::K_ELEMS;
+    if (loads_k) {
 #pragma unroll
-    for (int t = 0; t < C::KCH; ++t) {
-      const int ch = tid + t * C::NT;
-      const int row = ch / C::CPR;
-      const int c8 = ch - row * C::CPR;
-      *reinterpret_cast<uint4*>(ks + row * C::KS + c8 * 8) = kst[t];
-    }
+      for (int t = 0; t < C::KCH; ++t) {
+        const int ch = lt + t * (C::NT / 2);
+        const int row = ch / C::CPR;
+        const int c8 = ch - row * C::CPR;
+        *reinterpret_cast<uint4*>(ks + row * C::KS + c8 * 8) = st[t];
+      }
+    } else {
 #pragma unroll
-    for (int t = 0; t < C::VQ; ++t) {
-      const int qd = tid + t * C::NT;
-      const int rq = qd / C::CPR;
-      const int c8 = qd - rq * C::CPR;
-      uint16_t* dst = vt + (c8 * 8) * C::VS + kv_perm(4 * rq);
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vst[t][0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vst[t][1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vst[t][2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vst[t][3]);
+      for (int t = 0; t < C::VQ; ++t) {
+        // Consecutive lanes take consecutive key quads of one 8-column chunk, so
+        // each 8-byte store of a half-wave lands on 64 distinct LDS banks.
+        const int qd = lt + t * (C::NT / 2);
+        const int rq = qd % (BLK / 4);
+        const int c8 = qd / (BLK / 4);
+        uint16_t* dst = vt + (c8 * 8) * C::VS + kv_perm(4 * rq);
+        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&st[4 * t + 0]);
+        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&st[4 * t + 1]);
+        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&st[4 * t + 2]);
+        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&st[4 * t + 3]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = 8*c8 + 2w takes the low halves, d + 1 the high halves.
-        const uint2 even = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u),
-                                      __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u));
-        const uint2 odd = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u),
-                                     __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u));
-        *reinterpret_cast<uint2*>(dst + (2 * w) * C::VS) = even;
-        *reinterpret_cast<uint2*>(dst + (2 * w + 1) * C::VS) = odd;
+        for (int w = 0; w < 4; ++w) {
+          // d = 8*c8 + 2w takes the low halves, d + 1 the high halves.
+          const uint2 even = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u),
+                                        __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u));
+          const uint2 odd = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u),
+                                       __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u));
+          *reinterpret_cast<uint2*>(dst + (2 * w) * C::VS) = even;
+          *reinterpret_cast<uint2*>(dst + (2 * w + 1) * C::VS) = odd;
+        }
       }
     }
   };
@@ -194,17 +218,19 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
 
-  // One KV tile from LDS; keys >= valid (only in a partial last block or an
-  // out-of-range column) are masked to -inf on a rarely taken branch.
+  // This wave's key half of one KV tile from LDS; keys >= valid (only in a
+  // partial last block or an out-of-range column) are masked to -inf on a
+  // rarely taken branch.
   auto compute_tile = [&](const uint16_t* ks, const uint16_t* vt, int valid) {
     const f32x16 zero = {};
     f32x16 s[C::NKT];
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) {
+      const int key0 = (kh * C::NKT + kt) * 32;
 #pragma unroll
       for (int c = 0; c < C::NDC; ++c) {
         const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(ks + (32 * kt + ql) * C::KS + 16 * c + 8 * hh);
+            *reinterpret_cast<const bf16x8*>(ks + (key0 + ql) * C::KS + 16 * c + 8 * hh);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? zero : s[kt], 0, 0, 0);
       }
     }
@@ -213,7 +239,7 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int kv = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const int kv = (kh * C::NKT + kt) * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
           if (kv >= valid) s[kt][i] = -INFINITY;
         }
     }
@@ -256,8 +282,9 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int u = 0; u < C::NDT; ++u) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * u + ql) * C::VS +
-                                                            32 * kt + 16 * c2 + 8 * hh);
+          const int key0 = (kh * C::NKT + kt) * 32 + 16 * c2;
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(vt + (32 * u + ql) * C::VS + key0 + 8 * hh);
           acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c2], acc[u], 0, 0, 0);
         }
   };
@@ -272,12 +299,44 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
     // Prefetch the next tile (the last iteration harmlessly reloads its own).
     load_tile(col_idx[start + min(t + 1, cnt - 1)]);
     const uint16_t* ks = smem + buf * C::STAGE;
-    const uint16_t* vt = ks + C::K_ELEMS;
-    compute_tile(ks, vt, tile_valid(j));
+    compute_tile(ks, ks + C::K_ELEMS, tile_valid(j));
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // Merge the two key halves: wave (g, 1) hands (m, l, acc) to wave (g, 0).
+  float l_half = l_run + __shfl_xor(l_run, 32);
+  __syncthreads();  // every wave is done reading the stage buffers
+  float* mg = reinterpret_cast<float*>(smem) + size_t(qg) * 64 * (C::NDT * 16 + 4);
+  if (kh == 1) {
+#pragma unroll
+    for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(mg + ((u * 4 + g) * 64 + lane) * 4) =
+            f32x4{acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
+    mg[C::NDT * 16 * 64 + lane] = m_run;
+    mg[C::NDT * 16 * 64 + 64 + lane] = l_half;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float m1 = mg[C::NDT * 16 * 64 + lane];
+    const float l1 = mg[C::NDT * 16 * 64 + 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    l_half = l_half * a0 + l1 * a1;
+    m_run = m;
+#pragma unroll
+    for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(mg + ((u * 4 + g) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[u][4 * g + e] = acc[u][4 * g + e] * a0 + o1[e] * a1;
+      }
+  }
+
+  const float inv = l_half > 0.f ? 1.f / l_half : 0.f;
   if (qrow < N) {
     uint16_t* orow = O + head + size_t(qrow) * HD;
 #pragma unroll
@@ -291,7 +350,8 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(
       }
     if (hh == 0 && LSE != nullptr) {
       LSE[size_t(bh) * N + qrow] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+          l_half > 0.f ? (m_run + __builtin_amdgcn_logf(l_half)) * 0.69314718055994531f
+                       : -INFINITY;
     }
   }
 }
