@@ -142,7 +142,7 @@ def main():
     def step():
         if dynamic:
             bsa.build_mask(qd, kd, w.block, plan=plan, col_idx=col_idx)
-        bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, order=plan.order, out=o, lse=lse)
+        bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, work=plan, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -160,7 +160,7 @@ def main():
            for _ in range(reps)]
     for a, b in evs:
         a.record(stream)
-        bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, order=plan.order, out=o, lse=lse)
+        bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, work=plan, out=o, lse=lse)
         b.record(stream)
     torch.cuda.synchronize()
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -202,7 +202,7 @@ def main():
         for d in (0.05, 0.10, 0.15, 0.25, 0.50, 1.0):
             p2 = bsa.Plan.create(w.B, w.H, w.N, w.D, w.block, d, None, None, True, dev)
             rp2, ci2 = bsa.build_mask(qd, kd, w.block, plan=p2)
-            t = time_launches(lambda: bsa.forward(qd, kd, vd, rp2, ci2, w.block, order=p2.order,
+            t = time_launches(lambda: bsa.forward(qd, kd, vd, rp2, ci2, w.block, work=p2,
                                                   out=o, lse=lse))
             sweep.append({"density": p2.nnz / (n_rows * nb), "nnz": p2.nnz, "fwd_ms": t})
         x = np.array([s["nnz"] for s in sweep], float)

@@ -29,8 +29,9 @@ import torch
 
 __all__ = [
     "BsaError", "lib", "LIB_PATH", "status_string", "abi_version", "budget_from_density",
-    "mask_plan", "schedule_host", "validate_csr_host", "build_mask_workspace_bytes",
-    "build_mask", "build_mask_status", "schedule", "forward", "Plan", "n_blocks",
+    "mask_plan", "work_plan", "validate_csr_host", "build_mask_workspace_bytes",
+    "forward_workspace_bytes", "build_mask", "build_mask_status", "schedule", "forward",
+    "Plan", "Work", "n_blocks", "default_max_tiles",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,16 +45,17 @@ _SIGS = {
     "bsa_abi_version": (_i32, []),
     "bsa_budget_from_density": (_i32, [_i32, _f64]),
     "bsa_mask_plan": (_i32, [_i32, _i32, _i32, _f64, _vp, _i32, _vp, _i32, _vp, _vp]),
-    "bsa_schedule_host": (_i32, [_vp, _i32, _vp]),
+    "bsa_work_plan_ints": (_i64, [_i32, _i64, _i32]),
+    "bsa_work_plan_host": (_i32, [_vp, _i32, _i32, _vp, _i64, _vp, _vp, _vp]),
     "bsa_validate_csr_host": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "bsa_build_mask_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "bsa_build_mask": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp, _i32,
                               _i32, _vp, _vp, _vp, _sz, _vp]),
     "bsa_build_mask_status": (_i32, [_vp, _vp, _vp]),
-    "bsa_schedule_workspace_bytes": (_sz, [_i32]),
-    "bsa_schedule": (_i32, [_vp, _i32, _i32, _vp, _vp, _sz, _vp]),
-    "bsa_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _f32,
-                           _vp, _vp, _vp]),
+    "bsa_schedule": (_i32, [_vp, _i32, _i32, _vp, _vp]),
+    "bsa_forward_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "bsa_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
+                           _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -147,12 +149,24 @@ def mask_plan(B: int, H: int, nb: int, density: float = 0.0, prior=None, budgets
     return row_ptr, int(nnz.value)
 
 
-def schedule_host(row_ptr) -> np.ndarray:
+def work_plan(row_ptr, max_tiles: int = 0):
+    """Host work list: (work int32 array, n_items, n_merges, n_slots).
+
+    Rows longer than `max_tiles` KV blocks are cut into near-equal chunks
+    (max_tiles <= 0: never); items are ordered longest first.
+    """
     rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
     n_rows = rp.shape[0] - 1
-    order = np.empty(n_rows, dtype=np.int32)
-    _check(lib.bsa_schedule_host(_np_ptr(rp), n_rows, _np_ptr(order)), "bsa_schedule_host")
-    return order
+    cap = int(lib.bsa_work_plan_ints(n_rows, int(rp[-1]), int(max_tiles)))
+    if cap < 0:
+        raise BsaError("bsa_work_plan_ints: invalid arguments")
+    work = np.empty(max(cap, 4), dtype=np.int32)
+    ni, nm, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.bsa_work_plan_host(_np_ptr(rp), n_rows, int(max_tiles), _np_ptr(work), cap,
+                                  ctypes.byref(ni), ctypes.byref(nm), ctypes.byref(ns)),
+           "bsa_work_plan_host")
+    used = 4 * ni.value + 3 * nm.value
+    return work[:used].copy(), ni.value, nm.value, ns.value
 
 
 def validate_csr_host(row_ptr, col_idx, nb: int, strict: bool = True) -> int:
@@ -167,6 +181,41 @@ def validate_csr_host(row_ptr, col_idx, nb: int, strict: bool = True) -> int:
 
 def build_mask_workspace_bytes(B: int, H: int, N: int, D: int, block: int) -> int:
     return int(lib.bsa_build_mask_workspace_bytes(B, H, N, D, block))
+
+
+def forward_workspace_bytes(n_slots: int, D: int, block: int) -> int:
+    return int(lib.bsa_forward_workspace_bytes(n_slots, D, block))
+
+
+def _fwd_lds_bytes(block: int, D: int) -> int:
+    """LDS bytes of one forward workgroup (two stages of K and V^T tiles)."""
+    return 2 * 2 * (block * (D + 8) + D * (block + 8))
+
+
+def default_max_tiles(nnz: int, block: int, D: int, n_cu: int, lds_per_cu: int = 160 * 1024):
+    """Cut rows longer than about half the average work of one resident workgroup slot."""
+    slots = n_cu * max(1, lds_per_cu // _fwd_lds_bytes(block, D))
+    return max(8, -(-nnz // (2 * slots)))
+
+
+@dataclass
+class Work:
+    """Device work list of the forward plus the workspace its cut rows need."""
+    work: torch.Tensor
+    n_items: int
+    n_merges: int
+    n_slots: int
+    workspace: Optional[torch.Tensor]
+    max_tiles: int
+
+    @classmethod
+    def from_host(cls, row_ptr_host, D: int, block: int, max_tiles: int, device):
+        w, ni, nm, ns = work_plan(row_ptr_host, max_tiles)
+        ws = None
+        if nm > 0:
+            ws = torch.empty(max(forward_workspace_bytes(ns, D, block), 16), dtype=torch.uint8,
+                             device=device)
+        return cls(torch.from_numpy(w).to(device), ni, nm, ns, ws, int(max_tiles))
 
 
 def _check_qkv(*ts):
@@ -200,10 +249,9 @@ class Plan:
     density: float
     force_diag: bool
     row_ptr_host: np.ndarray
-    order_host: np.ndarray
     nnz: int
     row_ptr: torch.Tensor
-    order: torch.Tensor
+    work: Work
     prior: Optional[torch.Tensor]
     prior_per_head: int
     budgets: Optional[torch.Tensor]
@@ -215,16 +263,21 @@ class Plan:
 
     @classmethod
     def create(cls, B, H, N, D, block, density=0.0, prior=None, budgets=None, force_diag=True,
-               device="cuda"):
+               device="cuda", max_tiles: Optional[int] = None):
+        """Host plan of the CSR and of the forward's work list (rows cut at max_tiles;
+        None picks `default_max_tiles` for the device, 0 never cuts)."""
         nb = n_blocks(N, block)
         p, per_head = _prior_host(prior, B, H, nb)
         b = _budgets_host(budgets, nb)
         row_ptr_h, nnz = mask_plan(B, H, nb, density, p, b, force_diag)
-        order_h = schedule_host(row_ptr_h)
+        if max_tiles is None:
+            n_cu = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+            max_tiles = default_max_tiles(nnz, block, D, n_cu)
+        work = Work.from_host(row_ptr_h, D, block, max_tiles, device)
         ws = torch.empty(build_mask_workspace_bytes(B, H, N, D, block), dtype=torch.uint8,
                          device=device)
-        return cls(B, H, N, D, block, float(density), bool(force_diag), row_ptr_h, order_h, nnz,
-                   _dev_i32(row_ptr_h, device), _dev_i32(order_h, device),
+        return cls(B, H, N, D, block, float(density), bool(force_diag), row_ptr_h, nnz,
+                   _dev_i32(row_ptr_h, device), work,
                    None if p is None else torch.from_numpy(p).to(device), per_head,
                    None if b is None else torch.from_numpy(b).to(device), ws)
 
@@ -261,20 +314,23 @@ def build_mask_status(plan: Plan) -> int:
     return int(v.value)
 
 
-def schedule(row_ptr: torch.Tensor, max_len: int) -> torch.Tensor:
-    """Longest-first row order computed on the device."""
+def schedule(row_ptr: torch.Tensor, max_len: int) -> Work:
+    """Longest-first work list (no row cut) computed on the device from row_ptr."""
     n_rows = row_ptr.numel() - 1
-    order = torch.empty(n_rows, dtype=torch.int32, device=row_ptr.device)
-    _check(lib.bsa_schedule(_t_ptr(row_ptr), n_rows, max_len, _t_ptr(order), None, 0,
+    work = torch.empty(4 * n_rows, dtype=torch.int32, device=row_ptr.device)
+    _check(lib.bsa_schedule(_t_ptr(row_ptr), n_rows, max_len, _t_ptr(work),
                             _stream_ptr(row_ptr.device)), "bsa_schedule")
-    return order
+    return Work(work, n_rows, 0, 0, None, 0)
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx, block: int,
-            scale: Optional[float] = None, order: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            return_lse: bool = True):
-    """Block-sparse attention forward -> (O bf16 [B,H,N,D], LSE fp32 [B,H,N] or None)."""
+            scale: Optional[float] = None, work=None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """Block-sparse attention forward -> (O bf16 [B,H,N,D], LSE fp32 [B,H,N] or None).
+
+    `work` is a `Work`, a `Plan` (its work list is used) or None (one workgroup
+    per row, natural order).
+    """
     B, H, N, D = _check_qkv(q, k, v)
     dev = q.device
     nb = n_blocks(N, block)
@@ -284,10 +340,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx,
         raise ValueError(f"row_ptr must have B*H*nb+1 = {B * H * nb + 1} entries")
     if col_idx.numel() == 0:
         col_idx = torch.zeros(1, dtype=torch.int32, device=dev)
-    if order is not None:
-        order = _dev_i32(order, dev)
-        if order.numel() != B * H * nb:
-            raise ValueError("order must have B*H*nb entries")
+    if isinstance(work, Plan):
+        work = work.work
+    if work is not None and not isinstance(work, Work):
+        raise TypeError("work must be a Work, a Plan or None")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -295,8 +351,14 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx,
     s = -1.0 if scale is None else float(scale)
     if scale is not None and not s > 0.0:
         raise ValueError("scale must be positive (or None for 1/sqrt(D))")
+    if work is None:
+        wp, ni, nm, ns, ws, wsb = None, 0, 0, 0, None, 0
+    else:
+        wp, ni, nm, ns = _t_ptr(work.work), work.n_items, work.n_merges, work.n_slots
+        ws = work.workspace
+        wsb = 0 if ws is None else ws.numel()
     _check(lib.bsa_forward(_t_ptr(q), _t_ptr(k), _t_ptr(v), B, H, N, D, block, _t_ptr(row_ptr),
-                           _t_ptr(col_idx), _t_ptr(order), s, _t_ptr(out),
-                           _t_ptr(lse) if return_lse else None, _stream_ptr(dev)),
-           "bsa_forward")
+                           _t_ptr(col_idx), wp, ni, nm, ns, s, _t_ptr(out),
+                           _t_ptr(lse) if return_lse else None, _t_ptr(ws), wsb,
+                           _stream_ptr(dev)), "bsa_forward")
     return out, (lse if return_lse else None)

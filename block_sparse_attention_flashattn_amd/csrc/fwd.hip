@@ -95,8 +95,9 @@ template <int BLK, int HD>
 __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order, int32_t N,
-    int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O, float* __restrict__ LSE) {
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t N,
+    int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    float* __restrict__ part) {
   using C = FwdCfg<BLK, HD>;
   extern __shared__ __align__(16) uint16_t smem[];
 
@@ -108,7 +109,18 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
   const int ql = lane & 31;      // query column of this lane in the MFMA tiles
   const int hh = lane >> 5;      // which half of the k / row dimension the lane feeds
 
-  const int r = order ? order[blockIdx.x] : static_cast<int>(blockIdx.x);
+  // Work item: tiles [tb, te) of row r; slot >= 0 sends a partial result to
+  // the workspace instead of O (the row was cut into chunks).
+  int r, tb = 0, te = INT32_MAX, slot = -1;
+  if (work) {
+    const int4 it = *reinterpret_cast<const int4*>(work + 4 * size_t(blockIdx.x));
+    r = it.x;
+    tb = it.y;
+    te = it.z;
+    slot = it.w;
+  } else {
+    r = static_cast<int>(blockIdx.x);
+  }
   if (r < 0 || r >= n_rows) return;
   const int bh = r / nb;
   const int qb = r - bh * nb;
@@ -122,7 +134,10 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
   int end = row_ptr[r + 1];
   start = min(max(start, 0), nnz);
   end = min(max(end, start), nnz);
-  const int cnt = end - start;
+  tb = max(tb, 0);
+  te = min(te, end - start);
+  start += tb;
+  const int cnt = max(te - tb, 0);
 
   // Query fragment (B operand of S^T = K Q^T): lane holds d = 16c + 8hh .. +7.
   // Rows past N read as zeros through the buffer bound.
@@ -336,6 +351,24 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       }
   }
 
+  if (slot >= 0) {
+    // Partial result of one chunk: unnormalised acc, running max (log2 units)
+    // and running sum, merged with the row's other chunks by merge_kernel.
+    float* po = part + size_t(slot) * BLK * (HD + 2);
+    const int q = qg * 32 + ql;
+#pragma unroll
+    for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(po + q * HD + 32 * u + 8 * g + 4 * hh) =
+            f32x4{acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
+    if (hh == 0) {
+      po[BLK * HD + q] = m_run;
+      po[BLK * HD + BLK + q] = l_half;
+    }
+    return;
+  }
+
   const float inv = l_half > 0.f ? 1.f / l_half : 0.f;
   if (qrow < N) {
     uint16_t* orow = O + head + size_t(qrow) * HD;
@@ -356,10 +389,55 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
   }
 }
 
+// Combines the chunk partials of every cut row: with M = max_c m_c,
+// O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c and LSE = (M + log2 L) ln 2.
+template <int BLK, int HD>
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ merges,
+                                                    const float* __restrict__ part, int32_t N,
+                                                    int32_t nb, int32_t n_rows,
+                                                    uint16_t* __restrict__ O,
+                                                    float* __restrict__ LSE) {
+  const int3 mg = *reinterpret_cast<const int3*>(merges + 3 * size_t(blockIdx.x));
+  const int r = mg.x, slot0 = mg.y, nch = mg.z;
+  if (r < 0 || r >= n_rows) return;
+  const int bh = r / nb;
+  const int qb = r - bh * nb;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+  constexpr int D4 = HD / 4;
+  for (int idx = threadIdx.x; idx < BLK * D4; idx += 256) {
+    const int q = idx / D4;
+    const int d = (idx - q * D4) * 4;
+    const int qrow = qb * BLK + q;
+    if (qrow >= N) continue;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c)
+      M = fmaxf(M, part[size_t(slot0 + c) * BLK * (HD + 2) + BLK * HD + q]);
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int c = 0; c < nch; ++c) {
+        const float* pc = part + size_t(slot0 + c) * BLK * (HD + 2);
+        const float mc = pc[BLK * HD + q];
+        const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+        L += w * pc[BLK * HD + BLK + q];
+        const f32x4 oc = *reinterpret_cast<const f32x4*>(pc + q * HD + d);
+        o += w * oc;
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *reinterpret_cast<uint2*>(O + head + size_t(qrow) * HD + d) =
+        make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+    if (d == 0 && LSE != nullptr)
+      LSE[size_t(bh) * N + qrow] =
+          L > 0.f ? (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
 template <int BLK, int HD>
 bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
                       int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
-                      const int32_t* order, float sl2, void* o, float* lse, hipStream_t stream) {
+                      const int32_t* work, int32_t n_items, int32_t n_merges, float sl2, void* o,
+                      float* lse, float* part, hipStream_t stream) {
   using C = FwdCfg<BLK, HD>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
@@ -369,22 +447,39 @@ bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, in
                                static_cast<int>(C::LDS_BYTES));
   });
   if (attr != hipSuccess) return BSA_ERR_HIP;
-  hipLaunchKernelGGL((fwd_kernel<BLK, HD>), dim3(n_rows), dim3(C::NT), C::LDS_BYTES, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), row_ptr, col_idx, order, N, nb, n_rows,
-                     sl2, static_cast<uint16_t*>(o), lse);
-  BSA_HIP_CHECK_LAUNCH();
+  const int32_t grid = work ? n_items : n_rows;
+  if (grid > 0) {
+    hipLaunchKernelGGL((fwd_kernel<BLK, HD>), dim3(grid), dim3(C::NT), C::LDS_BYTES, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), row_ptr, col_idx, work, N, nb, n_rows,
+                       sl2, static_cast<uint16_t*>(o), lse, part);
+    BSA_HIP_CHECK_LAUNCH();
+  }
+  if (work && n_merges > 0) {
+    hipLaunchKernelGGL((merge_kernel<BLK, HD>), dim3(n_merges), dim3(256), 0, stream,
+                       work + 4 * size_t(n_items), part, N, nb, n_rows,
+                       static_cast<uint16_t*>(o), lse);
+    BSA_HIP_CHECK_LAUNCH();
+  }
   return BSA_OK;
 }
 
 }  // namespace
 }  // namespace bsa
 
+extern "C" BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D,
+                                                      int32_t block) {
+  if (n_slots < 0 || D < 1 || block < 1) return 0;
+  return size_t(n_slots) * size_t(block) * size_t(D + 2) * sizeof(float);
+}
+
 extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v,
                                           int32_t B, int32_t H, int32_t N, int32_t D,
                                           int32_t block, const int32_t* row_ptr_dev,
-                                          const int32_t* col_idx_dev, const int32_t* order_dev,
-                                          float scale, void* o, float* lse, void* stream) {
+                                          const int32_t* col_idx_dev, const int32_t* work_dev,
+                                          int32_t n_items, int32_t n_merges, int32_t n_slots,
+                                          float scale, void* o, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
   using namespace bsa;
   if (!q || !k || !v || !o || !row_ptr_dev || !col_idx_dev) return BSA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return BSA_ERR_INVALID_ARG;
@@ -398,18 +493,27 @@ extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const vo
   const int64_t rows = int64_t(B) * H * nb;
   if (rows > INT32_MAX - 1) return BSA_ERR_UNSUPPORTED;
   const int32_t n_rows = static_cast<int32_t>(rows);
+  if (work_dev) {
+    if (!aligned16(work_dev) || n_items < 0 || n_merges < 0 || n_slots < 0)
+      return BSA_ERR_INVALID_ARG;
+    if (n_merges > 0) {
+      if (!workspace || !aligned16(workspace)) return BSA_ERR_INVALID_ARG;
+      if (workspace_bytes < bsa_forward_workspace_bytes(n_slots, D, block))
+        return BSA_ERR_CAPACITY;
+    }
+  } else {
+    n_items = n_merges = 0;
+  }
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
   const float sl2 = sc * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (block == 64 && D == 64)
-    return launch_fwd<64, 64>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2, o,
-                              lse, s);
-  if (block == 64 && D == 128)
-    return launch_fwd<64, 128>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2,
-                               o, lse, s);
-  if (block == 128 && D == 64)
-    return launch_fwd<128, 64>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2,
-                               o, lse, s);
-  return launch_fwd<128, 128>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, order_dev, sl2, o,
-                              lse, s);
+  float* part = static_cast<float*>(workspace);
+#define BSA_FWD_ARGS                                                                            \
+  q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items, n_merges, sl2, o, lse, \
+      part, s
+  if (block == 64 && D == 64) return launch_fwd<64, 64>(BSA_FWD_ARGS);
+  if (block == 64 && D == 128) return launch_fwd<64, 128>(BSA_FWD_ARGS);
+  if (block == 128 && D == 64) return launch_fwd<128, 64>(BSA_FWD_ARGS);
+  return launch_fwd<128, 128>(BSA_FWD_ARGS);
+#undef BSA_FWD_ARGS
 }

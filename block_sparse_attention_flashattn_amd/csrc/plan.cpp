@@ -71,21 +71,65 @@ extern "C" BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, do
   return BSA_OK;
 }
 
-extern "C" BSA_API bsa_status bsa_schedule_host(const int32_t* row_ptr, int32_t n_rows,
-                                                int32_t* order_out) {
-  if (!row_ptr || !order_out || n_rows < 1) return BSA_ERR_INVALID_ARG;
+extern "C" BSA_API int64_t bsa_work_plan_ints(int32_t n_rows, int64_t nnz, int32_t max_tiles) {
+  if (n_rows < 1 || nnz < 0) return -1;
+  // Cutting a row of length L into ceil(L/T) chunks adds at most L/T items.
+  const int64_t extra = max_tiles > 0 ? nnz / max_tiles : 0;
+  return 4 * (int64_t(n_rows) + extra) + 3 * int64_t(n_rows);
+}
+
+extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows,
+                                                 int32_t max_tiles, int32_t* work_out,
+                                                 int64_t capacity, int32_t* n_items,
+                                                 int32_t* n_merges, int32_t* n_slots) {
+  if (!row_ptr || !work_out || !n_items || !n_merges || !n_slots || n_rows < 1)
+    return BSA_ERR_INVALID_ARG;
+  struct Item { int32_t row, b, e, slot; };
+  std::vector<Item> items;
+  std::vector<int32_t> merges;
+  items.reserve(size_t(n_rows));
+  int32_t slots = 0;
   int32_t max_len = 0;
   for (int32_t r = 0; r < n_rows; ++r) {
     const int32_t len = row_ptr[r + 1] - row_ptr[r];
     if (len < 0) return BSA_ERR_INVALID_ARG;
-    if (len > max_len) max_len = len;
+    if (max_tiles > 0 && len > max_tiles) {
+      // Near-equal chunks: the first (len % n) chunks carry one extra tile.
+      const int32_t n = (len + max_tiles - 1) / max_tiles;
+      const int32_t base = len / n, rem = len % n;
+      merges.push_back(r);
+      merges.push_back(slots);
+      merges.push_back(n);
+      int32_t b = 0;
+      for (int32_t c = 0; c < n; ++c) {
+        const int32_t e = b + base + (c < rem ? 1 : 0);
+        items.push_back({r, b, e, slots + c});
+        if (e - b > max_len) max_len = e - b;
+        b = e;
+      }
+      slots += n;
+    } else {
+      items.push_back({r, 0, len, -1});
+      if (len > max_len) max_len = len;
+    }
   }
-  // Stable counting sort by descending length.
-  std::vector<int32_t> start(size_t(max_len) + 2, 0);
-  for (int32_t r = 0; r < n_rows; ++r) ++start[size_t(max_len - (row_ptr[r + 1] - row_ptr[r])) + 1];
-  for (size_t b = 1; b < start.size(); ++b) start[b] += start[b - 1];
-  for (int32_t r = 0; r < n_rows; ++r)
-    order_out[start[size_t(max_len - (row_ptr[r + 1] - row_ptr[r]))]++] = r;
+  const int64_t need = 4 * int64_t(items.size()) + int64_t(merges.size());
+  if (need > capacity) return BSA_ERR_CAPACITY;
+  // Stable counting sort of the items by descending length.
+  std::vector<int64_t> pos(size_t(max_len) + 2, 0);
+  for (const Item& it : items) ++pos[size_t(max_len - (it.e - it.b)) + 1];
+  for (size_t i = 1; i < pos.size(); ++i) pos[i] += pos[i - 1];
+  for (const Item& it : items) {
+    const int64_t k = pos[size_t(max_len - (it.e - it.b))]++;
+    work_out[4 * k + 0] = it.row;
+    work_out[4 * k + 1] = it.b;
+    work_out[4 * k + 2] = it.e;
+    work_out[4 * k + 3] = it.slot;
+  }
+  memcpy(work_out + 4 * items.size(), merges.data(), merges.size() * sizeof(int32_t));
+  *n_items = static_cast<int32_t>(items.size());
+  *n_merges = static_cast<int32_t>(merges.size() / 3);
+  *n_slots = slots;
   return BSA_OK;
 }
 

@@ -7,8 +7,9 @@
 // so the long rows start while the short ones fill in behind them.
 //
 // One workgroup of 1024 threads: LDS histogram by (max_len - length), a
-// two-level exclusive scan, then an atomic scatter.  Rows of equal length come
-// out in an unspecified order; the forward's results do not depend on it.
+// two-level exclusive scan, then an atomic scatter of {row, 0, length, -1}
+// work items (no row is cut).  Rows of equal length come out in an
+// unspecified order; the forward's results do not depend on it.
 #include "common.h"
 
 namespace bsa {
@@ -19,7 +20,7 @@ constexpr int kSchedMaxLen = 8191;
 
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __restrict__ row_ptr,
                                                               int32_t n_rows, int32_t max_len,
-                                                              int32_t* __restrict__ order) {
+                                                              int32_t* __restrict__ work) {
   __shared__ int32_t bins[kSchedMaxLen + 1];
   __shared__ int32_t part[kSchedThreads];
   const int tid = threadIdx.x;
@@ -53,29 +54,22 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __r
   }
   __syncthreads();
   for (int r = tid; r < n_rows; r += kSchedThreads) {
-    const int len = min(max(row_ptr[r + 1] - row_ptr[r], 0), max_len);
-    const int pos = atomicAdd(&bins[max_len - len], 1);
-    order[pos] = r;
+    const int full = max(row_ptr[r + 1] - row_ptr[r], 0);
+    const int pos = atomicAdd(&bins[max_len - min(full, max_len)], 1);
+    *reinterpret_cast<int4*>(work + 4 * size_t(pos)) = make_int4(r, 0, full, -1);
   }
 }
 
 }  // namespace
 }  // namespace bsa
 
-extern "C" BSA_API size_t bsa_schedule_workspace_bytes(int32_t max_len) {
-  (void)max_len;
-  return 0;
-}
-
 extern "C" BSA_API bsa_status bsa_schedule(const int32_t* row_ptr_dev, int32_t n_rows,
-                                           int32_t max_len, int32_t* order_dev, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  if (!row_ptr_dev || !order_dev || n_rows < 1 || max_len < 0) return BSA_ERR_INVALID_ARG;
+                                           int32_t max_len, int32_t* work_dev, void* stream) {
+  if (!row_ptr_dev || !work_dev || n_rows < 1 || max_len < 0) return BSA_ERR_INVALID_ARG;
   if (max_len > bsa::kSchedMaxLen) return BSA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(work_dev) & 15u) return BSA_ERR_INVALID_ARG;
   hipLaunchKernelGGL(bsa::sched_kernel, dim3(1), dim3(bsa::kSchedThreads), 0,
-                     static_cast<hipStream_t>(stream), row_ptr_dev, n_rows, max_len, order_dev);
+                     static_cast<hipStream_t>(stream), row_ptr_dev, n_rows, max_len, work_dev);
   BSA_HIP_CHECK_LAUNCH();
   return BSA_OK;
 }

@@ -88,14 +88,29 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
                                  int32_t* row_ptr_out, int64_t* nnz_out);
 
 /*
- * Longest-row-first work order (host, synchronous).  BSA-DiT §5.3: uneven
- * active counts per query block leave some workgroups busy and others idle;
- * the forward launches rows in this order so long rows start first.
- *   row_ptr  int32 [n_rows + 1]; order_out int32 [n_rows] (a permutation of
- *   0..n_rows-1, by descending row length, ties by ascending row index).
+ * Work list of bsa_forward (host, synchronous).  BSA-DiT §5.3: when query
+ * blocks have very different active counts, one workgroup per query block
+ * leaves some workgroups busy long after the others went idle; it suggests
+ * sorting or merging the work, or per-block target counts.  Here every row
+ * longer than max_tiles KV blocks is cut into near-equal chunks of at most
+ * max_tiles blocks (max_tiles <= 0: rows are never cut), and all items are
+ * ordered longest first (ties: ascending row, then chunk).  The chunks of a
+ * cut row write fp32 partial results to the forward's workspace and a second
+ * kernel merges them.
+ *   row_ptr   int32 [n_rows + 1] host copy of the CSR row pointer.
+ *   work_out  int32 [capacity], written: n_items records {row, tile_begin,
+ *             tile_end, slot} (slot = -1: the item covers its whole row and
+ *             writes O directly; tiles are positions inside the row's column
+ *             list), then n_merges records {row, first_slot, n_chunks}.
+ *   capacity  >= bsa_work_plan_ints(n_rows, nnz, max_tiles) int32 entries.
+ *   n_items, n_merges, n_slots  written (n_slots = partial slots used).
+ * Errors: INVALID_ARG for a NULL pointer, n_rows < 1 or a decreasing row_ptr;
+ * CAPACITY if capacity is too small.
  */
-BSA_API bsa_status bsa_schedule_host(const int32_t* row_ptr, int32_t n_rows,
-                                     int32_t* order_out);
+BSA_API int64_t bsa_work_plan_ints(int32_t n_rows, int64_t nnz, int32_t max_tiles);
+BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows, int32_t max_tiles,
+                                      int32_t* work_out, int64_t capacity, int32_t* n_items,
+                                      int32_t* n_merges, int32_t* n_slots);
 
 /*
  * Structural CSR check (host, synchronous): row_ptr[0] == 0, non-decreasing,
@@ -154,16 +169,22 @@ BSA_API bsa_status bsa_build_mask_status(const void* workspace, void* stream,
                                          int32_t* mismatched_rows);
 
 /*
- * Longest-row-first work order on the device (async): a counting sort of the
- * rows by length, descending (order among equal lengths unspecified).
- *   row_ptr_dev int32 [n_rows+1]; order_dev int32 [n_rows] written;
- *   max_len = an upper bound of any row length (nb).
- *   workspace   >= bsa_schedule_workspace_bytes(max_len) bytes.
+ * Longest-row-first work list built on the device (async), for a CSR whose
+ * row lengths the host does not hold: the work_dev layout of
+ * bsa_work_plan_host with no row cut (n_items = n_rows, n_merges = 0),
+ * produced by a counting sort of the rows by length, longest first (order
+ * among equal lengths unspecified; results do not depend on it).
+ *   row_ptr_dev int32 [n_rows+1]; work_dev int32 [4*n_rows] written;
+ *   max_len >= every row length (e.g. nb); at most 8191.
  */
-BSA_API size_t bsa_schedule_workspace_bytes(int32_t max_len);
 BSA_API bsa_status bsa_schedule(const int32_t* row_ptr_dev, int32_t n_rows, int32_t max_len,
-                                int32_t* order_dev, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                int32_t* work_dev, void* stream);
+
+/*
+ * Bytes of device workspace bsa_forward needs for n_slots partial results
+ * (fp32 O [block x D] plus running max and sum per query row, per slot).
+ */
+BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D, int32_t block);
 
 /*
  * Block-sparse attention forward (device, async on `stream`).
@@ -177,18 +198,24 @@ BSA_API bsa_status bsa_schedule(const int32_t* row_ptr_dev, int32_t n_rows, int3
  *   q, k, v     bf16 [B,H,N,D] device; o bf16 [B,H,N,D] device (written);
  *   lse         fp32 [B,H,N] device (written), or NULL to skip it.
  *   row_ptr_dev, col_idx_dev  the CSR (see conventions); entries outside
- *               [0, nb) are skipped, row bounds are clamped to [0, nnz].
- *   order_dev   int32 [B*H*nb] launch order of rows (bsa_schedule or
- *               bsa_schedule_host), or NULL for natural order.
+ *               [0, nb) contribute nothing, row bounds are clamped to [0, nnz].
+ *   work_dev    device copy of a work list (bsa_work_plan_host or
+ *               bsa_schedule) with n_items items and n_merges merges, or NULL
+ *               for one item per row in natural order (n_items, n_merges
+ *               ignored).  Every row must be covered exactly once.
+ *   workspace   >= bsa_forward_workspace_bytes(n_slots, D, block) bytes of
+ *               device memory when the work list cuts rows (n_merges > 0),
+ *               else may be NULL; contents need no initialisation.
  *   scale       softmax scale; <= 0 means 1/sqrt(D).
  * A row with no active block yields O = 0 and LSE = -inf.
- * Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED, CAPACITY (workspace too small), HIP.
  */
 BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t B,
                                int32_t H, int32_t N, int32_t D, int32_t block,
                                const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
-                               const int32_t* order_dev, float scale, void* o, float* lse,
-                               void* stream);
+                               const int32_t* work_dev, int32_t n_items, int32_t n_merges,
+                               int32_t n_slots, float scale, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

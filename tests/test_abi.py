@@ -71,14 +71,51 @@ def test_mask_plan_workload_totals():
     assert nnz == 24 * 3125
 
 
-def test_schedule_host_is_stable_longest_first():
-    rng = np.random.default_rng(5)
-    lens = rng.integers(0, 9, 200)
+def check_work(work, ni, nm, ns, rp, max_tiles):
+    """Every row covered exactly once, chunks <= max_tiles, longest first, merges consistent."""
+    lens = np.diff(rp)
+    items = work[:4 * ni].reshape(ni, 4)
+    merges = work[4 * ni:4 * ni + 3 * nm].reshape(nm, 3)
+    sizes = items[:, 2] - items[:, 1]
+    assert (np.diff(sizes) <= 0).all()
+    cover = {}
+    for row, b, e, slot in items.tolist():
+        cover.setdefault(row, []).append((b, e, slot))
+    assert sorted(cover) == list(range(len(lens)))
+    cut = {m[0]: (m[1], m[2]) for m in merges.tolist()}
+    used_slots = []
+    for row, parts in cover.items():
+        parts.sort()
+        assert parts[0][0] == 0 and parts[-1][1] == lens[row]
+        assert all(parts[i][1] == parts[i + 1][0] for i in range(len(parts) - 1))
+        if row in cut:
+            s0, n = cut[row]
+            assert len(parts) == n and [p[2] for p in parts] == list(range(s0, s0 + n))
+            assert all(e - b <= max_tiles for b, e, _ in parts) and max(e - b for b, e, _ in parts) - min(e - b for b, e, _ in parts) <= 1
+            used_slots += list(range(s0, s0 + n))
+        else:
+            assert len(parts) == 1 and parts[0][2] == -1
+            assert max_tiles <= 0 or lens[row] <= max_tiles
+    assert sorted(used_slots) == list(range(ns))
+
+
+@pytest.mark.parametrize("max_tiles", [0, 1, 3, 8, 100])
+def test_work_plan(max_tiles):
+    rng = np.random.default_rng(max_tiles)
+    lens = rng.integers(0, 30, 300)
     rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    order = bsa.schedule_host(rp)
-    assert sorted(order.tolist()) == list(range(200))
-    key = [(-lens[r], r) for r in order]
-    assert key == sorted(key)
+    work, ni, nm, ns = bsa.work_plan(rp, max_tiles)
+    check_work(work, ni, nm, ns, rp, max_tiles)
+    if max_tiles <= 0:
+        assert nm == 0 and ni == 300
+
+
+def test_work_plan_t2i_text_rows_are_cut():
+    import workloads as W
+    rp, nnz = bsa.mask_plan(2, 24, 66, 0.0, W.t2i_prior())
+    work, ni, nm, ns = bsa.work_plan(rp, 16)
+    check_work(work, ni, nm, ns, rp, 16)
+    assert nm == 96 and ns == 96 * 5 and ni == 3168 - 96 + 480
 
 
 def test_validate_csr_host():
@@ -94,19 +131,22 @@ def test_device_entry_points_reject_bad_arguments():
     L = bsa.lib
     fake = ctypes.c_void_p(4096)      # never dereferenced: every call below fails validation
     odd = ctypes.c_void_p(4097)
-    args = lambda q=fake, D=64, blk=64, N=128: (q, fake, fake, 1, 1, N, D, blk, fake, fake, None,
-                                                0.125, fake, None, None)
+    args = lambda q=fake, D=64, blk=64, N=128, ws_bytes=0: (
+        q, fake, fake, 1, 1, N, D, blk, fake, fake, fake, 4, 1, 3, 0.125, fake, None, fake,
+        ws_bytes, None)
     assert L.bsa_forward(*args(q=None)) == -1
     assert L.bsa_forward(*args(D=96)) == -2
     assert L.bsa_forward(*args(blk=32)) == -2
     assert L.bsa_forward(*args(q=odd)) == -1
     assert L.bsa_forward(*args(N=0)) == -1
+    assert L.bsa_forward(*args(ws_bytes=16)) == -4       # 3 partial slots need more workspace
     mk = lambda ws_bytes=0, D=64, N=128, ws=fake: L.bsa_build_mask(
         fake, fake, 1, 1, N, D, 64, 0.1, None, None, 0, 1, fake, fake, ws, ws_bytes, None)
     assert mk(ws=None) == -1
     assert mk(D=80) == -2
     assert mk(N=64 * 1025) == -2                      # more than 1024 blocks
     assert mk(ws_bytes=16) == -4                      # workspace too small
-    assert L.bsa_schedule(None, 4, 4, fake, None, 0, None) == -1
-    assert L.bsa_schedule(fake, 4, 100000, fake, None, 0, None) == -2
+    assert L.bsa_schedule(None, 4, 4, fake, None) == -1
+    assert L.bsa_schedule(fake, 4, 100000, fake, None) == -2
+    assert L.bsa_forward_workspace_bytes(3, 64, 64) == 3 * 64 * 66 * 4
     assert L.bsa_build_mask_workspace_bytes(1, 1, 128, 64, 64) >= 256 + 2 * 2 * 64 * 4 + 4 * 4

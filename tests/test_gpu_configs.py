@@ -28,7 +28,7 @@ def test_full_config(name):
                            w.force_diag, "cuda")
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     rp, ci = bsa.build_mask(qd, kd, w.block, plan=plan)
-    o, lse = bsa.forward(qd, kd, vd, rp, ci, w.block, order=plan.order)
+    o, lse = bsa.forward(qd, kd, vd, rp, ci, w.block, work=plan)
     torch.cuda.synchronize()
     assert bsa.build_mask_status(plan) == 0
     nb, n_rows = w.nb, w.B * w.H * w.nb
@@ -49,4 +49,11 @@ def test_full_config(name):
     rows = sample_rows(plan.row_ptr_host, nb, n_rows, 12, seed=len(name))
     O, L = OA.block_sparse_attention(q, k, v, plan.row_ptr_host, ci_h, w.block, w.scale, rows=rows)
     stats = compare_attention(o, lse, O, L, token_rows(rows, nb, w.block, w.N, w.H))
-    print(f"attention on {len(rows)} rows: {stats}", flush=True)
+    print(f"attention on {len(rows)} rows: {stats}; work items {plan.work.n_items}, "
+          f"cut rows {plan.work.n_merges} (max_tiles {plan.work.max_tiles})", flush=True)
+    if plan.work.n_merges:
+        cut = plan.work.work.cpu().numpy()[4 * plan.work.n_items:].reshape(-1, 3)[:, 0]
+        rows2 = sorted(set(cut[:6].tolist()))
+        O2, L2 = OA.block_sparse_attention(q, k, v, plan.row_ptr_host, ci_h, w.block, w.scale,
+                                           rows=rows2)
+        print("cut rows:", compare_attention(o, lse, O2, L2, token_rows(rows2, nb, w.block, w.N, w.H)))

@@ -25,11 +25,11 @@ def rand_csr(rng, B, H, nb, p, empty_rows=()):
     return rp, ci
 
 
-def run_and_compare(bsa, q, k, v, rp, ci, block, scale=None, order=None):
+def run_and_compare(bsa, q, k, v, rp, ci, block, scale=None, work=None):
     B, H, N, D = q.shape
     dev = "cuda"
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o, lse = bsa.forward(qd, kd, vd, rp, ci, block, scale=scale, order=order)
+    o, lse = bsa.forward(qd, kd, vd, rp, ci, block, scale=scale, work=work)
     torch.cuda.synchronize()
     sc = scale if scale is not None else 1 / math.sqrt(D)
     O, L = OA.block_sparse_attention(q, k, v, rp, ci, block, sc)
@@ -131,20 +131,43 @@ def test_launch_order_and_invalid_columns():
     nb = 11
     rp, ci = rand_csr(rng, B, H, nb, 0.3)
     o0, l0 = bsa.forward(q, k, v, rp, ci, block)
-    order_h = bsa.schedule_host(rp)
-    o1, l1 = bsa.forward(q, k, v, rp, ci, block, order=order_h)
-    order_d = bsa.schedule(torch.from_numpy(rp).cuda(), nb)
-    o2, l2 = bsa.forward(q, k, v, rp, ci, block, order=order_d)
+    w_host = bsa.Work.from_host(rp, D, block, 0, "cuda")
+    o1, l1 = bsa.forward(q, k, v, rp, ci, block, work=w_host)
+    w_dev = bsa.schedule(torch.from_numpy(rp).cuda(), nb)
+    o2, l2 = bsa.forward(q, k, v, rp, ci, block, work=w_dev)
     assert torch.equal(o0, o1) and torch.equal(o0, o2) and torch.equal(l0, l1) and torch.equal(l0, l2)
-    od = order_d.cpu().numpy()
+    items = w_dev.work.cpu().numpy().reshape(-1, 4)
     lens = np.diff(rp)
-    assert sorted(od.tolist()) == list(range(B * H * nb)) and (np.diff(lens[od]) <= 0).all()
+    assert sorted(items[:, 0].tolist()) == list(range(B * H * nb))
+    assert (items[:, 1] == 0).all() and (items[:, 3] == -1).all()
+    assert np.array_equal(items[:, 2], lens[items[:, 0]]) and (np.diff(items[:, 2]) <= 0).all()
     # insert junk columns (-1 and nb) at the front of every row
     rows = [np.concatenate([[-1, nb], ci[rp[r]:rp[r + 1]]]) for r in range(B * H * nb)]
     rp2 = np.concatenate([[0], np.cumsum([len(x) for x in rows])]).astype(np.int32)
     ci2 = np.concatenate(rows).astype(np.int32)
     o3, l3 = bsa.forward(q, k, v, rp2, ci2, block)
     assert torch.equal(o0, o3) and torch.equal(l0, l3)
+
+
+@pytest.mark.parametrize("block,D,max_tiles", [(64, 64, 1), (64, 64, 3), (64, 128, 2),
+                                               (128, 64, 4), (128, 128, 1)])
+def test_cut_rows_match_oracle(block, D, max_tiles):
+    """Rows cut into chunks (partials in the workspace + merge kernel) against the oracle."""
+    bsa = need_gpu()
+    print(f"case block={block} D={D} max_tiles={max_tiles}", flush=True)
+    rng = np.random.default_rng(block + D + max_tiles)
+    B, H, N = 1, 3, 9 * block - 17
+    q, k, v = W.gaussian_qkv(200 + max_tiles, B, H, N, D)
+    nb = 9
+    rp, ci = rand_csr(rng, B, H, nb, 0.6, empty_rows=(4,))
+    ci = ci.copy()
+    ci[rp[5]:rp[6]] = ci[rp[5]:rp[6]][::-1].copy()     # any column order is allowed
+    work = bsa.Work.from_host(rp, D, block, max_tiles, "cuda")
+    assert work.n_merges > 0
+    stats, o, lse = run_and_compare(bsa, q, k, v, rp, ci, block, work=work)
+    print(stats)
+    assert (o[0, 0, 4 * block:5 * block].float() == 0).all()       # CSR row 4 is empty
+    assert torch.isneginf(lse[0, 0, 4 * block:5 * block]).all()
 
 
 def test_no_lse_output():
