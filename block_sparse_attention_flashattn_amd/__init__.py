@@ -46,7 +46,7 @@ _SIGS = {
     "bsa_budget_from_density": (_i32, [_i32, _f64]),
     "bsa_mask_plan": (_i32, [_i32, _i32, _i32, _f64, _vp, _i32, _vp, _i32, _vp, _vp]),
     "bsa_work_plan_ints": (_i64, [_i32, _i64, _i32]),
-    "bsa_work_plan_host": (_i32, [_vp, _i32, _i32, _vp, _i64, _vp, _vp, _vp]),
+    "bsa_work_plan_host": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _vp]),
     "bsa_validate_csr_host": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "bsa_build_mask_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "bsa_build_mask": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp, _i32,
@@ -149,11 +149,12 @@ def mask_plan(B: int, H: int, nb: int, density: float = 0.0, prior=None, budgets
     return row_ptr, int(nnz.value)
 
 
-def work_plan(row_ptr, max_tiles: int = 0):
+def work_plan(row_ptr, max_tiles: int = 0, nb: int = 0, n_groups: int = 1):
     """Host work list: (work int32 array, n_items, n_merges, n_slots).
 
     Rows longer than `max_tiles` KV blocks are cut into near-equal chunks
-    (max_tiles <= 0: never); items are ordered longest first.
+    (max_tiles <= 0: never).  With n_groups > 1 items are laid out so that item
+    k serves die k % n_groups with whole heads (row // nb); otherwise longest first.
     """
     rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
     n_rows = rp.shape[0] - 1
@@ -162,9 +163,9 @@ def work_plan(row_ptr, max_tiles: int = 0):
         raise BsaError("bsa_work_plan_ints: invalid arguments")
     work = np.empty(max(cap, 4), dtype=np.int32)
     ni, nm, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(lib.bsa_work_plan_host(_np_ptr(rp), n_rows, int(max_tiles), _np_ptr(work), cap,
-                                  ctypes.byref(ni), ctypes.byref(nm), ctypes.byref(ns)),
-           "bsa_work_plan_host")
+    _check(lib.bsa_work_plan_host(_np_ptr(rp), n_rows, int(nb), int(max_tiles), int(n_groups),
+                                  _np_ptr(work), cap, ctypes.byref(ni), ctypes.byref(nm),
+                                  ctypes.byref(ns)), "bsa_work_plan_host")
     used = 4 * ni.value + 3 * nm.value
     return work[:used].copy(), ni.value, nm.value, ns.value
 
@@ -198,6 +199,10 @@ def default_max_tiles(nnz: int, block: int, D: int, n_cu: int, lds_per_cu: int =
     return max(8, -(-nnz // (2 * slots)))
 
 
+# Accelerator dies (XCDs) of an MI355X; workgroups are dealt to them round robin.
+XCDS = 8
+
+
 @dataclass
 class Work:
     """Device work list of the forward plus the workspace its cut rows need."""
@@ -209,8 +214,9 @@ class Work:
     max_tiles: int
 
     @classmethod
-    def from_host(cls, row_ptr_host, D: int, block: int, max_tiles: int, device):
-        w, ni, nm, ns = work_plan(row_ptr_host, max_tiles)
+    def from_host(cls, row_ptr_host, D: int, block: int, max_tiles: int, device, nb: int = 0,
+                  n_groups: int = 1):
+        w, ni, nm, ns = work_plan(row_ptr_host, max_tiles, nb, n_groups)
         ws = None
         if nm > 0:
             ws = torch.empty(max(forward_workspace_bytes(ns, D, block), 16), dtype=torch.uint8,
@@ -263,9 +269,10 @@ class Plan:
 
     @classmethod
     def create(cls, B, H, N, D, block, density=0.0, prior=None, budgets=None, force_diag=True,
-               device="cuda", max_tiles: Optional[int] = None):
+               device="cuda", max_tiles: Optional[int] = None, n_groups: int = XCDS):
         """Host plan of the CSR and of the forward's work list (rows cut at max_tiles;
-        None picks `default_max_tiles` for the device, 0 never cuts)."""
+        None picks `default_max_tiles` for the device, 0 never cuts; items grouped
+        by head onto `n_groups` dies, 1 for plain longest-first order)."""
         nb = n_blocks(N, block)
         p, per_head = _prior_host(prior, B, H, nb)
         b = _budgets_host(budgets, nb)
@@ -273,7 +280,7 @@ class Plan:
         if max_tiles is None:
             n_cu = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
             max_tiles = default_max_tiles(nnz, block, D, n_cu)
-        work = Work.from_host(row_ptr_h, D, block, max_tiles, device)
+        work = Work.from_host(row_ptr_h, D, block, max_tiles, device, nb, n_groups)
         ws = torch.empty(build_mask_workspace_bytes(B, H, N, D, block), dtype=torch.uint8,
                          device=device)
         return cls(B, H, N, D, block, float(density), bool(force_diag), row_ptr_h, nnz,

@@ -86,6 +86,15 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Value of lane l ^ 32 (the other half of the wavefront), without LDS.
+__device__ __forceinline__ float other_half(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  // Lanes < 32 receive the upper half in the second result, lanes >= 32 the
+  // lower half in the first.
+  return __uint_as_float((threadIdx.x & 32) ? sw[0] : sw[1]);
+}
+
 // Largest growth of the running max (log2 units) tolerated before the
 // accumulator is rescaled; probabilities then stay below 2^8 before the final
 // division, well inside fp32 and bf16 range.
@@ -150,6 +159,10 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     for (int c = 0; c < C::NDC; ++c)
       qf[c] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qoff + (2 * c + hh) * 16));
   }
+  // Retire the query loads here: otherwise the wait-count bookkeeping still sees
+  // them pending inside the tile loop and drains the K/V prefetch before every
+  // product.  (vmcnt = 0, expcnt and lgkmcnt left at their maxima.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // Staging registers: threads [0, NT/2) fetch V quads, threads [NT/2, NT) fetch K.
   const bool loads_k = tid >= C::NT / 2;
@@ -263,7 +276,7 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, other_half(mx));
     const float mt = mx * sl2;
     // Lazy rescale: only when some row's max grew by more than the slack.
     const bool need = mt > m_run + kRescaleSlack;
@@ -278,17 +291,21 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-    float ls = 0.f;
+    // Row sums in four independent chains (no long serial add dependency).
+    float ls[4];
     bf16x8 pb[C::NKT][2];
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_use));
-        ls += p;
+        if (kt == 0 && i < 4)
+          ls[i] = p;
+        else
+          ls[i & 3] += p;
         pb[kt][i >> 3][i & 7] = static_cast<__bf16>(p);
       }
-    l_run += ls;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // O^T += V^T P^T: A = V^T rows d = 32u + ql, keys at permuted positions 8hh..8hh+7.
 #pragma unroll
@@ -304,21 +321,35 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
         }
   };
 
-  if (cnt > 0) load_tile(col_idx[start]);
-
-  for (int t = 0; t < cnt; ++t) {
-    const int buf = t & 1;
-    const int j = col_idx[start + t];
-    store_tile(buf);
-    __syncthreads();
-    // Prefetch the next tile (the last iteration harmlessly reloads its own).
-    load_tile(col_idx[start + min(t + 1, cnt - 1)]);
-    const uint16_t* ks = smem + buf * C::STAGE;
-    compute_tile(ks, ks + C::K_ELEMS, tile_valid(j));
+  // Tiles run in windows of 64: lane i of `colw` holds the window's column i
+  // (one vector load per window, read back with v_readlane), so nothing the
+  // inner loop carries from one tile to the next comes from memory.
+  int t = 0;
+  for (int w0 = 0; w0 < cnt; w0 += 64) {
+    const int wn = min(64, cnt - w0);
+    const int colw = lane < wn ? col_idx[start + w0 + lane] : -1;
+    // First column of the next window, or this window's last if there is none.
+    const int next_first = w0 + 64 < cnt ? col_idx[start + w0 + 64] : -1;
+    // Retire the window load now (once per 64 tiles) so the inner loop never
+    // has to drain the tile prefetch just to read a column index.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (w0 == 0) load_tile(__builtin_amdgcn_readfirstlane(colw));
+    for (int u = 0; u < wn; ++u, ++t) {
+      const int buf = t & 1;
+      const int j = __builtin_amdgcn_readlane(colw, u);
+      // Prefetch target: the next tile (the very last tile harmlessly reloads itself).
+      const int jn = u + 1 < wn ? __builtin_amdgcn_readlane(colw, u + 1)
+                                : (t + 1 < cnt ? next_first : j);
+      store_tile(buf);
+      __syncthreads();
+      load_tile(jn);
+      const uint16_t* ks = smem + buf * C::STAGE;
+      compute_tile(ks, ks + C::K_ELEMS, tile_valid(j));
+    }
   }
 
   // Merge the two key halves: wave (g, 1) hands (m, l, acc) to wave (g, 0).
-  float l_half = l_run + __shfl_xor(l_run, 32);
+  float l_half = l_run + other_half(l_run);
   __syncthreads();  // every wave is done reading the stage buffers
   float* mg = reinterpret_cast<float*>(smem) + size_t(qg) * 64 * (C::NDT * 16 + 4);
   if (kh == 1) {

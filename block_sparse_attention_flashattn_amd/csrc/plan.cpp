@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "bsa.h"
@@ -79,9 +80,10 @@ extern "C" BSA_API int64_t bsa_work_plan_ints(int32_t n_rows, int64_t nnz, int32
 }
 
 extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows,
-                                                 int32_t max_tiles, int32_t* work_out,
-                                                 int64_t capacity, int32_t* n_items,
-                                                 int32_t* n_merges, int32_t* n_slots) {
+                                                 int32_t nb, int32_t max_tiles, int32_t n_groups,
+                                                 int32_t* work_out, int64_t capacity,
+                                                 int32_t* n_items, int32_t* n_merges,
+                                                 int32_t* n_slots) {
   if (!row_ptr || !work_out || !n_items || !n_merges || !n_slots || n_rows < 1)
     return BSA_ERR_INVALID_ARG;
   struct Item { int32_t row, b, e, slot; };
@@ -89,7 +91,6 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
   std::vector<int32_t> merges;
   items.reserve(size_t(n_rows));
   int32_t slots = 0;
-  int32_t max_len = 0;
   for (int32_t r = 0; r < n_rows; ++r) {
     const int32_t len = row_ptr[r + 1] - row_ptr[r];
     if (len < 0) return BSA_ERR_INVALID_ARG;
@@ -104,30 +105,51 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
       for (int32_t c = 0; c < n; ++c) {
         const int32_t e = b + base + (c < rem ? 1 : 0);
         items.push_back({r, b, e, slots + c});
-        if (e - b > max_len) max_len = e - b;
         b = e;
       }
       slots += n;
     } else {
       items.push_back({r, 0, len, -1});
-      if (len > max_len) max_len = len;
     }
   }
-  const int64_t need = 4 * int64_t(items.size()) + int64_t(merges.size());
-  if (need > capacity) return BSA_ERR_CAPACITY;
-  // Stable counting sort of the items by descending length.
-  std::vector<int64_t> pos(size_t(max_len) + 2, 0);
-  for (const Item& it : items) ++pos[size_t(max_len - (it.e - it.b)) + 1];
-  for (size_t i = 1; i < pos.size(); ++i) pos[i] += pos[i - 1];
-  for (const Item& it : items) {
-    const int64_t k = pos[size_t(max_len - (it.e - it.b))]++;
-    work_out[4 * k + 0] = it.row;
-    work_out[4 * k + 1] = it.b;
-    work_out[4 * k + 2] = it.e;
-    work_out[4 * k + 3] = it.slot;
+  const auto longer = [](const Item& a, const Item& b) { return a.e - a.b > b.e - b.b; };
+  std::vector<Item> out;
+  bool grouped = false;
+  if (n_groups > 1 && nb > 0) {
+    // Workgroup i runs on accelerator die (XCD) i % n_groups.  Give every die the
+    // heads h with h % n_groups == its index and walk them head by head (longest
+    // items of a head first), so each die's L2 holds the K/V of about one head
+    // at a time.  Used only when the groups come out equally long (no padding).
+    std::vector<std::vector<Item>> g(static_cast<size_t>(n_groups));
+    for (const Item& it : items) g[size_t((it.row / nb) % n_groups)].push_back(it);
+    bool equal = true;
+    for (const auto& x : g) equal = equal && x.size() == g[0].size();
+    if (equal && !g[0].empty()) {
+      for (auto& x : g)
+        std::stable_sort(x.begin(), x.end(), [nb, &longer](const Item& a, const Item& b) {
+          const int32_t ha = a.row / nb, hb = b.row / nb;
+          return ha != hb ? ha < hb : longer(a, b);
+        });
+      out.reserve(items.size());
+      for (size_t k = 0; k < g[0].size(); ++k)
+        for (int32_t q = 0; q < n_groups; ++q) out.push_back(g[size_t(q)][k]);
+      grouped = true;
+    }
   }
-  memcpy(work_out + 4 * items.size(), merges.data(), merges.size() * sizeof(int32_t));
-  *n_items = static_cast<int32_t>(items.size());
+  if (!grouped) {
+    out = items;
+    std::stable_sort(out.begin(), out.end(), longer);  // longest first
+  }
+  const int64_t need = 4 * int64_t(out.size()) + int64_t(merges.size());
+  if (need > capacity) return BSA_ERR_CAPACITY;
+  for (size_t k = 0; k < out.size(); ++k) {
+    work_out[4 * k + 0] = out[k].row;
+    work_out[4 * k + 1] = out[k].b;
+    work_out[4 * k + 2] = out[k].e;
+    work_out[4 * k + 3] = out[k].slot;
+  }
+  memcpy(work_out + 4 * out.size(), merges.data(), merges.size() * sizeof(int32_t));
+  *n_items = static_cast<int32_t>(out.size());
   *n_merges = static_cast<int32_t>(merges.size() / 3);
   *n_slots = slots;
   return BSA_OK;

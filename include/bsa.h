@@ -93,11 +93,17 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
  * leaves some workgroups busy long after the others went idle; it suggests
  * sorting or merging the work, or per-block target counts.  Here every row
  * longer than max_tiles KV blocks is cut into near-equal chunks of at most
- * max_tiles blocks (max_tiles <= 0: rows are never cut), and all items are
- * ordered longest first (ties: ascending row, then chunk).  The chunks of a
- * cut row write fp32 partial results to the forward's workspace and a second
+ * max_tiles blocks (max_tiles <= 0: rows are never cut); the chunks of a cut
+ * row write fp32 partial results to the forward's workspace and a second
  * kernel merges them.
+ * Order: with n_groups > 1 (the number of accelerator dies, XCDs, whose L2
+ * caches are separate), item k is meant for die k % n_groups, which gets the
+ * heads h = row / nb with h % n_groups equal to its index, walked head by head
+ * with each head's longest items first; this needs every die to get the same
+ * number of items, otherwise (or with n_groups <= 1) all items are simply
+ * ordered longest first.  Ties keep ascending row, then chunk.
  *   row_ptr   int32 [n_rows + 1] host copy of the CSR row pointer.
+ *   nb        blocks per head (rows of one head are consecutive).
  *   work_out  int32 [capacity], written: n_items records {row, tile_begin,
  *             tile_end, slot} (slot = -1: the item covers its whole row and
  *             writes O directly; tiles are positions inside the row's column
@@ -108,9 +114,10 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
  * CAPACITY if capacity is too small.
  */
 BSA_API int64_t bsa_work_plan_ints(int32_t n_rows, int64_t nnz, int32_t max_tiles);
-BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows, int32_t max_tiles,
-                                      int32_t* work_out, int64_t capacity, int32_t* n_items,
-                                      int32_t* n_merges, int32_t* n_slots);
+BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows, int32_t nb,
+                                      int32_t max_tiles, int32_t n_groups, int32_t* work_out,
+                                      int64_t capacity, int32_t* n_items, int32_t* n_merges,
+                                      int32_t* n_slots);
 
 /*
  * Structural CSR check (host, synchronous): row_ptr[0] == 0, non-decreasing,

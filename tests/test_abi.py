@@ -110,6 +110,36 @@ def test_work_plan(max_tiles):
         assert nm == 0 and ni == 300
 
 
+@pytest.mark.parametrize("n_groups", [2, 8])
+def test_work_plan_grouped_by_head(n_groups):
+    """Item k belongs to a head h with h % n_groups == k % n_groups; heads walked in order."""
+    rng = np.random.default_rng(n_groups)
+    nb, n_heads = 10, 16
+    lens = np.tile(rng.integers(0, 25, nb), n_heads)     # one row profile shared by all heads
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    work, ni, nm, ns = bsa.work_plan(rp, 7, nb, n_groups)
+    items = work[:4 * ni].reshape(ni, 4)
+    heads = items[:, 0] // nb
+    assert (heads % n_groups == np.arange(ni) % n_groups).all()
+    for g in range(n_groups):
+        h = heads[g::n_groups]
+        assert (np.diff(h) >= 0).all()
+        sz = (items[g::n_groups, 2] - items[g::n_groups, 1])
+        for hh in np.unique(h):
+            assert (np.diff(sz[h == hh]) <= 0).all()
+    # coverage and chunking are unchanged by the order
+    lens_sorted_items = work.copy()
+    order = np.argsort(-(items[:, 2] - items[:, 1]), kind="stable")
+    lens_sorted_items[:4 * ni] = items[order].reshape(-1)
+    check_work(lens_sorted_items, ni, nm, ns, rp, 7)
+
+
+def test_work_plan_unequal_groups_fall_back_to_longest_first():
+    rp = np.array([0, 3, 5, 9], np.int32)    # one head of 3 rows, 8 groups
+    work, ni, nm, ns = bsa.work_plan(rp, 0, 3, 8)
+    assert work[:4 * ni].reshape(ni, 4)[:, 0].tolist() == [2, 0, 1]
+
+
 def test_work_plan_t2i_text_rows_are_cut():
     import workloads as W
     rp, nnz = bsa.mask_plan(2, 24, 66, 0.0, W.t2i_prior())
