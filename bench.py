@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--extra", action="store_true",
                     help="also time the all-ones (dense) CSR and a density sweep")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run 10 device-to-device copies of this many MiB (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a copy of known size) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -121,6 +124,15 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.copy_mb > 0:
+        n = args.copy_mb * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 10}))
+        return
     dev = "cuda"
     w = W.make(args.workload)
     q, k, v = w.tensors()
