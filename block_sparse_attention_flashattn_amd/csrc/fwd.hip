@@ -7,24 +7,30 @@
 // their true total at the end, which is exactly the softmax with skipped
 // blocks at -inf.
 //
-// Kernel design (one workgroup per CSR row = one query block of one head):
+// Kernel design
+//   * Persistent workgroups: workgroup w runs work items w, w + G, w + 2G, ...
+//     (G = resident workgroups).  An item is a query block of one head (a CSR
+//     row) or a chunk of one.  The tiles of consecutive items form one stream,
+//     so the next item's first K/V tiles, its query fragment, metadata and
+//     column indices are already in flight while the current item finishes.
 //   * 2*BLK/32 wavefronts: BLK/32 query groups of 32 rows times 2 key halves.
 //     Wave (g, h) keeps its own online-softmax state for query rows
-//     32g..32g+31 over keys h*BLK/2 .. (h+1)*BLK/2-1 of every visited tile;
-//     the two halves are merged through LDS once, after the last tile.  This
-//     halves both the serial chain of each wave and the registers it needs.
-//   * Per active KV block: K [BLK x D] row-major and V^T [D x BLK] are staged
-//     in LDS, double buffered, from 16-byte buffer loads issued one tile ahead
-//     (register staging: half of the waves fetch K, the other half V), so one
-//     barrier per tile.  Buffer bounds turn keys past N and invalid columns
-//     into zeros without branches.
+//     32g..32g+31 over keys h*BLK/2 .. (h+1)*BLK/2-1 of every tile; the halves
+//     merge through LDS once per item.
+//   * K and V tiles go from HBM straight into an LDS ring (buffer loads with
+//     the `lds` bit, 16 bytes per lane, no VGPR staging), NSTAGE-1 tiles ahead
+//     of the computation.  Both tiles are row-major with 16-byte chunks XOR-
+//     swizzled by row, which keeps the LDS read patterns below free of bank
+//     conflicts.  Buffer bounds turn keys past N and invalid columns into
+//     zeros without branches.  The wait for a tile is an explicit vmcnt that
+//     leaves the younger tiles in flight.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator of a lane holds
 //     16 keys of ONE query, so row max / row sum are in-lane plus one
-//     cross-half exchange, and P^T leaves the accumulator already in the
+//     v_permlane32_swap, and P^T leaves the accumulator already in the
 //     B-operand layout of the next product.
-//   * O^T += V^T P^T on the same MFMA; V^T is stored with bits 2 and 3 of the
-//     key index swapped inside each 16-key group, which puts the 8 keys a lane
-//     needs for one MFMA step in 16 contiguous bytes.
+//   * O^T += V^T P^T on the same MFMA; the V^T operand is read from the
+//     row-major V tile with the transposing LDS read ds_read_b64_tr_b16 (two
+//     per 16-key step), so V is never transposed in registers.
 //   * Softmax in the exp2 domain with scale*log2(e) folded into one FMA;
 //     fp32 state (m, l, acc); the running sum stays lane-partial until the
 //     epilogue; the accumulator is rescaled only when a row maximum grows by
@@ -41,33 +47,36 @@
 namespace bsa {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define BSA_LDS __attribute__((address_space(3)))
+
 template <int BLK, int HD>
 struct FwdCfg {
-  static constexpr int NQG = BLK / 32;            // query groups of 32 rows
-  static constexpr int NW = 2 * NQG;              // wavefronts: query group x key half
-  static constexpr int NT = 64 * NW;              // threads per workgroup (= 4 * BLK)
-  static constexpr int KS = HD + 8;               // LDS row stride of K (bf16 elements)
-  static constexpr int VS = BLK + 8;              // LDS row stride of V^T (bf16 elements)
-  static constexpr int K_ELEMS = BLK * KS;
-  static constexpr int V_ELEMS = HD * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;  // bf16 elements per pipeline stage
-  static constexpr size_t LDS_BYTES = size_t(2) * STAGE * 2;
-  static constexpr int CPR = HD / 8;               // 16-byte chunks per token row
-  static constexpr int KCH = BLK * CPR / (NT / 2); // K chunks per K-loading thread
-  static constexpr int VQ = BLK * CPR / 4 / (NT / 2);  // V quads per V-loading thread
-  static constexpr int NDC = HD / 16;              // k-steps of the QK^T product
-  static constexpr int NKT = BLK / 64;             // 32-key subtiles per key half
-  static constexpr int NDT = HD / 32;              // 32-wide d subtiles of the output
-  static_assert(KCH * (NT / 2) == BLK * CPR, "K chunks must divide evenly");
-  static_assert(VQ * (NT / 2) * 4 == BLK * CPR, "V quads must divide evenly");
-  // Merge area (reuses the stage buffers): per query group 64 lanes x (acc + m + l).
-  static constexpr size_t MERGE_BYTES = size_t(NQG) * 64 * (NDT * 16 + 4) * 4;
-  static_assert(MERGE_BYTES <= LDS_BYTES, "merge area must fit in the stage buffers");
+  static constexpr int NQG = BLK / 32;              // query groups of 32 rows
+  static constexpr int NW = 2 * NQG;                // wavefronts: query group x key half
+  static constexpr int NT = 64 * NW;                // threads per workgroup (= 4 * BLK)
+  static constexpr int ROWB = HD * 2;               // bytes of one K/V/Q row
+  static constexpr int CPR = HD / 8;                // 16-byte chunks per row
+  static constexpr int TILEB = BLK * ROWB;          // bytes of one K or V tile
+  static constexpr int STAGEB = 2 * TILEB;          // K tile then V tile
+  static constexpr int NSTAGE = TILEB <= 8192 ? 3 : 2;
+  static constexpr int DPW = STAGEB / 1024 / NW;    // 16-byte-per-lane loads per wave per tile
+  static constexpr int ML_FLOATS = NQG * 64 * 2;    // merge area: running max and sum
+  static constexpr size_t LDS_BYTES = size_t(NSTAGE) * STAGEB + ML_FLOATS * 4;
+  static constexpr int NDC = HD / 16;               // k-steps of the QK^T product
+  static constexpr int NKT = BLK / 64;              // 32-key subtiles per key half
+  static constexpr int NDT = HD / 32;               // 32-wide d subtiles of the output
+  static_assert(DPW * NW * 1024 == STAGEB, "loads must cover a stage exactly");
+  static_assert(size_t(NQG) * 64 * NDT * 16 * 4 <= size_t(STAGEB),
+                "the accumulator merge must fit in one stage");
+  static_assert(BLK <= 255, "valid counts are queued in 8-bit fields");
 };
 
-// Position of key kv inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int kv_perm(int kv) {
-  return (kv & ~12) | ((kv & 4) << 1) | ((kv & 8) >> 1);
+// Byte offset of the 16-byte chunk c of row r inside a swizzled tile.
+template <int ROWB>
+__device__ __forceinline__ uint32_t swz(int r, int c) {
+  return uint32_t(r) * ROWB + uint32_t((c ^ (r & 7)) << 4);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -76,14 +85,46 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return uint32_t(lo) | (uint32_t(hi) << 16);
 }
 
-// Buffer resource over [base, base + bytes): loads past the end return zeros.
+// Raw buffer descriptor over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i{static_cast<int>(static_cast<uint32_t>(a)),
+             static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffff), static_cast<int>(bytes),
+             0x00020000};
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
                                            0x00020000);
 }
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+// 16 bytes per lane from buffer offset `voff` into LDS at lds + 16 * lane.
+// Issued as inline assembly so that the compiler's wait-count bookkeeping,
+// which cannot tell LDS ring stages apart, does not drain the ring before
+// every LDS read; the waits for these loads are the explicit vmcnt below.
+// M0 (the LDS destination) is saved and restored inside the statement.
+__device__ __forceinline__ void dma16(v4i desc, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(desc)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n): n vector-memory operations may still be outstanding.
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 16)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 8)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 4)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Value of lane l ^ 32 (the other half of the wavefront), without LDS.
@@ -95,6 +136,14 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float((threadIdx.x & 32) ? sw[0] : sw[1]);
 }
 
+__device__ __forceinline__ v4s lds_read_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS v4s*)(static_cast<uintptr_t>(addr)));
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  return *((const BSA_LDS bf16x8*)(static_cast<uintptr_t>(addr)));
+}
+
 // Largest growth of the running max (log2 units) tolerated before the
 // accumulator is rescaled; probabilities then stay below 2^8 before the final
 // division, well inside fp32 and bf16 range.
@@ -104,320 +153,355 @@ template <int BLK, int HD>
 __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t N,
-    int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    float* __restrict__ part) {
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
+    int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, float* __restrict__ part) {
   using C = FwdCfg<BLK, HD>;
-  extern __shared__ __align__(16) uint16_t smem[];
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
+  float* ml = reinterpret_cast<float*>(smem + size_t(C::NSTAGE) * C::STAGEB);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int qg = wave % C::NQG;  // query group
   const int kh = wave / C::NQG;  // key half
   const int ql = lane & 31;      // query column of this lane in the MFMA tiles
   const int hh = lane >> 5;      // which half of the k / row dimension the lane feeds
-
-  // Work item: tiles [tb, te) of row r; slot >= 0 sends a partial result to
-  // the workspace instead of O (the row was cut into chunks).
-  int r, tb = 0, te = INT32_MAX, slot = -1;
-  if (work) {
-    const int4 it = *reinterpret_cast<const int4*>(work + 4 * size_t(blockIdx.x));
-    r = it.x;
-    tb = it.y;
-    te = it.z;
-    slot = it.w;
-  } else {
-    r = static_cast<int>(blockIdx.x);
-  }
-  if (r < 0 || r >= n_rows) return;
-  const int bh = r / nb;
-  const int qb = r - bh * nb;
-  const size_t head = size_t(bh) * size_t(N) * HD;
-  const uint32_t head_bytes = static_cast<uint32_t>(size_t(N) * HD * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + head, head_bytes);
-
+  const int G = gridDim.x;
+  const uint32_t head_bytes = static_cast<uint32_t>(size_t(N) * C::ROWB);
   const int nnz = row_ptr[n_rows];
-  int start = row_ptr[r];
-  int end = row_ptr[r + 1];
-  start = min(max(start, 0), nnz);
-  end = min(max(end, start), nnz);
-  tb = max(tb, 0);
-  te = min(te, end - start);
-  start += tb;
-  const int cnt = max(te - tb, 0);
 
-  // Query fragment (B operand of S^T = K Q^T): lane holds d = 16c + 8hh .. +7.
-  // Rows past N read as zeros through the buffer bound.
-  const int qrow = qb * BLK + qg * 32 + ql;
-  bf16x8 qf[C::NDC];
-  {
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + head, head_bytes);
-    const uint32_t qoff = static_cast<uint32_t>(qrow) * HD * 2;
+  // Work item k -> (row, first column position, column count, slot); row = -1
+  // when k is past the end.  Everything here is wavefront-uniform.
+  auto load_item = [&](int k, int& row, int& c0, int& cnt, int& slot) {
+    row = -1;
+    c0 = cnt = 0;
+    slot = -1;
+    if (k >= n_items) return;
+    int r, b, e, sl;
+    if (work) {
+      r = work[4 * k];
+      b = work[4 * k + 1];
+      e = work[4 * k + 2];
+      sl = work[4 * k + 3];
+    } else {
+      r = k;
+      b = row_ptr[k];
+      e = row_ptr[k + 1];
+      sl = -1;
+    }
+    if (r < 0 || r >= n_rows) return;
+    b = min(max(b, 0), nnz);
+    e = min(max(e, b), nnz);
+    row = r;
+    c0 = b;
+    cnt = e - b;
+    slot = sl;
+  };
+
+  // This wave's share of a stage: DPW loads of 64 chunks; waves [0, NW/2) fill
+  // the K tile, the others the V tile.  doff = source offset of the chunk that
+  // lands at this lane's (swizzled) LDS position.
+  const bool loads_v = wave >= C::NW / 2;
+  uint32_t doff[C::DPW];
+#pragma unroll
+  for (int i = 0; i < C::DPW; ++i) {
+    const int g = (wave * C::DPW + i) * 64 + lane - (loads_v ? BLK * C::CPR : 0);
+    const int row = g / C::CPR;
+    const int pos = g - row * C::CPR;
+    doff[i] = uint32_t(row) * C::ROWB + uint32_t((pos ^ (row & 7)) << 4);
+  }
+
+  // Issue the K/V loads of tile `j` of head `bh` into ring stage `st`.
+  auto issue_tile = [&](int bh, int j, int st) {
+    const size_t head = size_t(bh) * size_t(N) * HD;
+    v4i desc = make_desc((loads_v ? V : K) + head, head_bytes);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) desc[w] = __builtin_amdgcn_readfirstlane(desc[w]);
+    const uint32_t tb = (j >= 0 && j < nb) ? uint32_t(j) * C::TILEB : head_bytes;
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(
+        lds0 + uint32_t(st) * C::STAGEB + uint32_t(wave * C::DPW) * 1024u);
+#pragma unroll
+    for (int i = 0; i < C::DPW; ++i) dma16(desc, tb + doff[i], l0 + uint32_t(i) * 1024u);
+  };
+
+  // Query fragment of the item on CSR row `row` (B operand of S^T = K Q^T):
+  // lane holds d = 16c + 8hh .. +7 of query row 32*qg + ql.  Rows past N, and
+  // every row of an empty item (row < 0), read as zeros.
+  auto load_q = [&](int row, bf16x8* qf) {
+    const int bh = row >= 0 ? row / nb : 0;
+    const int qrow = (row >= 0 ? row - bh * nb : 0) * BLK + qg * 32 + ql;
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc(Q + size_t(bh) * size_t(N) * HD, row >= 0 ? head_bytes : 0u);
+    const uint32_t qoff = static_cast<uint32_t>(qrow) * C::ROWB;
 #pragma unroll
     for (int c = 0; c < C::NDC; ++c)
-      qf[c] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qoff + (2 * c + hh) * 16));
-  }
-  // Retire the query loads here: otherwise the wait-count bookkeeping still sees
-  // them pending inside the tile loop and drains the K/V prefetch before every
-  // product.  (vmcnt = 0, expcnt and lgkmcnt left at their maxima.)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-
-  // Staging registers: threads [0, NT/2) fetch V quads, threads [NT/2, NT) fetch K.
-  const bool loads_k = tid >= C::NT / 2;
-  const int lt = loads_k ? tid - C::NT / 2 : tid;
-  constexpr int NREG = C::KCH > 4 * C::VQ ? C::KCH : 4 * C::VQ;
-  uint4 st[NREG];
-
-  auto tile_valid = [&](int j) -> int {
-    return (j >= 0 && j < nb) ? min(BLK, N - j * BLK) : 0;
+      qf[c] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + (2 * c + hh) * 16, 0, 0));
   };
 
-  // Global -> registers for KV block j.  Keys past N, and every key of a
-  // column outside [0, nb), read as zeros through the buffer bound.
-  auto load_tile = [&](int j) {
-    const uint32_t tb = (j >= 0 && j < nb) ? static_cast<uint32_t>(j) * BLK * HD * 2 : head_bytes;
-    if (loads_k) {
-#pragma unroll
-      for (int t = 0; t < C::KCH; ++t) {
-        const int ch = lt + t * (C::NT / 2);
-        const int row = ch / C::CPR;
-        const int c8 = ch - row * C::CPR;
-        st[t] = buf_load16(krs, tb + row * HD * 2 + c8 * 16);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < C::VQ; ++t) {
-        const int qd = lt + t * (C::NT / 2);
-        const int rq = qd % (BLK / 4);
-        const int c8 = qd / (BLK / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st[4 * t + e] = buf_load16(vrs, tb + (4 * rq + e) * HD * 2 + c8 * 16);
-      }
+  // ---- stream state -------------------------------------------------------
+  int k_cur = blockIdx.x;
+  if (k_cur >= n_items) return;
+  int cur_row, cur_c0, cur_cnt, cur_slot, nxt_row, nxt_c0, nxt_cnt, nxt_slot;
+  load_item(k_cur, cur_row, cur_c0, cur_cnt, cur_slot);
+  load_item(k_cur + G, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+  bf16x8 qf[C::NDC], qn[C::NDC];
+  load_q(cur_row, qf);
+  load_q(nxt_row, qn);
+
+  // Prefetch cursor: tile p_pos of the current item (p_in_next == 0) or of
+  // the next one (1).  p_src() is the column position of the tile it would
+  // issue, or -1 when it has run past the next item or the ring is full.
+  int p_in_next = 0, p_pos = 0;
+  int inflight = 0;  // tiles issued and not yet computed
+  int st_next = 0;   // ring stage of the next issued tile
+  uint32_t vq = 0;   // valid key counts of the tiles in flight, 8 bits each, oldest lowest
+  auto p_src = [&]() -> int {
+    if (inflight >= C::NSTAGE) return -1;
+    if (!p_in_next && p_pos >= cur_cnt) {
+      p_in_next = 1;
+      p_pos = 0;
+    }
+    const int row = p_in_next ? nxt_row : cur_row;
+    const int c0 = p_in_next ? nxt_c0 : cur_c0;
+    const int cnt = p_in_next ? nxt_cnt : cur_cnt;
+    return (row < 0 || p_pos >= cnt) ? -1 : c0 + p_pos;
+  };
+  // Issue the tile whose column index `j` was read from position p_src().
+  auto p_issue = [&](int j) {
+    const int row = p_in_next ? nxt_row : cur_row;
+    issue_tile(row / nb, j, st_next);
+    const uint32_t valid = (j >= 0 && j < nb) ? uint32_t(min(BLK, N - j * BLK)) : 0u;
+    vq |= valid << (8 * inflight);
+    ++inflight;
+    st_next = st_next + 1 == C::NSTAGE ? 0 : st_next + 1;
+    ++p_pos;
+  };
+  // Fill the ring (all but one stage) with the next tiles of the stream.
+  auto refill = [&]() {
+    while (inflight + 1 < C::NSTAGE) {
+      const int src = p_src();
+      if (src < 0) break;
+      p_issue(col_idx[src]);
     }
   };
 
-  // Registers -> LDS: K row-major; V transposed, four keys per 8-byte store.
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * C::STAGE;
-    uint16_t* vt = ks + C::K_ELEMS;
-    if (loads_k) {
+  // Retire the query loads before any tile load is issued, so that the wait
+  // bookkeeping never holds them pending inside the tile loop.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  refill();
+
+  int st_cur = 0;  // stage of the tile being computed
+  for (;;) {
+    // ---- one item ---------------------------------------------------------
+    float m_run = -INFINITY;  // running max of scale*log2(e)*s (possibly stale by < slack)
+    float l_run = 0.f;        // lane-partial running sum
+    f32x16 acc[C::NDT];
 #pragma unroll
-      for (int t = 0; t < C::KCH; ++t) {
-        const int ch = lt + t * (C::NT / 2);
-        const int row = ch / C::CPR;
-        const int c8 = ch - row * C::CPR;
-        *reinterpret_cast<uint4*>(ks + row * C::KS + c8 * 8) = st[t];
-      }
-    } else {
+    for (int u = 0; u < C::NDT; ++u)
 #pragma unroll
-      for (int t = 0; t < C::VQ; ++t) {
-        // Consecutive lanes take consecutive key quads of one 8-column chunk, so
-        // each 8-byte store of a half-wave lands on 64 distinct LDS banks.
-        const int qd = lt + t * (C::NT / 2);
-        const int rq = qd % (BLK / 4);
-        const int c8 = qd / (BLK / 4);
-        uint16_t* dst = vt + (c8 * 8) * C::VS + kv_perm(4 * rq);
-        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&st[4 * t + 0]);
-        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&st[4 * t + 1]);
-        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&st[4 * t + 2]);
-        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&st[4 * t + 3]);
+      for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+
+    for (int u = 0; u < cur_cnt; ++u) {
+      // Column of the tile to prefetch this step (scalar load, consumed after
+      // the barrier).  The tiles issued after the current one are the only
+      // loads allowed in flight; the barrier then makes every wave's part of
+      // the current tile visible and frees the stage computed one step ago.
+      const int src = p_src();
+      const int jn = src >= 0 ? col_idx[src] : -1;
+      wait_vm(C::DPW * (inflight - 1));
+      __syncthreads();
+      if (src >= 0) p_issue(jn);
+      const uint32_t ks = lds0 + uint32_t(st_cur) * C::STAGEB;
+      const uint32_t vs = ks + C::TILEB;
+      const int valid = static_cast<int>(vq & 0xffu);
+
+      // S^T tile: lane (ql, hh) holds keys key0 + 8(i/4) + 4hh + (i%4) of query ql.
+      const f32x16 zero = {};
+      f32x16 s[C::NKT];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // d = 8*c8 + 2w takes the low halves, d + 1 the high halves.
-          const uint2 even = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u),
-                                        __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u));
-          const uint2 odd = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u),
-                                       __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u));
-          *reinterpret_cast<uint2*>(dst + (2 * w) * C::VS) = even;
-          *reinterpret_cast<uint2*>(dst + (2 * w + 1) * C::VS) = odd;
+      for (int kt = 0; kt < C::NKT; ++kt) {
+        const int key = (kh * C::NKT + kt) * 32 + ql;
+#pragma unroll
+        for (int c = 0; c < C::NDC; ++c) {
+          const bf16x8 a = lds_read16(ks + swz<C::ROWB>(key, 2 * c + hh));
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? zero : s[kt], 0, 0,
+                                                          0);
         }
       }
-    }
-  };
-
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s (possibly stale by < slack)
-  float l_run = 0.f;        // lane-partial running sum
-  f32x16 acc[C::NDT];
+      if (__builtin_expect(valid < BLK, 0)) {
 #pragma unroll
-  for (int u = 0; u < C::NDT; ++u)
+        for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
-
-  // This wave's key half of one KV tile from LDS; keys >= valid (only in a
-  // partial last block or an out-of-range column) are masked to -inf on a
-  // rarely taken branch.
-  auto compute_tile = [&](const uint16_t* ks, const uint16_t* vt, int valid) {
-    const f32x16 zero = {};
-    f32x16 s[C::NKT];
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
-      const int key0 = (kh * C::NKT + kt) * 32;
-#pragma unroll
-      for (int c = 0; c < C::NDC; ++c) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(ks + (key0 + ql) * C::KS + 16 * c + 8 * hh);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? zero : s[kt], 0, 0, 0);
+          for (int i = 0; i < 16; ++i) {
+            const int kv = (kh * C::NKT + kt) * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (kv >= valid) s[kt][i] = -INFINITY;
+          }
       }
-    }
-    if (__builtin_expect(valid < BLK, 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+      mx = fmaxf(mx, other_half(mx));
+      const float mt = mx * sl2;
+      // Lazy rescale: only when some row's max grew by more than the slack.
+      const bool need = mt > m_run + kRescaleSlack;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+        m_run = need ? mt : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int u2 = 0; u2 < C::NDT; ++u2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[u2][i] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+      // Row sums in four independent chains (no long serial add dependency).
+      float ls[4];
+      bf16x8 pb[C::NKT][2];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int kv = (kh * C::NKT + kt) * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (kv >= valid) s[kt][i] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_use));
+          if (kt == 0 && i < 4)
+            ls[i] = p;
+          else
+            ls[i & 3] += p;
+          pb[kt][i >> 3][i & 7] = static_cast<__bf16>(p);
         }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+      // O^T += V^T P^T.  For the 16-key step kb, V^T rows d = 32u + (lane % 32)
+      // need keys kb + 4hh + e and kb + 8 + 4hh + e (e = 0..3): lane t of each
+      // 16-lane block points at key row t / 4 and columns 4 (t % 4) .. +3 of its
+      // block's 16 d values, and the transposing read returns to every lane the
+      // four keys of its own d column.
+      const int tr_row = 4 * hh + ((lane & 15) >> 2);
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int kb = (kh * C::NKT + kt) * 32 + 16 * c2;
+#pragma unroll
+          for (int u2 = 0; u2 < C::NDT; ++u2) {
+            const int col = 32 * u2 + tr_col;
+            const v4s lo = lds_read_tr(vs + swz<C::ROWB>(kb + tr_row, col >> 3) + (col & 7) * 2);
+            const v4s hi =
+                lds_read_tr(vs + swz<C::ROWB>(kb + 8 + tr_row, col >> 3) + (col & 7) * 2);
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c2], acc[u2], 0, 0, 0);
+          }
+        }
+
+      // Retire the tile.
+      st_cur = st_cur + 1 == C::NSTAGE ? 0 : st_cur + 1;
+      vq >>= 8;
+      --inflight;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-    mx = fmaxf(mx, other_half(mx));
-    const float mt = mx * sl2;
-    // Lazy rescale: only when some row's max grew by more than the slack.
-    const bool need = mt > m_run + kRescaleSlack;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
-      m_run = need ? mt : m_run;
-      l_run *= alpha;
+
+    // ---- epilogue: merge the key halves through the stage before st_cur ---
+    // (the last computed tile's stage; no load targets it until the next
+    // barrier of the tile loop).
+    const int st_free = st_cur == 0 ? C::NSTAGE - 1 : st_cur - 1;
+    float l_half = l_run + other_half(l_run);
+    __syncthreads();  // every wave is done with that stage and the merge area
+    float* mg = reinterpret_cast<float*>(smem + size_t(st_free) * C::STAGEB) +
+                size_t(qg) * 64 * C::NDT * 16;
+    if (kh == 1) {
 #pragma unroll
       for (int u = 0; u < C::NDT; ++u)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[u][i] *= alpha;
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(mg + ((u * 4 + g) * 64 + lane) * 4) =
+              f32x4{acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
+      ml[(qg * 2) * 64 + lane] = m_run;
+      ml[(qg * 2 + 1) * 64 + lane] = l_half;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // Row sums in four independent chains (no long serial add dependency).
-    float ls[4];
-    bf16x8 pb[C::NKT][2];
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = ml[(qg * 2) * 64 + lane];
+      const float l1 = ml[(qg * 2 + 1) * 64 + lane];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      l_half = l_half * a0 + l1 * a1;
+      m_run = m;
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
+      for (int u = 0; u < C::NDT; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_use));
-        if (kt == 0 && i < 4)
-          ls[i] = p;
-        else
-          ls[i & 3] += p;
-        pb[kt][i >> 3][i & 7] = static_cast<__bf16>(p);
-      }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-    // O^T += V^T P^T: A = V^T rows d = 32u + ql, keys at permuted positions 8hh..8hh+7.
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(mg + ((u * 4 + g) * 64 + lane) * 4);
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int u = 0; u < C::NDT; ++u) {
-          const int key0 = (kh * C::NKT + kt) * 32 + 16 * c2;
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(vt + (32 * u + ql) * C::VS + key0 + 8 * hh);
-          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c2], acc[u], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) acc[u][4 * g + e] = acc[u][4 * g + e] * a0 + o1[e] * a1;
         }
-  };
+      const int bh = cur_row / nb;
+      const int q = qg * 32 + ql;
+      const int qrow = (cur_row - bh * nb) * BLK + q;
+      if (cur_slot >= 0) {
+        // Partial result of one chunk: unnormalised acc, running max (log2
+        // units) and running sum, combined with the row's other chunks by
+        // merge_kernel.
+        float* po = part + size_t(cur_slot) * BLK * (HD + 2);
+#pragma unroll
+        for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(po + q * HD + 32 * u + 8 * g + 4 * hh) =
+                f32x4{acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
+        if (hh == 0) {
+          po[BLK * HD + q] = m_run;
+          po[BLK * HD + BLK + q] = l_half;
+        }
+      } else if (qrow < N) {
+        const size_t head = size_t(bh) * size_t(N) * HD;
+        const float inv = l_half > 0.f ? 1.f / l_half : 0.f;
+        uint16_t* orow = O + head + size_t(qrow) * HD;
+#pragma unroll
+        for (int u = 0; u < C::NDT; ++u)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * u + 8 * g + 4 * hh;
+            const uint32_t w0 = pack_bf16x2(acc[u][4 * g + 0] * inv, acc[u][4 * g + 1] * inv);
+            const uint32_t w1 = pack_bf16x2(acc[u][4 * g + 2] * inv, acc[u][4 * g + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+          }
+        if (hh == 0 && LSE != nullptr) {
+          LSE[size_t(bh) * N + qrow] =
+              l_half > 0.f ? (m_run + __builtin_amdgcn_logf(l_half)) * 0.69314718055994531f
+                           : -INFINITY;
+        }
+      }
+    }
 
-  // Tiles run in windows of 64: lane i of `colw` holds the window's column i
-  // (one vector load per window, read back with v_readlane), so nothing the
-  // inner loop carries from one tile to the next comes from memory.
-  int t = 0;
-  for (int w0 = 0; w0 < cnt; w0 += 64) {
-    const int wn = min(64, cnt - w0);
-    const int colw = lane < wn ? col_idx[start + w0 + lane] : -1;
-    // First column of the next window, or this window's last if there is none.
-    const int next_first = w0 + 64 < cnt ? col_idx[start + w0 + 64] : -1;
-    // Retire the window load now (once per 64 tiles) so the inner loop never
-    // has to drain the tile prefetch just to read a column index.
+    // ---- advance to the next item ----------------------------------------
+    k_cur += G;
+    if (k_cur >= n_items) break;
+    cur_row = nxt_row;
+    cur_c0 = nxt_c0;
+    cur_cnt = nxt_cnt;
+    cur_slot = nxt_slot;
+#pragma unroll
+    for (int c = 0; c < C::NDC; ++c) qf[c] = qn[c];
+    // The copy above waited for the query loads; make that explicit so they
+    // are never seen as pending inside the tile loop.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (w0 == 0) load_tile(__builtin_amdgcn_readfirstlane(colw));
-    for (int u = 0; u < wn; ++u, ++t) {
-      const int buf = t & 1;
-      const int j = __builtin_amdgcn_readlane(colw, u);
-      // Prefetch target: the next tile (the very last tile harmlessly reloads itself).
-      const int jn = u + 1 < wn ? __builtin_amdgcn_readlane(colw, u + 1)
-                                : (t + 1 < cnt ? next_first : j);
-      store_tile(buf);
-      __syncthreads();
-      load_tile(jn);
-      const uint16_t* ks = smem + buf * C::STAGE;
-      compute_tile(ks, ks + C::K_ELEMS, tile_valid(j));
+    load_item(k_cur + G, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+    load_q(nxt_row, qn);
+    if (p_in_next) {
+      p_in_next = 0;  // the prefetch cursor is already inside the new item
+    } else {
+      p_pos = 0;      // it never reached it: start at its first tile
     }
+    refill();
   }
-
-  // Merge the two key halves: wave (g, 1) hands (m, l, acc) to wave (g, 0).
-  float l_half = l_run + other_half(l_run);
-  __syncthreads();  // every wave is done reading the stage buffers
-  float* mg = reinterpret_cast<float*>(smem) + size_t(qg) * 64 * (C::NDT * 16 + 4);
-  if (kh == 1) {
-#pragma unroll
-    for (int u = 0; u < C::NDT; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(mg + ((u * 4 + g) * 64 + lane) * 4) =
-            f32x4{acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
-    mg[C::NDT * 16 * 64 + lane] = m_run;
-    mg[C::NDT * 16 * 64 + 64 + lane] = l_half;
-  }
-  __syncthreads();
-  if (kh == 1) return;
-  {
-    const float m1 = mg[C::NDT * 16 * 64 + lane];
-    const float l1 = mg[C::NDT * 16 * 64 + 64 + lane];
-    const float m = fmaxf(m_run, m1);
-    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-    l_half = l_half * a0 + l1 * a1;
-    m_run = m;
-#pragma unroll
-    for (int u = 0; u < C::NDT; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(mg + ((u * 4 + g) * 64 + lane) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[u][4 * g + e] = acc[u][4 * g + e] * a0 + o1[e] * a1;
-      }
-  }
-
-  if (slot >= 0) {
-    // Partial result of one chunk: unnormalised acc, running max (log2 units)
-    // and running sum, merged with the row's other chunks by merge_kernel.
-    float* po = part + size_t(slot) * BLK * (HD + 2);
-    const int q = qg * 32 + ql;
-#pragma unroll
-    for (int u = 0; u < C::NDT; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(po + q * HD + 32 * u + 8 * g + 4 * hh) =
-            f32x4{acc[u][4 * g], acc[u][4 * g + 1], acc[u][4 * g + 2], acc[u][4 * g + 3]};
-    if (hh == 0) {
-      po[BLK * HD + q] = m_run;
-      po[BLK * HD + BLK + q] = l_half;
-    }
-    return;
-  }
-
-  const float inv = l_half > 0.f ? 1.f / l_half : 0.f;
-  if (qrow < N) {
-    uint16_t* orow = O + head + size_t(qrow) * HD;
-#pragma unroll
-    for (int u = 0; u < C::NDT; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * u + 8 * g + 4 * hh;
-        const uint32_t w0 = pack_bf16x2(acc[u][4 * g + 0] * inv, acc[u][4 * g + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(acc[u][4 * g + 2] * inv, acc[u][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
-      }
-    if (hh == 0 && LSE != nullptr) {
-      LSE[size_t(bh) * N + qrow] =
-          l_half > 0.f ? (m_run + __builtin_amdgcn_logf(l_half)) * 0.69314718055994531f
-                       : -INFINITY;
-    }
-  }
+  wait_vm(0);  // no load may still target LDS when the workgroup retires
 }
 
 // Combines the chunk partials of every cut row: with M = max_c m_c,
@@ -464,6 +548,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Resident workgroups of fwd_kernel<BLK, HD> on the current device (cached).
+template <int BLK, int HD>
+int resident_workgroups() {
+  using C = FwdCfg<BLK, HD>;
+  static std::once_flag once;
+  static int n = 0;
+  std::call_once(once, [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&fwd_kernel<BLK, HD>), C::NT,
+            C::LDS_BYTES) != hipSuccess)
+      return;
+    n = cus * (per_cu > 0 ? per_cu : 1);
+  });
+  return n;
+}
+
 template <int BLK, int HD>
 bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
                       int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
@@ -478,12 +582,15 @@ bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, in
                                static_cast<int>(C::LDS_BYTES));
   });
   if (attr != hipSuccess) return BSA_ERR_HIP;
-  const int32_t grid = work ? n_items : n_rows;
+  const int32_t items = work ? n_items : n_rows;
+  const int resident = resident_workgroups<BLK, HD>();
+  if (resident <= 0) return BSA_ERR_HIP;
+  const int32_t grid = items < resident ? items : resident;
   if (grid > 0) {
     hipLaunchKernelGGL((fwd_kernel<BLK, HD>), dim3(grid), dim3(C::NT), C::LDS_BYTES, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), row_ptr, col_idx, work, N, nb, n_rows,
-                       sl2, static_cast<uint16_t*>(o), lse, part);
+                       static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, N, nb,
+                       n_rows, sl2, static_cast<uint16_t*>(o), lse, part);
     BSA_HIP_CHECK_LAUNCH();
   }
   if (work && n_merges > 0) {

@@ -143,9 +143,11 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
   const int64_t need = 4 * int64_t(out.size()) + int64_t(merges.size());
   if (need > capacity) return BSA_ERR_CAPACITY;
   for (size_t k = 0; k < out.size(); ++k) {
+    // Column positions are absolute indices into col_idx.
+    const int32_t base = row_ptr[out[k].row];
     work_out[4 * k + 0] = out[k].row;
-    work_out[4 * k + 1] = out[k].b;
-    work_out[4 * k + 2] = out[k].e;
+    work_out[4 * k + 1] = base + out[k].b;
+    work_out[4 * k + 2] = base + out[k].e;
     work_out[4 * k + 3] = out[k].slot;
   }
   memcpy(work_out + 4 * out.size(), merges.data(), merges.size() * sizeof(int32_t));

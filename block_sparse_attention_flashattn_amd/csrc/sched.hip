@@ -7,7 +7,7 @@
 // so the long rows start while the short ones fill in behind them.
 //
 // One workgroup of 1024 threads: LDS histogram by (max_len - length), a
-// two-level exclusive scan, then an atomic scatter of {row, 0, length, -1}
+// two-level exclusive scan, then an atomic scatter of {row, begin, end, -1}
 // work items (no row is cut).  Rows of equal length come out in an
 // unspecified order; the forward's results do not depend on it.
 #include "common.h"
@@ -54,9 +54,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __r
   }
   __syncthreads();
   for (int r = tid; r < n_rows; r += kSchedThreads) {
-    const int full = max(row_ptr[r + 1] - row_ptr[r], 0);
+    const int b = row_ptr[r];
+    const int full = max(row_ptr[r + 1] - b, 0);
     const int pos = atomicAdd(&bins[max_len - min(full, max_len)], 1);
-    *reinterpret_cast<int4*>(work + 4 * size_t(pos)) = make_int4(r, 0, full, -1);
+    *reinterpret_cast<int4*>(work + 4 * size_t(pos)) = make_int4(r, b, b + full, -1);
   }
 }
 

@@ -104,10 +104,11 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
  * ordered longest first.  Ties keep ascending row, then chunk.
  *   row_ptr   int32 [n_rows + 1] host copy of the CSR row pointer.
  *   nb        blocks per head (rows of one head are consecutive).
- *   work_out  int32 [capacity], written: n_items records {row, tile_begin,
- *             tile_end, slot} (slot = -1: the item covers its whole row and
- *             writes O directly; tiles are positions inside the row's column
- *             list), then n_merges records {row, first_slot, n_chunks}.
+ *   work_out  int32 [capacity], written: n_items records {row, col_begin,
+ *             col_end, slot}: the item covers col_idx[col_begin, col_end) of
+ *             CSR row `row` (absolute positions; slot = -1: the item covers
+ *             the whole row and writes O directly), then n_merges records
+ *             {row, first_slot, n_chunks}.
  *   capacity  >= bsa_work_plan_ints(n_rows, nnz, max_tiles) int32 entries.
  *   n_items, n_merges, n_slots  written (n_slots = partial slots used).
  * Errors: INVALID_ARG for a NULL pointer, n_rows < 1 or a decreasing row_ptr;
@@ -178,7 +179,8 @@ BSA_API bsa_status bsa_build_mask_status(const void* workspace, void* stream,
 /*
  * Longest-row-first work list built on the device (async), for a CSR whose
  * row lengths the host does not hold: the work_dev layout of
- * bsa_work_plan_host with no row cut (n_items = n_rows, n_merges = 0),
+ * bsa_work_plan_host with no row cut (n_items = n_rows, n_merges = 0, every
+ * item {row, row_ptr[row], row_ptr[row + 1], -1}),
  * produced by a counting sort of the rows by length, longest first (order
  * among equal lengths unspecified; results do not depend on it).
  *   row_ptr_dev int32 [n_rows+1]; work_dev int32 [4*n_rows] written;
@@ -209,7 +211,10 @@ BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D, int32_t b
  *   work_dev    device copy of a work list (bsa_work_plan_host or
  *               bsa_schedule) with n_items items and n_merges merges, or NULL
  *               for one item per row in natural order (n_items, n_merges
- *               ignored).  Every row must be covered exactly once.
+ *               ignored).  Every row must be covered exactly once; column
+ *               ranges are clamped to [0, nnz].  Workgroups stay resident and
+ *               each runs items blockIdx, blockIdx + G, ... (G = resident
+ *               workgroups), so the order of the list is the launch order.
  *   workspace   >= bsa_forward_workspace_bytes(n_slots, D, block) bytes of
  *               device memory when the work list cuts rows (n_merges > 0),
  *               else may be NULL; contents need no initialisation.

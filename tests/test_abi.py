@@ -74,7 +74,9 @@ def test_mask_plan_workload_totals():
 def check_work(work, ni, nm, ns, rp, max_tiles):
     """Every row covered exactly once, chunks <= max_tiles, longest first, merges consistent."""
     lens = np.diff(rp)
-    items = work[:4 * ni].reshape(ni, 4)
+    items = work[:4 * ni].reshape(ni, 4).copy()
+    items[:, 1] -= rp[items[:, 0]]          # absolute column positions -> positions in the row
+    items[:, 2] -= rp[items[:, 0]]
     merges = work[4 * ni:4 * ni + 3 * nm].reshape(nm, 3)
     sizes = items[:, 2] - items[:, 1]
     assert (np.diff(sizes) <= 0).all()

@@ -139,8 +139,9 @@ def test_launch_order_and_invalid_columns():
     items = w_dev.work.cpu().numpy().reshape(-1, 4)
     lens = np.diff(rp)
     assert sorted(items[:, 0].tolist()) == list(range(B * H * nb))
-    assert (items[:, 1] == 0).all() and (items[:, 3] == -1).all()
-    assert np.array_equal(items[:, 2], lens[items[:, 0]]) and (np.diff(items[:, 2]) <= 0).all()
+    assert np.array_equal(items[:, 1], rp[items[:, 0]]) and (items[:, 3] == -1).all()
+    sizes = items[:, 2] - items[:, 1]
+    assert np.array_equal(sizes, lens[items[:, 0]]) and (np.diff(sizes) <= 0).all()
     # insert junk columns (-1 and nb) at the front of every row
     rows = [np.concatenate([[-1, nb], ci[rp[r]:rp[r + 1]]]) for r in range(B * H * nb)]
     rp2 = np.concatenate([[0], np.cumsum([len(x) for x in rows])]).astype(np.int32)
