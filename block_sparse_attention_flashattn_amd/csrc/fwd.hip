@@ -20,8 +20,8 @@
 //   * K and V tiles go from HBM straight into an LDS ring (buffer loads with
 //     the `lds` bit, 16 bytes per lane, no VGPR staging), NSTAGE-1 tiles ahead
 //     of the computation.  Both tiles are row-major with 16-byte chunks XOR-
-//     swizzled by row, which keeps the LDS read patterns below free of bank
-//     conflicts.  Buffer bounds turn keys past N and invalid columns into
+//     swizzled by row (chunk_swizzle), which keeps the LDS read patterns
+//     below free of bank conflicts.  Buffer bounds turn keys past N and invalid columns into
 //     zeros without branches.  The wait for a tile is an explicit vmcnt that
 //     leaves the younger tiles in flight.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator of a lane holds
@@ -73,10 +73,30 @@ struct FwdCfg {
   static_assert(BLK <= 255, "valid counts are queued in 8-bit fields");
 };
 
+// Swizzle of the 16-byte chunks of tile row r (64 banks of 4 bytes; a
+// 16-byte read serves 16 lanes per cycle, an 8-byte read 32 lanes).
+//  * 128-byte rows (D = 64): a bank group is 8 (r & 1) + chunk.  Reversing the
+//    bits of (r >> 1) & 7 gives the 8 same-parity rows of any aligned 16-row
+//    group distinct chunks (16 lanes reading one logical chunk of 16 rows), and
+//    rows r, r + 2 of an aligned 4-row group different aligned 4-chunk blocks
+//    (the transposing V read: 4 rows x 4 chunks per half-wave).
+//  * 256-byte rows (D = 128): a bank group is the chunk.  Swapping the two
+//    2-bit fields of r & 15 is a bijection on 16 rows and sends the 4 rows of an
+//    aligned 4-row group to 4 different aligned 4-chunk blocks.
+template <int ROWB>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+  if constexpr (ROWB == 128) {
+    const int m = (r >> 1) & 7;
+    return ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
+  } else {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  }
+}
+
 // Byte offset of the 16-byte chunk c of row r inside a swizzled tile.
 template <int ROWB>
 __device__ __forceinline__ uint32_t swz(int r, int c) {
-  return uint32_t(r) * ROWB + uint32_t((c ^ (r & 7)) << 4);
+  return uint32_t(r) * ROWB + uint32_t((c ^ chunk_swizzle<ROWB>(r)) << 4);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -210,18 +230,25 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const int g = (wave * C::DPW + i) * 64 + lane - (loads_v ? BLK * C::CPR : 0);
     const int row = g / C::CPR;
     const int pos = g - row * C::CPR;
-    doff[i] = uint32_t(row) * C::ROWB + uint32_t((pos ^ (row & 7)) << 4);
+    doff[i] = uint32_t(row) * C::ROWB + uint32_t((pos ^ chunk_swizzle<C::ROWB>(row)) << 4);
   }
 
-  // Issue the K/V loads of tile `j` of head `bh` into ring stage `st`.
-  auto issue_tile = [&](int bh, int j, int st) {
-    const size_t head = size_t(bh) * size_t(N) * HD;
-    v4i desc = make_desc((loads_v ? V : K) + head, head_bytes);
+  // This wave's K or V buffer descriptor for the head of CSR row `row`
+  // (rows < 0: an empty range).  Built once per item.
+  auto kv_desc = [&](int row) -> v4i {
+    const int bh = row >= 0 ? row / nb : 0;
+    v4i d = make_desc((loads_v ? V : K) + size_t(bh) * size_t(N) * HD, row >= 0 ? head_bytes : 0u);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) desc[w] = __builtin_amdgcn_readfirstlane(desc[w]);
+    for (int w = 0; w < 4; ++w) d[w] = __builtin_amdgcn_readfirstlane(d[w]);
+    return d;
+  };
+  const uint32_t lds_wave = lds0 + uint32_t(wave * C::DPW) * 1024u;
+
+  // Issue this wave's loads of tile `j` (through descriptor `desc`) into ring
+  // stage `st`.  Out-of-range columns point past the end: zeros.
+  auto issue_tile = [&](const v4i& desc, int j, int st) {
     const uint32_t tb = (j >= 0 && j < nb) ? uint32_t(j) * C::TILEB : head_bytes;
-    const uint32_t l0 = __builtin_amdgcn_readfirstlane(
-        lds0 + uint32_t(st) * C::STAGEB + uint32_t(wave * C::DPW) * 1024u);
+    const uint32_t l0 = lds_wave + uint32_t(st) * C::STAGEB;
 #pragma unroll
     for (int i = 0; i < C::DPW; ++i) dma16(desc, tb + doff[i], l0 + uint32_t(i) * 1024u);
   };
@@ -247,51 +274,46 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
   int cur_row, cur_c0, cur_cnt, cur_slot, nxt_row, nxt_c0, nxt_cnt, nxt_slot;
   load_item(k_cur, cur_row, cur_c0, cur_cnt, cur_slot);
   load_item(k_cur + G, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+  v4i desc_cur = kv_desc(cur_row), desc_nxt = kv_desc(nxt_row);
   bf16x8 qf[C::NDC], qn[C::NDC];
   load_q(cur_row, qf);
   load_q(nxt_row, qn);
 
-  // Prefetch cursor: tile p_pos of the current item (p_in_next == 0) or of
-  // the next one (1).  p_src() is the column position of the tile it would
-  // issue, or -1 when it has run past the next item or the ring is full.
-  int p_in_next = 0, p_pos = 0;
+  // The stream is the current item's tiles followed by the next item's.  With
+  // u tiles of the current item computed and `inflight` issued ahead, the next
+  // tile to issue is stream tile u + inflight.
   int inflight = 0;  // tiles issued and not yet computed
   int st_next = 0;   // ring stage of the next issued tile
   uint32_t vq = 0;   // valid key counts of the tiles in flight, 8 bits each, oldest lowest
-  auto p_src = [&]() -> int {
-    if (inflight >= C::NSTAGE) return -1;
-    if (!p_in_next && p_pos >= cur_cnt) {
-      p_in_next = 1;
-      p_pos = 0;
-    }
-    const int row = p_in_next ? nxt_row : cur_row;
-    const int c0 = p_in_next ? nxt_c0 : cur_c0;
-    const int cnt = p_in_next ? nxt_cnt : cur_cnt;
-    return (row < 0 || p_pos >= cnt) ? -1 : c0 + p_pos;
+  // Column position of stream tile t (or -1 past the next item), and whether
+  // it belongs to the next item.
+  auto stream_src = [&](int t, bool& in_next) -> int {
+    in_next = t >= cur_cnt;
+    const int tn = t - cur_cnt;
+    return !in_next ? cur_c0 + t : (tn < nxt_cnt ? nxt_c0 + tn : -1);
   };
-  // Issue the tile whose column index `j` was read from position p_src().
-  auto p_issue = [&](int j) {
-    const int row = p_in_next ? nxt_row : cur_row;
-    issue_tile(row / nb, j, st_next);
+  auto issue = [&](int j, bool in_next) {
+    issue_tile(in_next ? desc_nxt : desc_cur, j, st_next);
     const uint32_t valid = (j >= 0 && j < nb) ? uint32_t(min(BLK, N - j * BLK)) : 0u;
     vq |= valid << (8 * inflight);
     ++inflight;
     st_next = st_next + 1 == C::NSTAGE ? 0 : st_next + 1;
-    ++p_pos;
   };
-  // Fill the ring (all but one stage) with the next tiles of the stream.
-  auto refill = [&]() {
+  // Fill the ring (all but one stage) with the next tiles of the stream; `u`
+  // tiles of the current item have been computed.
+  auto refill = [&](int u) {
     while (inflight + 1 < C::NSTAGE) {
-      const int src = p_src();
+      bool in_next;
+      const int src = stream_src(u + inflight, in_next);
       if (src < 0) break;
-      p_issue(col_idx[src]);
+      issue(col_idx[src], in_next);
     }
   };
 
   // Retire the query loads before any tile load is issued, so that the wait
   // bookkeeping never holds them pending inside the tile loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  refill();
+  refill(0);
 
   int st_cur = 0;  // stage of the tile being computed
   for (;;) {
@@ -309,11 +331,15 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       // the barrier).  The tiles issued after the current one are the only
       // loads allowed in flight; the barrier then makes every wave's part of
       // the current tile visible and frees the stage computed one step ago.
-      const int src = p_src();
+      bool in_next;
+      const int src = inflight < C::NSTAGE ? stream_src(u + inflight, in_next) : -1;
       const int jn = src >= 0 ? col_idx[src] : -1;
-      wait_vm(C::DPW * (inflight - 1));
+      if (inflight > 1)
+        wait_vm(C::DPW);
+      else
+        wait_vm(0);
       __syncthreads();
-      if (src >= 0) p_issue(jn);
+      if (src >= 0) issue(jn, in_next);
       const uint32_t ks = lds0 + uint32_t(st_cur) * C::STAGEB;
       const uint32_t vs = ks + C::TILEB;
       const int valid = static_cast<int>(vq & 0xffu);
@@ -487,65 +513,91 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     cur_c0 = nxt_c0;
     cur_cnt = nxt_cnt;
     cur_slot = nxt_slot;
+    desc_cur = desc_nxt;
 #pragma unroll
     for (int c = 0; c < C::NDC; ++c) qf[c] = qn[c];
     // The copy above waited for the query loads; make that explicit so they
     // are never seen as pending inside the tile loop.
     __builtin_amdgcn_s_waitcnt(0x0F70);
     load_item(k_cur + G, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+    desc_nxt = kv_desc(nxt_row);
     load_q(nxt_row, qn);
-    if (p_in_next) {
-      p_in_next = 0;  // the prefetch cursor is already inside the new item
-    } else {
-      p_pos = 0;      // it never reached it: start at its first tile
-    }
-    refill();
+    refill(0);
   }
   wait_vm(0);  // no load may still target LDS when the workgroup retires
 }
 
 // Combines the chunk partials of every cut row: with M = max_c m_c,
 // O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c and LSE = (M + log2 L) ln 2.
+// One thread per (query row, 4 output columns); the loads of up to kUnroll
+// chunks are issued together, so a merge costs about one memory round trip.
+constexpr int kMergeThreads = 256;
+constexpr int kUnroll = 8;
+
 template <int BLK, int HD>
-__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ merges,
-                                                    const float* __restrict__ part, int32_t N,
-                                                    int32_t nb, int32_t n_rows,
-                                                    uint16_t* __restrict__ O,
-                                                    float* __restrict__ LSE) {
-  const int3 mg = *reinterpret_cast<const int3*>(merges + 3 * size_t(blockIdx.x));
-  const int r = mg.x, slot0 = mg.y, nch = mg.z;
-  if (r < 0 || r >= n_rows) return;
-  const int bh = r / nb;
-  const int qb = r - bh * nb;
-  const size_t head = size_t(bh) * size_t(N) * HD;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* __restrict__ merges,
+                                                              const float* __restrict__ part,
+                                                              int32_t N, int32_t nb,
+                                                              int32_t n_rows,
+                                                              uint16_t* __restrict__ O,
+                                                              float* __restrict__ LSE) {
   constexpr int D4 = HD / 4;
-  for (int idx = threadIdx.x; idx < BLK * D4; idx += 256) {
-    const int q = idx / D4;
-    const int d = (idx - q * D4) * 4;
-    const int qrow = qb * BLK + q;
-    if (qrow >= N) continue;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c)
-      M = fmaxf(M, part[size_t(slot0 + c) * BLK * (HD + 2) + BLK * HD + q]);
-    float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int c = 0; c < nch; ++c) {
-        const float* pc = part + size_t(slot0 + c) * BLK * (HD + 2);
-        const float mc = pc[BLK * HD + q];
-        const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-        L += w * pc[BLK * HD + BLK + q];
-        const f32x4 oc = *reinterpret_cast<const f32x4*>(pc + q * HD + d);
-        o += w * oc;
+  constexpr int WG_PER_ROW = BLK * D4 / kMergeThreads;
+  constexpr size_t SLOT = size_t(BLK) * (HD + 2);
+  const int m = blockIdx.x / WG_PER_ROW;
+  const int idx = (blockIdx.x - m * WG_PER_ROW) * kMergeThreads + threadIdx.x;
+  const int r = merges[3 * m], slot0 = merges[3 * m + 1], nch = merges[3 * m + 2];
+  if (r < 0 || r >= n_rows || nch < 1) return;
+  const int bh = r / nb;
+  const int q = idx / D4;
+  const int d = (idx - q * D4) * 4;
+  const int qrow = (r - bh * nb) * BLK + q;
+  if (qrow >= N) return;
+  const float* base = part + size_t(slot0) * SLOT;
+
+  float mc[kUnroll], lc[kUnroll];
+  f32x4 oc[kUnroll];
+  const int n0 = min(nch, kUnroll);
+#pragma unroll
+  for (int c = 0; c < kUnroll; ++c) {
+    if (c < n0) {
+      const float* pc = base + size_t(c) * SLOT;
+      mc[c] = pc[BLK * HD + q];
+      lc[c] = pc[BLK * HD + BLK + q];
+      oc[c] = *reinterpret_cast<const f32x4*>(pc + q * HD + d);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kUnroll; ++c)
+    if (c < n0) M = fmaxf(M, mc[c]);
+  for (int c = kUnroll; c < nch; ++c) M = fmaxf(M, base[size_t(c) * SLOT + BLK * HD + q]);
+  float L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < kUnroll; ++c) {
+      if (c < n0) {
+        const float w = mc[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc[c] - M);
+        L += w * lc[c];
+        o += w * oc[c];
       }
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    *reinterpret_cast<uint2*>(O + head + size_t(qrow) * HD + d) =
-        make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
-    if (d == 0 && LSE != nullptr)
-      LSE[size_t(bh) * N + qrow] =
-          L > 0.f ? (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f : -INFINITY;
+    for (int c = kUnroll; c < nch; ++c) {
+      const float* pc = base + size_t(c) * SLOT;
+      const float mm = pc[BLK * HD + q];
+      const float w = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm - M);
+      L += w * pc[BLK * HD + BLK + q];
+      o += w * *reinterpret_cast<const f32x4*>(pc + q * HD + d);
+    }
   }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+  *reinterpret_cast<uint2*>(O + head + size_t(qrow) * HD + d) =
+      make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+  if (d == 0 && LSE != nullptr)
+    LSE[size_t(bh) * N + qrow] =
+        L > 0.f ? (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // Resident workgroups of fwd_kernel<BLK, HD> on the current device (cached).
@@ -594,7 +646,9 @@ bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, in
     BSA_HIP_CHECK_LAUNCH();
   }
   if (work && n_merges > 0) {
-    hipLaunchKernelGGL((merge_kernel<BLK, HD>), dim3(n_merges), dim3(256), 0, stream,
+    constexpr int wg_per_row = BLK * (HD / 4) / kMergeThreads;
+    hipLaunchKernelGGL((merge_kernel<BLK, HD>), dim3(n_merges * wg_per_row), dim3(kMergeThreads),
+                       0, stream,
                        work + 4 * size_t(n_items), part, N, nb, n_rows,
                        static_cast<uint16_t*>(o), lse);
     BSA_HIP_CHECK_LAUNCH();
