@@ -59,6 +59,10 @@ _SIGS = {
 }
 
 
+# BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
+ABI_VERSION = 2
+
+
 class BsaError(RuntimeError):
     """A libbsa entry point returned a non-zero status."""
 
@@ -72,6 +76,9 @@ def _load():
         fn = getattr(handle, name)
         fn.restype = res
         fn.argtypes = args
+    if handle.bsa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {handle.bsa_abi_version()}, this binding "
+                          f"expects {ABI_VERSION}; rebuild the library")
     return handle
 
 
@@ -153,8 +160,10 @@ def work_plan(row_ptr, max_tiles: int = 0, nb: int = 0, n_groups: int = 1):
     """Host work list: (work int32 array, n_items, n_merges, n_slots).
 
     Rows longer than `max_tiles` KV blocks are cut into near-equal chunks
-    (max_tiles <= 0: never).  With n_groups > 1 items are laid out so that item
-    k serves die k % n_groups with whole heads (row // nb); otherwise longest first.
+    (max_tiles <= 0: never).  Items come in n_groups groups (heads h with
+    h % n_groups == g in group g; one group if n_groups <= 1), head by head and
+    longest first inside a head, followed by the merge records and the group
+    table {n_groups, start_0, ..., start_n_groups}.
     """
     rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
     n_rows = rp.shape[0] - 1
@@ -166,7 +175,8 @@ def work_plan(row_ptr, max_tiles: int = 0, nb: int = 0, n_groups: int = 1):
     _check(lib.bsa_work_plan_host(_np_ptr(rp), n_rows, int(nb), int(max_tiles), int(n_groups),
                                   _np_ptr(work), cap, ctypes.byref(ni), ctypes.byref(nm),
                                   ctypes.byref(ns)), "bsa_work_plan_host")
-    used = 4 * ni.value + 3 * nm.value
+    tab = 4 * ni.value + 3 * nm.value
+    used = tab + 2 + int(work[tab])
     return work[:used].copy(), ni.value, nm.value, ns.value
 
 
@@ -189,8 +199,12 @@ def forward_workspace_bytes(n_slots: int, D: int, block: int) -> int:
 
 
 def _fwd_lds_bytes(block: int, D: int) -> int:
-    """LDS bytes of one forward workgroup (two stages of K and V^T tiles)."""
-    return 2 * 2 * (block * (D + 8) + D * (block + 8))
+    """LDS bytes of one forward workgroup, as the kernels allocate them."""
+    if block == 64 and D == 64:
+        return 40960  # per-wave two-stage K/V rings plus the query staging tile
+    tile = block * D * 2
+    stages = 3 if tile <= 8192 else 2
+    return stages * 2 * tile + (block // 32) * 64 * 2 * 4 + 16
 
 
 def default_max_tiles(nnz: int, block: int, D: int, n_cu: int, lds_per_cu: int = 160 * 1024):
@@ -217,10 +231,9 @@ class Work:
     def from_host(cls, row_ptr_host, D: int, block: int, max_tiles: int, device, nb: int = 0,
                   n_groups: int = 1):
         w, ni, nm, ns = work_plan(row_ptr_host, max_tiles, nb, n_groups)
-        ws = None
-        if nm > 0:
-            ws = torch.empty(max(forward_workspace_bytes(ns, D, block), 16), dtype=torch.uint8,
-                             device=device)
+        # The item counters at the start of the workspace must start at zero;
+        # every forward call leaves them zero again.
+        ws = torch.zeros(forward_workspace_bytes(ns, D, block), dtype=torch.uint8, device=device)
         return cls(torch.from_numpy(w).to(device), ni, nm, ns, ws, int(max_tiles))
 
 
@@ -324,10 +337,13 @@ def build_mask_status(plan: Plan) -> int:
 def schedule(row_ptr: torch.Tensor, max_len: int) -> Work:
     """Longest-first work list (no row cut) computed on the device from row_ptr."""
     n_rows = row_ptr.numel() - 1
-    work = torch.empty(4 * n_rows, dtype=torch.int32, device=row_ptr.device)
+    work = torch.empty(4 * n_rows + 3, dtype=torch.int32, device=row_ptr.device)
     _check(lib.bsa_schedule(_t_ptr(row_ptr), n_rows, max_len, _t_ptr(work),
                             _stream_ptr(row_ptr.device)), "bsa_schedule")
-    return Work(work, n_rows, 0, 0, None, 0)
+    # Zeroed item counters (one group, no partial slots); D and block do not
+    # change the size of a workspace without partial slots.
+    ws = torch.zeros(forward_workspace_bytes(0, 1, 1), dtype=torch.uint8, device=row_ptr.device)
+    return Work(work, n_rows, 0, 0, ws, 0)
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx, block: int,

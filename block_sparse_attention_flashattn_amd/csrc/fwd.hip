@@ -63,7 +63,7 @@ struct FwdCfg {
   static constexpr int NSTAGE = TILEB <= 8192 ? 3 : 2;
   static constexpr int DPW = STAGEB / 1024 / NW;    // 16-byte-per-lane loads per wave per tile
   static constexpr int ML_FLOATS = NQG * 64 * 2;    // merge area: running max and sum
-  static constexpr size_t LDS_BYTES = size_t(NSTAGE) * STAGEB + ML_FLOATS * 4;
+  static constexpr size_t LDS_BYTES = size_t(NSTAGE) * STAGEB + ML_FLOATS * 4 + 16;
   static constexpr int NDC = HD / 16;               // k-steps of the QK^T product
   static constexpr int NKT = BLK / 64;              // 32-key subtiles per key half
   static constexpr int NDT = HD / 32;               // 32-wide d subtiles of the output
@@ -164,6 +164,78 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
   return *((const BSA_LDS bf16x8*)(static_cast<uintptr_t>(addr)));
 }
 
+// Uniform load of a read-only table entry through the constant address space:
+// the compiler then always uses a scalar load, whatever it can prove about the
+// kernel's stores and atomics aliasing the table.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p, size_t i) {
+  return reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      reinterpret_cast<uintptr_t>(p))[i];
+}
+
+// Item counters at the start of the forward workspace (with a work list): one
+// per group, each on its own 4-KB page so that claims on different groups do
+// not queue behind each other in one memory channel.
+constexpr int kCounterStride = 1024;  // int32 entries
+constexpr size_t kCounterBytes = size_t(BSA_MAX_GROUPS) * kCounterStride * sizeof(int32_t);
+
+// Where a persistent workgroup's items come from.
+//  * No work list: workgroup w runs CSR rows w, w + G, w + 2G, ... (static).
+//  * Work list: the items come in groups (table after the merge records);
+//    workgroup w serves group w % ng, runs its items w / ng and w / ng + Gg
+//    (Gg = workgroups of the group) and claims the rest in list order from
+//    the group's counter, one item before it needs it.  A workgroup claims
+//    while its previous claim (or its second static item) was an item, so the
+//    group's claims are the items past the static rounds plus one failed claim
+//    per claiming workgroup; whoever receives the last claim number resets
+//    the counter for the next call.  Claims are vector atomics from one lane.
+struct ItemSource {
+  int32_t ng, grp, lw, gx, base, size, total;
+
+  __device__ void init(const int32_t* w, int32_t n_items, int32_t n_merges, int32_t n_rows) {
+    const int G = gridDim.x;
+    if (w) {
+      const int32_t* gt = w + 4 * size_t(n_items) + 3 * size_t(n_merges);
+      ng = min(max(ld_uniform(gt, 0), 1), BSA_MAX_GROUPS);
+      grp = blockIdx.x % ng;
+      lw = blockIdx.x / ng;
+      gx = (G - grp + ng - 1) / ng;
+      base = min(max(ld_uniform(gt, 1 + grp), 0), n_items);
+      size = min(max(ld_uniform(gt, 2 + grp), base), n_items) - base;
+    } else {
+      ng = 1;
+      grp = 0;
+      lw = blockIdx.x;
+      gx = G;
+      base = 0;
+      size = n_rows;
+    }
+    total = max(size - 2 * gx, 0) + min(gx, max(size - gx, 0));
+  }
+  // Item of static round r of this workgroup, or -1.
+  __device__ int stat(int r) const {
+    const int64_t p = lw + int64_t(r) * gx;
+    return p < size ? base + static_cast<int>(p) : -1;
+  }
+  // Item won by claim number `ticket` of the group, or -1.
+  __device__ int claimed(int ticket) const {
+    const int64_t p = 2 * int64_t(gx) + ticket;
+    return (ticket >= 0 && p < size) ? base + static_cast<int>(p) : -1;
+  }
+  // One claim (call from a single lane); the result is the claim number.
+  __device__ int claim(int32_t* ctr) const {
+    return __hip_atomic_fetch_add(ctr + size_t(grp) * kCounterStride, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // After claim number `ticket` returned (single lane): the last claim of the
+  // group resets its counter.
+  __device__ void retire(int32_t* ctr, int ticket) const {
+    if (ticket == total - 1)
+      __hip_atomic_store(ctr + size_t(grp) * kCounterStride, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
 // Largest growth of the running max (log2 units) tolerated before the
 // accumulator is rescaled; probabilities then stay below 2^8 before the final
 // division, well inside fp32 and bf16 range.
@@ -174,8 +246,8 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
-    int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, float* __restrict__ part) {
+    int32_t n_merges, int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr) {
   using C = FwdCfg<BLK, HD>;
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
@@ -188,9 +260,8 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
   const int kh = wave / C::NQG;  // key half
   const int ql = lane & 31;      // query column of this lane in the MFMA tiles
   const int hh = lane >> 5;      // which half of the k / row dimension the lane feeds
-  const int G = gridDim.x;
   const uint32_t head_bytes = static_cast<uint32_t>(size_t(N) * C::ROWB);
-  const int nnz = row_ptr[n_rows];
+  const int nnz = ld_uniform(row_ptr, n_rows);
 
   // Work item k -> (row, first column position, column count, slot); row = -1
   // when k is past the end.  Everything here is wavefront-uniform.
@@ -198,17 +269,17 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     row = -1;
     c0 = cnt = 0;
     slot = -1;
-    if (k >= n_items) return;
+    if (k < 0 || k >= n_items) return;
     int r, b, e, sl;
     if (work) {
-      r = work[4 * k];
-      b = work[4 * k + 1];
-      e = work[4 * k + 2];
-      sl = work[4 * k + 3];
+      r = ld_uniform(work, 4 * size_t(k));
+      b = ld_uniform(work, 4 * size_t(k) + 1);
+      e = ld_uniform(work, 4 * size_t(k) + 2);
+      sl = ld_uniform(work, 4 * size_t(k) + 3);
     } else {
       r = k;
-      b = row_ptr[k];
-      e = row_ptr[k + 1];
+      b = ld_uniform(row_ptr, k);
+      e = ld_uniform(row_ptr, k + 1);
       sl = -1;
     }
     if (r < 0 || r >= n_rows) return;
@@ -268,12 +339,22 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + (2 * c + hh) * 16, 0, 0));
   };
 
+  // ---- item source --------------------------------------------------------
+  ItemSource src;
+  src.init(work, n_items, n_merges, n_rows);
+  const bool queue = work != nullptr;
+  int k_cur = src.stat(0), k_nxt = src.stat(1);
+  int round = 2;           // static round of the item after next (no work list)
+  bool claim_out = false;  // a claim for the item after next is in flight
+  int ticket = -1;         // its claim number, in lane 0 of wave 0
+  if (k_cur < 0) return;
+  claim_out = queue && k_nxt >= 0;
+  if (claim_out && wave == 0 && lane == 0) ticket = src.claim(ctr);
+
   // ---- stream state -------------------------------------------------------
-  int k_cur = blockIdx.x;
-  if (k_cur >= n_items) return;
   int cur_row, cur_c0, cur_cnt, cur_slot, nxt_row, nxt_c0, nxt_cnt, nxt_slot;
   load_item(k_cur, cur_row, cur_c0, cur_cnt, cur_slot);
-  load_item(k_cur + G, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+  load_item(k_nxt, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
   v4i desc_cur = kv_desc(cur_row), desc_nxt = kv_desc(nxt_row);
   bf16x8 qf[C::NDC], qn[C::NDC];
   load_q(cur_row, qf);
@@ -306,7 +387,7 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       bool in_next;
       const int src = stream_src(u + inflight, in_next);
       if (src < 0) break;
-      issue(col_idx[src], in_next);
+      issue(ld_uniform(col_idx, src), in_next);
     }
   };
 
@@ -333,7 +414,7 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       // the current tile visible and frees the stage computed one step ago.
       bool in_next;
       const int src = inflight < C::NSTAGE ? stream_src(u + inflight, in_next) : -1;
-      const int jn = src >= 0 ? col_idx[src] : -1;
+      const int jn = src >= 0 ? ld_uniform(col_idx, src) : -1;
       if (inflight > 1)
         wait_vm(C::DPW);
       else
@@ -374,16 +455,18 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       mx = fmaxf(mx, other_half(mx));
       const float mt = mx * sl2;
       // Lazy rescale: only when some row's max grew by more than the slack.
+      // A row's first finite max is adopted without touching its (zero) state.
       const bool need = mt > m_run + kRescaleSlack;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
-        m_run = need ? mt : m_run;
+      const bool rescale = need && m_run != -INFINITY;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(rescale) != 0, 0)) {
+        const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
         l_run *= alpha;
 #pragma unroll
         for (int u2 = 0; u2 < C::NDT; ++u2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[u2][i] *= alpha;
       }
+      m_run = need ? mt : m_run;
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
       // Row sums in four independent chains (no long serial add dependency).
@@ -450,7 +533,18 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       ml[(qg * 2) * 64 + lane] = m_run;
       ml[(qg * 2 + 1) * 64 + lane] = l_half;
     }
+    // The item after next: the claim made one item ago (work list) or the
+    // next static round; wave 0 publishes it after the merge area.
+    int* xk = reinterpret_cast<int*>(ml + C::ML_FLOATS);
+    if (queue && wave == 0) {
+      const int t = claim_out ? __builtin_amdgcn_readfirstlane(ticket) : -1;
+      if (lane == 0) {
+        *xk = src.claimed(t);
+        if (claim_out) src.retire(ctr, t);
+      }
+    }
     __syncthreads();
+    const int k_nn = queue ? *xk : src.stat(round);
     if (kh == 0) {
       const float m1 = ml[(qg * 2) * 64 + lane];
       const float l1 = ml[(qg * 2 + 1) * 64 + lane];
@@ -507,8 +601,10 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     }
 
     // ---- advance to the next item ----------------------------------------
-    k_cur += G;
-    if (k_cur >= n_items) break;
+    k_cur = k_nxt;
+    k_nxt = k_nn;
+    ++round;
+    if (k_cur < 0) break;
     cur_row = nxt_row;
     cur_c0 = nxt_c0;
     cur_cnt = nxt_cnt;
@@ -519,10 +615,533 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     // The copy above waited for the query loads; make that explicit so they
     // are never seen as pending inside the tile loop.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    load_item(k_cur + G, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+    load_item(k_nxt, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+    claim_out = queue && k_nxt >= 0;
+    if (claim_out && wave == 0 && lane == 0) ticket = src.claim(ctr);
     desc_nxt = kv_desc(nxt_row);
     load_q(nxt_row, qn);
     refill(0);
+  }
+  wait_vm(0);  // no load may still target LDS when the workgroup retires
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads and stores, so tile loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Wide wavefronts for 64-row blocks at head dim 64.
+//
+// Two wavefronts per workgroup.  Wave h owns keys 32h .. 32h+31 of every
+// 64-key tile for all 64 query rows of the block (two 32-row query groups),
+// so every K or V^T operand it reads from LDS feeds two MFMAs: half the LDS
+// traffic, DMA issue and scalar work per FLOP of 32-row wavefronts.  The waves
+// share no tile data: each streams its own halves of K and V into its own
+// two-stage LDS ring (one tile ahead) and waits only on its own loads, so the
+// tile loop has no barrier.  The next item's query tile is staged in LDS while
+// the current item runs; the two key halves meet once per item, in the
+// epilogue, through the stages the last tile freed.
+struct Wide {
+  static constexpr int BLK = 64, HD = 64, ROWB = 128;
+  static constexpr int NT = 128;                     // two wavefronts
+  static constexpr int HALFB = 32 * ROWB;            // one wave's half of a K or V tile
+  static constexpr int STAGEB = 2 * HALFB;           // K half, then V half
+  static constexpr int RINGB = 2 * STAGEB;           // two stages per wave
+  static constexpr int QB = BLK * ROWB;              // staged query tile
+  static constexpr size_t LDS_BYTES = 2 * RINGB + QB;  // 40 KB: four workgroups per CU
+  static_assert(2 * 16 * 4 * 64 == STAGEB, "one query group's accumulator fills a stage");
+};
+
+// Four 1-KB segments (rows 8s .. 8s+7, s = 0..3) of one 32-row half tile from
+// buffer `desc` into LDS at dst: lane l's 16 bytes land at dst + 1024 s + 16 l.
+// The immediate offset moves the source and the LDS destination together, so
+// one M0 serves all four; `ve` addresses segments 0 and 2, `vo` segments 1 and
+// 3 (their swizzle differs).  The immediate is range-checked with the offset.
+__device__ __forceinline__ void dma_half(v4i desc, uint32_t ve, uint32_t vo, uint32_t dst) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %2, %4, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %3, %4, 0 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(dst), "v"(ve), "v"(vo), "s"(desc)
+      : "memory");
+}
+
+__global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
+    int32_t n_merges, int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr) {
+  using W = Wide;
+  constexpr int BLK = W::BLK, HD = W::HD;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
+
+  const int lane = threadIdx.x & 63;
+  const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // key half of this wave
+  const int ql = lane & 31;  // query column (within a group) / key row of the MFMA tiles
+  const int hh = lane >> 5;  // which half of the k / row dimension the lane feeds
+  const uint32_t head_bytes = static_cast<uint32_t>(size_t(N) * W::ROWB);
+  const int nnz = ld_uniform(row_ptr, n_rows);
+  const uint32_t ring = lds0 + uint32_t(kh) * W::RINGB;
+  const uint32_t qarea = lds0 + 2u * W::RINGB;
+  // head(row) = row / nb.  For nb >= 2, with magic = floor(2^32 / nb) + 1 the
+  // multiply-high estimate is never low and, for row < 2^31, at most one too
+  // high; one correction makes it exact.  (nb = 1 would need magic = 2^32 + 1.)
+  const uint32_t nb_magic =
+      nb > 1 ? static_cast<uint32_t>((uint64_t(1) << 32) / uint32_t(nb)) + 1u : 0u;
+  auto head_of = [&](int row) -> int {
+    if (nb == 1) return row;
+    int h = static_cast<int>(__umulhi(static_cast<uint32_t>(row), nb_magic));
+    if (row - h * nb < 0) --h;
+    return h;
+  };
+
+  auto load_item = [&](int k, int& row, int& c0, int& cnt, int& slot) {
+    row = -1;
+    c0 = cnt = 0;
+    slot = -1;
+    if (k < 0 || k >= n_items) return;
+    int r, b, e, sl;
+    if (work) {
+      r = ld_uniform(work, 4 * size_t(k));
+      b = ld_uniform(work, 4 * size_t(k) + 1);
+      e = ld_uniform(work, 4 * size_t(k) + 2);
+      sl = ld_uniform(work, 4 * size_t(k) + 3);
+    } else {
+      r = k;
+      b = ld_uniform(row_ptr, k);
+      e = ld_uniform(row_ptr, k + 1);
+      sl = -1;
+    }
+    if (r < 0 || r >= n_rows) return;
+    b = min(max(b, 0), nnz);
+    e = min(max(e, b), nnz);
+    row = r;
+    c0 = b;
+    cnt = e - b;
+    slot = sl;
+  };
+
+  // Source offsets of the chunks that land at this lane's swizzled LDS
+  // positions in segments 0 and 1 (relative to their segment).
+  uint32_t ve, vo;
+  {
+    const int r0 = lane >> 3, p = lane & 7;
+    ve = uint32_t(r0) * W::ROWB + uint32_t((p ^ chunk_swizzle<W::ROWB>(r0)) << 4);
+    vo = uint32_t(r0) * W::ROWB + uint32_t((p ^ chunk_swizzle<W::ROWB>(8 + r0)) << 4);
+  }
+
+  // Buffer descriptor over head bh of tensor T (an empty range when row < 0).
+  auto head_desc = [&](const uint16_t* T, int row, int bh) -> v4i {
+    v4i d = make_desc(T + size_t(bh) * size_t(N) * HD, row >= 0 ? head_bytes : 0u);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) d[w] = __builtin_amdgcn_readfirstlane(d[w]);
+    return d;
+  };
+
+  // This wave's half of the query tile of CSR row `row` into the staging area.
+  // q_newest: no tile load has been issued since (the epilogue's wait for the
+  // staged tile must then not leave the newest loads in flight).
+  bool q_newest = false;
+  auto stage_q = [&](int row, int bh) {
+    if (row < 0) return;
+    q_newest = true;
+    const int qb = row - bh * nb;
+    const uint32_t tb = uint32_t(qb) * (BLK * W::ROWB) + uint32_t(kh) * W::HALFB;
+    dma_half(head_desc(Q, row, bh), ve + tb, vo + tb, qarea + uint32_t(kh) * W::HALFB);
+  };
+  // Query fragments (B operand of S^T = K Q^T) from the staging area: lane
+  // holds d = 16c + 8hh .. +7 of query row 32g + ql.
+  auto read_q = [&](bf16x8 (&qf)[2][4]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qf[g][c] = lds_read16(qarea + swz<W::ROWB>(32 * g + ql, 2 * c + hh));
+  };
+
+  // ---- item source --------------------------------------------------------
+  ItemSource src;
+  src.init(work, n_items, n_merges, n_rows);
+  const bool queue = work != nullptr;
+  int k_cur = src.stat(0), k_nxt = src.stat(1);
+  int round = 2;           // static round of the item after next (no work list)
+  bool claim_out = false;  // a claim for the item after next is in flight
+  int ticket = -1;         // its claim number, in lane 0 of wave 0
+  if (k_cur < 0) return;
+  claim_out = queue && k_nxt >= 0;
+  if (claim_out && kh == 0 && lane == 0) ticket = src.claim(ctr);
+
+  // The claimed item after next, resolved by wave 0 one step before the
+  // current item ends and published to wave 1 in the epilogue.
+  bool nn_known = false;
+  int nn_k = -1, nn_row = -1, nn_c0 = 0, nn_cnt = 0, nn_slot = -1;
+
+  // ---- stream state -------------------------------------------------------
+  int cur_row, cur_c0, cur_cnt, cur_slot, nxt_row, nxt_c0, nxt_cnt, nxt_slot;
+  load_item(k_cur, cur_row, cur_c0, cur_cnt, cur_slot);
+  load_item(k_nxt, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+  int cur_bh = cur_row >= 0 ? head_of(cur_row) : 0;
+  int nxt_bh = nxt_row >= 0 ? head_of(nxt_row) : 0;
+  v4i kd_cur = head_desc(K, cur_row, cur_bh), vd_cur = head_desc(V, cur_row, cur_bh);
+  v4i kd_nxt = head_desc(K, nxt_row, nxt_bh), vd_nxt = head_desc(V, nxt_row, nxt_bh);
+  // Wave 0: read the claim for the item after next and start loading its
+  // record.  Called where the only load in flight is the tile about to be
+  // used, so the wait for the claim costs nothing extra.
+  auto resolve_claim = [&]() {
+    const int t = __builtin_amdgcn_readfirstlane(ticket);
+    nn_k = src.claimed(t);
+    if (lane == 0) src.retire(ctr, t);
+    nn_known = true;
+    load_item(nn_k, nn_row, nn_c0, nn_cnt, nn_slot);
+  };
+
+  // Column position of stream tile p (counted from the current item's first
+  // tile), or -1 past the next item.
+  auto stream_src = [&](int p, bool& in_next) -> int {
+    in_next = p >= cur_cnt;
+    const int pn = p - cur_cnt;
+    return !in_next ? cur_c0 + p : (pn < nxt_cnt ? nxt_c0 + pn : -1);
+  };
+
+  int st_cur = 0;     // ring stage of the tile being computed
+  int pending = 0;    // tiles issued beyond the current one (0 or 1)
+  int pf = 0;         // stream position of the next tile to issue
+  int valid_pf = 0;   // valid keys of the prefetched tile
+  // Issue stream tile `pf` (column j) into stage st; returns its valid key count.
+  auto issue = [&](int j, bool in_next, int st) -> int {
+    const bool ok = j >= 0 && j < nb;
+    const uint32_t tb = ok ? uint32_t(j) * (BLK * W::ROWB) + uint32_t(kh) * W::HALFB : head_bytes;
+    const uint32_t dst = ring + uint32_t(st) * W::STAGEB;
+    dma_half(in_next ? kd_nxt : kd_cur, ve + tb, vo + tb, dst);
+    dma_half(in_next ? vd_nxt : vd_cur, ve + tb, vo + tb, dst + W::HALFB);
+    q_newest = false;
+    ++pf;
+    return ok ? min(BLK, N - j * BLK) : 0;
+  };
+
+  // Start-up: the first query tile and the first K/V tile load together.
+  bf16x8 qf[2][4];
+  stage_q(cur_row, cur_bh);
+  int valid_cur = 0;
+  {
+    bool in_next;
+    const int src = stream_src(0, in_next);
+    if (src >= 0) {
+      valid_cur = issue(ld_uniform(col_idx, src), in_next, 0);
+      pending = 1;  // counts the current tile until the loop takes it
+    }
+  }
+  if (pending)
+    wait_vm(8);
+  else
+    wait_vm(0);
+  lds_barrier();
+  read_q(qf);
+  lds_barrier();
+  stage_q(nxt_row, nxt_bh);
+  // Column of stream tile `pf`, looked up one step before it is issued.
+  int j_pf = 0;
+  bool has_pf = false, pf_next = false;
+  auto lookup = [&]() {
+    const int src = stream_src(pf, pf_next);
+    has_pf = src >= 0;
+    j_pf = has_pf ? ld_uniform(col_idx, src) : 0;
+  };
+  lookup();
+
+  for (;;) {
+    // ---- one item ---------------------------------------------------------
+    float m_run[2] = {-INFINITY, -INFINITY};  // running max of scale*log2(e)*s
+    float l_run[2] = {0.f, 0.f};              // lane-partial running sums
+    f32x16 acc[2][2];                          // [query group][d half]
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][u][i] = 0.f;
+
+    for (int u = 0; u < cur_cnt; ++u) {
+      // Tile u was issued one step ago (or at the item transition).  Issue the
+      // next stream tile into the other stage, which this wave finished
+      // reading in the previous step, then wait for tile u only.
+      if (queue && kh == 0 && claim_out && !nn_known && u == cur_cnt - 1) resolve_claim();
+      pending = 0;
+      if (has_pf) {
+        valid_pf = issue(j_pf, pf_next, st_cur ^ 1);
+        pending = 1;
+        lookup();
+        wait_vm(8);
+      } else {
+        wait_vm(0);
+      }
+      const uint32_t ks = ring + uint32_t(st_cur) * W::STAGEB;
+      const uint32_t vs = ks + W::HALFB;
+
+      // S^T tiles: lane (ql, hh) holds keys 8(i/4) + 4hh + (i%4) (of this
+      // half) of query 32g + ql.
+      const f32x16 zero = {};
+      f32x16 s[2];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 a = lds_read16(ks + swz<W::ROWB>(ql, 2 * c + hh));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          s[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][c], c == 0 ? zero : s[g], 0, 0,
+                                                         0);
+      }
+      if (__builtin_expect(valid_cur < BLK, 0)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kv = 32 * kh + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (kv >= valid_cur) {
+            s[0][i] = -INFINITY;
+            s[1][i] = -INFINITY;
+          }
+        }
+      }
+      // Lazy rescale: only when some row's max grew by more than the slack;
+      // a row's first finite max is adopted without touching its zero state.
+      float mt[2];
+      bool need[2], rescale[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float mx = s[g][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[g][i]);
+        mx = fmaxf(mx, other_half(mx));
+        mt[g] = mx * sl2;
+        need[g] = mt[g] > m_run[g] + kRescaleSlack;
+        rescale[g] = need[g] && m_run[g] != -INFINITY;
+      }
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(rescale[0] || rescale[1]) != 0, 0)) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float alpha = rescale[g] ? __builtin_amdgcn_exp2f(m_run[g] - mt[g]) : 1.f;
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[g][u2][i] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) m_run[g] = need[g] ? mt[g] : m_run[g];
+
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float m_use = (m_run[g] == -INFINITY) ? 0.f : m_run[g];
+        float ls[4];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[g][i], sl2, -m_use));
+          if (i < 4)
+            ls[i] = p;
+          else
+            ls[i & 3] += p;
+          pb[g][i >> 3][i & 7] = static_cast<__bf16>(p);
+        }
+        l_run[g] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      }
+
+      // O^T += V^T P^T, one V^T operand (two transposing reads) per 16-key
+      // step and d half, shared by both query groups.
+      const int tr_row = 4 * hh + ((lane & 15) >> 2);
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+          const int col = 32 * u2 + tr_col;
+          const v4s lo = lds_read_tr(vs + swz<W::ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
+          const v4s hi =
+              lds_read_tr(vs + swz<W::ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
+          const bf16x8 a =
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            acc[g][u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][c2], acc[g][u2], 0, 0, 0);
+        }
+
+      st_cur ^= 1;
+      valid_cur = valid_pf;
+    }
+
+    // ---- epilogue -----------------------------------------------------------
+    // The next item's query tile: this wave's half is complete once only the
+    // prefetched tile may be outstanding, provided that tile was issued after
+    // the query tile (not so when an item without tiles follows start-up).
+    if (pending && !q_newest)
+      wait_vm(8);
+    else
+      wait_vm(0);
+    const bool more = k_nxt >= 0;
+    lds_barrier();  // both halves of the staged query tile are in LDS
+    if (more) read_q(qf);
+    float l_half[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) l_half[g] = l_run[g] + other_half(l_run[g]);
+    lds_barrier();  // the staging area is free for the exchange of m and l
+
+    // Wave kh finalises query group kh; it sends its state of group 1 - kh
+    // through its own last-computed stage, and m, l through the staging area.
+    // (Branches on kh keep every register array index a compile-time constant.)
+    const int st_free = st_cur ^ 1;
+    float* xml = reinterpret_cast<float*>(smem + 2 * size_t(W::RINGB));
+    auto send = [&](const f32x16 (&a)[2], float m, float l) {
+      float* xo = reinterpret_cast<float*>(smem + size_t(kh) * W::RINGB +
+                                           size_t(st_free) * W::STAGEB);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(xo + ((u * 4 + g4) * 64 + lane) * 4) =
+              f32x4{a[u][4 * g4], a[u][4 * g4 + 1], a[u][4 * g4 + 2], a[u][4 * g4 + 3]};
+      if (hh == 0) {
+        xml[kh * 64 + ql] = m;
+        xml[kh * 64 + 32 + ql] = l;
+      }
+    };
+    auto finish = [&](const f32x16 (&a)[2], float m0, float l0) {
+      const int go = 1 - kh;
+      const float* xi = reinterpret_cast<const float*>(smem + size_t(go) * W::RINGB +
+                                                       size_t(st_free) * W::STAGEB);
+      const float m1 = xml[go * 64 + ql];
+      const float l1 = xml[go * 64 + 32 + ql];
+      const float m = fmaxf(m0, m1);
+      const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      const float l = l0 * a0 + l1 * a1;
+      f32x16 o[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(xi + ((u * 4 + g4) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[u][4 * g4 + e] = a[u][4 * g4 + e] * a0 + o1[e] * a1;
+        }
+      const int bh = cur_bh;
+      const int q = kh * 32 + ql;
+      const int qrow = (cur_row - bh * nb) * BLK + q;
+      if (cur_row >= 0 && cur_slot >= 0) {
+        // Partial result of one chunk of a cut row (unnormalised acc, max in
+        // log2 units, sum), combined with the row's other chunks by merge_kernel.
+        float* po = part + size_t(cur_slot) * BLK * (HD + 2);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f32x4*>(po + q * HD + 32 * u + 8 * g4 + 4 * hh) =
+                f32x4{o[u][4 * g4], o[u][4 * g4 + 1], o[u][4 * g4 + 2], o[u][4 * g4 + 3]};
+        if (hh == 0) {
+          po[BLK * HD + q] = m;
+          po[BLK * HD + BLK + q] = l;
+        }
+      } else if (cur_row >= 0 && qrow < N) {
+        const size_t head = size_t(bh) * size_t(N) * HD;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* orow = O + head + size_t(qrow) * HD;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * u + 8 * g4 + 4 * hh;
+            const uint32_t w0 = pack_bf16x2(o[u][4 * g4 + 0] * inv, o[u][4 * g4 + 1] * inv);
+            const uint32_t w1 = pack_bf16x2(o[u][4 * g4 + 2] * inv, o[u][4 * g4 + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+          }
+        if (hh == 0 && LSE != nullptr)
+          LSE[size_t(bh) * N + qrow] =
+              l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+      }
+    };
+    if (kh == 0)
+      send(acc[1], m_run[1], l_half[1]);
+    else
+      send(acc[0], m_run[0], l_half[0]);
+    // The item after next: the claim made one item ago (work list; wave 0
+    // publishes its record through the staging area) or the next static round.
+    int* xk = reinterpret_cast<int*>(xml + 128);
+    if (queue && kh == 0) {
+      if (claim_out && !nn_known) resolve_claim();  // an item without tiles
+      if (lane == 0) {
+        xk[0] = nn_k;
+        xk[1] = nn_row;
+        xk[2] = nn_c0;
+        xk[3] = nn_cnt;
+        xk[4] = nn_slot;
+      }
+    }
+    lds_barrier();
+    int k_nn;
+    if (queue) {
+      k_nn = xk[0];
+      nn_row = xk[1];
+      nn_c0 = xk[2];
+      nn_cnt = xk[3];
+      nn_slot = xk[4];
+    } else {
+      k_nn = src.stat(round);
+    }
+    if (kh == 0)
+      finish(acc[0], m_run[0], l_half[0]);
+    else
+      finish(acc[1], m_run[1], l_half[1]);
+    lds_barrier();  // exchange areas free before loads target them again
+
+    // ---- advance to the next item ------------------------------------------
+    k_cur = k_nxt;
+    k_nxt = k_nn;
+    ++round;
+    if (k_cur < 0) break;
+    pf -= cur_cnt;
+    cur_row = nxt_row;
+    cur_c0 = nxt_c0;
+    cur_cnt = nxt_cnt;
+    cur_slot = nxt_slot;
+    cur_bh = nxt_bh;
+    kd_cur = kd_nxt;
+    vd_cur = vd_nxt;
+    if (queue) {
+      nxt_row = nn_row;
+      nxt_c0 = nn_c0;
+      nxt_cnt = nn_cnt;
+      nxt_slot = nn_slot;
+    } else {
+      load_item(k_nxt, nxt_row, nxt_c0, nxt_cnt, nxt_slot);
+    }
+    nxt_bh = nxt_row >= 0 ? head_of(nxt_row) : 0;
+    claim_out = queue && k_nxt >= 0;
+    nn_known = false;
+    nn_k = -1;
+    nn_row = -1;
+    nn_c0 = nn_cnt = 0;
+    nn_slot = -1;
+    if (claim_out && kh == 0 && lane == 0) ticket = src.claim(ctr);
+    kd_nxt = head_desc(K, nxt_row, nxt_bh);
+    vd_nxt = head_desc(V, nxt_row, nxt_bh);
+    stage_q(nxt_row, nxt_bh);
+    // The prefetched column was looked up before the next item was known.
+    lookup();
+    if (!pending && cur_cnt > 0) {
+      // Nothing was prefetched for the new item (its predecessor had no tile
+      // to look ahead to): issue its first tile now.
+      valid_cur = issue(j_pf, pf_next, st_cur);
+      lookup();
+    }
   }
   wait_vm(0);  // no load may still target LDS when the workgroup retires
 }
@@ -620,11 +1239,71 @@ int resident_workgroups() {
   return n;
 }
 
+// Workgroups to launch for `items` items with `resident` resident slots.  With
+// a work list every group needs at least one workgroup, so the grid never
+// drops below BSA_MAX_GROUPS (workgroups without an item leave at once).
+int32_t launch_grid(int32_t items, int resident, bool queued) {
+  if (items <= 0) return 0;
+  int32_t g = items < resident ? items : resident;
+  if (queued && g < BSA_MAX_GROUPS) g = BSA_MAX_GROUPS;
+  return g;
+}
+
+int resident_wide_workgroups() {
+  static std::once_flag once;
+  static int n = 0;
+  std::call_once(once, [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&fwd_wide_kernel), Wide::NT,
+            Wide::LDS_BYTES) != hipSuccess)
+      return;
+    n = cus * (per_cu > 0 ? per_cu : 1);
+  });
+  return n;
+}
+
+bsa_status launch_wide(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
+                       int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                       const int32_t* work, int32_t n_items, int32_t n_merges, float sl2, void* o,
+                       float* lse, float* part, int32_t* ctr, hipStream_t stream) {
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_wide_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(Wide::LDS_BYTES));
+  });
+  if (attr != hipSuccess) return BSA_ERR_HIP;
+  const int32_t items = work ? n_items : n_rows;
+  const int resident = resident_wide_workgroups();
+  if (resident <= 0) return BSA_ERR_HIP;
+  const int32_t grid = launch_grid(items, resident, work != nullptr);
+  if (grid > 0) {
+    hipLaunchKernelGGL(fwd_wide_kernel, dim3(grid), dim3(Wide::NT), Wide::LDS_BYTES, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, n_merges,
+                       N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr);
+    BSA_HIP_CHECK_LAUNCH();
+  }
+  if (work && n_merges > 0) {
+    constexpr int wg_per_row = 64 * (64 / 4) / kMergeThreads;
+    hipLaunchKernelGGL((merge_kernel<64, 64>), dim3(n_merges * wg_per_row), dim3(kMergeThreads),
+                       0, stream, work + 4 * size_t(n_items), part, N, nb, n_rows,
+                       static_cast<uint16_t*>(o), lse);
+    BSA_HIP_CHECK_LAUNCH();
+  }
+  return BSA_OK;
+}
+
 template <int BLK, int HD>
 bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
                       int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
                       const int32_t* work, int32_t n_items, int32_t n_merges, float sl2, void* o,
-                      float* lse, float* part, hipStream_t stream) {
+                      float* lse, float* part, int32_t* ctr, hipStream_t stream) {
   using C = FwdCfg<BLK, HD>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
@@ -637,12 +1316,12 @@ bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, in
   const int32_t items = work ? n_items : n_rows;
   const int resident = resident_workgroups<BLK, HD>();
   if (resident <= 0) return BSA_ERR_HIP;
-  const int32_t grid = items < resident ? items : resident;
+  const int32_t grid = launch_grid(items, resident, work != nullptr);
   if (grid > 0) {
     hipLaunchKernelGGL((fwd_kernel<BLK, HD>), dim3(grid), dim3(C::NT), C::LDS_BYTES, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, N, nb,
-                       n_rows, sl2, static_cast<uint16_t*>(o), lse, part);
+                       static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, n_merges,
+                       N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr);
     BSA_HIP_CHECK_LAUNCH();
   }
   if (work && n_merges > 0) {
@@ -662,7 +1341,7 @@ bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, in
 extern "C" BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D,
                                                       int32_t block) {
   if (n_slots < 0 || D < 1 || block < 1) return 0;
-  return size_t(n_slots) * size_t(block) * size_t(D + 2) * sizeof(float);
+  return bsa::kCounterBytes + size_t(n_slots) * size_t(block) * size_t(D + 2) * sizeof(float);
 }
 
 extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v,
@@ -688,22 +1367,22 @@ extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const vo
   if (work_dev) {
     if (!aligned16(work_dev) || n_items < 0 || n_merges < 0 || n_slots < 0)
       return BSA_ERR_INVALID_ARG;
-    if (n_merges > 0) {
-      if (!workspace || !aligned16(workspace)) return BSA_ERR_INVALID_ARG;
-      if (workspace_bytes < bsa_forward_workspace_bytes(n_slots, D, block))
-        return BSA_ERR_CAPACITY;
-    }
+    if (!workspace || !aligned16(workspace)) return BSA_ERR_INVALID_ARG;
+    if (workspace_bytes < bsa_forward_workspace_bytes(n_slots, D, block)) return BSA_ERR_CAPACITY;
   } else {
     n_items = n_merges = 0;
   }
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
   const float sl2 = sc * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* part = static_cast<float*>(workspace);
+  int32_t* ctr = work_dev ? static_cast<int32_t*>(workspace) : nullptr;
+  float* part = work_dev ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                    kCounterBytes)
+                         : nullptr;
 #define BSA_FWD_ARGS                                                                            \
   q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items, n_merges, sl2, o, lse, \
-      part, s
-  if (block == 64 && D == 64) return launch_fwd<64, 64>(BSA_FWD_ARGS);
+      part, ctr, s
+  if (block == 64 && D == 64) return launch_wide(BSA_FWD_ARGS);
   if (block == 64 && D == 128) return launch_fwd<64, 128>(BSA_FWD_ARGS);
   if (block == 128 && D == 64) return launch_fwd<128, 64>(BSA_FWD_ARGS);
   return launch_fwd<128, 128>(BSA_FWD_ARGS);

@@ -74,9 +74,10 @@ extern "C" BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, do
 
 extern "C" BSA_API int64_t bsa_work_plan_ints(int32_t n_rows, int64_t nnz, int32_t max_tiles) {
   if (n_rows < 1 || nnz < 0) return -1;
-  // Cutting a row of length L into ceil(L/T) chunks adds at most L/T items.
+  // Cutting a row of length L into ceil(L/T) chunks adds at most L/T items;
+  // the group table takes at most 2 + BSA_MAX_GROUPS ints.
   const int64_t extra = max_tiles > 0 ? nnz / max_tiles : 0;
-  return 4 * (int64_t(n_rows) + extra) + 3 * int64_t(n_rows);
+  return 4 * (int64_t(n_rows) + extra) + 3 * int64_t(n_rows) + 2 + BSA_MAX_GROUPS;
 }
 
 extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows,
@@ -86,6 +87,7 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
                                                  int32_t* n_slots) {
   if (!row_ptr || !work_out || !n_items || !n_merges || !n_slots || n_rows < 1)
     return BSA_ERR_INVALID_ARG;
+  if (n_groups < 0 || n_groups > BSA_MAX_GROUPS) return BSA_ERR_INVALID_ARG;
   struct Item { int32_t row, b, e, slot; };
   std::vector<Item> items;
   std::vector<int32_t> merges;
@@ -112,46 +114,44 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
       items.push_back({r, 0, len, -1});
     }
   }
-  const auto longer = [](const Item& a, const Item& b) { return a.e - a.b > b.e - b.b; };
-  std::vector<Item> out;
-  bool grouped = false;
-  if (n_groups > 1 && nb > 0) {
-    // Workgroup i runs on accelerator die (XCD) i % n_groups.  Give every die the
-    // heads h with h % n_groups == its index and walk them head by head (longest
-    // items of a head first), so each die's L2 holds the K/V of about one head
-    // at a time.  Used only when the groups come out equally long (no padding).
-    std::vector<std::vector<Item>> g(static_cast<size_t>(n_groups));
-    for (const Item& it : items) g[size_t((it.row / nb) % n_groups)].push_back(it);
-    bool equal = true;
-    for (const auto& x : g) equal = equal && x.size() == g[0].size();
-    if (equal && !g[0].empty()) {
-      for (auto& x : g)
-        std::stable_sort(x.begin(), x.end(), [nb, &longer](const Item& a, const Item& b) {
-          const int32_t ha = a.row / nb, hb = b.row / nb;
-          return ha != hb ? ha < hb : longer(a, b);
-        });
-      out.reserve(items.size());
-      for (size_t k = 0; k < g[0].size(); ++k)
-        for (int32_t q = 0; q < n_groups; ++q) out.push_back(g[size_t(q)][k]);
-      grouped = true;
+  // Groups: head h = row / nb goes to group h % n_groups (the die whose
+  // workgroups serve that group; workgroup i runs on die i % n_groups).  Inside
+  // a group the chunks of cut rows (the largest items) come first, then the
+  // whole rows; each class head by head with a head's longest items first.
+  // Heads in order keep the die's L2 on the K/V of about one head at a time;
+  // big items first leave small ones for the end, where the workgroups that
+  // finish early claim them.
+  const int32_t ng = (nb > 0 && n_groups > 1) ? n_groups : 1;
+  std::vector<std::vector<Item>> g(static_cast<size_t>(ng));
+  for (const Item& it : items) g[ng > 1 ? size_t((it.row / nb) % ng) : 0].push_back(it);
+  for (auto& x : g)
+    std::stable_sort(x.begin(), x.end(), [nb](const Item& a, const Item& b) {
+      const bool ca = a.slot >= 0, cb = b.slot >= 0;
+      if (ca != cb) return ca;
+      const int32_t ha = nb > 0 ? a.row / nb : 0, hb = nb > 0 ? b.row / nb : 0;
+      return ha != hb ? ha < hb : a.e - a.b > b.e - b.b;
+    });
+  const int64_t need = 4 * int64_t(items.size()) + int64_t(merges.size()) + 2 + ng;
+  if (need > capacity) return BSA_ERR_CAPACITY;
+  size_t k = 0;
+  std::vector<int32_t> table;
+  table.push_back(ng);
+  for (const auto& x : g) {
+    table.push_back(static_cast<int32_t>(k));
+    for (const Item& it : x) {
+      // Column positions are absolute indices into col_idx.
+      const int32_t base = row_ptr[it.row];
+      work_out[4 * k + 0] = it.row;
+      work_out[4 * k + 1] = base + it.b;
+      work_out[4 * k + 2] = base + it.e;
+      work_out[4 * k + 3] = it.slot;
+      ++k;
     }
   }
-  if (!grouped) {
-    out = items;
-    std::stable_sort(out.begin(), out.end(), longer);  // longest first
-  }
-  const int64_t need = 4 * int64_t(out.size()) + int64_t(merges.size());
-  if (need > capacity) return BSA_ERR_CAPACITY;
-  for (size_t k = 0; k < out.size(); ++k) {
-    // Column positions are absolute indices into col_idx.
-    const int32_t base = row_ptr[out[k].row];
-    work_out[4 * k + 0] = out[k].row;
-    work_out[4 * k + 1] = base + out[k].b;
-    work_out[4 * k + 2] = base + out[k].e;
-    work_out[4 * k + 3] = out[k].slot;
-  }
-  memcpy(work_out + 4 * out.size(), merges.data(), merges.size() * sizeof(int32_t));
-  *n_items = static_cast<int32_t>(out.size());
+  table.push_back(static_cast<int32_t>(k));
+  memcpy(work_out + 4 * k, merges.data(), merges.size() * sizeof(int32_t));
+  memcpy(work_out + 4 * k + merges.size(), table.data(), table.size() * sizeof(int32_t));
+  *n_items = static_cast<int32_t>(k);
   *n_merges = static_cast<int32_t>(merges.size() / 3);
   *n_slots = slots;
   return BSA_OK;

@@ -8,8 +8,8 @@
 //
 // One workgroup of 1024 threads: LDS histogram by (max_len - length), a
 // two-level exclusive scan, then an atomic scatter of {row, begin, end, -1}
-// work items (no row is cut).  Rows of equal length come out in an
-// unspecified order; the forward's results do not depend on it.
+// work items (no row is cut), then a one-group table.  Rows of equal length
+// come out in an unspecified order; the forward's results do not depend on it.
 #include "common.h"
 
 namespace bsa {
@@ -58,6 +58,12 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __r
     const int full = max(row_ptr[r + 1] - b, 0);
     const int pos = atomicAdd(&bins[max_len - min(full, max_len)], 1);
     *reinterpret_cast<int4*>(work + 4 * size_t(pos)) = make_int4(r, b, b + full, -1);
+  }
+  if (tid == 0) {
+    // Group table: one group holding every item.
+    work[4 * size_t(n_rows) + 0] = 1;
+    work[4 * size_t(n_rows) + 1] = 0;
+    work[4 * size_t(n_rows) + 2] = n_rows;
   }
 }
 

@@ -51,7 +51,10 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2
+
+/* Largest number of item groups a work list may have (see bsa_work_plan_host). */
+#define BSA_MAX_GROUPS 64
 BSA_API int32_t bsa_abi_version(void);
 
 /* ---------------------------------------------------------------- host plan */
@@ -96,23 +99,30 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
  * max_tiles blocks (max_tiles <= 0: rows are never cut); the chunks of a cut
  * row write fp32 partial results to the forward's workspace and a second
  * kernel merges them.
- * Order: with n_groups > 1 (the number of accelerator dies, XCDs, whose L2
- * caches are separate), item k is meant for die k % n_groups, which gets the
- * heads h = row / nb with h % n_groups equal to its index, walked head by head
- * with each head's longest items first; this needs every die to get the same
- * number of items, otherwise (or with n_groups <= 1) all items are simply
- * ordered longest first.  Ties keep ascending row, then chunk.
+ * Groups and order: the items are split into n_groups groups (n_groups <= 1:
+ * one group; at most BSA_MAX_GROUPS), meant for the accelerator dies (XCDs),
+ * whose L2 caches are separate: workgroup i of the forward runs on die
+ * i % n_groups and serves group i % n_groups.  Group g holds the heads
+ * h = row / nb with h % n_groups == g.  Inside a group the chunks of cut rows
+ * come first, then the whole rows; each class head by head, each head's
+ * longest items first; ties keep ascending row, then chunk.
+ * The forward's workgroups take the items of their group in that order (the
+ * first two rounds statically, the rest from a per-group counter), so the
+ * order is the dispatch order within a group.
  *   row_ptr   int32 [n_rows + 1] host copy of the CSR row pointer.
  *   nb        blocks per head (rows of one head are consecutive).
  *   work_out  int32 [capacity], written: n_items records {row, col_begin,
  *             col_end, slot}: the item covers col_idx[col_begin, col_end) of
  *             CSR row `row` (absolute positions; slot = -1: the item covers
- *             the whole row and writes O directly), then n_merges records
- *             {row, first_slot, n_chunks}.
+ *             the whole row and writes O directly), grouped as above; then
+ *             n_merges records {row, first_slot, n_chunks}; then the group
+ *             table {G, s_0, s_1, ..., s_G}: G groups, group g being items
+ *             [s_g, s_(g+1)) (s_0 = 0, s_G = n_items).  The list takes
+ *             4 n_items + 3 n_merges + G + 2 ints.
  *   capacity  >= bsa_work_plan_ints(n_rows, nnz, max_tiles) int32 entries.
  *   n_items, n_merges, n_slots  written (n_slots = partial slots used).
- * Errors: INVALID_ARG for a NULL pointer, n_rows < 1 or a decreasing row_ptr;
- * CAPACITY if capacity is too small.
+ * Errors: INVALID_ARG for a NULL pointer, n_rows < 1, a decreasing row_ptr or
+ * n_groups outside [0, BSA_MAX_GROUPS]; CAPACITY if capacity is too small.
  */
 BSA_API int64_t bsa_work_plan_ints(int32_t n_rows, int64_t nnz, int32_t max_tiles);
 BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows, int32_t nb,
@@ -179,19 +189,21 @@ BSA_API bsa_status bsa_build_mask_status(const void* workspace, void* stream,
 /*
  * Longest-row-first work list built on the device (async), for a CSR whose
  * row lengths the host does not hold: the work_dev layout of
- * bsa_work_plan_host with no row cut (n_items = n_rows, n_merges = 0, every
- * item {row, row_ptr[row], row_ptr[row + 1], -1}),
- * produced by a counting sort of the rows by length, longest first (order
- * among equal lengths unspecified; results do not depend on it).
- *   row_ptr_dev int32 [n_rows+1]; work_dev int32 [4*n_rows] written;
+ * bsa_work_plan_host with one group and no row cut (n_items = n_rows,
+ * n_merges = 0, every item {row, row_ptr[row], row_ptr[row + 1], -1}, then
+ * the group table {1, 0, n_rows}), produced by a counting sort of the rows by
+ * length, longest first (order among equal lengths unspecified; results do
+ * not depend on it).
+ *   row_ptr_dev int32 [n_rows+1]; work_dev int32 [4*n_rows + 3] written;
  *   max_len >= every row length (e.g. nb); at most 8191.
  */
 BSA_API bsa_status bsa_schedule(const int32_t* row_ptr_dev, int32_t n_rows, int32_t max_len,
                                 int32_t* work_dev, void* stream);
 
 /*
- * Bytes of device workspace bsa_forward needs for n_slots partial results
- * (fp32 O [block x D] plus running max and sum per query row, per slot).
+ * Bytes of device workspace bsa_forward needs with a work list: 256 KiB of
+ * item counters (one int32 per group, 4 KiB apart), then n_slots partial
+ * results (fp32 O [block x D] plus running max and sum per query row, per slot).
  */
 BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D, int32_t block);
 
@@ -212,15 +224,23 @@ BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D, int32_t b
  *               bsa_schedule) with n_items items and n_merges merges, or NULL
  *               for one item per row in natural order (n_items, n_merges
  *               ignored).  Every row must be covered exactly once; column
- *               ranges are clamped to [0, nnz].  Workgroups stay resident and
- *               each runs items blockIdx, blockIdx + G, ... (G = resident
- *               workgroups), so the order of the list is the launch order.
- *   workspace   >= bsa_forward_workspace_bytes(n_slots, D, block) bytes of
- *               device memory when the work list cuts rows (n_merges > 0),
- *               else may be NULL; contents need no initialisation.
+ *               ranges are clamped to [0, nnz].  Workgroups stay resident:
+ *               without a list, workgroup w runs rows w, w + G, ... (G =
+ *               workgroups launched); with one, workgroup w serves group
+ *               w % n_groups, runs that group's items w / n_groups and
+ *               w / n_groups + G_g (G_g = its group's workgroups) and then
+ *               claims the group's remaining items in list order from a
+ *               counter in the workspace.
+ *   workspace   with a work list: >= bsa_forward_workspace_bytes(n_slots, D,
+ *               block) bytes of device memory, 16-byte aligned, whose first
+ *               256 KiB (the counters) are zero before the first call; every
+ *               call that completes leaves them zero again, so calls that use
+ *               one workspace must be ordered on one stream.  Without a list
+ *               it may be NULL.  The rest needs no initialisation.
  *   scale       softmax scale; <= 0 means 1/sqrt(D).
  * A row with no active block yields O = 0 and LSE = -inf.
- * Errors: INVALID_ARG, UNSUPPORTED, CAPACITY (workspace too small), HIP.
+ * Errors: INVALID_ARG (also a work list without a workspace), UNSUPPORTED,
+ * CAPACITY (workspace too small), HIP.
  */
 BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t B,
                                int32_t H, int32_t N, int32_t D, int32_t block,

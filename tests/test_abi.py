@@ -33,7 +33,7 @@ def test_status_strings_and_version():
     assert bsa.status_string(-1) == "BSA_ERR_INVALID_ARG"
     assert bsa.status_string(-5) == "BSA_ERR_PLAN_MISMATCH"
     assert bsa.status_string(-99) == "BSA_ERR_UNKNOWN"
-    assert bsa.abi_version() == 1
+    assert bsa.abi_version() == bsa.ABI_VERSION == 2
 
 
 def test_budget_matches_oracle():
@@ -71,15 +71,31 @@ def test_mask_plan_workload_totals():
     assert nnz == 24 * 3125
 
 
-def check_work(work, ni, nm, ns, rp, max_tiles):
-    """Every row covered exactly once, chunks <= max_tiles, longest first, merges consistent."""
+def check_work(work, ni, nm, ns, rp, max_tiles, nb=0, n_groups=1):
+    """Every row covered exactly once, chunks <= max_tiles, merges consistent, and the
+    group table: group g holds the heads h % G == g, head by head, longest items first."""
     lens = np.diff(rp)
     items = work[:4 * ni].reshape(ni, 4).copy()
     items[:, 1] -= rp[items[:, 0]]          # absolute column positions -> positions in the row
     items[:, 2] -= rp[items[:, 0]]
     merges = work[4 * ni:4 * ni + 3 * nm].reshape(nm, 3)
+    table = work[4 * ni + 3 * nm:]
+    G = int(table[0])
+    assert G == (n_groups if nb > 0 and n_groups > 1 else 1) and len(table) == G + 2
+    starts = table[1:]
+    assert starts[0] == 0 and starts[-1] == ni and (np.diff(starts) >= 0).all()
     sizes = items[:, 2] - items[:, 1]
-    assert (np.diff(sizes) <= 0).all()
+    heads = items[:, 0] // nb if nb > 0 else np.zeros(ni, np.int64)
+    cut_item = items[:, 3] >= 0
+    for g in range(G):
+        a, b = starts[g], starts[g + 1]
+        c = cut_item[a:b]
+        assert (np.diff(c.astype(int)) <= 0).all()          # chunks of cut rows first
+        for cls in (True, False):
+            h, sz = heads[a:b][c == cls], sizes[a:b][c == cls]
+            assert (h % G == g).all() and (np.diff(h) >= 0).all()
+            for hv in np.unique(h):
+                assert (np.diff(sz[h == hv]) <= 0).all()
     cover = {}
     for row, b, e, slot in items.tolist():
         cover.setdefault(row, []).append((b, e, slot))
@@ -112,34 +128,24 @@ def test_work_plan(max_tiles):
         assert nm == 0 and ni == 300
 
 
-@pytest.mark.parametrize("n_groups", [2, 8])
-def test_work_plan_grouped_by_head(n_groups):
-    """Item k belongs to a head h with h % n_groups == k % n_groups; heads walked in order."""
-    rng = np.random.default_rng(n_groups)
-    nb, n_heads = 10, 16
-    lens = np.tile(rng.integers(0, 25, nb), n_heads)     # one row profile shared by all heads
+@pytest.mark.parametrize("n_groups,n_heads", [(2, 16), (8, 16), (8, 13), (3, 2)])
+def test_work_plan_grouped_by_head(n_groups, n_heads):
+    """Group g holds the heads h % n_groups == g, walked head by head, longest first."""
+    rng = np.random.default_rng(n_groups * 100 + n_heads)
+    nb = 10
+    lens = rng.integers(0, 25, nb * n_heads)
     rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     work, ni, nm, ns = bsa.work_plan(rp, 7, nb, n_groups)
-    items = work[:4 * ni].reshape(ni, 4)
-    heads = items[:, 0] // nb
-    assert (heads % n_groups == np.arange(ni) % n_groups).all()
-    for g in range(n_groups):
-        h = heads[g::n_groups]
-        assert (np.diff(h) >= 0).all()
-        sz = (items[g::n_groups, 2] - items[g::n_groups, 1])
-        for hh in np.unique(h):
-            assert (np.diff(sz[h == hh]) <= 0).all()
-    # coverage and chunking are unchanged by the order
-    lens_sorted_items = work.copy()
-    order = np.argsort(-(items[:, 2] - items[:, 1]), kind="stable")
-    lens_sorted_items[:4 * ni] = items[order].reshape(-1)
-    check_work(lens_sorted_items, ni, nm, ns, rp, 7)
+    check_work(work, ni, nm, ns, rp, 7, nb, n_groups)
 
 
-def test_work_plan_unequal_groups_fall_back_to_longest_first():
+def test_work_plan_groups_may_be_empty():
     rp = np.array([0, 3, 5, 9], np.int32)    # one head of 3 rows, 8 groups
     work, ni, nm, ns = bsa.work_plan(rp, 0, 3, 8)
     assert work[:4 * ni].reshape(ni, 4)[:, 0].tolist() == [2, 0, 1]
+    assert work[4 * ni:].tolist() == [8, 0, 3, 3, 3, 3, 3, 3, 3, 3]
+    with pytest.raises(bsa.BsaError):
+        bsa.work_plan(rp, 0, 3, 65)        # more groups than the forward supports
 
 
 def test_work_plan_t2i_text_rows_are_cut():
@@ -171,7 +177,8 @@ def test_device_entry_points_reject_bad_arguments():
     assert L.bsa_forward(*args(blk=32)) == -2
     assert L.bsa_forward(*args(q=odd)) == -1
     assert L.bsa_forward(*args(N=0)) == -1
-    assert L.bsa_forward(*args(ws_bytes=16)) == -4       # 3 partial slots need more workspace
+    assert L.bsa_forward(*args(ws_bytes=16)) == -4       # counters + 3 partial slots need more
+    assert L.bsa_forward(*(args()[:17] + (None, 10 ** 6, None))) == -1   # a work list needs a workspace
     mk = lambda ws_bytes=0, D=64, N=128, ws=fake: L.bsa_build_mask(
         fake, fake, 1, 1, N, D, 64, 0.1, None, None, 0, 1, fake, fake, ws, ws_bytes, None)
     assert mk(ws=None) == -1
@@ -180,5 +187,6 @@ def test_device_entry_points_reject_bad_arguments():
     assert mk(ws_bytes=16) == -4                      # workspace too small
     assert L.bsa_schedule(None, 4, 4, fake, None) == -1
     assert L.bsa_schedule(fake, 4, 100000, fake, None) == -2
-    assert L.bsa_forward_workspace_bytes(3, 64, 64) == 3 * 64 * 66 * 4
+    assert L.bsa_forward_workspace_bytes(3, 64, 64) == 64 * 4096 + 3 * 64 * 66 * 4
+    assert L.bsa_forward_workspace_bytes(0, 64, 64) == 64 * 4096
     assert L.bsa_build_mask_workspace_bytes(1, 1, 128, 64, 64) >= 256 + 2 * 2 * 64 * 4 + 4 * 4

@@ -52,7 +52,8 @@ def test_full_config(name):
     print(f"attention on {len(rows)} rows: {stats}; work items {plan.work.n_items}, "
           f"cut rows {plan.work.n_merges} (max_tiles {plan.work.max_tiles})", flush=True)
     if plan.work.n_merges:
-        cut = plan.work.work.cpu().numpy()[4 * plan.work.n_items:].reshape(-1, 3)[:, 0]
+        ni, nm = plan.work.n_items, plan.work.n_merges
+        cut = plan.work.work.cpu().numpy()[4 * ni:4 * ni + 3 * nm].reshape(-1, 3)[:, 0]
         rows2 = sorted(set(cut[:6].tolist()))
         O2, L2 = OA.block_sparse_attention(q, k, v, plan.row_ptr_host, ci_h, w.block, w.scale,
                                            rows=rows2)

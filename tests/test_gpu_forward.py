@@ -136,7 +136,10 @@ def test_launch_order_and_invalid_columns():
     w_dev = bsa.schedule(torch.from_numpy(rp).cuda(), nb)
     o2, l2 = bsa.forward(q, k, v, rp, ci, block, work=w_dev)
     assert torch.equal(o0, o1) and torch.equal(o0, o2) and torch.equal(l0, l1) and torch.equal(l0, l2)
-    items = w_dev.work.cpu().numpy().reshape(-1, 4)
+    wk = w_dev.work.cpu().numpy()
+    n = B * H * nb
+    items = wk[:4 * n].reshape(-1, 4)
+    assert wk[4 * n:].tolist() == [1, 0, n]                 # one group holding every item
     lens = np.diff(rp)
     assert sorted(items[:, 0].tolist()) == list(range(B * H * nb))
     assert np.array_equal(items[:, 1], rp[items[:, 0]]) and (items[:, 3] == -1).all()
@@ -148,6 +151,29 @@ def test_launch_order_and_invalid_columns():
     ci2 = np.concatenate(rows).astype(np.int32)
     o3, l3 = bsa.forward(q, k, v, rp2, ci2, block)
     assert torch.equal(o0, o3) and torch.equal(l0, l3)
+
+
+@pytest.mark.parametrize("block,D,n_groups", [(64, 64, 8), (64, 64, 1), (64, 128, 8),
+                                               (128, 64, 3)])
+def test_item_queue_matches_static_order_and_resets(block, D, n_groups):
+    """Items claimed from the per-group counters give the same bits as the static row
+    order, call after call, and every call leaves the counters at zero.  The head count
+    makes the item count exceed two static rounds of resident workgroups."""
+    bsa = need_gpu()
+    print(f"case block={block} D={D} n_groups={n_groups}", flush=True)
+    rng = np.random.default_rng(block + D + n_groups)
+    B, H, nb = 1, 48, 50
+    N = nb * block - 5
+    rp, ci = rand_csr(rng, B, H, nb, 0.12, empty_rows=(7, 300))
+    work = bsa.Work.from_host(rp, D, block, 0, "cuda", nb=nb, n_groups=n_groups)
+    assert work.n_items == B * H * nb
+    for seed in (1, 2, 3):
+        q, k, v = (t.cuda() for t in W.gaussian_qkv(300 + seed, B, H, N, D))
+        o0, l0 = bsa.forward(q, k, v, rp, ci, block)
+        o1, l1 = bsa.forward(q, k, v, rp, ci, block, work=work)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+        assert int(work.workspace[:64 * 4096].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("block,D,max_tiles", [(64, 64, 1), (64, 64, 3), (64, 128, 2),
