@@ -241,6 +241,16 @@ struct ItemSource {
 // division, well inside fp32 and bf16 range.
 constexpr float kRescaleSlack = 8.0f;
 
+// Running-max start value of the wide kernel: finite, so that it can enter the
+// exponent argument directly (scores of -inf still give exp2 = 0), and far
+// below any score.
+constexpr float kNoMax = -1.0e30f;
+
+// IEEE maximum (NaN-propagating): lowers to v_maximum3_f32 chains with no
+// NaN-quieting copies in front, unlike fmaxf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+
 template <int BLK, int HD>
 __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -862,7 +872,7 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
 
   for (;;) {
     // ---- one item ---------------------------------------------------------
-    float m_run[2] = {-INFINITY, -INFINITY};  // running max of scale*log2(e)*s
+    float m_run[2] = {kNoMax, kNoMax};  // running max of scale*log2(e)*s
     float l_run[2] = {0.f, 0.f};              // lane-partial running sums
     f32x16 acc[2][2];                          // [query group][d half]
 #pragma unroll
@@ -889,18 +899,40 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       const uint32_t ks = ring + uint32_t(st_cur) * W::STAGEB;
       const uint32_t vs = ks + W::HALFB;
 
+      // All LDS reads of the tile are issued up front: the four K operands
+      // (one round trip instead of four) and the eight V^T halves, which then
+      // land while the softmax runs.  For the 16-key step c2, V^T rows
+      // d = 32u + (lane % 32) need keys 16c2 + 4hh + e and 16c2 + 8 + 4hh + e
+      // (e = 0..3): lane t of each 16-lane block points at key row t / 4 and
+      // columns 4 (t % 4) .. +3 of its block's 16 d values, and the
+      // transposing read returns to every lane the four keys of its own d.
+      bf16x8 ka[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ka[c] = lds_read16(ks + swz<W::ROWB>(ql, 2 * c + hh));
+      const int tr_row = 4 * hh + ((lane & 15) >> 2);
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      v4s vlo[2][2], vhi[2][2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+          const int col = 32 * u2 + tr_col;
+          vlo[c2][u2] = lds_read_tr(vs + swz<W::ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
+          vhi[c2][u2] =
+              lds_read_tr(vs + swz<W::ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+
       // S^T tiles: lane (ql, hh) holds keys 8(i/4) + 4hh + (i%4) (of this
       // half) of query 32g + ql.
       const f32x16 zero = {};
       f32x16 s[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = lds_read16(ks + swz<W::ROWB>(ql, 2 * c + hh));
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          s[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][c], c == 0 ? zero : s[g], 0, 0,
-                                                         0);
-      }
+          s[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s[g], 0,
+                                                         0, 0);
       if (__builtin_expect(valid_cur < BLK, 0)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -917,13 +949,16 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       bool need[2], rescale[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        float mx = s[g][0];
+        float mx = vmax(s[g][0], s[g][1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[g][i]);
-        mx = fmaxf(mx, other_half(mx));
+        for (int i = 2; i < 16; ++i) mx = vmax(mx, s[g][i]);
+        // The other half-wave holds the other 16 keys of the same queries.
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         mt[g] = mx * sl2;
         need[g] = mt[g] > m_run[g] + kRescaleSlack;
-        rescale[g] = need[g] && m_run[g] != -INFINITY;
+        rescale[g] = need[g] && m_run[g] != kNoMax;
       }
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(rescale[0] || rescale[1]) != 0, 0)) {
 #pragma unroll
@@ -939,14 +974,15 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
 #pragma unroll
       for (int g = 0; g < 2; ++g) m_run[g] = need[g] ? mt[g] : m_run[g];
 
+      // P in bf16 only as the MFMA operand; the row sums add the fp32 values,
+      // in four independent chains.
       bf16x8 pb[2][2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const float m_use = (m_run[g] == -INFINITY) ? 0.f : m_run[g];
         float ls[4];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[g][i], sl2, -m_use));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[g][i], sl2, -m_run[g]));
           if (i < 4)
             ls[i] = p;
           else
@@ -956,20 +992,14 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
         l_run[g] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       }
 
-      // O^T += V^T P^T, one V^T operand (two transposing reads) per 16-key
-      // step and d half, shared by both query groups.
-      const int tr_row = 4 * hh + ((lane & 15) >> 2);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      // O^T += V^T P^T, one V^T operand per 16-key step and d half, shared by
+      // both query groups.
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int u2 = 0; u2 < 2; ++u2) {
-          const int col = 32 * u2 + tr_col;
-          const v4s lo = lds_read_tr(vs + swz<W::ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
-          const v4s hi =
-              lds_read_tr(vs + swz<W::ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
-          const bf16x8 a =
-              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(vlo[c2][u2], vhi[c2][u2], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int g = 0; g < 2; ++g)
             acc[g][u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][c2], acc[g][u2], 0, 0, 0);
@@ -1047,21 +1077,38 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
             *reinterpret_cast<f32x4*>(po + q * HD + 32 * u + 8 * g4 + 4 * hh) =
                 f32x4{o[u][4 * g4], o[u][4 * g4 + 1], o[u][4 * g4 + 2], o[u][4 * g4 + 3]};
         if (hh == 0) {
-          po[BLK * HD + q] = m;
+          po[BLK * HD + q] = m > kNoMax ? m : -INFINITY;
           po[BLK * HD + BLK + q] = l;
         }
       } else if (cur_row >= 0 && qrow < N) {
         const size_t head = size_t(bh) * size_t(N) * HD;
         const float inv = l > 0.f ? 1.f / l : 0.f;
         uint16_t* orow = O + head + size_t(qrow) * HD;
+        // Lane (ql, hh) holds columns 32u + 8g4 + 4hh .. +3.  Swapping the odd-g4
+        // pieces of the lower half-wave with the even-g4 pieces of the upper one
+        // leaves every lane 8 contiguous columns (32u + 16p + 8hh .. +7), so four
+        // 16-byte stores write the row.
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * u + 8 * g4 + 4 * hh;
-            const uint32_t w0 = pack_bf16x2(o[u][4 * g4 + 0] * inv, o[u][4 * g4 + 1] * inv);
-            const uint32_t w1 = pack_bf16x2(o[u][4 * g4 + 2] * inv, o[u][4 * g4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+          for (int pq = 0; pq < 2; ++pq) {
+            const int ge = 2 * pq, go2 = 2 * pq + 1;
+            const uint32_t e0 = pack_bf16x2(o[u][4 * ge + 0] * inv, o[u][4 * ge + 1] * inv);
+            const uint32_t e1 = pack_bf16x2(o[u][4 * ge + 2] * inv, o[u][4 * ge + 3] * inv);
+            const uint32_t d0v = pack_bf16x2(o[u][4 * go2 + 0] * inv, o[u][4 * go2 + 1] * inv);
+            const uint32_t d1v = pack_bf16x2(o[u][4 * go2 + 2] * inv, o[u][4 * go2 + 3] * inv);
+            // swap(X, Y): the upper lanes of the first result get the lower
+            // lanes' Y, the lower lanes of the second result the upper lanes'
+            // X.  Lower lanes need the upper half's even piece, upper lanes the
+            // lower half's odd piece.
+            const auto s0 = __builtin_amdgcn_permlane32_swap(e0, d0v, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(e1, d1v, false, false);
+            uint4 w;
+            if (hh == 0)
+              w = make_uint4(e0, e1, s0[1], s1[1]);
+            else
+              w = make_uint4(s0[0], s1[0], d0v, d1v);
+            *reinterpret_cast<uint4*>(orow + 32 * u + 16 * pq + 8 * hh) = w;
           }
         if (hh == 0 && LSE != nullptr)
           LSE[size_t(bh) * N + qrow] =
