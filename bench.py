@@ -59,6 +59,13 @@ def compulsory_bytes(B, H, N, D, nnz, n_rows):
     return float(4 * B * H * N * D * 2 + B * H * N * 4 + (nnz + 2 * n_rows + 1) * 4)
 
 
+def fwd_kernel_name(block, D):
+    """The forward kernel that serves (block, D), as rocprofv3 names it."""
+    if block == 64 and D == 64:
+        return "bsa_forward (fwd_wide_kernel + merge_kernel<64, 64>)"
+    return f"bsa_forward (fwd_kernel<{block}, {D}> + merge_kernel<{block}, {D}>)"
+
+
 def traffic_for(fwd_sha):
     """HBM bytes per launch from the committed PMC summary, if the kernel is unchanged."""
     try:
@@ -243,7 +250,7 @@ def main():
         "pct_of_bf16_peak": 100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_for(fwd_sha), "kernel": f"bsa_forward (fwd_kernel<{w.block},{w.D}>)",
+                     "traffic": traffic_for(fwd_sha), "kernel": fwd_kernel_name(w.block, w.D),
                      "flops_per_launch": flops},
         "cpu_baseline": None,
         "extra": extra,
