@@ -117,9 +117,11 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
   // Groups: head h = row / nb goes to group h % n_groups (the die whose
   // workgroups serve that group; workgroup i runs on die i % n_groups).  Inside
   // a group the chunks of cut rows (the largest items) come first, then the
-  // whole rows; each class longest first, equal lengths head by head.  Big
-  // items first leave the small ones for the end, where the workgroups that
-  // finish early claim them; equal lengths in head order keep some L2 reuse.
+  // whole rows; each class head by head, a head's longest items first.  Heads
+  // in order keep the die's L2 on the K/V of about one head at a time (ordering
+  // rows by length across heads instead ran as fast but doubled the L2 misses);
+  // big items first leave small ones for the end, where early finishers claim
+  // them.
   const int32_t ng = (nb > 0 && n_groups > 1) ? n_groups : 1;
   std::vector<std::vector<Item>> g(static_cast<size_t>(ng));
   for (const Item& it : items) g[ng > 1 ? size_t((it.row / nb) % ng) : 0].push_back(it);
@@ -127,10 +129,8 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
     std::stable_sort(x.begin(), x.end(), [nb](const Item& a, const Item& b) {
       const bool ca = a.slot >= 0, cb = b.slot >= 0;
       if (ca != cb) return ca;
-      const int32_t la = a.e - a.b, lb = b.e - b.b;
-      if (la != lb) return la > lb;
       const int32_t ha = nb > 0 ? a.row / nb : 0, hb = nb > 0 ? b.row / nb : 0;
-      return ha < hb;
+      return ha != hb ? ha < hb : a.e - a.b > b.e - b.b;
     });
   const int64_t need = 4 * int64_t(items.size()) + int64_t(merges.size()) + 2 + ng;
   if (need > capacity) return BSA_ERR_CAPACITY;

@@ -104,8 +104,8 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
  * whose L2 caches are separate: workgroup i of the forward runs on die
  * i % n_groups and serves group i % n_groups.  Group g holds the heads
  * h = row / nb with h % n_groups == g.  Inside a group the chunks of cut rows
- * come first, then the whole rows; each class longest first, equal lengths
- * head by head; ties keep ascending row, then chunk.
+ * come first, then the whole rows; each class head by head, each head's
+ * longest items first; ties keep ascending row, then chunk.
  * The forward's workgroups take the items of their group in that order (the
  * first two rounds statically, the rest from a per-group counter), so the
  * order is the dispatch order within a group.

@@ -74,7 +74,7 @@ def test_mask_plan_workload_totals():
 def check_work(work, ni, nm, ns, rp, max_tiles, nb=0, n_groups=1):
     """Every row covered exactly once, chunks <= max_tiles, merges consistent, and the
     group table: group g holds the heads h % G == g, chunks of cut rows first, then
-    rows; each class longest first, equal lengths in head order."""
+    rows; each class head by head, a head's longest items first."""
     lens = np.diff(rp)
     items = work[:4 * ni].reshape(ni, 4).copy()
     items[:, 1] -= rp[items[:, 0]]          # absolute column positions -> positions in the row
@@ -95,9 +95,9 @@ def check_work(work, ni, nm, ns, rp, max_tiles, nb=0, n_groups=1):
         assert (heads[a:b] % G == g).all()
         for cls in (True, False):
             h, sz = heads[a:b][c == cls], sizes[a:b][c == cls]
-            assert (np.diff(sz) <= 0).all()
-            for sv in np.unique(sz):
-                assert (np.diff(h[sz == sv]) >= 0).all()
+            assert (np.diff(h) >= 0).all()
+            for hv in np.unique(h):
+                assert (np.diff(sz[h == hv]) <= 0).all()
     cover = {}
     for row, b, e, slot in items.tolist():
         cover.setdefault(row, []).append((b, e, slot))
