@@ -48,6 +48,7 @@ namespace bsa {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define BSA_LDS __attribute__((address_space(3)))
 
@@ -145,6 +146,23 @@ __device__ __forceinline__ void wait_vm(int n) {
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31] (larger n waits as for 31).
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n < 31 ? n : 31) {
+#define BSA_VM_CASE(k) \
+  case k:              \
+    asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); \
+    break;
+    BSA_VM_CASE(0) BSA_VM_CASE(1) BSA_VM_CASE(2) BSA_VM_CASE(3) BSA_VM_CASE(4) BSA_VM_CASE(5)
+    BSA_VM_CASE(6) BSA_VM_CASE(7) BSA_VM_CASE(8) BSA_VM_CASE(9) BSA_VM_CASE(10) BSA_VM_CASE(11)
+    BSA_VM_CASE(12) BSA_VM_CASE(13) BSA_VM_CASE(14) BSA_VM_CASE(15) BSA_VM_CASE(16)
+    BSA_VM_CASE(17) BSA_VM_CASE(18) BSA_VM_CASE(19) BSA_VM_CASE(20) BSA_VM_CASE(21)
+    BSA_VM_CASE(22) BSA_VM_CASE(23) BSA_VM_CASE(24) BSA_VM_CASE(25) BSA_VM_CASE(26)
+    BSA_VM_CASE(27) BSA_VM_CASE(28) BSA_VM_CASE(29) BSA_VM_CASE(30) BSA_VM_CASE(31)
+#undef BSA_VM_CASE
+  }
 }
 
 // Value of lane l ^ 32 (the other half of the wavefront), without LDS.
@@ -686,6 +704,31 @@ __device__ __forceinline__ void dma_half(v4i desc, uint32_t ve, uint32_t vo, uin
       : "memory");
 }
 
+// dma_half for the K half tile into kdst and the V half tile into kdst + HALFB
+// (same source offsets, different buffers) under one M0 save/restore.
+__device__ __forceinline__ void dma_kv_half(v4i kdesc, v4i vdesc, uint32_t ve, uint32_t vo,
+                                            uint32_t kdst, uint32_t vdst) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %6, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %4, %6, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %6, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %6, 0 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(kdst), "s"(vdst), "v"(ve), "v"(vo), "s"(kdesc), "s"(vdesc)
+      : "memory");
+}
+
 __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
@@ -825,6 +868,7 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
   };
 
   int st_cur = 0;     // ring stage of the tile being computed
+  int vm_after = 0;   // operations issued after the current tile before the loop
   int pending = 0;    // tiles issued beyond the current one (0 or 1)
   int pf = 0;         // stream position of the next tile to issue
   int valid_pf = 0;   // valid keys of the prefetched tile
@@ -833,8 +877,10 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     const bool ok = j >= 0 && j < nb;
     const uint32_t tb = ok ? uint32_t(j) * (BLK * W::ROWB) + uint32_t(kh) * W::HALFB : head_bytes;
     const uint32_t dst = ring + uint32_t(st) * W::STAGEB;
-    dma_half(in_next ? kd_nxt : kd_cur, ve + tb, vo + tb, dst);
-    dma_half(in_next ? vd_nxt : vd_cur, ve + tb, vo + tb, dst + W::HALFB);
+    if (in_next)
+      dma_kv_half(kd_nxt, vd_nxt, ve + tb, vo + tb, dst, dst + W::HALFB);
+    else
+      dma_kv_half(kd_cur, vd_cur, ve + tb, vo + tb, dst, dst + W::HALFB);
     q_newest = false;
     ++pf;
     return ok ? min(BLK, N - j * BLK) : 0;
@@ -887,15 +933,20 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       // next stream tile into the other stage, which this wave finished
       // reading in the previous step, then wait for tile u only.
       if (queue && kh == 0 && claim_out && !nn_known && u == cur_cnt - 1) resolve_claim();
+      // Tile u is complete once at most `allowed` younger operations are
+      // outstanding: the tile issued now and, at an item's first step, the
+      // previous epilogue's stores, a claim and the query staging, all issued
+      // after tile u (vector memory operations retire in order).
+      int allowed = vm_after;
+      vm_after = 0;
       pending = 0;
       if (has_pf) {
         valid_pf = issue(j_pf, pf_next, st_cur ^ 1);
         pending = 1;
         lookup();
-        wait_vm(8);
-      } else {
-        wait_vm(0);
+        allowed += 8;
       }
+      wait_vm_n(allowed);
       const uint32_t ks = ring + uint32_t(st_cur) * W::STAGEB;
       const uint32_t vs = ks + W::HALFB;
 
@@ -1044,6 +1095,7 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
         xml[kh * 64 + 32 + ql] = l;
       }
     };
+    int n_stores = 0;  // vector-memory stores this wave issues in the epilogue
     auto finish = [&](const f32x16 (&a)[2], float m0, float l0) {
       const int go = 1 - kh;
       const float* xi = reinterpret_cast<const float*>(smem + size_t(go) * W::RINGB +
@@ -1066,24 +1118,33 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       const int bh = cur_bh;
       const int q = kh * 32 + ql;
       const int qrow = (cur_row - bh * nb) * BLK + q;
+      // Buffer stores with bounds: rows past N (and the lanes that carry no
+      // m, l or LSE) address past the end and are dropped, so every wave
+      // issues the same, known number of stores.
       if (cur_row >= 0 && cur_slot >= 0) {
         // Partial result of one chunk of a cut row (unnormalised acc, max in
         // log2 units, sum), combined with the row's other chunks by merge_kernel.
-        float* po = part + size_t(cur_slot) * BLK * (HD + 2);
+        constexpr uint32_t kSlotBytes = BLK * (HD + 2) * 4;
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(part + size_t(cur_slot) * BLK * (HD + 2), kSlotBytes);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<f32x4*>(po + q * HD + 32 * u + 8 * g4 + 4 * hh) =
-                f32x4{o[u][4 * g4], o[u][4 * g4 + 1], o[u][4 * g4 + 2], o[u][4 * g4 + 3]};
-        if (hh == 0) {
-          po[BLK * HD + q] = m > kNoMax ? m : -INFINITY;
-          po[BLK * HD + BLK + q] = l;
-        }
-      } else if (cur_row >= 0 && qrow < N) {
-        const size_t head = size_t(bh) * size_t(N) * HD;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(v4u, f32x4{o[u][4 * g4], o[u][4 * g4 + 1], o[u][4 * g4 + 2],
+                                              o[u][4 * g4 + 3]}),
+                pr, uint32_t(q * HD + 32 * u + 8 * g4 + 4 * hh) * 4u, 0, 0);
+        const float mw = m > kNoMax ? m : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mw), pr,
+                                              hh == 0 ? uint32_t(BLK * HD + q) * 4u : kSlotBytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(l), pr, hh == 0 ? uint32_t(BLK * HD + BLK + q) * 4u : kSlotBytes, 0, 0);
+        n_stores = 10;
+      } else if (cur_row >= 0) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* orow = O + head + size_t(qrow) * HD;
+        const __amdgpu_buffer_rsrc_t orsc =
+            make_rsrc(O + size_t(bh) * size_t(N) * HD, head_bytes);
+        const uint32_t orow = uint32_t(qrow) * W::ROWB;
         // Lane (ql, hh) holds columns 32u + 8g4 + 4hh .. +3.  Swapping the odd-g4
         // pieces of the lower half-wave with the even-g4 pieces of the upper one
         // leaves every lane 8 contiguous columns (32u + 16p + 8hh .. +7), so four
@@ -1103,16 +1164,23 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
             // lower half's odd piece.
             const auto s0 = __builtin_amdgcn_permlane32_swap(e0, d0v, false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(e1, d1v, false, false);
-            uint4 w;
+            v4u w;
             if (hh == 0)
-              w = make_uint4(e0, e1, s0[1], s1[1]);
+              w = v4u{e0, e1, s0[1], s1[1]};
             else
-              w = make_uint4(s0[0], s1[0], d0v, d1v);
-            *reinterpret_cast<uint4*>(orow + 32 * u + 16 * pq + 8 * hh) = w;
+              w = v4u{s0[0], s1[0], d0v, d1v};
+            __builtin_amdgcn_raw_buffer_store_b128(w, orsc, orow + uint32_t(32 * u + 16 * pq + 8 * hh) * 2u,
+                                                   0, 0);
           }
-        if (hh == 0 && LSE != nullptr)
-          LSE[size_t(bh) * N + qrow] =
-              l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+        n_stores = 4;
+        if (LSE != nullptr) {
+          const __amdgpu_buffer_rsrc_t lrsc =
+              make_rsrc(LSE + size_t(bh) * size_t(N), static_cast<uint32_t>(N) * 4u);
+          const float lv = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lrsc,
+                                                hh == 0 ? uint32_t(qrow) * 4u : uint32_t(N) * 4u, 0, 0);
+          n_stores = 5;
+        }
       }
     };
     if (kh == 0)
@@ -1181,8 +1249,16 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     kd_nxt = head_desc(K, nxt_row, nxt_bh);
     vd_nxt = head_desc(V, nxt_row, nxt_bh);
     stage_q(nxt_row, nxt_bh);
-    // The prefetched column was looked up before the next item was known.
-    lookup();
+    // Operations issued after the prefetched first tile of the new item: the
+    // epilogue's stores, this wave's claim and the query staging.
+    vm_after = pending ? n_stores + ((claim_out && kh == 0) ? 1 : 0) + (nxt_row >= 0 ? 4 : 0) : 0;
+    // The looked-up column, if any, lies in the old next item, which is now
+    // the current one; a lookup that ran past it is redone now that the item
+    // after it is known.
+    if (has_pf)
+      pf_next = false;
+    else
+      lookup();
     if (!pending && cur_cnt > 0) {
       // Nothing was prefetched for the new item (its predecessor had no tile
       // to look ahead to): issue its first tile now.
