@@ -60,7 +60,7 @@ _SIGS = {
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class BsaError(RuntimeError):
@@ -82,7 +82,20 @@ def _load():
     return handle
 
 
-lib = _load()
+class _Lib:
+    """The ctypes handle of libbsa.so, opened at the first call (so that the
+    build module can run while the library is missing or stale); a missing or
+    mismatched library raises ImportError there."""
+
+    _handle = None
+
+    def __getattr__(self, name):
+        if _Lib._handle is None:
+            _Lib._handle = _load()
+        return getattr(_Lib._handle, name)
+
+
+lib = _Lib()
 
 
 def status_string(code: int) -> str:
@@ -162,8 +175,9 @@ def work_plan(row_ptr, max_tiles: int = 0, nb: int = 0, n_groups: int = 1):
     Rows longer than `max_tiles` KV blocks are cut into near-equal chunks
     (max_tiles <= 0: never).  Items come in n_groups groups (heads h with
     h % n_groups == g in group g; one group if n_groups <= 1), head by head and
-    longest first inside a head, followed by the merge records and the group
-    table {n_groups, start_0, ..., start_n_groups}.
+    longest first inside a head, followed by the merge records, the group
+    table {n_groups, start_0, ..., start_n_groups} and the slot map (the merge
+    record of every partial slot).
     """
     rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
     n_rows = rp.shape[0] - 1
@@ -176,7 +190,7 @@ def work_plan(row_ptr, max_tiles: int = 0, nb: int = 0, n_groups: int = 1):
                                   _np_ptr(work), cap, ctypes.byref(ni), ctypes.byref(nm),
                                   ctypes.byref(ns)), "bsa_work_plan_host")
     tab = 4 * ni.value + 3 * nm.value
-    used = tab + 2 + int(work[tab])
+    used = tab + 2 + int(work[tab]) + ns.value
     return work[:used].copy(), ni.value, nm.value, ns.value
 
 
@@ -231,8 +245,8 @@ class Work:
     def from_host(cls, row_ptr_host, D: int, block: int, max_tiles: int, device, nb: int = 0,
                   n_groups: int = 1):
         w, ni, nm, ns = work_plan(row_ptr_host, max_tiles, nb, n_groups)
-        # The item counters at the start of the workspace must start at zero;
-        # every forward call leaves them zero again.
+        # The item and merge counters at the start of the workspace must start
+        # at zero; every forward call leaves them zero again.
         ws = torch.zeros(forward_workspace_bytes(ns, D, block), dtype=torch.uint8, device=device)
         return cls(torch.from_numpy(w).to(device), ni, nm, ns, ws, int(max_tiles))
 

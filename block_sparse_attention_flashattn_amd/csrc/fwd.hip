@@ -114,6 +114,10 @@ __device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
              0x00020000};
 }
 
+// Cache policy of buffer accesses shared between workgroups on different dies
+// (sc1): coherent at device scope, as the agent-scope atomic accesses are.
+constexpr int kAgentScope = 16;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
                                            0x00020000);
@@ -196,6 +200,11 @@ __device__ __forceinline__ T ld_uniform(const T* p, size_t i) {
 // not queue behind each other in one memory channel.
 constexpr int kCounterStride = 1024;  // int32 entries
 constexpr size_t kCounterBytes = size_t(BSA_MAX_GROUPS) * kCounterStride * sizeof(int32_t);
+// Merge counters: one int32 per query group of a 64-query block (two) and
+// partial slot, rounded up to 256 bytes; they follow the item counters.
+inline size_t merge_counter_bytes(int32_t n_slots) {
+  return (size_t(n_slots) * 2 * sizeof(int32_t) + 255) & ~size_t(255);
+}
 
 // Where a persistent workgroup's items come from.
 //  * No work list: workgroup w runs CSR rows w, w + G, w + 2G, ... (static).
@@ -734,7 +743,8 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
     int32_t n_merges, int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr) {
+    float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr, int32_t n_slots,
+    int32_t* __restrict__ mctr) {
   using W = Wide;
   constexpr int BLK = W::BLK, HD = W::HD;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -906,6 +916,98 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
   read_q(qf);
   lds_barrier();
   stage_q(nxt_row, nxt_bh);
+  // Chunk partials and their merge.  A wave's partial stores (agent-scope
+  // coherent) are known complete one epilogue later, where the wait for the
+  // query tile covers them (after the last item: at once, by a full wait); the
+  // wave then counts its query group of that chunk in, and the wave that
+  // brings the count to the number of chunks combines the group's partials of
+  // every chunk of the row.
+  int rel_slot = -1;  // chunk whose partial this wave stored, not yet counted in
+  const int32_t* slot_merge =
+      work ? work + 4 * size_t(n_items) + 3 * size_t(n_merges) + 2 + src.ng : nullptr;
+  const int32_t* merges = work ? work + 4 * size_t(n_items) : nullptr;
+  auto merge_of = [&](int slot) -> int {
+    const int m = (slot >= 0 && slot < n_slots) ? ld_uniform(slot_merge, slot) : -1;
+    return (m >= 0 && m < n_merges && m < n_slots) ? m : -1;
+  };
+  // Count this wave's query group of chunk `slot` in (lane 0 holds the old
+  // count; the result is read after a wait that covers it).
+  auto count_in = [&](int m) -> int {
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(mctr + 2 * m + kh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return old;
+  };
+  // Combine query group kh of cut row `merges[m]` from its chunks' partials:
+  // with M = max_c m_c, O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c and
+  // LSE = (M + log2 L) ln 2.  Lane (ql, hh) owns query 32 kh + ql, columns
+  // 32 hh .. +31.  Returns the number of stores issued.
+  auto merge_group = [&](int m) -> int {
+    if (lane == 0)
+      __hip_atomic_store(mctr + 2 * m + kh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int r = ld_uniform(merges, 3 * size_t(m));
+    const int slot0 = ld_uniform(merges, 3 * size_t(m) + 1);
+    const int nch = ld_uniform(merges, 3 * size_t(m) + 2);
+    if (r < 0 || r >= n_rows || nch < 1 || slot0 < 0 || slot0 >= n_slots) return 0;
+    constexpr uint32_t kSlotFloats = BLK * (HD + 2);
+    const int nc = min(nch, n_slots - slot0);
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(part + size_t(slot0) * kSlotFloats, uint32_t(nc) * kSlotFloats * 4u);
+    const int q = 32 * kh + ql;
+    const uint32_t qoff = uint32_t(q * HD + 32 * hh) * 4u;
+    float M = -INFINITY, L = 0.f;
+    f32x4 o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nc; c0 += 4) {
+      f32x4 a[4][8];
+      float mc[4], lc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // Chunks past the row's last read past the range: zeros, weight 0.
+        const uint32_t cb = uint32_t(c0 + t) * kSlotFloats * 4u;
+        mc[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            pr, cb + uint32_t(BLK * HD + q) * 4u, 0, kAgentScope));
+        lc[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            pr, cb + uint32_t(BLK * HD + BLK + q) * 4u, 0, kAgentScope));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          a[t][j] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, cb + qoff + 16u * j, 0, kAgentScope));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (c0 + t >= nc) break;
+        const float mn = fmaxf(M, mc[t]);
+        const float wo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+        const float wc = mc[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc[t] - mn);
+        L = L * wo + lc[t] * wc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = o[j] * wo + a[t][j] * wc;
+        M = mn;
+      }
+    }
+    const int bh = head_of(r);
+    const int qrow = (r - bh * nb) * BLK + q;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const __amdgpu_buffer_rsrc_t orsc = make_rsrc(O + size_t(bh) * size_t(N) * HD, head_bytes);
+    const uint32_t ob = uint32_t(qrow) * W::ROWB + uint32_t(32 * hh) * 2u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = o[2 * j], y = o[2 * j + 1];
+      const v4u w = v4u{pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv),
+                        pack_bf16x2(y[0] * inv, y[1] * inv), pack_bf16x2(y[2] * inv, y[3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b128(w, orsc, ob + 16u * j, 0, 0);
+    }
+    if (LSE == nullptr) return 4;
+    const __amdgpu_buffer_rsrc_t lrsc =
+        make_rsrc(LSE + size_t(bh) * size_t(N), static_cast<uint32_t>(N) * 4u);
+    const float lv = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f : -INFINITY;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lrsc,
+                                          hh == 0 ? uint32_t(qrow) * 4u : uint32_t(N) * 4u, 0, 0);
+    return 5;
+  };
+
   // Column of stream tile `pf`, looked up one step before it is issued.
   int j_pf = 0;
   bool has_pf = false, pf_next = false;
@@ -950,28 +1052,17 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       const uint32_t ks = ring + uint32_t(st_cur) * W::STAGEB;
       const uint32_t vs = ks + W::HALFB;
 
-      // All LDS reads of the tile are issued up front: the four K operands
-      // (one round trip instead of four) and the eight V^T halves, which then
-      // land while the softmax runs.  For the 16-key step c2, V^T rows
-      // d = 32u + (lane % 32) need keys 16c2 + 4hh + e and 16c2 + 8 + 4hh + e
-      // (e = 0..3): lane t of each 16-lane block points at key row t / 4 and
-      // columns 4 (t % 4) .. +3 of its block's 16 d values, and the
-      // transposing read returns to every lane the four keys of its own d.
+      // The four K operands are read up front (one round trip instead of
+      // four).  The eight V^T halves are issued between the S MFMAs, whose
+      // issue they then hide, and land while the softmax runs.  For the 16-key
+      // step c2, V^T rows d = 32u + (lane % 32) need keys 16c2 + 4hh + e and
+      // 16c2 + 8 + 4hh + e (e = 0..3): lane t of each 16-lane block points at
+      // key row t / 4 and columns 4 (t % 4) .. +3 of its block's 16 d values,
+      // and the transposing read returns to every lane the four keys of its
+      // own d.
       bf16x8 ka[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) ka[c] = lds_read16(ks + swz<W::ROWB>(ql, 2 * c + hh));
-      const int tr_row = 4 * hh + ((lane & 15) >> 2);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      v4s vlo[2][2], vhi[2][2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int u2 = 0; u2 < 2; ++u2) {
-          const int col = 32 * u2 + tr_col;
-          vlo[c2][u2] = lds_read_tr(vs + swz<W::ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
-          vhi[c2][u2] =
-              lds_read_tr(vs + swz<W::ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
-        }
       __builtin_amdgcn_sched_barrier(0);
 
       // S^T tiles: lane (ql, hh) holds keys 8(i/4) + 4hh + (i%4) (of this
@@ -984,6 +1075,23 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
         for (int g = 0; g < 2; ++g)
           s[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s[g], 0,
                                                          0, 0);
+      const int tr_row = 4 * hh + ((lane & 15) >> 2);
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      v4s vlo[2][2], vhi[2][2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+          const int col = 32 * u2 + tr_col;
+          vlo[c2][u2] = lds_read_tr(vs + swz<W::ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
+          vhi[c2][u2] =
+              lds_read_tr(vs + swz<W::ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
       if (__builtin_expect(valid_cur < BLK, 0)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -1068,6 +1176,13 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       wait_vm(8);
     else
       wait_vm(0);
+    // The previous epilogue's partial stores are complete: count them in.
+    int rel_m = -1, rel_old = 0;
+    if (rel_slot >= 0) {
+      rel_m = merge_of(rel_slot);
+      if (rel_m >= 0) rel_old = count_in(rel_m);
+      rel_slot = -1;
+    }
     const bool more = k_nxt >= 0;
     lds_barrier();  // both halves of the staged query tile are in LDS
     if (more) read_q(qf);
@@ -1133,12 +1248,14 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
             __builtin_amdgcn_raw_buffer_store_b128(
                 __builtin_bit_cast(v4u, f32x4{o[u][4 * g4], o[u][4 * g4 + 1], o[u][4 * g4 + 2],
                                               o[u][4 * g4 + 3]}),
-                pr, uint32_t(q * HD + 32 * u + 8 * g4 + 4 * hh) * 4u, 0, 0);
+                pr, uint32_t(q * HD + 32 * u + 8 * g4 + 4 * hh) * 4u, 0, kAgentScope);
         const float mw = m > kNoMax ? m : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mw), pr,
-                                              hh == 0 ? uint32_t(BLK * HD + q) * 4u : kSlotBytes, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __float_as_uint(l), pr, hh == 0 ? uint32_t(BLK * HD + BLK + q) * 4u : kSlotBytes, 0, 0);
+                                              hh == 0 ? uint32_t(BLK * HD + q) * 4u : kSlotBytes, 0,
+                                              kAgentScope);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), pr,
+                                              hh == 0 ? uint32_t(BLK * HD + BLK + q) * 4u : kSlotBytes,
+                                              0, kAgentScope);
         n_stores = 10;
       } else if (cur_row >= 0) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1216,6 +1333,38 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     else
       finish(acc[1], m_run[1], l_half[1]);
     lds_barrier();  // exchange areas free before loads target them again
+    // Merges this wave completes: the previous chunk's (counted in above) and,
+    // after the last item, this one's (its stores are waited for here).
+    int mg_a = -1, mg_b = -1;
+    if (rel_m >= 0) {
+      wait_vm_n(n_stores);  // the count-in (issued before this epilogue's stores)
+      if (__builtin_amdgcn_readfirstlane(rel_old) == ld_uniform(merges, 3 * size_t(rel_m) + 2) - 1)
+        mg_a = rel_m;
+    }
+    if (cur_row >= 0 && cur_slot >= 0) {
+      if (more) {
+        rel_slot = cur_slot;
+      } else {
+        const int m = merge_of(cur_slot);
+        if (m >= 0) {
+          wait_vm(0);
+          const int old = count_in(m);
+          wait_vm(0);
+          if (__builtin_amdgcn_readfirstlane(old) == ld_uniform(merges, 3 * size_t(m) + 2) - 1)
+            mg_b = m;
+        }
+      }
+    }
+    int merge_stores = 0;
+    while (mg_a >= 0 || mg_b >= 0) {
+      const int m = mg_a >= 0 ? mg_a : mg_b;
+      if (mg_a >= 0)
+        mg_a = -1;
+      else
+        mg_b = -1;
+      merge_stores += merge_group(m);
+    }
+    merge_stores = __builtin_amdgcn_readfirstlane(merge_stores);
 
     // ---- advance to the next item ------------------------------------------
     k_cur = k_nxt;
@@ -1251,7 +1400,9 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     stage_q(nxt_row, nxt_bh);
     // Operations issued after the prefetched first tile of the new item: the
     // epilogue's stores, this wave's claim and the query staging.
-    vm_after = pending ? n_stores + ((claim_out && kh == 0) ? 1 : 0) + (nxt_row >= 0 ? 4 : 0) : 0;
+    vm_after = pending ? n_stores + merge_stores + ((claim_out && kh == 0) ? 1 : 0) +
+                             (nxt_row >= 0 ? 4 : 0)
+                       : 0;
     // The looked-up column, if any, lies in the old next item, which is now
     // the current one; a lookup that ran past it is redone now that the item
     // after it is known.
@@ -1391,8 +1542,9 @@ int resident_wide_workgroups() {
 
 bsa_status launch_wide(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
                        int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
-                       const int32_t* work, int32_t n_items, int32_t n_merges, float sl2, void* o,
-                       float* lse, float* part, int32_t* ctr, hipStream_t stream) {
+                       const int32_t* work, int32_t n_items, int32_t n_merges, int32_t n_slots,
+                       float sl2, void* o, float* lse, float* part, int32_t* ctr, int32_t* mctr,
+                       hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
@@ -1409,14 +1561,8 @@ bsa_status launch_wide(const void* q, const void* k, const void* v, int32_t N, i
     hipLaunchKernelGGL(fwd_wide_kernel, dim3(grid), dim3(Wide::NT), Wide::LDS_BYTES, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, n_merges,
-                       N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr);
-    BSA_HIP_CHECK_LAUNCH();
-  }
-  if (work && n_merges > 0) {
-    constexpr int wg_per_row = 64 * (64 / 4) / kMergeThreads;
-    hipLaunchKernelGGL((merge_kernel<64, 64>), dim3(n_merges * wg_per_row), dim3(kMergeThreads),
-                       0, stream, work + 4 * size_t(n_items), part, N, nb, n_rows,
-                       static_cast<uint16_t*>(o), lse);
+                       N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr,
+                       work ? n_slots : 0, mctr);
     BSA_HIP_CHECK_LAUNCH();
   }
   return BSA_OK;
@@ -1464,7 +1610,8 @@ bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, in
 extern "C" BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D,
                                                       int32_t block) {
   if (n_slots < 0 || D < 1 || block < 1) return 0;
-  return bsa::kCounterBytes + size_t(n_slots) * size_t(block) * size_t(D + 2) * sizeof(float);
+  return bsa::kCounterBytes + bsa::merge_counter_bytes(n_slots) +
+         size_t(n_slots) * size_t(block) * size_t(D + 2) * sizeof(float);
 }
 
 extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v,
@@ -1499,13 +1646,18 @@ extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const vo
   const float sl2 = sc * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* ctr = work_dev ? static_cast<int32_t*>(workspace) : nullptr;
+  int32_t* mctr = work_dev ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
+                                                        kCounterBytes)
+                           : nullptr;
   float* part = work_dev ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                                    kCounterBytes)
+                                                    kCounterBytes + merge_counter_bytes(n_slots))
                          : nullptr;
 #define BSA_FWD_ARGS                                                                            \
   q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items, n_merges, sl2, o, lse, \
       part, ctr, s
-  if (block == 64 && D == 64) return launch_wide(BSA_FWD_ARGS);
+  if (block == 64 && D == 64)
+    return launch_wide(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items,
+                       n_merges, n_slots, sl2, o, lse, part, ctr, mctr, s);
   if (block == 64 && D == 128) return launch_fwd<64, 128>(BSA_FWD_ARGS);
   if (block == 128 && D == 64) return launch_fwd<128, 64>(BSA_FWD_ARGS);
   return launch_fwd<128, 128>(BSA_FWD_ARGS);

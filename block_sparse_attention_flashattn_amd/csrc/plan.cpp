@@ -74,10 +74,12 @@ extern "C" BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, do
 
 extern "C" BSA_API int64_t bsa_work_plan_ints(int32_t n_rows, int64_t nnz, int32_t max_tiles) {
   if (n_rows < 1 || nnz < 0) return -1;
-  // Cutting a row of length L into ceil(L/T) chunks adds at most L/T items;
-  // the group table takes at most 2 + BSA_MAX_GROUPS ints.
+  // Cutting a row of length L > T into ceil(L/T) chunks adds at most L/T items
+  // and uses at most 2L/T partial slots (one map entry each); the group table
+  // takes at most 2 + BSA_MAX_GROUPS ints.
   const int64_t extra = max_tiles > 0 ? nnz / max_tiles : 0;
-  return 4 * (int64_t(n_rows) + extra) + 3 * int64_t(n_rows) + 2 + BSA_MAX_GROUPS;
+  const int64_t slots = max_tiles > 0 ? 2 * nnz / max_tiles : 0;
+  return 4 * (int64_t(n_rows) + extra) + 3 * int64_t(n_rows) + 2 + BSA_MAX_GROUPS + slots;
 }
 
 extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows,
@@ -132,7 +134,7 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
       const int32_t ha = nb > 0 ? a.row / nb : 0, hb = nb > 0 ? b.row / nb : 0;
       return ha != hb ? ha < hb : a.e - a.b > b.e - b.b;
     });
-  const int64_t need = 4 * int64_t(items.size()) + int64_t(merges.size()) + 2 + ng;
+  const int64_t need = 4 * int64_t(items.size()) + int64_t(merges.size()) + 2 + ng + slots;
   if (need > capacity) return BSA_ERR_CAPACITY;
   size_t k = 0;
   std::vector<int32_t> table;
@@ -152,6 +154,10 @@ extern "C" BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t
   table.push_back(static_cast<int32_t>(k));
   memcpy(work_out + 4 * k, merges.data(), merges.size() * sizeof(int32_t));
   memcpy(work_out + 4 * k + merges.size(), table.data(), table.size() * sizeof(int32_t));
+  // Slot map: the merge record of every partial slot.
+  int32_t* slot_merge = work_out + 4 * k + merges.size() + table.size();
+  for (size_t m = 0; m < merges.size() / 3; ++m)
+    for (int32_t c = 0; c < merges[3 * m + 2]; ++c) slot_merge[merges[3 * m + 1] + c] = int32_t(m);
   *n_items = static_cast<int32_t>(k);
   *n_merges = static_cast<int32_t>(merges.size() / 3);
   *n_slots = slots;

@@ -51,7 +51,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 2
+#define BSA_ABI_VERSION 3
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -97,8 +97,8 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
  * sorting or merging the work, or per-block target counts.  Here every row
  * longer than max_tiles KV blocks is cut into near-equal chunks of at most
  * max_tiles blocks (max_tiles <= 0: rows are never cut); the chunks of a cut
- * row write fp32 partial results to the forward's workspace and a second
- * kernel merges them.
+ * row write fp32 partial results to the forward's workspace, and the forward
+ * combines them once the last one is stored.
  * Groups and order: the items are split into n_groups groups (n_groups <= 1:
  * one group; at most BSA_MAX_GROUPS), meant for the accelerator dies (XCDs),
  * whose L2 caches are separate: workgroup i of the forward runs on die
@@ -117,8 +117,9 @@ BSA_API bsa_status bsa_mask_plan(int32_t B, int32_t H, int32_t nb, double densit
  *             the whole row and writes O directly), grouped as above; then
  *             n_merges records {row, first_slot, n_chunks}; then the group
  *             table {G, s_0, s_1, ..., s_G}: G groups, group g being items
- *             [s_g, s_(g+1)) (s_0 = 0, s_G = n_items).  The list takes
- *             4 n_items + 3 n_merges + G + 2 ints.
+ *             [s_g, s_(g+1)) (s_0 = 0, s_G = n_items); then the slot map:
+ *             n_slots ints, the merge record index of every partial slot.
+ *             The list takes 4 n_items + 3 n_merges + G + 2 + n_slots ints.
  *   capacity  >= bsa_work_plan_ints(n_rows, nnz, max_tiles) int32 entries.
  *   n_items, n_merges, n_slots  written (n_slots = partial slots used).
  * Errors: INVALID_ARG for a NULL pointer, n_rows < 1, a decreasing row_ptr or
@@ -202,8 +203,9 @@ BSA_API bsa_status bsa_schedule(const int32_t* row_ptr_dev, int32_t n_rows, int3
 
 /*
  * Bytes of device workspace bsa_forward needs with a work list: 256 KiB of
- * item counters (one int32 per group, 4 KiB apart), then n_slots partial
- * results (fp32 O [block x D] plus running max and sum per query row, per slot).
+ * item counters (one int32 per group, 4 KiB apart), then 2 n_slots int32 merge
+ * counters (rounded up to 256 bytes), then n_slots partial results (fp32 O
+ * [block x D] plus running max and sum per query row, per slot).
  */
 BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D, int32_t block);
 
@@ -232,11 +234,12 @@ BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D, int32_t b
  *               claims the group's remaining items in list order from a
  *               counter in the workspace.
  *   workspace   with a work list: >= bsa_forward_workspace_bytes(n_slots, D,
- *               block) bytes of device memory, 16-byte aligned, whose first
- *               256 KiB (the counters) are zero before the first call; every
- *               call that completes leaves them zero again, so calls that use
- *               one workspace must be ordered on one stream.  Without a list
- *               it may be NULL.  The rest needs no initialisation.
+ *               block) bytes of device memory, 16-byte aligned, whose
+ *               counters (item and merge counters) are zero before the first
+ *               call; every call that completes leaves them zero again, so
+ *               calls that use one workspace must be ordered on one stream.
+ *               Without a list it may be NULL.  The partial results need no
+ *               initialisation.
  *   scale       softmax scale; <= 0 means 1/sqrt(D).
  * A row with no active block yields O = 0 and LSE = -inf.
  * Errors: INVALID_ARG (also a work list without a workspace), UNSUPPORTED,

@@ -33,7 +33,7 @@ def test_status_strings_and_version():
     assert bsa.status_string(-1) == "BSA_ERR_INVALID_ARG"
     assert bsa.status_string(-5) == "BSA_ERR_PLAN_MISMATCH"
     assert bsa.status_string(-99) == "BSA_ERR_UNKNOWN"
-    assert bsa.abi_version() == bsa.ABI_VERSION == 2
+    assert bsa.abi_version() == bsa.ABI_VERSION == 3
 
 
 def test_budget_matches_oracle():
@@ -82,7 +82,9 @@ def check_work(work, ni, nm, ns, rp, max_tiles, nb=0, n_groups=1):
     merges = work[4 * ni:4 * ni + 3 * nm].reshape(nm, 3)
     table = work[4 * ni + 3 * nm:]
     G = int(table[0])
-    assert G == (n_groups if nb > 0 and n_groups > 1 else 1) and len(table) == G + 2
+    assert G == (n_groups if nb > 0 and n_groups > 1 else 1) and len(table) == G + 2 + ns
+    slot_map = table[G + 2:]
+    table = table[:G + 2]
     starts = table[1:]
     assert starts[0] == 0 and starts[-1] == ni and (np.diff(starts) >= 0).all()
     sizes = items[:, 2] - items[:, 1]
@@ -113,6 +115,8 @@ def check_work(work, ni, nm, ns, rp, max_tiles, nb=0, n_groups=1):
             assert len(parts) == n and [p[2] for p in parts] == list(range(s0, s0 + n))
             assert all(e - b <= max_tiles for b, e, _ in parts) and max(e - b for b, e, _ in parts) - min(e - b for b, e, _ in parts) <= 1
             used_slots += list(range(s0, s0 + n))
+            m = [i for i, r in enumerate(merges[:, 0].tolist()) if r == row]
+            assert len(m) == 1 and (slot_map[s0:s0 + n] == m[0]).all()
         else:
             assert len(parts) == 1 and parts[0][2] == -1
             assert max_tiles <= 0 or lens[row] <= max_tiles
@@ -189,6 +193,18 @@ def test_device_entry_points_reject_bad_arguments():
     assert mk(ws_bytes=16) == -4                      # workspace too small
     assert L.bsa_schedule(None, 4, 4, fake, None) == -1
     assert L.bsa_schedule(fake, 4, 100000, fake, None) == -2
-    assert L.bsa_forward_workspace_bytes(3, 64, 64) == 64 * 4096 + 3 * 64 * 66 * 4
+    assert L.bsa_forward_workspace_bytes(3, 64, 64) == 64 * 4096 + 256 + 3 * 64 * 66 * 4
+    assert L.bsa_forward_workspace_bytes(40, 64, 64) == 64 * 4096 + 512 + 40 * 64 * 66 * 4
     assert L.bsa_forward_workspace_bytes(0, 64, 64) == 64 * 4096
     assert L.bsa_build_mask_workspace_bytes(1, 1, 128, 64, 64) >= 256 + 2 * 2 * 64 * 4 + 4 * 4
+
+
+def test_import_does_not_open_the_library():
+    """The package and its build module import without opening libbsa.so (so a
+    missing or stale library can be rebuilt); the first call opens it."""
+    import subprocess
+    import sys
+    code = ("import block_sparse_attention_flashattn_amd as b, block_sparse_attention_flashattn_amd.build;"
+            "assert b._Lib._handle is None; b.abi_version(); assert b._Lib._handle is not None")
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__import__("os").path.abspath(__file__)))
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=root)

@@ -176,10 +176,38 @@ def test_item_queue_matches_static_order_and_resets(block, D, n_groups):
         assert int(work.workspace[:64 * 4096].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("block,D,max_tiles,n_groups", [(64, 64, 2, 8), (64, 64, 3, 1),
+                                                         (64, 64, 1, 8), (64, 128, 2, 8)])
+def test_cut_rows_repeat_bitwise_and_counters_reset(block, D, max_tiles, n_groups):
+    """Cut rows combined once their last chunk is stored: the oracle's values, the same
+    bits call after call, and every item and merge counter back at zero after each call.
+    Enough items that most of them are claimed from the per-group counters."""
+    bsa = need_gpu()
+    print(f"case block={block} D={D} max_tiles={max_tiles} n_groups={n_groups}", flush=True)
+    rng = np.random.default_rng(7 * block + D + max_tiles + n_groups)
+    B, H, nb = 1, 16, 20
+    N = nb * block - 9
+    rp, ci = rand_csr(rng, B, H, nb, 0.5, empty_rows=(3, 100))
+    work = bsa.Work.from_host(rp, D, block, max_tiles, "cuda", nb=nb, n_groups=n_groups)
+    assert work.n_merges > 0
+    n_cnt = bsa.forward_workspace_bytes(work.n_slots, D, block) - work.n_slots * block * (D + 2) * 4
+    assert n_cnt >= 64 * 4096 + 8 * work.n_slots
+    q, k, v = W.gaussian_qkv(400 + max_tiles, B, H, N, D)
+    stats, o0, l0 = run_and_compare(bsa, q, k, v, rp, ci, block, work=work)
+    print(stats)
+    assert int(work.workspace[:n_cnt].count_nonzero()) == 0
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for _ in range(2):
+        o1, l1 = bsa.forward(qd, kd, vd, rp, ci, block, work=work)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+        assert int(work.workspace[:n_cnt].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("block,D,max_tiles", [(64, 64, 1), (64, 64, 3), (64, 128, 2),
                                                (128, 64, 4), (128, 128, 1)])
 def test_cut_rows_match_oracle(block, D, max_tiles):
-    """Rows cut into chunks (partials in the workspace + merge kernel) against the oracle."""
+    """Rows cut into chunks (partials in the workspace, then combined) against the oracle."""
     bsa = need_gpu()
     print(f"case block={block} D={D} max_tiles={max_tiles}", flush=True)
     rng = np.random.default_rng(block + D + max_tiles)
