@@ -918,25 +918,33 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
   stage_q(nxt_row, nxt_bh);
   // Chunk partials and their merge.  A wave's partial stores (agent-scope
   // coherent) are known complete one epilogue later, where the wait for the
-  // query tile covers them (after the last item: at once, by a full wait); the
-  // wave then counts its query group of that chunk in, and the wave that
-  // brings the count to the number of chunks combines the group's partials of
-  // every chunk of the row.
+  // query tile covers them (after the last item: at once, by a full wait).
+  // The wave then counts its query group of that chunk in; the wave whose
+  // count-in completes the number of chunks combines the group's partials of
+  // every chunk of the row and clears the count.  The count-in's result is
+  // read on every path before the epilogue's stores, so that no memory result
+  // is left in flight into the loop (the compiler's wait bookkeeping would
+  // then drain the tile prefetch there).
   int rel_slot = -1;  // chunk whose partial this wave stored, not yet counted in
   const int32_t* slot_merge =
       work ? work + 4 * size_t(n_items) + 3 * size_t(n_merges) + 2 + src.ng : nullptr;
   const int32_t* merges = work ? work + 4 * size_t(n_items) : nullptr;
+  // (Merge indices pass through readfirstlane: they are wave-uniform, and the
+  // compiler must keep them, and the loads they address, scalar.)
   auto merge_of = [&](int slot) -> int {
     const int m = (slot >= 0 && slot < n_slots) ? ld_uniform(slot_merge, slot) : -1;
-    return (m >= 0 && m < n_merges && m < n_slots) ? m : -1;
+    return __builtin_amdgcn_readfirstlane((m >= 0 && m < n_merges && m < n_slots) ? m : -1);
   };
-  // Count this wave's query group of chunk `slot` in (lane 0 holds the old
-  // count; the result is read after a wait that covers it).
+  // Count this wave's query group of merge m in; lane 0 gets the count before.
   auto count_in = [&](int m) -> int {
     int old = 0;
     if (lane == 0)
       old = __hip_atomic_fetch_add(mctr + 2 * m + kh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return old;
+  };
+  // Whether a count-in (old count in lane 0) completed merge m (m >= 0).
+  auto completes = [&](int m, int old) -> bool {
+    return old == ld_uniform(merges, 3 * size_t(m) + 2) - 1;
   };
   // Combine query group kh of cut row `merges[m]` from its chunks' partials:
   // with M = max_c m_c, O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c and
@@ -1328,6 +1336,14 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     } else {
       k_nn = src.stat(round);
     }
+    // The count-in's result, before this epilogue's stores (the wait then
+    // covers only the prefetched tile and the count-in).
+    int mg_a = -1, mg_b = -1;
+    {
+      const int old = __builtin_amdgcn_readfirstlane(rel_old);  // on every path
+      if (rel_m >= 0 && completes(rel_m, old)) mg_a = rel_m;
+    }
+    mg_a = __builtin_amdgcn_readfirstlane(mg_a);
     if (kh == 0)
       finish(acc[0], m_run[0], l_half[0]);
     else
@@ -1335,12 +1351,6 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     lds_barrier();  // exchange areas free before loads target them again
     // Merges this wave completes: the previous chunk's (counted in above) and,
     // after the last item, this one's (its stores are waited for here).
-    int mg_a = -1, mg_b = -1;
-    if (rel_m >= 0) {
-      wait_vm_n(n_stores);  // the count-in (issued before this epilogue's stores)
-      if (__builtin_amdgcn_readfirstlane(rel_old) == ld_uniform(merges, 3 * size_t(rel_m) + 2) - 1)
-        mg_a = rel_m;
-    }
     if (cur_row >= 0 && cur_slot >= 0) {
       if (more) {
         rel_slot = cur_slot;
@@ -1348,13 +1358,11 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
         const int m = merge_of(cur_slot);
         if (m >= 0) {
           wait_vm(0);
-          const int old = count_in(m);
-          wait_vm(0);
-          if (__builtin_amdgcn_readfirstlane(old) == ld_uniform(merges, 3 * size_t(m) + 2) - 1)
-            mg_b = m;
+          if (completes(m, __builtin_amdgcn_readfirstlane(count_in(m)))) mg_b = m;
         }
       }
     }
+    mg_b = __builtin_amdgcn_readfirstlane(mg_b);
     int merge_stores = 0;
     while (mg_a >= 0 || mg_b >= 0) {
       const int m = mg_a >= 0 ? mg_a : mg_b;
