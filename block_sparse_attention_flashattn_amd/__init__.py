@@ -222,9 +222,14 @@ def _fwd_lds_bytes(block: int, D: int) -> int:
 
 
 def default_max_tiles(nnz: int, block: int, D: int, n_cu: int, lds_per_cu: int = 160 * 1024):
-    """Cut rows longer than about half the average work of one resident workgroup slot."""
+    """Cut rows longer than 1.5x the average work of one resident workgroup slot.
+
+    A row well above the average keeps its workgroup busy after the others are
+    done; cutting it into a few chunks of about that size balances it, while
+    every extra chunk costs an epilogue, a partial result and a share of a merge
+    (on the t2i mask, text rows cut in two ran faster than in three or five)."""
     slots = n_cu * max(1, lds_per_cu // _fwd_lds_bytes(block, D))
-    return max(8, -(-nnz // (2 * slots)))
+    return max(8, -(-3 * nnz // (2 * slots)))
 
 
 # Accelerator dies (XCDs) of an MI355X; workgroups are dealt to them round robin.
