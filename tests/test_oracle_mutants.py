@@ -144,3 +144,74 @@ def test_mutant_scaled_scores_are_harmless_for_ranking(monkeypatch):
     monkeypatch.setattr(Bd, "block_scores", lambda pq, pk: 0.125 * orig(pq, pk))
     assert fails(TB.test_hand_block_constant, 8)      # the hand scores are exact integers
     assert not fails(TB.test_bruteforce_subsets, 0)   # but selections are unchanged
+
+
+# ---- block-mass oracle -------------------------------------------------------
+import test_oracle_mass as TM
+from oracle import mass as Ms
+
+MASS_PINS = [
+    (TM.test_rows_sum_to_query_count, (150, 64)),
+    (TM.test_brute_force_tiny, ()),
+    (TM.test_equal_keys_give_uniform_mass, ()),
+    (TM.test_two_pass_form_matches, ()),
+    (TM.test_oracle_csr_hand_row, ()),
+    (TM.test_oracle_keeps_the_most_mass, ()),
+    (TM.test_full_csr_retains_everything, ()),
+]
+
+
+def any_mass_pin_fails():
+    return any(fails(f, *a) for f, a in MASS_PINS)
+
+
+def test_unmodified_mass_oracle_passes():
+    assert not any_mass_pin_fails()
+
+
+def test_mass_mutant_transposed_probabilities(monkeypatch):
+    """Block sums of P^T (queries and keys swapped)."""
+    orig = Ms.dense_probabilities
+    monkeypatch.setattr(Ms, "dense_probabilities", lambda q, k, s: orig(q, k, s).T.copy())
+    assert any_mass_pin_fails()
+
+
+def test_mass_mutant_normalised_over_queries(monkeypatch):
+    """Softmax taken down the columns instead of along each query's row."""
+    def bad(q, k, scale):
+        s = scale * (Ms._as64(q) @ Ms._as64(k).T)
+        e = np.exp(s - s.max(axis=0, keepdims=True))
+        return e / e.sum(axis=0, keepdims=True)
+    monkeypatch.setattr(Ms, "dense_probabilities", bad)
+    assert any_mass_pin_fails()
+
+
+def test_mass_mutant_scale_dropped(monkeypatch):
+    orig = Ms.dense_probabilities
+    monkeypatch.setattr(Ms, "dense_probabilities", lambda q, k, s: orig(q, k, 1.0))
+    assert any_mass_pin_fails()
+
+
+def test_mass_mutant_oracle_ties_to_higher_block(monkeypatch):
+    def bad(mass, row_ptr):
+        m = np.asarray(mass, dtype=np.float64).reshape(-1, mass.shape[-1])
+        rp = np.asarray(row_ptr)
+        nb = m.shape[1]
+        out = []
+        for r in range(m.shape[0]):
+            order = np.lexsort((-np.arange(nb), -m[r]))
+            out.append(np.sort(order[:rp[r + 1] - rp[r]]))
+        return np.concatenate(out).astype(np.int32)
+    monkeypatch.setattr(Ms, "oracle_csr", bad)
+    assert any_mass_pin_fails()
+
+
+def test_mass_mutant_oracle_smallest_first(monkeypatch):
+    def bad(mass, row_ptr):
+        m = np.asarray(mass, dtype=np.float64).reshape(-1, mass.shape[-1])
+        rp = np.asarray(row_ptr)
+        nb = m.shape[1]
+        return np.concatenate([np.sort(np.lexsort((np.arange(nb), m[r]))[:rp[r + 1] - rp[r]])
+                               for r in range(m.shape[0])]).astype(np.int32)
+    monkeypatch.setattr(Ms, "oracle_csr", bad)
+    assert any_mass_pin_fails()
