@@ -31,6 +31,7 @@ __all__ = [
     "BsaError", "lib", "LIB_PATH", "status_string", "abi_version", "budget_from_density",
     "mask_plan", "work_plan", "validate_csr_host", "build_mask_workspace_bytes",
     "forward_workspace_bytes", "build_mask", "build_mask_status", "schedule", "forward",
+    "block_mass", "select_by_mass", "csr_mass", "block_oracle",
     "Plan", "Work", "n_blocks", "default_max_tiles",
 ]
 
@@ -56,11 +57,14 @@ _SIGS = {
     "bsa_forward_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "bsa_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                            _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "bsa_block_mass": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
+    "bsa_select_by_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "bsa_csr_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
 }
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class BsaError(RuntimeError):
@@ -404,3 +408,82 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx,
                            _t_ptr(lse) if return_lse else None, _t_ptr(ws), wsb,
                            _stream_ptr(dev)), "bsa_forward")
     return out, (lse if return_lse else None)
+
+
+def block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, block: int,
+               scale: Optional[float] = None) -> torch.Tensor:
+    """Exact attention mass per block pair -> fp32 [B,H,nb,nb].
+
+    mass[b,h,i,j] = sum over queries of block i and keys of block j of
+    exp(scale q.k - lse): with the dense LSE (`forward` over an all-ones CSR),
+    the block sums of the dense attention probabilities.
+    """
+    B, H, N, D = _check_qkv(q, k)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be contiguous fp32 [B,H,N]")
+    nb = n_blocks(N, block)
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not s > 0.0:
+        raise ValueError("scale must be positive (or None for 1/sqrt(D))")
+    mass = torch.empty((B, H, nb, nb), dtype=torch.float32, device=q.device)
+    _check(lib.bsa_block_mass(_t_ptr(q), _t_ptr(k), _t_ptr(lse), B, H, N, D, block, s,
+                              _t_ptr(mass), _stream_ptr(q.device)), "bsa_block_mass")
+    return mass
+
+
+def select_by_mass(mass: torch.Tensor, row_ptr, check: bool = True) -> torch.Tensor:
+    """Block oracle at the density of a CSR: per row, as many blocks as row_ptr gives it,
+    the ones of largest mass (ties to the lower block), ascending -> col_idx (device)."""
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or mass.dim() < 2:
+        raise ValueError("mass must be contiguous fp32 [..., nb]")
+    nb = mass.shape[-1]
+    n_rows = mass.numel() // nb
+    dev = mass.device
+    row_ptr = _dev_i32(row_ptr, dev)
+    if row_ptr.numel() != n_rows + 1:
+        raise ValueError("row_ptr must have one entry per mass row plus one")
+    nnz = int(row_ptr[-1].item())
+    col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.bsa_select_by_mass(_t_ptr(mass), n_rows, nb, _t_ptr(row_ptr), _t_ptr(col_idx),
+                                  _t_ptr(status), _stream_ptr(dev)), "bsa_select_by_mass")
+    if check and int(status.item()) != 0:
+        raise BsaError(f"bsa_select_by_mass: {int(status.item())} rows longer than nb or out of range")
+    return col_idx[:nnz]
+
+
+def csr_mass(mass: torch.Tensor, row_ptr, col_idx) -> torch.Tensor:
+    """Retained mass of a CSR per row -> fp32 [n_rows] (device)."""
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or mass.dim() < 2:
+        raise ValueError("mass must be contiguous fp32 [..., nb]")
+    nb = mass.shape[-1]
+    n_rows = mass.numel() // nb
+    dev = mass.device
+    row_ptr = _dev_i32(row_ptr, dev)
+    col_idx = _dev_i32(col_idx, dev)
+    if row_ptr.numel() != n_rows + 1:
+        raise ValueError("row_ptr must have one entry per mass row plus one")
+    if col_idx.numel() == 0:
+        col_idx = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty(n_rows, dtype=torch.float32, device=dev)
+    _check(lib.bsa_csr_mass(_t_ptr(mass), n_rows, nb, _t_ptr(row_ptr), _t_ptr(col_idx),
+                            _t_ptr(out), _stream_ptr(dev)), "bsa_csr_mass")
+    return out
+
+
+def block_oracle(q: torch.Tensor, k: torch.Tensor, row_ptr, block: int,
+                 scale: Optional[float] = None):
+    """Two-pass exact block selection at the density of a CSR.
+
+    Pass 1: dense LSE (`forward` over the all-ones CSR).  Pass 2: `block_mass`.
+    Then `select_by_mass` with row_ptr's row lengths.  Returns (col_idx, mass).
+    """
+    B, H, N, D = _check_qkv(q, k)
+    nb = n_blocks(N, block)
+    dev = q.device
+    rows = B * H * nb
+    rp1 = torch.arange(rows + 1, dtype=torch.int32, device=dev) * nb
+    ci1 = torch.arange(nb, dtype=torch.int32, device=dev).repeat(rows)
+    _, lse = forward(q, k, k, rp1, ci1, block, scale=scale)
+    mass = block_mass(q, k, lse, block, scale)
+    return select_by_mass(mass, row_ptr), mass

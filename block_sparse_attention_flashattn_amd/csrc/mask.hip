@@ -140,7 +140,12 @@ __global__ __launch_bounds__(256) void select_kernel(
       prior ? prior + (prior_per_head ? size_t(bh) * nb * nb : size_t(0)) + size_t(i) * nb
             : nullptr;
   const float* srow = S ? S + (size_t(bh) * nb + i) * nb : nullptr;
-  const int ki = budgets ? min(max(budgets[i], 0), nb) : k_density;
+  const int nnz = row_ptr[n_rows];
+  const int start = row_ptr[r];
+  const int cnt = row_ptr[r + 1] - start;
+  // k_density < 0: the row keeps as many blocks as its CSR row has (the block
+  // oracle at the density of a given CSR).
+  const int ki = budgets ? min(max(budgets[i], 0), nb) : (k_density >= 0 ? k_density : min(max(cnt, 0), nb));
 
   uint64_t key[CM];
   bool insel[CM];
@@ -158,9 +163,6 @@ __global__ __launch_bounds__(256) void select_kernel(
     nsel += __popcll(__ballot(in));
   }
   const int fill = max(0, ki - nsel);
-  const int nnz = row_ptr[n_rows];
-  const int start = row_ptr[r];
-  const int cnt = row_ptr[r + 1] - start;
   if (cnt != nsel + fill || start < 0 || start + cnt > nnz) {
     if (lane == 0) atomicAdd(status, 1);
     return;
@@ -290,6 +292,32 @@ extern "C" BSA_API bsa_status bsa_build_mask(const void* q, const void* k, int32
   else
     launch_select<16>(Sp, prior_dev, ph, budgets_dev, kd, diag, nb, n_rows, row_ptr_dev,
                       col_idx_dev, status, s);
+  BSA_HIP_CHECK_LAUNCH();
+  return BSA_OK;
+}
+
+extern "C" BSA_API bsa_status bsa_select_by_mass(const float* mass_dev, int32_t n_rows, int32_t nb,
+                                                 const int32_t* row_ptr_dev, int32_t* col_idx_dev,
+                                                 int32_t* status_dev, void* stream) {
+  using namespace bsa;
+  if (!mass_dev || !row_ptr_dev || !col_idx_dev || !status_dev || n_rows < 1 || nb < 1)
+    return BSA_ERR_INVALID_ARG;
+  if (nb > kMaxBlocks) return BSA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(zero_status_kernel, dim3(1), dim3(1), 0, s, status_dev);
+  BSA_HIP_CHECK_LAUNCH();
+  // Rows are (head, block) pairs of nb rows each: prior none, no forced diagonal,
+  // k from the row lengths.
+  if (nb <= 64)
+    launch_select<1>(mass_dev, nullptr, 0, nullptr, -1, 0, nb, n_rows, row_ptr_dev, col_idx_dev, status_dev, s);
+  else if (nb <= 128)
+    launch_select<2>(mass_dev, nullptr, 0, nullptr, -1, 0, nb, n_rows, row_ptr_dev, col_idx_dev, status_dev, s);
+  else if (nb <= 256)
+    launch_select<4>(mass_dev, nullptr, 0, nullptr, -1, 0, nb, n_rows, row_ptr_dev, col_idx_dev, status_dev, s);
+  else if (nb <= 512)
+    launch_select<8>(mass_dev, nullptr, 0, nullptr, -1, 0, nb, n_rows, row_ptr_dev, col_idx_dev, status_dev, s);
+  else
+    launch_select<16>(mass_dev, nullptr, 0, nullptr, -1, 0, nb, n_rows, row_ptr_dev, col_idx_dev, status_dev, s);
   BSA_HIP_CHECK_LAUNCH();
   return BSA_OK;
 }

@@ -51,7 +51,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 3
+#define BSA_ABI_VERSION 4
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -251,6 +251,61 @@ BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v, int3
                                const int32_t* work_dev, int32_t n_items, int32_t n_merges,
                                int32_t n_slots, float scale, void* o, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Exact attention mass per block pair (device, async): the second pass of
+ * exact block selection.  Page "Can sparse attention close the quality gap in
+ * diffusion transformers": its oracle sections compare sparse attention, at
+ * equal density, with oracles that keep the most mass of the exact dense
+ * attention probabilities (the block oracle chooses KV blocks per query block);
+ * its section on token-level selection notes that exact selection needs the
+ * scores, which a FlashAttention pass does not expose, hence two passes.  The
+ * first is bsa_forward with an all-ones CSR (its LSE); this is the second:
+ *   mass[r, j] = sum over queries t of block i and keys c of block j (t, c < N)
+ *                of exp(scale q_t.k_c - lse[bi,h,t]),   r = (bi*H + h)*nb + i.
+ * With the dense LSE a mass row sums to the query count of its block.
+ *   q, k       bf16 [B,H,N,D] device, 16-byte aligned.
+ *   lse        fp32 [B,H,N] device: the dense natural-log LSE (queries with a
+ *              non-finite LSE contribute nothing).
+ *   scale      softmax scale; <= 0 means 1/sqrt(D) (must match the LSE's).
+ *   mass_out   fp32 [B*H*nb, nb] device, written.
+ * (block, D) as bsa_forward.  Errors: INVALID_ARG, UNSUPPORTED (shape, or a head
+ * of 2^31 bytes or more), HIP.
+ */
+BSA_API bsa_status bsa_block_mass(const void* q, const void* k, const float* lse, int32_t B,
+                                  int32_t H, int32_t N, int32_t D, int32_t block, float scale,
+                                  float* mass_out, void* stream);
+
+/*
+ * Block oracle at the density of a given CSR (device, async): for every row r,
+ * the row_ptr[r+1] - row_ptr[r] KV blocks of largest mass[r, :] (ties to the
+ * lower block index), written ascending to col_idx[row_ptr[r] ...].  Page "Can
+ * sparse attention close the quality gap in diffusion transformers", oracle
+ * sections: equal density, most retained mass.
+ *   mass_dev     fp32 [n_rows, nb] device (bsa_block_mass), n_rows = B*H*nb.
+ *   row_ptr_dev  int32 [n_rows + 1] device (the CSR whose density is matched).
+ *   col_idx_dev  int32 [row_ptr[n_rows]] device, written.
+ *   status_dev   int32 device word, set to the number of rows left unwritten
+ *                (a row longer than nb or outside [0, nnz]); read it after the
+ *                stream completes.
+ * nb at most 1024.  Errors: INVALID_ARG, UNSUPPORTED (nb), HIP.
+ */
+BSA_API bsa_status bsa_select_by_mass(const float* mass_dev, int32_t n_rows, int32_t nb,
+                                      const int32_t* row_ptr_dev, int32_t* col_idx_dev,
+                                      int32_t* status_dev, void* stream);
+
+/*
+ * Retained mass of a CSR (device, async): out[r] = sum of mass[r, j] over the
+ * blocks j listed in row r (columns outside [0, nb) ignored, row bounds clamped
+ * to [0, nnz]); divided by the block's query count it is the mean attention
+ * probability the row's queries keep.
+ *   mass  fp32 [n_rows, nb] device; row_ptr int32 [n_rows + 1], col_idx int32
+ *   [nnz] device; out fp32 [n_rows] device, written.
+ * Errors: INVALID_ARG, HIP.
+ */
+BSA_API bsa_status bsa_csr_mass(const float* mass, int32_t n_rows, int32_t nb,
+                                const int32_t* row_ptr, const int32_t* col_idx, float* out,
+                                void* stream);
 
 #ifdef __cplusplus
 }
