@@ -208,6 +208,39 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "cu_count": torch.cuda.get_device_properties(0).multi_processor_count,
     }
+    # Exact block selection at this workload's density (two passes: dense LSE, then the
+    # block mass; the block oracle keeps the most mass per row), timed per kernel, and
+    # the mass and output error of this workload's CSR against it.
+    rp_all = torch.arange(n_rows + 1, dtype=torch.int32, device=dev) * nb
+    ci_all = torch.arange(nb, dtype=torch.int32, device=dev).repeat(n_rows)
+    o_dense = torch.empty_like(qd)
+    lse_dense = torch.empty_like(lse)
+    dense_once_ms = time_launches(lambda: bsa.forward(qd, kd, vd, rp_all, ci_all, w.block,
+                                                      out=o_dense, lse=lse_dense), n=5)
+    mass = bsa.block_mass(qd, kd, lse_dense, w.block)
+    mass_ms = time_launches(lambda: bsa.block_mass(qd, kd, lse_dense, w.block), n=10)
+    ci_or = bsa.select_by_mass(mass, plan.row_ptr)
+    select_ms = time_launches(lambda: bsa.select_by_mass(mass, plan.row_ptr, check=False,
+                                                                  nnz=plan.nnz), n=10)
+    kept_csr = bsa.csr_mass(mass, plan.row_ptr, col_idx[:plan.nnz]).double().sum().item()
+    kept_or = bsa.csr_mass(mass, plan.row_ptr, ci_or).double().sum().item()
+    o_or = torch.empty_like(qd)
+    bsa.forward(qd, kd, vd, plan.row_ptr, ci_or, w.block, out=o_or, lse=None, return_lse=False)
+    bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, work=plan, out=o, lse=lse)
+    torch.cuda.synchronize()
+    n_q = w.B * w.H * w.N
+    def rel_err(a):
+        d = (a.float() - o_dense.float()).norm().item()
+        return d / max(o_dense.float().norm().item(), 1e-30)
+    mass_flops = 2.0 * w.B * w.H * float(w.N) * float(w.N) * w.D   # the QK^T products
+    extra["block_oracle"] = {
+        "dense_forward_ms": dense_once_ms, "block_mass_ms": mass_ms, "select_ms": select_ms,
+        "block_mass_tflops": mass_flops / (mass_ms * 1e-3) / 1e12,
+        "block_mass_scores_per_ns": w.B * w.H * float(w.N) ** 2 / (mass_ms * 1e6),
+        "mean_kept_mass_csr": kept_csr / n_q, "mean_kept_mass_oracle": kept_or / n_q,
+        "rel_err_vs_dense_csr": rel_err(o), "rel_err_vs_dense_oracle": rel_err(o_or),
+    }
+
     if args.extra:
         rp1 = (np.arange(n_rows + 1) * nb).astype(np.int32)
         ci1 = torch.from_numpy(np.tile(np.arange(nb, dtype=np.int32), n_rows)).to(dev)

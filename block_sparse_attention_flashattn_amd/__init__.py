@@ -431,9 +431,13 @@ def block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, block: int,
     return mass
 
 
-def select_by_mass(mass: torch.Tensor, row_ptr, check: bool = True) -> torch.Tensor:
+def select_by_mass(mass: torch.Tensor, row_ptr, check: bool = True,
+                   nnz: Optional[int] = None) -> torch.Tensor:
     """Block oracle at the density of a CSR: per row, as many blocks as row_ptr gives it,
-    the ones of largest mass (ties to the lower block), ascending -> col_idx (device)."""
+    the ones of largest mass (ties to the lower block), ascending -> col_idx (device).
+
+    `nnz` (row_ptr's last entry), when the caller knows it, spares a device read;
+    `check` waits for the call and raises if a row was longer than nb."""
     if mass.dtype != torch.float32 or not mass.is_contiguous() or mass.dim() < 2:
         raise ValueError("mass must be contiguous fp32 [..., nb]")
     nb = mass.shape[-1]
@@ -442,7 +446,8 @@ def select_by_mass(mass: torch.Tensor, row_ptr, check: bool = True) -> torch.Ten
     row_ptr = _dev_i32(row_ptr, dev)
     if row_ptr.numel() != n_rows + 1:
         raise ValueError("row_ptr must have one entry per mass row plus one")
-    nnz = int(row_ptr[-1].item())
+    if nnz is None:
+        nnz = int(row_ptr[-1].item())
     col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
     status = torch.empty(1, dtype=torch.int32, device=dev)
     _check(lib.bsa_select_by_mass(_t_ptr(mass), n_rows, nb, _t_ptr(row_ptr), _t_ptr(col_idx),

@@ -29,80 +29,115 @@ __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// One workgroup (four wavefronts) per (query block, group of KV blocks).  A block
-// pair is cut into (BLK/32)^2 tiles of 32 keys x 32 queries, S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16: lane (ql, hh) holds, for query ql of its tile, the
-// keys 8(e/4) + 4hh + (e%4), e = 0..15.  A wavefront owns BLK*BLK/4096 tiles that
-// share one key group (BLK 64: one query group; BLK 128: all four), keeps their
-// query fragments in registers and reads its key fragments straight from memory
-// (16-byte buffer loads; rows past N read as zeros and are masked out).
+// One workgroup (four wavefronts) per (four 32-query groups of one head: two query
+// blocks at BLK 64, one at BLK 128; a group of KV blocks).  A block pair is cut
+// into tiles of 32 keys x 32 queries, S^T = K Q^T with v_mfma_f32_32x32x16_bf16:
+// lane (ql, hh) holds, for query ql of the tile, the keys 8(e/4) + 4hh + (e%4),
+// e = 0..15.  Each wavefront takes one 32-key group of a KV block against all four
+// query groups (whose fragments stay in registers), so every key fragment is read
+// once per workgroup and serves 128 queries, straight from memory (16-byte buffer
+// loads; rows past N read as zeros and are masked out); the four wavefronts cover
+// 128 keys per step (two KV blocks at BLK 64, one at BLK 128).  Per-lane partial
+// sums are kept per (query block, KV block) and reduced across the wavefront once
+// at the end.
 template <int BLK, int HD>
 __global__ __launch_bounds__(256) void mass_kernel(const uint16_t* __restrict__ Q,
                                                    const uint16_t* __restrict__ K,
                                                    const float* __restrict__ lse, int32_t N,
                                                    int32_t nb, float sl2,
                                                    float* __restrict__ mass) {
-  constexpr int QG = BLK / 32;
-  constexpr int PW = QG * QG / 4;  // tiles per wavefront
-  constexpr int NC = HD / 16;      // 16-deep MFMA steps
-  __shared__ float red[4][kMassBlocksPerWg];
+  constexpr int QG = BLK / 32;                // 32-row groups per block
+  constexpr int QB = 4 / QG;                  // query blocks per workgroup
+  constexpr int NC = HD / 16;                 // 16-deep MFMA steps
+  constexpr int JPS = 4 / QG;                 // KV blocks per step
+  constexpr int NS = kMassBlocksPerWg / JPS;  // steps
+  __shared__ float red[QB][4][kMassBlocksPerWg];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 31, hh = lane >> 5;
-  const int r = blockIdx.x;
-  const int bh = r / nb, i = r - bh * nb;
+  const int npair = (nb + QB - 1) / QB;       // query-block tuples per head
+  const int bh = blockIdx.x / npair;
+  const int i0 = (blockIdx.x - bh * npair) * QB;
   const int j0 = blockIdx.y * kMassBlocksPerWg;
   const int jn = min(kMassBlocksPerWg, nb - j0);
   const size_t head = size_t(bh) * size_t(N) * HD;
   const uint32_t hbytes = static_cast<uint32_t>(N) * HD * 2u;
   const __amdgpu_buffer_rsrc_t qr = rsrc(Q + head, hbytes);
   const __amdgpu_buffer_rsrc_t kr = rsrc(K + head, hbytes);
-  const int kg = (wave * PW) / QG;  // the key group of all this wavefront's tiles
+  const int kg = wave % QG;    // key group of this wavefront
+  const int jsub = wave / QG;  // which KV block of a step
 
-  bf16x8 qf[PW][NC];
-  float lq[PW];   // lse of the lane's query in log2 units
-  bool qv[PW];    // the query exists and has a finite normaliser
+  // Query group g = 0..3: block i0 + g / QG, rows 32 (g % QG) .. +31.
+  bf16x8 qf[4][NC];
+  float lq[4];  // lse of the lane's query in log2 units; +inf drops the query
 #pragma unroll
-  for (int t = 0; t < PW; ++t) {
-    const int qg = (wave * PW + t) % QG;
-    const int qrow = i * BLK + 32 * qg + ql;
+  for (int g = 0; g < 4; ++g) {
+    const int qb = i0 + g / QG;
+    const int qrow = qb * BLK + 32 * (g % QG) + ql;
+    const bool ok = qb < nb && qrow < N;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qf[t][c] = load16(qr, static_cast<uint32_t>(qrow * HD + 16 * c + 8 * hh) * 2u);
-    const float l = qrow < N ? lse[size_t(bh) * N + qrow] : -INFINITY;
-    qv[t] = l > -INFINITY && l < INFINITY;
-    lq[t] = qv[t] ? l * 1.4426950408889634f : 0.f;
+      qf[g][c] = load16(qr, ok ? static_cast<uint32_t>(qrow * HD + 16 * c + 8 * hh) * 2u : hbytes);
+    const float l = ok ? lse[size_t(bh) * N + qrow] : -INFINITY;
+    lq[g] = (l > -INFINITY && l < INFINITY) ? l * 1.4426950408889634f : INFINITY;
   }
 
-  for (int jj = 0; jj < jn; ++jj) {
-    const int j = j0 + jj;
-    const int krow = j * BLK + 32 * kg + ql;
-    bf16x8 kf[NC];
+  float part[QB][NS];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      kf[c] = load16(kr, static_cast<uint32_t>(krow * HD + 16 * c + 8 * hh) * 2u);
-    float sum = 0.f;
+  for (int t = 0; t < NS; ++t) {
 #pragma unroll
-    for (int t = 0; t < PW; ++t) {
-      f32x16 s = {};
+    for (int b = 0; b < QB; ++b) part[b][t] = 0.f;
+    const int jj = t * JPS + jsub;
+    if (jj < jn) {
+      const int j = j0 + jj;
+      const int kbase = j * BLK + 32 * kg;
+      bf16x8 kf[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[t][c], s, 0, 0, 0);
-      if (qv[t]) {
+      for (int c = 0; c < NC; ++c)
+        kf[c] = load16(kr, static_cast<uint32_t>((kbase + ql) * HD + 16 * c + 8 * hh) * 2u);
+      const bool full = kbase + 32 <= N;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = j * BLK + 32 * kg + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key < N) sum += __builtin_amdgcn_exp2f(s[e] * sl2 - lq[t]);
+      for (int g = 0; g < 4; ++g) {
+        f32x16 sv = {};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[g][c], sv, 0, 0, 0);
+        float a0 = 0.f, a1 = 0.f;
+        if (full) {
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            a0 += __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -lq[g]));
+            a1 += __builtin_amdgcn_exp2f(fmaf(sv[e + 1], sl2, -lq[g]));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kbase + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (key < N) a0 += __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -lq[g]));
+          }
         }
+        part[g / QG][t] += a0 + a1;
       }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-    if (lane == 0) red[wave][jj] = sum;
   }
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      float v = part[b][t];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      const int jj = t * JPS + jsub;
+      if (lane == 0 && jj < jn) red[b][kg][jj] = v;
+    }
   __syncthreads();
-  if (static_cast<int>(threadIdx.x) < jn) {
-    const int t = threadIdx.x;
-    mass[size_t(r) * nb + j0 + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+  const int t = threadIdx.x % kMassBlocksPerWg;
+  const int b = threadIdx.x / kMassBlocksPerWg;
+  if (b < QB && t < jn && i0 + b < nb) {
+    float m = red[b][0][t];
+#pragma unroll
+    for (int g = 1; g < QG; ++g) m += red[b][g][t];
+    mass[(size_t(bh) * nb + i0 + b) * nb + j0 + t] = m;
   }
 }
 
@@ -128,7 +163,10 @@ __global__ __launch_bounds__(256) void csr_mass_kernel(const float* __restrict__
 template <int BLK, int HD>
 bsa_status launch_mass(const void* q, const void* k, const float* lse, int32_t n_rows, int32_t N,
                        int32_t nb, float sl2, float* mass, hipStream_t s) {
-  const dim3 grid(n_rows, (nb + kMassBlocksPerWg - 1) / kMassBlocksPerWg);
+  constexpr int QB = 128 / BLK;  // query blocks per workgroup
+  const int64_t heads = n_rows / nb;
+  const dim3 grid(static_cast<uint32_t>(heads * ((nb + QB - 1) / QB)),
+                  (nb + kMassBlocksPerWg - 1) / kMassBlocksPerWg);
   hipLaunchKernelGGL((mass_kernel<BLK, HD>), grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, N, nb,
                      sl2, mass);
