@@ -215,3 +215,34 @@ def test_mass_mutant_oracle_smallest_first(monkeypatch):
                                for r in range(m.shape[0])]).astype(np.int32)
     monkeypatch.setattr(Ms, "oracle_csr", bad)
     assert any_mass_pin_fails()
+
+
+# ---- residual-compensation oracle --------------------------------------------
+import test_oracle_residual as TR
+from oracle import residual as Rs
+
+RES_PINS = [
+    (TR.test_anchor_step_is_exact, ()),
+    (TR.test_zero_drift_reuses_exactly, ()),
+    (TR.test_all_ones_csr_has_zero_residual, ()),
+    (TR.test_small_drift_compensation_beats_sparse, ()),
+    (TR.test_residual_sign, ()),
+]
+
+
+def any_res_pin_fails():
+    return any(fails(f, *a) for f, a in RES_PINS)
+
+
+def test_unmodified_residual_oracle_passes():
+    assert not any_res_pin_fails()
+
+
+def test_res_mutant_residual_sign_flipped(monkeypatch):
+    monkeypatch.setattr(Rs, "residual", lambda d, s: np.asarray(s, float) - np.asarray(d, float))
+    assert any_res_pin_fails()
+
+
+def test_res_mutant_compensation_subtracts(monkeypatch):
+    monkeypatch.setattr(Rs, "compensate", lambda s, r: np.asarray(s, float) - np.asarray(r, float))
+    assert any_res_pin_fails()

@@ -34,7 +34,7 @@ import torch
 
 __all__ = [
     "Workload", "CONFIGS", "make", "gaussian_qkv", "lowrank_qk", "tiny_prior",
-    "t2i_prior", "video_prior", "ragged_budgets", "n_blocks",
+    "t2i_prior", "video_prior", "ragged_budgets", "n_blocks", "drifting_qkv",
 ]
 
 
@@ -75,6 +75,18 @@ def lowrank_qk(seed: int, B: int, H: int, N: int, D: int, block: int, rank: int 
     q = zq + sq[:, :, tok_block, :]
     k = zk + sk[:, :, tok_block, :]
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def drifting_qkv(seed: int, steps: int, eps: float, B: int, H: int, N: int, D: int,
+                 block: int):
+    """Slowly drifting inputs: step t is the block-structured Q, K (lowrank_qk) and V plus
+    eps * t times one fixed N(0,1) direction per tensor, rounded to bf16 (RNE).  A list of
+    (q, k, v) per step; step 0 is the undrifted base."""
+    q0, k0, v0 = (x.float() for x in lowrank_qk(seed, B, H, N, D, block))
+    g = torch.Generator("cpu").manual_seed(seed + 1)
+    dq, dk, dv = (torch.randn((B, H, N, D), generator=g, dtype=torch.float32) for _ in range(3))
+    return [tuple((x + (eps * t) * d).to(torch.bfloat16) for x, d in ((q0, dq), (k0, dk), (v0, dv)))
+            for t in range(steps)]
 
 
 def tiny_prior(seed: int, B: int, H: int, nb: int) -> np.ndarray:
