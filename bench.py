@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective TFLOP/s over active blocks + % bf16 MFMA peak, N=4224 t2i mask"
 FWD_SRC = os.path.join(ROOT, "block_sparse_attention_flashattn_amd", "csrc", "fwd.hip")
@@ -239,6 +240,23 @@ def main():
         "block_mass_scores_per_ns": w.B * w.H * float(w.N) ** 2 / (mass_ms * 1e6),
         "mean_kept_mass_csr": kept_csr / n_q, "mean_kept_mass_oracle": kept_or / n_q,
         "rel_err_vs_dense_csr": rel_err(o), "rel_err_vs_dense_oracle": rel_err(o_or),
+    }
+
+    # Residual compensation at reuse steps: the two elementwise passes (memory-bound: two
+    # bf16 reads and one bf16 write per element) and the anchor and reuse steps.
+    r_buf = torch.empty_like(qd)
+    n_el = o.numel()
+    res_ms = time_launches(lambda: bsa.residual(o_dense, o, out=r_buf), n=20)
+    o_c = torch.empty_like(qd)
+    comp_ms = time_launches(lambda: bsa.compensate(o, r_buf, out=o_c), n=20)
+    ar = bsa.AnchorReuse(w.block)
+    anchor_ms = time_launches(lambda: ar.anchor(qd, kd, vd, plan.row_ptr, col_idx, work=plan), n=5)
+    reuse_ms = time_launches(lambda: ar.reuse(qd, kd, vd, out=o_c), n=20)
+    extra["residual_compensation"] = {
+        "residual_ms": res_ms, "compensate_ms": comp_ms,
+        "compensate_gbps": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9,
+        "compensate_frac_of_hbm_peak": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "anchor_step_ms": anchor_ms, "reuse_step_ms": reuse_ms,
     }
 
     if args.extra:

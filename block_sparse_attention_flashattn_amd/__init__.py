@@ -31,7 +31,8 @@ __all__ = [
     "BsaError", "lib", "LIB_PATH", "status_string", "abi_version", "budget_from_density",
     "mask_plan", "work_plan", "validate_csr_host", "build_mask_workspace_bytes",
     "forward_workspace_bytes", "build_mask", "build_mask_status", "schedule", "forward",
-    "block_mass", "select_by_mass", "csr_mass", "block_oracle",
+    "block_mass", "select_by_mass", "csr_mass", "block_oracle", "residual", "compensate",
+    "AnchorReuse",
     "Plan", "Work", "n_blocks", "default_max_tiles",
 ]
 
@@ -60,11 +61,13 @@ _SIGS = {
     "bsa_block_mass": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
     "bsa_select_by_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "bsa_csr_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "bsa_residual": (_i32, [_vp, _vp, _vp, _i64, _vp]),
+    "bsa_compensate": (_i32, [_vp, _vp, _vp, _i64, _vp]),
 }
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class BsaError(RuntimeError):
@@ -492,3 +495,69 @@ def block_oracle(q: torch.Tensor, k: torch.Tensor, row_ptr, block: int,
     _, lse = forward(q, k, k, rp1, ci1, block, scale=scale)
     mass = block_mass(q, k, lse, block, scale)
     return select_by_mass(mass, row_ptr), mass
+
+
+def _bf16_pair(a: torch.Tensor, b: torch.Tensor):
+    for t in (a, b):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 \
+                or not t.is_contiguous():
+            raise ValueError("operands must be contiguous bf16 CUDA (HIP) tensors")
+    if a.shape != b.shape or a.device != b.device:
+        raise ValueError("operands must share shape and device")
+
+
+def residual(o_dense: torch.Tensor, o_sparse: torch.Tensor,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """R = O_dense - O_sparse (bf16, formed in fp32, rounded once)."""
+    _bf16_pair(o_dense, o_sparse)
+    out = torch.empty_like(o_dense) if out is None else out
+    _bf16_pair(o_dense, out)
+    _check(lib.bsa_residual(_t_ptr(o_dense), _t_ptr(o_sparse), _t_ptr(out), o_dense.numel(),
+                            _stream_ptr(o_dense.device)), "bsa_residual")
+    return out
+
+
+def compensate(o_sparse: torch.Tensor, r: torch.Tensor,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O = O_sparse + R (bf16, formed in fp32, rounded once)."""
+    _bf16_pair(o_sparse, r)
+    out = torch.empty_like(o_sparse) if out is None else out
+    _bf16_pair(o_sparse, out)
+    _check(lib.bsa_compensate(_t_ptr(o_sparse), _t_ptr(r), _t_ptr(out), o_sparse.numel(),
+                              _stream_ptr(o_sparse.device)), "bsa_compensate")
+    return out
+
+
+class AnchorReuse:
+    """Anchor-step reuse with dense-sparse residual compensation.
+
+    `anchor(q, k, v, row_ptr, col_idx, work=None)` runs the dense and the sparse
+    forward, keeps the CSR (and work list) and the residual R = O_dense - O_sparse,
+    and returns the dense output.  `reuse(q, k, v)` runs the sparse forward with
+    the kept CSR and returns O_sparse + R.
+    """
+
+    def __init__(self, block: int, scale: Optional[float] = None):
+        self.block, self.scale = block, scale
+        self.row_ptr = self.col_idx = self.work = self.r = None
+
+    def anchor(self, q, k, v, row_ptr, col_idx, work=None):
+        B, H, N, D = _check_qkv(q, k, v)
+        nb = n_blocks(N, self.block)
+        rows = B * H * nb
+        dev = q.device
+        rp1 = torch.arange(rows + 1, dtype=torch.int32, device=dev) * nb
+        ci1 = torch.arange(nb, dtype=torch.int32, device=dev).repeat(rows)
+        o_dense, _ = forward(q, k, v, rp1, ci1, self.block, scale=self.scale, return_lse=False)
+        self.row_ptr, self.col_idx, self.work = _dev_i32(row_ptr, dev), _dev_i32(col_idx, dev), work
+        o_sparse, _ = forward(q, k, v, self.row_ptr, self.col_idx, self.block, scale=self.scale,
+                              work=work, return_lse=False)
+        self.r = residual(o_dense, o_sparse, out=o_sparse)
+        return o_dense
+
+    def reuse(self, q, k, v, out: Optional[torch.Tensor] = None):
+        if self.r is None:
+            raise RuntimeError("reuse() before anchor()")
+        o, _ = forward(q, k, v, self.row_ptr, self.col_idx, self.block, scale=self.scale,
+                       work=self.work, out=out, return_lse=False)
+        return compensate(o, self.r, out=o)

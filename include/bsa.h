@@ -51,7 +51,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 4
+#define BSA_ABI_VERSION 5
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -306,6 +306,24 @@ BSA_API bsa_status bsa_select_by_mass(const float* mass_dev, int32_t n_rows, int
 BSA_API bsa_status bsa_csr_mass(const float* mass, int32_t n_rows, int32_t nb,
                                 const int32_t* row_ptr, const int32_t* col_idx, float* out,
                                 void* stream);
+
+/*
+ * Dense-sparse residual compensation (device, async).  Page "Can sparse
+ * attention close the quality gap in diffusion transformers", section on
+ * residual compensation: at an anchor step the residual between the dense and
+ * the sparse attention outputs is recorded; at a reuse step (which reuses the
+ * anchor's CSR, per the section on reusing exact selection) the cached residual
+ * is added to the sparse output.
+ *   bsa_residual:   r_out = o_dense - o_sparse
+ *   bsa_compensate: o_out = o_sparse + r
+ * All bf16 device arrays of n elements (e.g. [B,H,N,D]), 16-byte aligned; each
+ * element is formed in fp32 from the two bf16 inputs and rounded once to bf16
+ * (nearest even).  The output may alias an input.  Errors: INVALID_ARG, HIP.
+ */
+BSA_API bsa_status bsa_residual(const void* o_dense, const void* o_sparse, void* r_out, int64_t n,
+                                void* stream);
+BSA_API bsa_status bsa_compensate(const void* o_sparse, const void* r, void* o_out, int64_t n,
+                                  void* stream);
 
 #ifdef __cplusplus
 }
