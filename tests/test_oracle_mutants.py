@@ -246,3 +246,45 @@ def test_res_mutant_residual_sign_flipped(monkeypatch):
 def test_res_mutant_compensation_subtracts(monkeypatch):
     monkeypatch.setattr(Rs, "compensate", lambda s, r: np.asarray(s, float) - np.asarray(r, float))
     assert any_res_pin_fails()
+
+
+# ---- token-level selection oracle ----------------------------------------------
+import test_oracle_tokensel as TT
+from oracle import tokensel as Tk
+
+TOK_PINS = [
+    (TT.test_principal_direction_is_the_top_eigenvector, ()),
+    (TT.test_partition_is_exact_and_tile_sized, ()),
+    (TT.test_separated_clusters_are_recovered, ()),
+    (TT.test_odd_group_count_cuts_at_a_tile_boundary, ()),
+    (TT.test_token_mass_conservation_and_block_sums, ()),
+    (TT.test_select_tokens_hand, ()),
+    (TT.test_gathered_attention_reduces_to_dense_and_block_sparse, ()),
+]
+
+
+def any_tok_pin_fails():
+    return any(fails(f, *a) for f, a in TOK_PINS)
+
+
+def test_unmodified_tokensel_oracle_passes():
+    assert not any_tok_pin_fails()
+
+
+def test_tok_mutant_direction_is_a_fixed_axis(monkeypatch):
+    """Projecting on the first coordinate instead of the principal direction."""
+    monkeypatch.setattr(Tk, "principal_direction",
+                        lambda x, iters=8: np.eye(x.shape[1])[0])
+    assert any_tok_pin_fails()
+
+
+def test_tok_mutant_mass_summed_over_keys(monkeypatch):
+    monkeypatch.setattr(Tk, "token_mass", lambda q, k, groups, scale: np.stack(
+        [Tk.M.dense_probabilities(q, k, scale)[:, g].sum(axis=1) for g in np.asarray(groups)]))
+    assert any_tok_pin_fails()
+
+
+def test_tok_mutant_selects_smallest(monkeypatch):
+    monkeypatch.setattr(Tk, "select_tokens", lambda m, k: np.stack(
+        [np.sort(np.lexsort((np.arange(m.shape[1]), r))[:k]) for r in np.asarray(m)]))
+    assert any_tok_pin_fails()
