@@ -32,7 +32,7 @@ __all__ = [
     "mask_plan", "work_plan", "validate_csr_host", "build_mask_workspace_bytes",
     "forward_workspace_bytes", "build_mask", "build_mask_status", "schedule", "forward",
     "block_mass", "select_by_mass", "csr_mass", "block_oracle", "residual", "compensate",
-    "AnchorReuse",
+    "AnchorReuse", "query_groups", "token_mass", "select_tokens",
     "Plan", "Work", "n_blocks", "default_max_tiles",
 ]
 
@@ -63,11 +63,14 @@ _SIGS = {
     "bsa_csr_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "bsa_residual": (_i32, [_vp, _vp, _vp, _i64, _vp]),
     "bsa_compensate": (_i32, [_vp, _vp, _vp, _i64, _vp]),
+    "bsa_query_groups": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "bsa_token_mass": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
+    "bsa_select_tokens": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),
 }
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class BsaError(RuntimeError):
@@ -561,3 +564,45 @@ class AnchorReuse:
         o, _ = forward(q, k, v, self.row_ptr, self.col_idx, self.block, scale=self.scale,
                        work=self.work, out=out, return_lse=False)
         return compensate(o, self.r, out=o)
+
+
+def query_groups(q: torch.Tensor, C: int) -> torch.Tensor:
+    """Tile-aligned query groups -> int32 [B,H,N/C,C] (token indices, ascending per group)."""
+    B, H, N, D = _check_qkv(q)
+    if N % C:
+        raise ValueError("N must be a multiple of the group size")
+    groups = torch.empty((B, H, N // C, C), dtype=torch.int32, device=q.device)
+    _check(lib.bsa_query_groups(_t_ptr(q), B, H, N, D, C, _t_ptr(groups),
+                                _stream_ptr(q.device)), "bsa_query_groups")
+    return groups
+
+
+def token_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, groups: torch.Tensor,
+               scale: Optional[float] = None) -> torch.Tensor:
+    """Per group and KV token, exp(scale q.k - lse) summed over the group's queries
+    -> fp32 [B,H,G,N]."""
+    B, H, N, D = _check_qkv(q, k)
+    if groups.dtype != torch.int32 or not groups.is_contiguous() or groups.dim() != 4 \
+            or tuple(groups.shape[:2]) != (B, H):
+        raise ValueError("groups must be contiguous int32 [B,H,G,C]")
+    G, C = groups.shape[2], groups.shape[3]
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be contiguous fp32 [B,H,N]")
+    s = -1.0 if scale is None else float(scale)
+    mass = torch.empty((B, H, G, N), dtype=torch.float32, device=q.device)
+    _check(lib.bsa_token_mass(_t_ptr(q), _t_ptr(k), _t_ptr(lse), _t_ptr(groups), B, H, N, D, C,
+                              s, _t_ptr(mass), _stream_ptr(q.device)), "bsa_token_mass")
+    return mass
+
+
+def select_tokens(mass: torch.Tensor, k: int) -> torch.Tensor:
+    """Per mass row, the k tokens of largest mass (ties to the lower token), ascending
+    -> int32 [..., k]."""
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or mass.dim() < 2:
+        raise ValueError("mass must be contiguous fp32 [..., N]")
+    N = mass.shape[-1]
+    rows = mass.numel() // N
+    out = torch.empty(tuple(mass.shape[:-1]) + (k,), dtype=torch.int32, device=mass.device)
+    _check(lib.bsa_select_tokens(_t_ptr(mass), rows, N, int(k), _t_ptr(out),
+                                 _stream_ptr(mass.device)), "bsa_select_tokens")
+    return out

@@ -51,7 +51,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 5
+#define BSA_ABI_VERSION 6
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -324,6 +324,38 @@ BSA_API bsa_status bsa_residual(const void* o_dense, const void* o_sparse, void*
                                 void* stream);
 BSA_API bsa_status bsa_compensate(const void* o_sparse, const void* r, void* o_out, int64_t n,
                                   void* stream);
+
+/*
+ * Token-level KV selection with tile-aligned query groups (device, async).  Page
+ * "Can sparse attention close the quality gap in diffusion transformers",
+ * section on token-level selection with tile-aligned query groups: KV tokens are
+ * chosen one by one per query group and gathered by index; the queries of a head
+ * form groups of C similar queries by the median-split version of
+ * principal-direction divisive partitioning; exact selection needs the scores.
+ *
+ * bsa_query_groups: groups_out int32 [B,H,N/C,C] (token indices, each group
+ *   ascending), from q bf16 [B,H,N,D].  Per head, a group of g*C queries (g > 1) is
+ *   projected on its principal direction (8 power-iteration steps from
+ *   u[d] = 1 + d/D, fp32) and cut into floor(g/2)*C and the rest, smallest
+ *   projections first (ties to the lower token), recursively; groups are
+ *   numbered depth first.  C in {64, 128}, N a multiple of C and at most 8192, D
+ *   in {64, 128}.
+ * bsa_token_mass: mass_out fp32 [B,H,N/C,N]: for group g and token c, the sum over
+ *   the group's queries t of exp(scale q_t.k_c - lse[t]) (with the dense LSE: the
+ *   dense attention probability mass of token c for the group).  Queries with a
+ *   non-finite LSE contribute nothing.
+ * bsa_select_tokens: tokens_out int32 [n_rows, k]: per mass row, the k tokens of
+ *   largest mass (ties to the lower token), ascending.  N at most 8192, 0 <= k <= N.
+ * Errors: INVALID_ARG, UNSUPPORTED (sizes above), HIP.
+ */
+BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t H, int32_t N, int32_t D,
+                                    int32_t C, int32_t* groups_out, void* stream);
+BSA_API bsa_status bsa_token_mass(const void* q, const void* k, const float* lse,
+                                  const int32_t* groups, int32_t B, int32_t H, int32_t N,
+                                  int32_t D, int32_t C, float scale, float* mass_out,
+                                  void* stream);
+BSA_API bsa_status bsa_select_tokens(const float* mass, int32_t n_rows, int32_t N, int32_t k,
+                                     int32_t* tokens_out, void* stream);
 
 #ifdef __cplusplus
 }
