@@ -32,7 +32,7 @@ __all__ = [
     "mask_plan", "work_plan", "validate_csr_host", "build_mask_workspace_bytes",
     "forward_workspace_bytes", "build_mask", "build_mask_status", "schedule", "forward",
     "block_mass", "select_by_mass", "csr_mass", "block_oracle", "residual", "compensate",
-    "AnchorReuse", "query_groups", "token_mass", "select_tokens",
+    "AnchorReuse", "query_groups", "token_mass", "select_tokens", "gather_forward",
     "Plan", "Work", "n_blocks", "default_max_tiles",
 ]
 
@@ -66,11 +66,13 @@ _SIGS = {
     "bsa_query_groups": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "bsa_token_mass": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
     "bsa_select_tokens": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),
+    "bsa_gather_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
+                                  _f32, _vp, _vp, _vp]),
 }
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class BsaError(RuntimeError):
@@ -606,3 +608,32 @@ def select_tokens(mass: torch.Tensor, k: int) -> torch.Tensor:
     _check(lib.bsa_select_tokens(_t_ptr(mass), rows, N, int(k), _t_ptr(out),
                                  _stream_ptr(mass.device)), "bsa_select_tokens")
     return out
+
+
+def gather_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, groups: torch.Tensor,
+                   tokens: torch.Tensor, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """Each group's 64 queries attend to exactly that group's tokens -> (O bf16 [B,H,N,D],
+    LSE fp32 [B,H,N] or None).  groups int32 [B,H,G,64], tokens int32 [B,H,G,T] (no
+    repeats); rows no group names keep the contents of `out` (zeros when it is None)."""
+    B, H, N, D = _check_qkv(q, k, v)
+    for name, t in (("groups", groups), ("tokens", tokens)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_contiguous() \
+                or t.dim() != 4 or tuple(t.shape[:2]) != (B, H) or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous int32 [B,H,G,...] on q's device")
+    G, T = groups.shape[2], tokens.shape[3]
+    if groups.shape[3] != 64 or tokens.shape[2] != G:
+        raise ValueError("groups must be [B,H,G,64] and tokens [B,H,G,T]")
+    if out is None:
+        out = torch.zeros_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be contiguous bf16 like q")
+    lse = torch.full((B, H, N), float("-inf"), dtype=torch.float32, device=q.device) \
+        if return_lse else None
+    s = -1.0 if scale is None else float(scale)
+    _check(lib.bsa_gather_forward(_t_ptr(q), _t_ptr(k), _t_ptr(v), B, H, N, D, _t_ptr(groups), G,
+                                  _t_ptr(tokens), T, s, _t_ptr(out),
+                                  _t_ptr(lse) if lse is not None else None,
+                                  _stream_ptr(q.device)), "bsa_gather_forward")
+    return out, lse

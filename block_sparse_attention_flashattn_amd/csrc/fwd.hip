@@ -1428,6 +1428,233 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
   wait_vm(0);  // no load may still target LDS when the workgroup retires
 }
 
+// Gathered attention for token-level KV selection (page "Can sparse attention
+// close the quality gap in diffusion transformers", section on token-level
+// selection with tile-aligned query groups: KV tokens chosen one by one per query
+// group and gathered by index, not repacked into blocks).  One workgroup of two
+// wavefronts per (head, group of 64 queries): the queries of group g are the
+// tokens groups[g][0..64), its keys and values the tokens tokens[g][0..T).  The
+// tile formulation is the block forward's (S^T = K Q^T, wave h owns keys 32h..+31
+// of every 64-token tile for all 64 queries); K operands and query rows are read
+// straight from memory by index, each wave's 32 V rows pass through its own 4-KiB
+// LDS area for the transposing reads.  O and LSE are written at the group's token
+// positions.
+constexpr int kGatherLds = 2 * 4096 + 2 * 8192 + 1024;  // V areas, key-half exchange, m and l
+
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void gather_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ groups,
+    const int32_t* __restrict__ tokens, int32_t T, int32_t N, int32_t G, float sl2,
+    uint16_t* __restrict__ O, float* __restrict__ LSE) {
+  constexpr int HD = 64, ROWB = 128;
+  __shared__ __align__(16) uint8_t smem[kGatherLds];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
+  const int lane = threadIdx.x & 63;
+  const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ql = lane & 31, hh = lane >> 5;
+  const int row = blockIdx.x;
+  const int bh = row / G;
+  const int32_t* ids = groups + size_t(row) * 64;
+  const int32_t* toks = tokens + size_t(row) * T;
+  const uint32_t hbytes = static_cast<uint32_t>(N) * ROWB;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, hbytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, hbytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, hbytes);
+  const uint32_t vs = lds0 + uint32_t(kh) * 4096u;
+
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int t = ids[32 * g + ql];
+    const uint32_t base = (t >= 0 && t < N) ? uint32_t(t) * ROWB : hbytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qf[g][c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                qr, base + uint32_t(32 * c + 16 * hh), 0, 0));
+  }
+  float m_run[2] = {kNoMax, kNoMax}, l_run[2] = {0.f, 0.f};
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[g][u][i] = 0.f;
+
+  // Token of this lane's key at list position idx (-1 past the list or out of range).
+  auto tok_at = [&](int idx) {
+    const int t = idx < T ? toks[idx] : -1;
+    return (t >= 0 && t < N) ? t : -1;
+  };
+  // K operand of this lane's key and the V chunks this lane stages (row r = 8i +
+  // lane / 8 of the wave's 32 keys, 16-byte chunk lane % 8); the V rows' tokens
+  // come from the lanes that hold those keys.
+  auto load_tile = [&](int ktok, bf16x8 (&ka)[4], v4u (&vx)[4]) {
+    const uint32_t kbase = ktok >= 0 ? uint32_t(ktok) * ROWB : hbytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      ka[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                             kr, kbase + uint32_t(32 * c + 16 * hh), 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int vt = __builtin_amdgcn_ds_bpermute(r << 2, ktok);
+      const uint32_t vb = vt >= 0 ? uint32_t(vt) * ROWB : hbytes;
+      vx[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, vb + uint32_t(16 * (lane & 7)), 0, 0);
+    }
+  };
+  // One 64-key tile: S^T for this wave's 32 keys (K operand ka, token ktok of the
+  // lane's key), online softmax, then P V with the V rows vx staged in LDS.
+  auto tile = [&](int ktok, const bf16x8 (&ka)[4], const v4u (&vx)[4]) {
+    // Keys of this wave's half of the tile that exist (bit j: key 32 kh + j).
+    const uint32_t kvalid = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(ktok >= 0));
+    const f32x16 zero = {};
+    f32x16 s[2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        s[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s[g], 0, 0, 0);
+    // Keys past the list (or out of range) get -inf.
+    if (kvalid != 0xffffffffu) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!((kvalid >> (8 * (i >> 2) + 4 * hh + (i & 3))) & 1u)) {
+          s[0][i] = -INFINITY;
+          s[1][i] = -INFINITY;
+        }
+    }
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float mx = vmax(s[g][0], s[g][1]);
+#pragma unroll
+      for (int i = 2; i < 16; ++i) mx = vmax(mx, s[g][i]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float mt = vmax(m_run[g], mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - mt);
+      l_run[g] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][u][i] *= alpha;
+      m_run[g] = mt;
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[g][i], sl2, -mt));
+        ls += p;
+        pb[g][i >> 3][i & 7] = static_cast<__bf16>(p);
+      }
+      l_run[g] += ls;
+    }
+    // This tile's V rows into the wave's LDS area (the previous tile's reads are
+    // done: one wavefront's LDS operations complete in order).
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<BSA_LDS v4u*>(static_cast<uintptr_t>(vs + swz<ROWB>(8 * i + (lane >> 3), lane & 7))) = vx[i];
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int col = 32 * u2 + tr_col;
+        const v4s lo = lds_read_tr(vs + swz<ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
+        const v4s hi = lds_read_tr(vs + swz<ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[g][u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][c2], acc[g][u2], 0, 0, 0);
+      }
+  };
+  // Two K/V register sets in turn: the next tile's rows are in flight while a
+  // tile is computed, and the token indices one tile further ahead.  Loads for
+  // tiles past the list use out-of-range offsets (zeros, no memory traffic).
+  const int ntiles = (T + 63) / 64;
+  int t_cur = tok_at(32 * kh + ql), t_next = tok_at(64 + 32 * kh + ql);
+  bf16x8 ka0[4], ka1[4];
+  v4u vx0[4], vx1[4];
+  load_tile(t_cur, ka0, vx0);
+  for (int tt = 0; tt < ntiles; tt += 2) {
+    {
+      const int t_nn = tok_at(64 * (tt + 2) + 32 * kh + ql);
+      load_tile(t_next, ka1, vx1);
+      tile(t_cur, ka0, vx0);
+      t_cur = t_next;
+      t_next = t_nn;
+    }
+    if (tt + 1 < ntiles) {
+      const int t_nn = tok_at(64 * (tt + 3) + 32 * kh + ql);
+      load_tile(t_next, ka0, vx0);
+      tile(t_cur, ka1, vx1);
+      t_cur = t_next;
+      t_next = t_nn;
+    }
+  }
+
+  // Key-half merge: wave kh finalises query group kh; it sends its state of group
+  // 1 - kh through the exchange area.
+  float l_half[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) l_half[g] = l_run[g] + other_half(l_run[g]);
+  float* xo_base = reinterpret_cast<float*>(smem + 8192);
+  float* xml = reinterpret_cast<float*>(smem + 8192 + 16384);
+  auto send = [&](const f32x16 (&a)[2], float m, float l) {
+    float* xo = xo_base + size_t(kh) * 2048;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(xo + ((u * 4 + g4) * 64 + lane) * 4) =
+            f32x4{a[u][4 * g4], a[u][4 * g4 + 1], a[u][4 * g4 + 2], a[u][4 * g4 + 3]};
+    if (hh == 0) {
+      xml[kh * 64 + ql] = m;
+      xml[kh * 64 + 32 + ql] = l;
+    }
+  };
+  auto finish = [&](const f32x16 (&a)[2], float m0, float l0) {
+    const int go = 1 - kh;
+    const float* xi = xo_base + size_t(go) * 2048;
+    const float m1 = xml[go * 64 + ql], l1 = xml[go * 64 + 32 + ql];
+    const float m = fmaxf(m0, m1);
+    const float a0 = m0 <= kNoMax ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
+    const float a1 = m1 <= kNoMax ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    const float l = l0 * a0 + l1 * a1;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int t = ids[32 * kh + ql];
+    const bool ok = t >= 0 && t < N;
+    uint16_t* orow = O + head + size_t(ok ? t : 0) * HD;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(xi + ((u * 4 + g4) * 64 + lane) * 4);
+        if (ok) {
+          const int d = 32 * u + 8 * g4 + 4 * hh;
+          const uint32_t w0 = pack_bf16x2((a[u][4 * g4] * a0 + o1[0] * a1) * inv,
+                                          (a[u][4 * g4 + 1] * a0 + o1[1] * a1) * inv);
+          const uint32_t w1 = pack_bf16x2((a[u][4 * g4 + 2] * a0 + o1[2] * a1) * inv,
+                                          (a[u][4 * g4 + 3] * a0 + o1[3] * a1) * inv);
+          *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
+        }
+      }
+    if (LSE != nullptr && ok && hh == 0)
+      LSE[size_t(bh) * N + t] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+  };
+  if (kh == 0)
+    send(acc[1], m_run[1], l_half[1]);
+  else
+    send(acc[0], m_run[0], l_half[0]);
+  __syncthreads();
+  if (kh == 0)
+    finish(acc[0], m_run[0], l_half[0]);
+  else
+    finish(acc[1], m_run[1], l_half[1]);
+}
+
 // Combines the chunk partials of every cut row: with M = max_c m_c,
 // O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c and LSE = (M + log2 L) ln 2.
 // One thread per (query row, 4 output columns); the loads of up to kUnroll
@@ -1670,4 +1897,24 @@ extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const vo
   if (block == 128 && D == 64) return launch_fwd<128, 64>(BSA_FWD_ARGS);
   return launch_fwd<128, 128>(BSA_FWD_ARGS);
 #undef BSA_FWD_ARGS
+}
+
+extern "C" BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* v,
+                                                 int32_t B, int32_t H, int32_t N, int32_t D,
+                                                 const int32_t* groups, int32_t G,
+                                                 const int32_t* tokens, int32_t T, float scale,
+                                                 void* o, float* lse, void* stream) {
+  using namespace bsa;
+  if (!q || !k || !v || !o || !groups || (!tokens && T > 0)) return BSA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || G < 1 || T < 0 || !(scale == scale)) return BSA_ERR_INVALID_ARG;
+  if (D != 64) return BSA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BSA_ERR_INVALID_ARG;
+  if (int64_t(N) * D * 2 >= (int64_t(1) << 31) || int64_t(B) * H * G > INT32_MAX) return BSA_ERR_UNSUPPORTED;
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
+  hipLaunchKernelGGL(gather_kernel, dim3(B * H * G), dim3(128), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), groups, tokens, T, N, G,
+                     sc * 1.4426950408889634f, static_cast<uint16_t*>(o), lse);
+  BSA_HIP_CHECK_LAUNCH();
+  return BSA_OK;
 }

@@ -51,7 +51,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 6
+#define BSA_ABI_VERSION 7
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -356,6 +356,29 @@ BSA_API bsa_status bsa_token_mass(const void* q, const void* k, const float* lse
                                   void* stream);
 BSA_API bsa_status bsa_select_tokens(const float* mass, int32_t n_rows, int32_t N, int32_t k,
                                      int32_t* tokens_out, void* stream);
+
+/*
+ * Gathered attention over selected tokens (device, async).  Same page and section:
+ * the selected KV tokens of a query group are gathered by index, not repacked into
+ * blocks, and the group's queries attend to exactly those tokens.
+ *
+ * q, k, v: bf16 [B,H,N,D], D = 64, 16-byte aligned.  groups: int32 [B,H,G,64], the
+ * token positions of each group's 64 queries (as bsa_query_groups writes them with
+ * C = 64).  tokens: int32 [B,H,G,T], the KV tokens of each group (as
+ * bsa_select_tokens writes them); a list must not repeat a token (a repeat counts
+ * twice), its order is free.  Entries outside [0, N) are skipped in both.  For
+ * every query t of group g: o[t] = softmax_j(scale q_t.k_j) v_j over j in tokens[g]
+ * (fp32 accumulation, bf16 result) and lse[t] = log sum_j exp(scale q_t.k_j),
+ * natural log, fp32 [B,H,N]; a group with no valid token writes o = 0 and
+ * lse = -inf.  Rows of o and lse that no group names are not written.  scale <= 0
+ * selects 1/sqrt(D); lse may be NULL.
+ * Errors: INVALID_ARG (null or misaligned pointer, non-positive sizes, NaN scale),
+ * UNSUPPORTED (D != 64, N*D*2 >= 2^31), HIP.
+ */
+BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* v, int32_t B,
+                                      int32_t H, int32_t N, int32_t D, const int32_t* groups,
+                                      int32_t G, const int32_t* tokens, int32_t T, float scale,
+                                      void* o, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

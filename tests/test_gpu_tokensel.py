@@ -6,7 +6,7 @@ import torch
 
 import workloads as W
 from oracle import tokensel as OT
-from parity import need_gpu
+from parity import LSE_ABS, O_MAX_ABS, O_MEAN_ABS, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +100,118 @@ def test_select_tokens_matches_oracle(N, k):
     toks = bsa.select_tokens(torch.from_numpy(m).cuda(), k)
     torch.cuda.synchronize()
     assert np.array_equal(toks.cpu().numpy(), OT.select_tokens(m.astype(np.float64), k))
+
+
+def random_lists(seed, G, N, T):
+    """Per group, T distinct tokens of [0, N) in random order (the order is free)."""
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.choice(N, T, replace=False) for _ in range(G)]).astype(np.int32)
+
+
+def run_gather(bsa, q, k, v, groups, tokens, out=None):
+    o, lse = bsa.gather_forward(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(groups).cuda(),
+                                torch.from_numpy(tokens).cuda(), out=out)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_rows(o, lse, O, L, rows):
+    err = np.abs(o[rows] - O[rows])
+    print(f"  o max {err.max():.3e} mean {err.mean():.3e}", flush=True)
+    assert err.max() <= O_MAX_ABS and err.mean() <= O_MEAN_ABS
+    fin = np.isfinite(L[rows])
+    assert np.array_equal(np.isfinite(lse[rows]), fin)
+    if fin.any():
+        assert np.abs(lse[rows][fin] - L[rows][fin]).max() <= LSE_ABS
+
+
+@pytest.mark.parametrize("N,T", [(512, 100), (512, 64), (1024, 1), (1024, 33), (1024, 640),
+                                 (320, 320)])
+def test_gather_forward_matches_oracle(N, T):
+    """Oracle groups (median split) and seeded token lists: ragged last tiles, a tile half
+    with no key, one token, every token."""
+    bsa = need_gpu()
+    print(f"case N={N} T={T}", flush=True)
+    B, H, D = 1, 2, 64
+    q, k, v = W.gaussian_qkv(N + T, B, H, N, D)
+    G = N // 64
+    groups = np.stack([OT.median_split_groups(q[0, h].float().numpy(), 64) for h in range(H)])
+    tokens = np.stack([random_lists(7 * h + T, G, N, T) for h in range(H)])
+    o, lse = run_gather(bsa, q, k, v, groups[None].astype(np.int32), tokens[None])
+    for h in range(H):
+        O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[h], tokens[h], 1 / 8.0)
+        check_rows(o[0, h], lse[0, h], O, L, np.arange(N))
+
+
+def test_gather_forward_t2i_head_length_sampled():
+    """A full t2i head (N = 4224, 66 groups, 640 tokens each, about 15 %); the oracle on
+    every eleventh group."""
+    bsa = need_gpu()
+    B, H, N, D, T = 1, 2, 4224, 64, 640
+    q, k, v = W.gaussian_qkv(4224, B, H, N, D)
+    G = N // 64
+    rng = np.random.default_rng(5)
+    groups = np.stack([rng.permutation(N).reshape(G, 64) for _ in range(H)]).astype(np.int32)
+    groups.sort(axis=-1)
+    tokens = np.stack([random_lists(h, G, N, T) for h in range(H)])
+    o, lse = run_gather(bsa, q, k, v, groups[None], tokens[None])
+    for h in range(H):
+        for g in range(0, G, 11):
+            O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[h, g:g + 1],
+                                         tokens[h, g:g + 1], 1 / 8.0)
+            check_rows(o[0, h], lse[0, h], O, L, groups[h, g])
+
+
+def test_gather_forward_skips_out_of_range_entries():
+    """Token entries outside [0, N) are skipped; so are group slots outside [0, N)."""
+    bsa = need_gpu()
+    B, H, N, D, T = 1, 1, 256, 64, 90
+    q, k, v = W.gaussian_qkv(31, B, H, N, D)
+    G = N // 64
+    groups = np.arange(N, dtype=np.int32).reshape(G, 64)
+    tokens = random_lists(3, G, N, T)
+    bad_t = tokens.copy()
+    bad_t[:, ::7] = -1
+    bad_t[:, 3::11] = N + 5
+    bad_g = groups.copy()
+    bad_g[1, 5] = -3
+    out = torch.full((B, H, N, D), 3.0, dtype=torch.bfloat16, device="cuda")
+    o, lse = run_gather(bsa, q, k, v, bad_g[None, None], bad_t[None, None], out=out)
+    for g in range(G):
+        keep = bad_t[g][(bad_t[g] >= 0) & (bad_t[g] < N)]
+        O, L = OT.gathered_attention(q[0, 0], k[0, 0], v[0, 0], groups[g:g + 1], keep[None],
+                                     1 / 8.0)
+        rows = bad_g[g][bad_g[g] >= 0]
+        check_rows(o[0, 0], lse[0, 0], O, L, rows)
+    assert (o[0, 0, 64 + 5] == 3.0).all() and np.isneginf(lse[0, 0, 64 + 5])
+
+
+def test_gather_forward_empty_lists_and_unnamed_rows():
+    """T = 0: every named row gets O = 0 and LSE = -inf; rows no group names keep `out`."""
+    bsa = need_gpu()
+    B, H, N, D = 1, 2, 384, 64
+    q, k, v = W.gaussian_qkv(8, B, H, N, D)
+    groups = np.arange(128, dtype=np.int32).reshape(1, 1, 2, 64).repeat(H, 1)
+    out = torch.full((B, H, N, D), -2.0, dtype=torch.bfloat16, device="cuda")
+    o, lse = run_gather(bsa, q, k, v, groups, np.zeros((1, H, 2, 0), np.int32), out=out)
+    assert (o[:, :, :128] == 0).all() and np.isneginf(lse[:, :, :128]).all()
+    assert (o[:, :, 128:] == -2.0).all() and np.isneginf(lse[:, :, 128:]).all()
+    # a few tokens, the same unnamed rows
+    tokens = np.stack([random_lists(h, 2, N, 5) for h in range(H)])[None]
+    o, lse = run_gather(bsa, q, k, v, groups, tokens, out=out)
+    assert (o[:, :, 128:] == -2.0).all()
+    for h in range(H):
+        O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[0, h], tokens[0, h], 1 / 8.0)
+        check_rows(o[0, h], lse[0, h], O, L, np.arange(128))
+
+
+def test_gather_forward_rejects_unsupported():
+    bsa = need_gpu()
+    q = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((1, 1, 2, 64), dtype=torch.int32, device="cuda")
+    t = torch.zeros((1, 1, 2, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(bsa.BsaError):
+        bsa.gather_forward(q, q, q, g, t)
+    q64 = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        bsa.gather_forward(q64, q64, q64, g[..., :32].contiguous(), t)
