@@ -259,6 +259,33 @@ def main():
         "anchor_step_ms": anchor_ms, "reuse_step_ms": reuse_ms,
     }
 
+    # Token-level selection at the same density: tile-aligned query groups of 64, token
+    # mass per group from the dense LSE, the top T tokens per group, and the gathered
+    # forward; the kept mass and the output error next to the block CSR's.
+    if w.D == 64 and w.N % 64 == 0:
+        T = int(round(plan.nnz / (n_rows * nb) * w.N))
+        groups = bsa.query_groups(qd, 64)
+        grp_ms = time_launches(lambda: bsa.query_groups(qd, 64), n=5)
+        tmass = bsa.token_mass(qd, kd, lse_dense, groups)
+        tmass_ms = time_launches(lambda: bsa.token_mass(qd, kd, lse_dense, groups), n=10)
+        toks = bsa.select_tokens(tmass, T)
+        sel_tok_ms = time_launches(lambda: bsa.select_tokens(tmass, T), n=10)
+        o_g = torch.zeros_like(qd)
+        bsa.gather_forward(qd, kd, vd, groups, toks, out=o_g, return_lse=False)
+        gather_ms = time_launches(lambda: bsa.gather_forward(qd, kd, vd, groups, toks, out=o_g,
+                                                             return_lse=False), n=20)
+        kept_tok = torch.gather(tmass, 3, toks.long()).double().sum().item()
+        n_groups = groups.shape[0] * groups.shape[1] * groups.shape[2]
+        gather_flops = 4.0 * n_groups * 64 * T * w.D
+        extra["token_selection"] = {
+            "tokens_per_group": T, "groups": n_groups,
+            "query_groups_ms": grp_ms, "token_mass_ms": tmass_ms, "select_tokens_ms": sel_tok_ms,
+            "gather_forward_ms": gather_ms,
+            "gather_forward_tflops": gather_flops / (gather_ms * 1e-3) / 1e12,
+            "mean_kept_mass_tokens": kept_tok / n_q, "mean_kept_mass_csr": kept_csr / n_q,
+            "rel_err_vs_dense_tokens": rel_err(o_g), "rel_err_vs_dense_csr": rel_err(o),
+        }
+
     if args.extra:
         rp1 = (np.arange(n_rows + 1) * nb).astype(np.int32)
         ci1 = torch.from_numpy(np.tile(np.arange(nb, dtype=np.int32), n_rows)).to(dev)
