@@ -288,3 +288,50 @@ def test_tok_mutant_selects_smallest(monkeypatch):
     monkeypatch.setattr(Tk, "select_tokens", lambda m, k: np.stack(
         [np.sort(np.lexsort((np.arange(m.shape[1]), r))[:k]) for r in np.asarray(m)]))
     assert any_tok_pin_fails()
+
+
+# ---- backward oracle -----------------------------------------------------------
+import test_oracle_backward as TBW
+from oracle import backward as Bw
+
+BWD_PINS = [
+    (TBW.test_closed_forms, ()),
+    (TBW.test_sparse_equals_torch_autograd_with_token_mask, ()),
+    (TBW.test_dense_equals_torch_autograd, (64, 16)),
+    (TBW.test_finite_differences, ()),
+]
+
+
+def any_bwd_pin_fails():
+    return any(fails(f, *a) for f, a in BWD_PINS)
+
+
+def test_unmodified_backward_oracle_passes():
+    assert not any_bwd_pin_fails()
+
+
+def test_bwd_mutant_delta_dropped(monkeypatch):
+    monkeypatch.setattr(Bw, "delta", lambda do, o: np.zeros(do.shape[0]))
+    assert any_bwd_pin_fails()
+
+
+def test_bwd_mutant_delta_averaged(monkeypatch):
+    monkeypatch.setattr(Bw, "delta", lambda do, o: (do * o).mean(axis=1))
+    assert any_bwd_pin_fails()
+
+
+def test_bwd_mutant_score_gradient_without_p(monkeypatch):
+    monkeypatch.setattr(Bw, "score_gradient", lambda p, dp, dl: dp - dl[:, None])
+    assert any_bwd_pin_fails()
+
+
+def test_bwd_mutant_score_gradient_sign(monkeypatch):
+    monkeypatch.setattr(Bw, "score_gradient", lambda p, dp, dl: p * (dl[:, None] - dp))
+    assert any_bwd_pin_fails()
+
+
+def test_bwd_mutant_mask_ignored(monkeypatch):
+    orig = Bw.probabilities
+    monkeypatch.setattr(Bw, "probabilities",
+                        lambda q, k, allowed, scale: orig(q, k, np.ones_like(allowed), scale))
+    assert any_bwd_pin_fails()
