@@ -33,6 +33,7 @@ __all__ = [
     "forward_workspace_bytes", "build_mask", "build_mask_status", "schedule", "forward",
     "block_mass", "select_by_mass", "csr_mass", "block_oracle", "residual", "compensate",
     "AnchorReuse", "query_groups", "token_mass", "select_tokens", "gather_forward",
+    "backward", "backward_workspace_bytes",
     "Plan", "Work", "n_blocks", "default_max_tiles",
 ]
 
@@ -68,11 +69,14 @@ _SIGS = {
     "bsa_select_tokens": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "bsa_gather_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
                                   _f32, _vp, _vp, _vp]),
+    "bsa_backward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i64]),
+    "bsa_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                            _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class BsaError(RuntimeError):
@@ -637,3 +641,31 @@ def gather_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, groups: to
                                   _t_ptr(lse) if lse is not None else None,
                                   _stream_ptr(q.device)), "bsa_gather_forward")
     return out, lse
+
+
+def backward_workspace_bytes(B: int, H: int, N: int, block: int, nnz: int) -> int:
+    return int(lib.bsa_backward_workspace_bytes(B, H, N, block, int(nnz)))
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             lse: torch.Tensor, do: torch.Tensor, row_ptr, col_idx, block: int,
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """dQ, dK, dV (bf16 [B,H,N,D]) of the CSR forward for the incoming gradient `do`, from the
+    forward's O and LSE over the same CSR and scale."""
+    B, H, N, D = _check_qkv(q, k, v, o, do)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, N) \
+            or lse.device != q.device:
+        raise ValueError("lse must be contiguous fp32 [B,H,N] on q's device")
+    rp = _dev_i32(row_ptr, q.device)
+    ci = _dev_i32(col_idx, q.device)
+    nnz = ci.numel()                 # an upper bound of row_ptr[-1]
+    need = backward_workspace_bytes(B, H, N, block, nnz)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    s = -1.0 if scale is None else float(scale)
+    _check(lib.bsa_backward(_t_ptr(q), _t_ptr(k), _t_ptr(v), _t_ptr(o), _t_ptr(do), _t_ptr(lse),
+                            B, H, N, D, block, _t_ptr(rp), _t_ptr(ci) if nnz else None, nnz, s,
+                            _t_ptr(dq), _t_ptr(dk), _t_ptr(dv), _t_ptr(workspace),
+                            workspace.numel(), _stream_ptr(q.device)), "bsa_backward")
+    return dq, dk, dv

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbsa.so")
-SOURCES = ["plan.cpp", "fwd.hip", "mask.hip", "sched.hip", "mass.hip", "residual.hip", "tokensel.hip"]
+SOURCES = ["plan.cpp", "fwd.hip", "mask.hip", "sched.hip", "mass.hip", "residual.hip", "tokensel.hip",
+           "bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -51,7 +51,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 7
+#define BSA_ABI_VERSION 8
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -379,6 +379,37 @@ BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* 
                                       int32_t H, int32_t N, int32_t D, const int32_t* groups,
                                       int32_t G, const int32_t* tokens, int32_t T, float scale,
                                       void* o, float* lse, void* stream);
+
+/*
+ * Backward of the CSR forward (device, async).  BSA-DiT §2.3 and §5.2 train with
+ * the block mask; the gradient is that of the forward's definition (§4.1, §4.3:
+ * listed blocks visited, skipped blocks as -inf scores) for an incoming dO of O:
+ *   P = exp(scale q.k - LSE) on listed keys < N (0 elsewhere), dV = P^T dO,
+ *   dP = dO V^T, delta_t = sum_d dO[t,d] O[t,d], dS = P (dP - delta),
+ *   dQ = scale dS K, dK = scale dS^T Q.
+ * q, k, v, o, d_o: bf16 [B,H,N,D]; lse fp32 [B,H,N]: O and LSE of bsa_forward over
+ * the same CSR and scale.  dq, dk, dv: bf16 [B,H,N,D], every row written (keys that
+ * no row lists and queries of empty rows get 0); they must not alias the inputs.
+ * row_ptr, col_idx: the forward's CSR (device); columns of a row must be distinct
+ * (a repeat counts once here but twice in the forward); columns outside [0, nb)
+ * are ignored.  nnz: an upper bound of row_ptr[B*H*nb] (sizes the workspace).
+ * scale <= 0 selects 1/sqrt(D).  Accumulation in fp32, P and dS rounded to bf16 as
+ * MFMA operands; no atomics on the gradients, so results are deterministic.
+ * workspace: device, bsa_backward_workspace_bytes(B, H, N, block, nnz) bytes, 16-byte
+ * aligned; it holds (LSE log2 e, delta) per query row and the transposed CSR, and
+ * needs no initial contents.
+ * Supported: D = 64, block = 64, nb <= 1024.
+ * Errors: INVALID_ARG (null or misaligned pointer, bad size, NaN scale),
+ * UNSUPPORTED (D, block, nb), CAPACITY (workspace too small), HIP.
+ */
+BSA_API size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t block,
+                                            int64_t nnz);
+BSA_API bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o,
+                                const void* d_o, const float* lse, int32_t B, int32_t H,
+                                int32_t N, int32_t D, int32_t block, const int32_t* row_ptr,
+                                const int32_t* col_idx, int64_t nnz, float scale, void* dq,
+                                void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

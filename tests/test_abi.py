@@ -33,7 +33,7 @@ def test_status_strings_and_version():
     assert bsa.status_string(-1) == "BSA_ERR_INVALID_ARG"
     assert bsa.status_string(-5) == "BSA_ERR_PLAN_MISMATCH"
     assert bsa.status_string(-99) == "BSA_ERR_UNKNOWN"
-    assert bsa.abi_version() == bsa.ABI_VERSION == 7
+    assert bsa.abi_version() == bsa.ABI_VERSION == 8
 
 
 def test_budget_matches_oracle():
@@ -208,3 +208,12 @@ def test_import_does_not_open_the_library():
             "assert b._Lib._handle is None; b.abi_version(); assert b._Lib._handle is not None")
     root = __import__("os").path.dirname(__import__("os").path.dirname(__import__("os").path.abspath(__file__)))
     subprocess.run([sys.executable, "-c", code], check=True, cwd=root)
+
+
+def test_backward_workspace_bytes():
+    L = bsa.lib
+    # (LSE log2 e, delta) per row, then col_ptr [B*H*nb + 1], then row_idx [nnz]; 256-B rounding
+    assert L.bsa_backward_workspace_bytes(1, 2, 512, 64, 100) == 8 * 1024 + 256 + 512
+    assert L.bsa_backward_workspace_bytes(2, 24, 4224, 64, 31968) == \
+        8 * 202752 + 12800 + 128000
+    assert L.bsa_backward_workspace_bytes(0, 2, 512, 64, 100) == 0

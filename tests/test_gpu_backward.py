@@ -1,0 +1,127 @@
+"""GPU parity of bsa_backward (dQ, dK, dV over the forward's CSR) against the fp64 backward
+oracle (oracle/backward.py), through the C ABI; the forward's own O and LSE feed it."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import backward as OB
+from parity import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+# bf16 unit roundoff; P and dS are rounded to bf16 once as MFMA operands and every
+# gradient once on output, O (for delta) is the forward's bf16 output.
+U = 2.0 ** -9
+MAX_REL = 8 * U      # max |err| over a tensor, relative to the tensor's max |ref|
+MEAN_REL = U         # mean |err| over a tensor, relative to the tensor's max |ref|
+
+
+def csr_from_cols(cols):
+    rp = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    ci = (np.concatenate([np.asarray(c, np.int32) for c in cols]) if rp[-1]
+          else np.zeros(0, np.int32)).astype(np.int32)
+    return rp, ci
+
+
+def run(bsa, q, k, v, do, rp, ci, block=64):
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = bsa.forward(qd, kd, vd, rp, ci, block)
+    g = bsa.backward(qd, kd, vd, o, lse, dod, rp, ci, block)
+    torch.cuda.synchronize()
+    return [x.float().cpu().numpy().astype(np.float64) for x in g]
+
+
+def compare(got, want, names=("dq", "dk", "dv")):
+    for n, g, w in zip(names, got, want):
+        assert np.isfinite(g).all(), n
+        scale = max(np.abs(w).max(), 1e-30)
+        err = np.abs(g - w)
+        print(f"  {n}: max {err.max() / scale:.2e} mean {err.mean() / scale:.2e} (of max |ref|)",
+              flush=True)
+        assert err.max() <= MAX_REL * scale and err.mean() <= MEAN_REL * scale, n
+
+
+@pytest.mark.parametrize("N,p,seed", [(512, 0.5, 0), (245, 0.6, 1), (64, 1.0, 2), (1000, 0.3, 3)])
+def test_backward_matches_oracle(N, p, seed):
+    """Random CSR (diagonal kept), ragged last blocks, one row left empty."""
+    bsa = need_gpu()
+    print(f"case N={N} p={p}", flush=True)
+    B, H, D, block = 1, 2, 64, 64
+    nb = -(-N // block)
+    q, k, v = W.gaussian_qkv(100 + seed, B, H, N, D)
+    do = W.gaussian_qkv(200 + seed, B, H, N, D)[0]
+    rng = np.random.default_rng(seed)
+    cols = [sorted(set(np.flatnonzero(rng.random(nb) < p).tolist()) | {r % nb})
+            for r in range(B * H * nb)]
+    if nb > 1:
+        cols[1] = []
+    rp, ci = csr_from_cols(cols)
+    got = run(bsa, q, k, v, do, rp, ci)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / 8.0, do)
+    compare(got, want)
+    if nb > 1:
+        assert np.all(got[0][0, 0, 64:128] == 0.0)       # the empty row's dQ
+
+
+def test_backward_unlisted_block_and_out_of_range_columns():
+    """A key block no row lists gets dK = dV = 0; columns outside [0, nb) are ignored."""
+    bsa = need_gpu()
+    B, H, N, D, block = 1, 1, 384, 64, 64
+    nb = N // block
+    q, k, v = W.gaussian_qkv(5, B, H, N, D)
+    do = W.gaussian_qkv(6, B, H, N, D)[0]
+    cols = [[c for c in range(nb) if c != 3 and (c + r) % 2 == 0] or [0] for r in range(nb)]
+    clean = csr_from_cols(cols)
+    noisy = csr_from_cols([c + [-1, nb + 2] for c in cols])
+    got = run(bsa, q, k, v, do, *noisy)
+    want = OB.block_sparse_backward(q, k, v, *clean, block, 1 / 8.0, do)
+    compare(got, want)
+    assert np.all(got[1][0, 0, 192:256] == 0.0) and np.all(got[2][0, 0, 192:256] == 0.0)
+
+
+def test_backward_dense_and_deterministic():
+    """All-ones CSR (every key block listed by every row); two calls give the same bits."""
+    bsa = need_gpu()
+    B, H, N, D, block = 2, 2, 320, 64, 64
+    nb = N // block
+    q, k, v = W.gaussian_qkv(9, B, H, N, D)
+    do = W.gaussian_qkv(10, B, H, N, D)[0]
+    rp, ci = csr_from_cols([list(range(nb))] * (B * H * nb))
+    got = run(bsa, q, k, v, do, rp, ci)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / 8.0, do)
+    compare(got, want)
+    again = run(bsa, q, k, v, do, rp, ci)
+    assert all(np.array_equal(a, b) for a, b in zip(got, again))
+
+
+def test_backward_t2i_sampled_heads():
+    """The t2i workload at full size (B2 H24 N4224, its static mask); the oracle on two
+    heads (each head's gradients depend on that head only)."""
+    bsa = need_gpu()
+    w = W.make("t2i")
+    q, k, v = w.tensors()
+    do = W.gaussian_qkv(w.seed + 1000, w.B, w.H, w.N, w.D)[0]
+    nb = w.nb
+    prior = w.prior() | np.eye(nb, dtype=bool)
+    rp, ci = csr_from_cols([np.flatnonzero(prior[r % nb]) for r in range(w.B * w.H * nb)])
+    assert rp[nb] == 666
+    got = run(bsa, q, k, v, do, rp, ci, w.block)
+    for b, h in ((0, 0), (1, 23)):
+        r0 = (b * w.H + h) * nb
+        sub_rp = (rp[r0:r0 + nb + 1] - rp[r0]).astype(np.int32)
+        sub_ci = ci[rp[r0]:rp[r0 + nb]]
+        want = OB.block_sparse_backward(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
+                                        v[b:b + 1, h:h + 1], sub_rp, sub_ci, w.block,
+                                        1 / np.sqrt(w.D), do[b:b + 1, h:h + 1])
+        compare([g[b:b + 1, h:h + 1] for g in got], want)
+
+
+def test_backward_rejects_unsupported():
+    bsa = need_gpu()
+    q = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 1, 128), dtype=torch.float32, device="cuda")
+    rp = np.array([0, 1, 2], np.int32)
+    ci = np.array([0, 1], np.int32)
+    with pytest.raises(bsa.BsaError):
+        bsa.backward(q, q, q, q, lse, q, rp, ci, 64)
