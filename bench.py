@@ -286,8 +286,28 @@ def main():
             "rel_err_vs_dense_tokens": rel_err(o_g), "rel_err_vs_dense_csr": rel_err(o),
         }
 
+    # Backward over the same CSR (block 64, D 64): dQ, dK, dV from the forward's O and LSE
+    # for a seeded N(0,1) incoming gradient; 10 * q_valid * k_valid * D FLOPs per active
+    # pair (the five products S, dP, dV, dS K, dS^T Q), all four launches in the timing.
+    if w.D == 64 and w.block == 64:
+        g = torch.Generator("cpu").manual_seed(1000 + w.N)
+        do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+        bws = torch.empty(max(bsa.backward_workspace_bytes(w.B, w.H, w.N, w.block, plan.nnz),
+                              256), dtype=torch.uint8, device=dev)
+        bsa.backward(qd, kd, vd, o, lse, do, plan.row_ptr, col_idx[:plan.nnz], w.block,
+                     workspace=bws)
+        bwd_ms = time_launches(lambda: bsa.backward(qd, kd, vd, o, lse, do, plan.row_ptr,
+                                                    col_idx[:plan.nnz], w.block,
+                                                    workspace=bws), n=20)
+        bwd_flops = 2.5 * flops
+        extra["backward"] = {
+            "backward_ms": bwd_ms, "active_gflop": bwd_flops / 1e9,
+            "tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        }
+
     if args.extra:
-        rp1 = (np.arange(n_rows + 1) * nb).astype(np.int32)
+        rp1 =(np.arange(n_rows + 1) * nb).astype(np.int32)
         ci1 = torch.from_numpy(np.tile(np.arange(nb, dtype=np.int32), n_rows)).to(dev)
         rp1d = torch.from_numpy(rp1).to(dev)
         dense_ms = time_launches(lambda: bsa.forward(qd, kd, vd, rp1d, ci1, w.block, out=o, lse=lse))
