@@ -5,19 +5,27 @@
 //   P = exp(scale q.k - LSE), dV = P^T dO, dP = dO V^T,
 //   delta_t = sum_d dO[t,d] O[t,d], dS = P (dP - delta), dQ = scale dS K,
 //   dK = scale dS^T Q.
-// Four launches on the caller's stream:
+// Five launches on the caller's stream:
 //   prep       per query row (LSE * log2(e), delta), fp32;
-//   transpose  per head, the query blocks that list each key block, ascending;
-//   dkdv       one workgroup per key block, walking its query blocks;
-//   dq         one workgroup per query block, walking its CSR row.
-// The two gradient kernels recompute S and P from the LSE; neither uses atomics
-// on the gradients, so results are deterministic.  Block 64 and D = 64.
+//   transpose  per head, the query blocks that list each key block, ascending,
+//              and the split of long key columns and query rows into chunks;
+//   dkdv       one workgroup per chunk of a key block's query blocks;
+//   dq         one workgroup per chunk of a query block's CSR row;
+//   reduce     per split block, the chunks' fp32 partials summed in chunk order.
+// A column or row longer than the chunk length (twice the mean row length, at
+// least 16) is cut into near-equal chunks so that a few long ones (text blocks,
+// anchor columns) do not set the length of the launch.  The two gradient
+// kernels recompute S and P from the LSE; nothing uses atomics on the
+// gradients, so results are deterministic.  Block 64 and D = 64.
 #include <math.h>
+
+#include <algorithm>
 
 #include <mutex>
 
 #include "common.h"
 #include "tile.h"
+#include "dma.h"
 
 namespace bsa {
 namespace {
@@ -26,6 +34,7 @@ constexpr int kBB = 64;     // block (query block = key block)
 constexpr int kBD = 64;     // head dimension
 constexpr int kRB = 128;    // bytes of one bf16 row
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kDqStages = 2;  // K/V ring depth of the dQ kernel
 
 __device__ __forceinline__ void lds_write16(uint32_t addr, v4u x) {
   *reinterpret_cast<BSA_LDS v4u*>(static_cast<uintptr_t>(addr)) = x;
@@ -48,11 +57,13 @@ __device__ __forceinline__ float dot8(v4u a, v4u b) {
 
 // Per query row t: (LSE_t * log2(e), delta_t); rows with LSE = -inf (no active key)
 // get +inf so that every probability of the row is exp2(-inf) = 0.  Eight lanes
-// per row, 16 bytes each.
+// per row, 16 bytes each.  Also clears the two partial-slot counters.
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ O,
                                                    const uint16_t* __restrict__ dO,
                                                    const float* __restrict__ LSE, int64_t rows,
-                                                   float2* __restrict__ out) {
+                                                   float2* __restrict__ out,
+                                                   int32_t* __restrict__ slot_ctr) {
+  if (blockIdx.x == 0 && threadIdx.x < 2) slot_ctr[threadIdx.x] = 0;  // read by transpose
   const int64_t t = (int64_t(blockIdx.x) * 256 + threadIdx.x) >> 3;
   const int c = threadIdx.x & 7;
   float acc = 0.f;
@@ -70,56 +81,184 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// 4 bytes per lane from buffer offset `voff` into LDS at lds + 4 * lane (each
+// dword checked against the buffer's range on its own).
+__device__ __forceinline__ void dma4(v4i desc, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(desc)
+      : "memory");
+}
+
+// Buffer descriptor with wave-uniform (scalar) fields.
+__device__ __forceinline__ v4i uniform_desc(const void* base, uint32_t bytes) {
+  v4i d = make_desc(base, bytes);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) d[w] = __builtin_amdgcn_readfirstlane(d[w]);
+  return d;
+}
+
+// Source offsets of the 16-byte chunks a lane moves in dma_half: segments 0, 2
+// (ve) and 1, 3 (vo) of a 32-row half tile, so that they land swizzled.
+__device__ __forceinline__ void dma_offsets(int lane, uint32_t& ve, uint32_t& vo) {
+  const int r0 = lane >> 3, p = lane & 7;
+  ve = uint32_t(r0) * kRB + uint32_t((p ^ chunk_swizzle<kRB>(r0)) << 4);
+  vo = uint32_t(r0) * kRB + uint32_t((p ^ chunk_swizzle<kRB>(8 + r0)) << 4);
+}
+
+// The entries idx[e] of a CSR range [e0, e1) a workgroup walks in order, 64 at a
+// time in one VGPR (lane l holds idx[base + l]); -1 past e1.
+struct IndexWindow {
+  const int32_t* idx;
+  int e1, base, v;
+  __device__ void init(const int32_t* p, int e0, int end, int lane) {
+    idx = p;
+    e1 = end;
+    base = e0;
+    v = e0 + lane < e1 ? idx[e0 + lane] : -1;
+    asm volatile("" ::"v"(v));  // complete here, not inside a DMA-pipelined loop
+  }
+  // Entry e (e >= base, called with non-decreasing e).
+  __device__ int at(int e, int lane) {
+    if (e >= e1) return -1;
+    if (e - base >= 64) {
+      base += 64;
+      v = base + lane < e1 ? idx[base + lane] : -1;
+      asm volatile("" ::"v"(v));
+    }
+    return __builtin_amdgcn_readlane(v, e - base);
+  }
+};
+
+// Number of chunks of a column or row of `len` entries: 1 up to the chunk
+// length, else ceil(len / chunk) capped at max_ch.
+__device__ __forceinline__ int n_chunks(int len, int chunk, int max_ch) {
+  return len > chunk ? min((len + chunk - 1) / chunk, max_ch) : 1;
+}
+
+// Exclusive prefix sum of a[0, n) in place by a 256-thread workgroup (n <= 1024);
+// returns the total.  tmp: 256 ints of LDS.
+__device__ int block_scan(int32_t* a, int n, int32_t* tmp) {
+  const int tid = threadIdx.x;
+  const int per = (n + 255) >> 8;
+  const int lo = min(tid * per, n), hi = min(lo + per, n);
+  int sum = 0;
+  for (int x = lo; x < hi; ++x) sum += a[x];
+  tmp[tid] = sum;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = tid >= d ? tmp[tid - d] : 0;
+    __syncthreads();
+    tmp[tid] += v;
+    __syncthreads();
+  }
+  int off = tid ? tmp[tid - 1] : 0;
+  const int total = tmp[255];
+  for (int x = lo; x < hi; ++x) {
+    const int v = a[x];
+    a[x] = off;
+    off += v;
+  }
+  __syncthreads();
+  return total;
+}
+
 // Transpose of one head's CSR: for key block j, the query blocks i whose row
 // lists j, ascending.  Head bh's entries keep the CSR's range
 // [row_ptr[bh nb], row_ptr[(bh+1) nb]); column j starts at col_ptr[bh nb + j].
 // A pair listed twice, or a column outside [0, nb), leaves a slot that is
 // filled with -1 at the end of the head's last column.  An LDS bitmap
-// (bit i of word j*W + i/32) orders each column without sorting.
+// (bit i of word j*W + i/32) orders each column without sorting; the entries
+// are read in parallel, each finding its row by binary search.
+// Splits: col_split[bh nb + j] = (first partial slot, chunks) of key column j,
+// row_split the same for the CSR rows; a head's split blocks take consecutive
+// slots from the counters (cleared by prep_kernel).  If the slots run out (they
+// cannot when the capacity is the bound the host sizes), the head is left
+// unsplit, which is slower but exact.
 __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restrict__ row_ptr,
                                                         const int32_t* __restrict__ col_idx,
                                                         int32_t nb, int32_t n_heads,
                                                         int32_t* __restrict__ col_ptr,
-                                                        int32_t* __restrict__ row_idx) {
+                                                        int32_t* __restrict__ row_idx,
+                                                        int32_t chunk, int32_t max_ch,
+                                                        int32_t* __restrict__ slot_ctr,
+                                                        int32_t cap_kv, int32_t cap_q,
+                                                        int2* __restrict__ col_split,
+                                                        int2* __restrict__ row_split) {
   extern __shared__ uint32_t bits[];
-  __shared__ int32_t start[kMaxBlocks];
-  __shared__ int32_t tail_sh;
+  __shared__ int32_t rp[kMaxBlocks + 1];
+  __shared__ int32_t start[kMaxBlocks], nch_c[kMaxBlocks], nch_r[kMaxBlocks];
+  __shared__ int32_t pre_c[kMaxBlocks], pre_r[kMaxBlocks], tmp[256];
+  __shared__ int32_t base_sh[2];
   const int tid = threadIdx.x;
   const int W = (nb + 31) >> 5;
   const int bh = blockIdx.x;
   const int r0 = bh * nb;
   for (int x = tid; x < nb * W; x += 256) bits[x] = 0u;
+  for (int i = tid; i <= nb; i += 256) rp[i] = row_ptr[r0 + i];
   __syncthreads();
+  const int begin = rp[0], end = rp[nb];
   for (int i = tid; i < nb; i += 256) {
-    const int e1 = row_ptr[r0 + i + 1];
-    for (int e = row_ptr[r0 + i]; e < e1; ++e) {
-      const int j = col_idx[e];
-      if (j >= 0 && j < nb) atomicOr(&bits[j * W + (i >> 5)], 1u << (i & 31));
+    const int n = n_chunks(rp[i + 1] - rp[i], chunk, max_ch);
+    nch_r[i] = n;
+    pre_r[i] = n > 1 ? n : 0;
+  }
+  for (int e = begin + tid; e < end; e += 256) {
+    int lo = 0, hi = nb - 1;  // the row i with rp[i] <= e < rp[i + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (rp[mid] <= e)
+        lo = mid;
+      else
+        hi = mid - 1;
     }
+    const int j = col_idx[e];
+    if (j >= 0 && j < nb) atomicOr(&bits[j * W + (lo >> 5)], 1u << (lo & 31));
   }
   __syncthreads();
   for (int j = tid; j < nb; j += 256) {
     int c = 0;
     for (int w = 0; w < W; ++w) c += __popc(bits[j * W + w]);
     start[j] = c;
+    nch_c[j] = c;  // the column's length (the last one gains the padding below)
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = row_ptr[r0];
-    for (int j = 0; j < nb; ++j) {
-      const int c = start[j];
-      start[j] = run;
-      col_ptr[r0 + j] = run;
-      run += c;
-    }
-    tail_sh = run;
-    if (bh == n_heads - 1) col_ptr[r0 + nb] = row_ptr[r0 + nb];
-  }
+  const int listed = block_scan(start, nb, tmp);
+  if (tid == 0) nch_c[nb - 1] += (end - begin) - listed;  // the head's -1 padding
   __syncthreads();
-  const int end = row_ptr[r0 + nb];
-  for (int e = tail_sh + tid; e < end; e += 256) row_idx[e] = -1;
   for (int j = tid; j < nb; j += 256) {
-    int pos = start[j];
+    const int n = n_chunks(nch_c[j], chunk, max_ch);
+    nch_c[j] = n;
+    pre_c[j] = n > 1 ? n : 0;
+  }
+  __syncthreads();
+  const int tot_kv = block_scan(pre_c, nb, tmp);
+  const int tot_q = block_scan(pre_r, nb, tmp);
+  if (tid == 0) {
+    int bk = tot_kv ? atomicAdd(slot_ctr, tot_kv) : 0;
+    int bq = tot_q ? atomicAdd(slot_ctr + 1, tot_q) : 0;
+    base_sh[0] = (bk < 0 || bk > cap_kv - tot_kv) ? -1 : bk;
+    base_sh[1] = (bq < 0 || bq > cap_q - tot_q) ? -1 : bq;
+    if (bh == n_heads - 1) col_ptr[r0 + nb] = end;
+  }
+  __syncthreads();
+  const int bk = base_sh[0], bq = base_sh[1];
+  for (int j = tid; j < nb; j += 256) {
+    col_ptr[r0 + j] = begin + start[j];
+    col_split[r0 + j] = (nch_c[j] > 1 && bk >= 0) ? make_int2(bk + pre_c[j], nch_c[j])
+                                                  : make_int2(-1, 1);
+    row_split[r0 + j] = (nch_r[j] > 1 && bq >= 0) ? make_int2(bq + pre_r[j], nch_r[j])
+                                                  : make_int2(-1, 1);
+  }
+  for (int e = begin + listed + tid; e < end; e += 256) row_idx[e] = -1;
+  for (int j = tid; j < nb; j += 256) {
+    int pos = begin + start[j];
     for (int w = 0; w < W; ++w) {
       uint32_t m = bits[j * W + w];
       while (m) {
@@ -131,34 +270,46 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
   }
 }
 
-// dK, dV of one key block j (workgroup (bh, j), two wavefronts; wave w owns keys
-// 32w .. 32w+31, which are the columns of its tiles).  For every query block i
-// of the column: the 64 Q and dO rows are staged in LDS (swizzled), then per
+// dK, dV of one chunk of key block j (workgroup (chunk, bh, j), two wavefronts;
+// wave w owns keys 32w .. 32w+31, which are the columns of its tiles).  For
+// every query block i of the chunk: the 64 Q and dO rows are staged in LDS (swizzled), then per
 // 32-query tile S = Q K^T and dP = dO V^T on MFMA (K, V rows of the wave's keys
 // are the B operands, held in registers), P = exp2(S scale log2e - LSE log2e),
 // dS = P (dP - delta), and dV^T += dO^T P, dK^T += Q^T dS with dO^T, Q^T read
-// transposed from LDS.
+// transposed from LDS.  An unsplit column writes bf16 dK, dV; a chunk of a
+// split one writes its fp32 sums (dK unscaled) to partial slot `slot + chunk`.
 __global__ __launch_bounds__(128) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ ld,
-    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, int32_t N,
-    int32_t nb, float c2, float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV) {
-  __shared__ __align__(16) uint8_t smem[2 * kBB * kRB + 2 * kBB * 4];
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
+    const int2* __restrict__ col_split, int32_t n_cols, int32_t N, int32_t nb, float c2,
+    float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part) {
+  // Two stages of (Q tile, dO tile, per-row (LSE log2 e, delta)) of one query
+  // block, each wave streaming its 32-row halves by LDS DMA one block ahead.
+  constexpr uint32_t kTile = kBB * kRB, kHalf = kTile / 2, kLd = kBB * 8;
+  constexpr uint32_t kStage = 2 * kTile + kLd;
+  __shared__ __align__(16) uint8_t smem[2 * kStage];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
-  const uint32_t qs = lds0, dss = lds0 + kBB * kRB;
-  float* lse_s = reinterpret_cast<float*>(smem + 2 * kBB * kRB);
-  float* del_s = lse_s + kBB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hh = lane >> 5;
-  const int r = blockIdx.x;
+  const int ch = blockIdx.x / n_cols;
+  const int r = blockIdx.x - ch * n_cols;
+  const int2 sp = col_split[r];
+  const int slot = __builtin_amdgcn_readfirstlane(sp.x);
+  const int nch = slot < 0 ? 1 : __builtin_amdgcn_readfirstlane(sp.y);
+  if (ch >= nch) return;
   const int bh = r / nb, j = r - bh * nb;
   const size_t head = size_t(bh) * size_t(N) * kBD;
   const uint32_t hbytes = static_cast<uint32_t>(N) * kRB;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, hbytes);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, hbytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, hbytes);
-  const __amdgpu_buffer_rsrc_t dr = make_rsrc(dO + head, hbytes);
+  const v4i qd = uniform_desc(Q + head, hbytes), dd = uniform_desc(dO + head, hbytes);
+  // (LSE log2 e, delta) of the head's rows; rows past N read zeros, which is
+  // harmless: their Q and dO rows are zeros too, so they add exactly nothing.
+  const v4i ldd = uniform_desc(ld + size_t(bh) * N, static_cast<uint32_t>(N) * 8u);
+  uint32_t ve, vo;
+  dma_offsets(lane, ve, vo);
   const int key = kBB * j + 32 * w + ql;
   const bool key_ok = key < N;
   bf16x8 kf[4], vf[4];
@@ -168,6 +319,9 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     kf[c] = __builtin_bit_cast(bf16x8, load16(kr, off));
     vf[c] = __builtin_bit_cast(bf16x8, load16(vr, off));
   }
+  // Complete these loads before the DMA-pipelined loop.
+#pragma unroll
+  for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(kf[c]), "v"(vf[c]));
   f32x16 dk[2], dv[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -178,27 +332,40 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     }
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int e0 = __builtin_amdgcn_readfirstlane(col_ptr[r]);
-  const int e1 = __builtin_amdgcn_readfirstlane(col_ptr[r + 1]);
-  for (int e = e0; e < e1; ++e) {
-    const int i = __builtin_amdgcn_readfirstlane(row_idx[e]);
+  const int c0 = __builtin_amdgcn_readfirstlane(col_ptr[r]);
+  const int c1 = __builtin_amdgcn_readfirstlane(col_ptr[r + 1]);
+  const int e0 = c0 + int(int64_t(c1 - c0) * ch / nch);
+  const int e1 = c0 + int(int64_t(c1 - c0) * (ch + 1) / nch);
+  IndexWindow rows;
+  rows.init(row_idx, e0, e1, lane);
+  // This wave's halves of query block i into stage st (9 loads); a block outside
+  // [0, nb) reads past the buffers, i.e. zeros.
+  auto issue = [&](int i, int st) {
+    const bool ok = i >= 0 && i < nb;
+    const uint32_t tb = ok ? uint32_t(i) * kTile + uint32_t(w) * kHalf : hbytes;
+    const uint32_t sb = lds0 + uint32_t(st) * kStage;
+    dma_half(qd, ve + tb, vo + tb, sb + uint32_t(w) * kHalf);
+    dma_half(dd, ve + tb, vo + tb, sb + kTile + uint32_t(w) * kHalf);
+    const uint32_t lo = ok ? uint32_t(kBB * i + 32 * w) * 8u + 4u * uint32_t(lane)
+                           : static_cast<uint32_t>(N) * 8u;
+    dma4(ldd, lo, sb + 2 * kTile + uint32_t(w) * (kLd / 2));
+  };
+  int i_next = rows.at(e0, lane);
+  if (e0 < e1) issue(i_next, 0);
+  for (int e = e0, st = 0; e < e1; ++e, st ^= 1) {
+    const int i = i_next;
+    lds_barrier();  // both waves are done reading the other stage (block e-1)
+    if (e + 1 < e1) {
+      i_next = rows.at(e + 1, lane);
+      issue(i_next, st ^ 1);
+      wait_vm_n(9);
+    } else {
+      wait_vm(0);
+    }
+    lds_barrier();  // both waves' halves of block e are in LDS
     if (i < 0 || i >= nb) continue;
-    __syncthreads();  // the previous block's LDS reads are done
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int idx = tid + 128 * x;
-      const int rr = idx >> 3, cc = idx & 7;
-      const uint32_t off = uint32_t(kBB * i + rr) * kRB + uint32_t(16 * cc);
-      lds_write16(qs + swz<kRB>(rr, cc), load16(qr, off));
-      lds_write16(dss + swz<kRB>(rr, cc), load16(dr, off));
-    }
-    if (tid < kBB) {
-      const int t = kBB * i + tid;
-      const float2 x = t < N ? ld[size_t(bh) * N + t] : make_float2(INFINITY, 0.f);
-      lse_s[tid] = x.x;
-      del_s[tid] = x.y;
-    }
-    __syncthreads();
+    const uint32_t qs = lds0 + uint32_t(st) * kStage, dss = qs + kTile;
+    const float* lds_ld = reinterpret_cast<const float*>(smem + size_t(st) * kStage + 2 * kTile);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const f32x16 zero = {};
@@ -214,8 +381,11 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4 L = *reinterpret_cast<const f32x4*>(lse_s + 32 * g + 8 * m + 4 * hh);
-        const f32x4 Dl = *reinterpret_cast<const f32x4*>(del_s + 32 * g + 8 * m + 4 * hh);
+        // (LSE, delta) of queries 32g + 8m + 4hh .. +3, interleaved
+        const f32x4 x01 = *reinterpret_cast<const f32x4*>(lds_ld + 2 * (32 * g + 8 * m + 4 * hh));
+        const f32x4 x23 = *reinterpret_cast<const f32x4*>(lds_ld + 2 * (32 * g + 8 * m + 4 * hh) + 4);
+        const f32x4 L = {x01[0], x01[2], x23[0], x23[2]};
+        const f32x4 Dl = {x01[1], x01[3], x23[1], x23[3]};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int ei = 4 * m + x;
@@ -244,7 +414,21 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     }
   }
   // register e of dv[u], dk[u]: dimension 32u + 8(e/4) + 4hh + e%4 of key `key`
-  if (key_ok) {
+  if (nch > 1) {
+    // [dK | dV] of the block's 64 keys, row-major, fp32; keys past N hold zeros
+    float* pk = part + size_t(slot + ch) * (2 * kBB * kBD) + size_t(32 * w + ql) * kBD;
+    float* pv = pk + kBB * kBD;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * u + 8 * g4 + 4 * hh;
+        *reinterpret_cast<f32x4*>(pk + d) =
+            f32x4{dk[u][4 * g4], dk[u][4 * g4 + 1], dk[u][4 * g4 + 2], dk[u][4 * g4 + 3]};
+        *reinterpret_cast<f32x4*>(pv + d) =
+            f32x4{dv[u][4 * g4], dv[u][4 * g4 + 1], dv[u][4 * g4 + 2], dv[u][4 * g4 + 3]};
+      }
+  } else if (key_ok) {
     uint16_t* vrow = dV + head + size_t(key) * kBD;
     uint16_t* krow = dK + head + size_t(key) * kBD;
 #pragma unroll
@@ -262,31 +446,44 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
   }
 }
 
-// dQ of one query block i (workgroup (bh, i), two wavefronts; wave kh owns keys
-// 32kh .. 32kh+31 of every key block of the row).  The forward's orientation:
+// dQ of one chunk of query block i's row (workgroup (chunk, bh, i), two
+// wavefronts; wave kh owns keys 32kh .. 32kh+31 of every key block of the row).  The forward's orientation:
 // S^T = K Q^T and dP^T = V dO^T with the queries as columns (Q^T, dO^T B
 // operands held in registers, one LSE and delta per lane), dS^T = P^T (dP^T -
 // delta), and dQ^T += K^T dS^T with K^T read transposed from the wave's LDS
-// area.  The two key halves are summed through LDS at the end.
+// area.  The two key halves are summed through LDS at the end; an unsplit row
+// writes bf16 dQ, a chunk of a split one its fp32 sum (unscaled) to partial
+// slot `slot + chunk`.
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ ld,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int32_t N,
-    int32_t nb, float c2, float scale, uint16_t* __restrict__ dQ) {
-  __shared__ __align__(16) uint8_t smem[2 * 32 * kRB + 2 * 8192];
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int2* __restrict__ row_split, int32_t n_rows, int32_t N, int32_t nb, float c2,
+    float scale, uint16_t* __restrict__ dQ, float* __restrict__ part) {
+  // Per wave: a ring of kDqStages stages of its 32 key rows of K and of V
+  // (4 KiB each per stage), streamed by LDS DMA kDqStages - 1 key blocks ahead;
+  // no barrier in the loop.
+  __shared__ __align__(16) uint8_t smem[2 * kDqStages * 2 * 32 * kRB];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
   const int lane = threadIdx.x & 63;
   const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 31, hh = lane >> 5;
-  const int r = blockIdx.x;
+  const int ch = blockIdx.x / n_rows;
+  const int r = blockIdx.x - ch * n_rows;
+  const int2 sp = row_split[r];
+  const int slot = __builtin_amdgcn_readfirstlane(sp.x);
+  const int nch = slot < 0 ? 1 : __builtin_amdgcn_readfirstlane(sp.y);
+  if (ch >= nch) return;
   const int bh = r / nb, i = r - bh * nb;
   const size_t head = size_t(bh) * size_t(N) * kBD;
   const uint32_t hbytes = static_cast<uint32_t>(N) * kRB;
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, hbytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, hbytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, hbytes);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(dO + head, hbytes);
-  const uint32_t ks = lds0 + uint32_t(kh) * (32 * kRB);
+  const v4i kd = uniform_desc(K + head, hbytes), vd = uniform_desc(V + head, hbytes);
+  constexpr uint32_t kHalf = 32 * kRB, kStage = 2 * kHalf;
+  const uint32_t ring = lds0 + uint32_t(kh) * (kDqStages * kStage);
+  uint32_t ve, vo;
+  dma_offsets(lane, ve, vo);
   bf16x8 qf[2][4], df[2][4];
   float L[2], Dl[2];
 #pragma unroll
@@ -302,6 +499,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     L[g] = x.x;
     Dl[g] = x.y;
   }
+  // Complete these loads before the DMA-pipelined loop (a load the compiler sees
+  // pending into the loop would make it wait for every DMA at each step).
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qf[g][c]), "v"(df[g][c]));
+    asm volatile("" ::"v"(L[g]), "v"(Dl[g]));
+  }
   f32x16 acc[2][2];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
@@ -311,24 +516,51 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
       for (int x = 0; x < 16; ++x) acc[g][u][x] = 0.f;
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[r]);
-  const int e1 = __builtin_amdgcn_readfirstlane(row_ptr[r + 1]);
-  for (int e = e0; e < e1; ++e) {
-    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
+  const int b0 = __builtin_amdgcn_readfirstlane(row_ptr[r]);
+  const int b1 = __builtin_amdgcn_readfirstlane(row_ptr[r + 1]);
+  const int e0 = b0 + int(int64_t(b1 - b0) * ch / nch);
+  const int e1 = b0 + int(int64_t(b1 - b0) * (ch + 1) / nch);
+  IndexWindow cols;
+  cols.init(col_idx, e0, e1, lane);
+  // This wave's half of key block j (K, then V) into ring stage st; a column
+  // outside [0, nb) reads past the buffers, i.e. zeros.
+  auto issue = [&](int j, int st) {
+    const bool ok = j >= 0 && j < nb;
+    const uint32_t tb = ok ? uint32_t(j) * (kBB * kRB) + uint32_t(kh) * kHalf : hbytes;
+    const uint32_t dst = ring + uint32_t(st) * kStage;
+    dma_kv_half(kd, vd, ve + tb, vo + tb, dst, dst + kHalf);
+  };
+  // Blocks e0 .. e0 + kDqStages - 2 go first; at step e, block e + kDqStages - 1
+  // goes into the stage block e - 1 used (its reads are complete), then the
+  // wait leaves the younger blocks (8 loads each) in flight.
+  int jq[kDqStages];
+#pragma unroll
+  for (int x = 0; x < kDqStages - 1; ++x) {
+    jq[x] = cols.at(e0 + x, lane);
+    if (e0 + x < e1) issue(jq[x], x);
+  }
+  for (int e = e0, st = 0; e < e1; ++e, st = st + 1 == kDqStages ? 0 : st + 1) {
+    const int ahead = e + kDqStages - 1;
+    const int sa = st == 0 ? kDqStages - 1 : st - 1;
+    int j = -1;
+#pragma unroll
+    for (int x = 0; x < kDqStages; ++x)
+      if (x == st) j = jq[x];
+    if (ahead < e1) {
+      const int ja = cols.at(ahead, lane);
+#pragma unroll
+      for (int x = 0; x < kDqStages; ++x)
+        if (x == sa) jq[x] = ja;
+      issue(ja, sa);
+    }
+    wait_vm_n(8 * (min(ahead, e1 - 1) - e));
     if (j < 0 || j >= nb) continue;
     const int kbase = kBB * j + 32 * kh;  // first key of this wave's half
-    // K rows of the wave's 32 keys into its LDS area (one wavefront's LDS
-    // operations complete in order, so the previous block's reads are done).
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int rr = 8 * x + (lane >> 3);
-      lds_write16(ks + swz<kRB>(rr, lane & 7),
-                  load16(kr, uint32_t(kbase + rr) * kRB + uint32_t(16 * (lane & 7))));
-    }
+    const uint32_t ks = ring + uint32_t(st) * kStage, vs = ks + kHalf;
     bf16x8 va[4], ka[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      va[c] = __builtin_bit_cast(bf16x8, load16(vr, uint32_t(kbase + ql) * kRB + uint32_t(32 * c + 16 * hh)));
+      va[c] = lds_read16(vs + swz<kRB>(ql, 2 * c + hh));
       ka[c] = lds_read16(ks + swz<kRB>(ql, 2 * c + hh));
     }
     bf16x8 sb[2][2];
@@ -365,9 +597,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
       }
   }
   // Key-half sum: wave kh finishes query group kh and hands group 1 - kh over.
-  float* xo = reinterpret_cast<float*>(smem + 2 * 32 * kRB);
+  // Exchange through the rings (each wave's own is free once its loop ends).
+  float* xo = reinterpret_cast<float*>(smem);
   auto send = [&](const f32x16 (&a)[2]) {
-    float* dst = xo + size_t(kh) * 2048;
+    float* dst = xo + size_t(kh) * (kDqStages * kStage / 4);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -377,8 +610,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   };
   auto finish = [&](const f32x16 (&a)[2]) {
     const int t = kBB * i + 32 * kh + ql;
+    const float* src = xo + size_t(1 - kh) * (kDqStages * kStage / 4);
+    if (nch > 1) {
+      // dQ of the block's 64 queries, row-major, fp32 (queries past N too)
+      float* pq = part + size_t(slot + ch) * (kBB * kBD) + size_t(32 * kh + ql) * kBD;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + ((u * 4 + g4) * 64 + lane) * 4);
+          const int d = 32 * u + 8 * g4 + 4 * hh;
+          *reinterpret_cast<f32x4*>(pq + d) =
+              f32x4{a[u][4 * g4] + o1[0], a[u][4 * g4 + 1] + o1[1], a[u][4 * g4 + 2] + o1[2],
+                    a[u][4 * g4 + 3] + o1[3]};
+        }
+      return;
+    }
     if (t >= N) return;
-    const float* src = xo + size_t(1 - kh) * 2048;
     uint16_t* qrow = dQ + head + size_t(t) * kBD;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -402,7 +650,90 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     finish(acc[1]);
 }
 
+// The split blocks: the chunks' fp32 partials summed in chunk order, then bf16
+// dK (times scale) and dV of key column r, and dQ (times scale) of CSR row r
+// (r = bh nb + block).  Rows past N are not stored.  Unsplit blocks were
+// written by the gradient kernels.
+__global__ __launch_bounds__(256) void reduce_kernel(const int2* __restrict__ col_split,
+                                                     const int2* __restrict__ row_split,
+                                                     const float* __restrict__ part_kv,
+                                                     const float* __restrict__ part_q, int32_t N,
+                                                     int32_t nb, float scale,
+                                                     uint16_t* __restrict__ dK,
+                                                     uint16_t* __restrict__ dV,
+                                                     uint16_t* __restrict__ dQ) {
+  const int r = blockIdx.x;
+  const int bh = r / nb, blk = r - bh * nb;
+  const size_t head = size_t(bh) * size_t(N) * kBD;
+  const int tid = threadIdx.x;
+  auto store4 = [&](uint16_t* T, int e, f32x4 x, float f) {
+    const int t = kBB * blk + (e >> 6);
+    if (t >= N) return;
+    *reinterpret_cast<uint2*>(T + head + size_t(t) * kBD + (e & 63)) =
+        make_uint2(pack_bf16x2(f * x[0], f * x[1]), pack_bf16x2(f * x[2], f * x[3]));
+  };
+  const int2 sk = col_split[r];
+  if (sk.x >= 0 && sk.y > 1) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = 4 * (tid + 256 * x);  // element of the 64 x 64 block
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < sk.y; ++c) {
+        const float* p = part_kv + size_t(sk.x + c) * (2 * kBB * kBD);
+        a += *reinterpret_cast<const f32x4*>(p + e);
+        b += *reinterpret_cast<const f32x4*>(p + kBB * kBD + e);
+      }
+      store4(dK, e, a, scale);
+      store4(dV, e, b, 1.f);
+    }
+  }
+  const int2 sq = row_split[r];
+  if (sq.x >= 0 && sq.y > 1) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = 4 * (tid + 256 * x);
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < sq.y; ++c)
+        a += *reinterpret_cast<const f32x4*>(part_q + size_t(sq.x + c) * (kBB * kBD) + e);
+      store4(dQ, e, a, scale);
+    }
+  }
+}
+
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Chunk length of the split: twice the mean CSR row length, at least 16.
+int32_t chunk_len(int64_t nnz, int64_t n_rows) {
+  const int64_t mean = n_rows > 0 ? (nnz + n_rows - 1) / n_rows : 0;
+  return static_cast<int32_t>(std::max<int64_t>(16, std::min<int64_t>(2 * mean, 1 << 20)));
+}
+
+// Partial slots for each of the two split kinds: a split block of L > chunk
+// entries takes ceil(L / chunk) < 2 L / chunk slots, and the blocks of each
+// kind partition at most nnz entries.
+int64_t slot_cap(int64_t nnz, int32_t chunk) { return 2 * nnz / chunk + 1; }
+
+struct BwdLayout {
+  size_t ld, col_ptr, row_idx, col_split, row_split, ctr, part_kv, part_q, total;
+};
+
+BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t block, int64_t nnz) {
+  BwdLayout L{};
+  const size_t rows = size_t(B) * H * N;
+  const size_t nrow = size_t(B) * H * n_blocks(N, block);
+  const int64_t cap = slot_cap(nnz, chunk_len(nnz, int64_t(nrow)));
+  size_t o = 0;
+  L.ld = o;        o += round256(rows * sizeof(float2));
+  L.col_ptr = o;   o += round256((nrow + 1) * sizeof(int32_t));
+  L.row_idx = o;   o += round256(size_t(nnz) * sizeof(int32_t));
+  L.col_split = o; o += round256(nrow * sizeof(int2));
+  L.row_split = o; o += round256(nrow * sizeof(int2));
+  L.ctr = o;       o += 256;
+  L.part_kv = o;   o += round256(size_t(cap) * 2 * kBB * kBD * sizeof(float));
+  L.part_q = o;    o += round256(size_t(cap) * kBB * kBD * sizeof(float));
+  L.total = o;
+  return L;
+}
 
 }  // namespace
 }  // namespace bsa
@@ -411,10 +742,7 @@ extern "C" BSA_API size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int
                                                       int32_t block, int64_t nnz) {
   using namespace bsa;
   if (B < 1 || H < 1 || N < 1 || block < 1 || nnz < 0) return 0;
-  const size_t rows = size_t(B) * H * N;
-  const size_t nrow = size_t(B) * H * n_blocks(N, block);
-  return round256(rows * sizeof(float2)) + round256((nrow + 1) * sizeof(int32_t)) +
-         round256(size_t(nnz) * sizeof(int32_t));
+  return bwd_layout(B, H, N, block, nnz).total;
 }
 
 extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const void* v,
@@ -440,11 +768,21 @@ extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const v
   if (workspace_bytes < bsa_backward_workspace_bytes(B, H, N, block, nnz)) return BSA_ERR_CAPACITY;
   const int64_t rows = int64_t(B) * H * N;
   const int32_t n_heads = B * H;
+  const int32_t n_rows = n_heads * nb;
+  const int32_t chunk = chunk_len(nnz, n_rows);
+  const int32_t max_ch = std::max(1, (nb + chunk - 1) / chunk);
+  const int64_t cap = slot_cap(nnz, chunk);
+  if (int64_t(n_rows) * max_ch > INT32_MAX || cap > INT32_MAX) return BSA_ERR_UNSUPPORTED;
+  const BwdLayout lay = bwd_layout(B, H, N, block, nnz);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float2* ld = reinterpret_cast<float2*>(ws);
-  int32_t* col_ptr = reinterpret_cast<int32_t*>(ws + round256(size_t(rows) * sizeof(float2)));
-  int32_t* row_idx = reinterpret_cast<int32_t*>(
-      reinterpret_cast<uint8_t*>(col_ptr) + round256((size_t(n_heads) * nb + 1) * sizeof(int32_t)));
+  float2* ld = reinterpret_cast<float2*>(ws + lay.ld);
+  int32_t* col_ptr = reinterpret_cast<int32_t*>(ws + lay.col_ptr);
+  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + lay.row_idx);
+  int2* col_split = reinterpret_cast<int2*>(ws + lay.col_split);
+  int2* row_split = reinterpret_cast<int2*>(ws + lay.row_split);
+  int32_t* ctr = reinterpret_cast<int32_t*>(ws + lay.ctr);
+  float* part_kv = reinterpret_cast<float*>(ws + lay.part_kv);
+  float* part_q = reinterpret_cast<float*>(ws + lay.part_q);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
 
@@ -459,23 +797,32 @@ extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const v
 
   hipLaunchKernelGGL(prep_kernel, dim3(static_cast<uint32_t>((rows * 8 + 255) / 256)), dim3(256),
                      0, s, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(d_o), lse,
-                     rows, ld);
+                     rows, ld, ctr);
   BSA_HIP_CHECK_LAUNCH();
   const size_t bits_bytes = size_t(nb) * ((nb + 31) / 32) * 4;
   hipLaunchKernelGGL(transpose_kernel, dim3(n_heads), dim3(256), bits_bytes, s, row_ptr, col_idx,
-                     nb, n_heads, col_ptr, row_idx);
+                     nb, n_heads, col_ptr, row_idx, chunk, max_ch, ctr, static_cast<int32_t>(cap),
+                     static_cast<int32_t>(cap), col_split, row_split);
   BSA_HIP_CHECK_LAUNCH();
   const float c2 = sc * kLog2e;
-  hipLaunchKernelGGL(dkdv_kernel, dim3(n_heads * nb), dim3(128), 0, s,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
-                     col_ptr, row_idx, N, nb, c2, sc, static_cast<uint16_t*>(dk),
-                     static_cast<uint16_t*>(dv));
+  const dim3 grid(static_cast<uint32_t>(n_rows * max_ch));
+  hipLaunchKernelGGL(dkdv_kernel, grid, dim3(128), 0, s, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<const uint16_t*>(d_o), ld, col_ptr, row_idx, col_split, n_rows,
+                     N, nb, c2, sc, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                     part_kv);
   BSA_HIP_CHECK_LAUNCH();
-  hipLaunchKernelGGL(dq_kernel, dim3(n_heads * nb), dim3(128), 0, s,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
-                     row_ptr, col_idx, N, nb, c2, sc, static_cast<uint16_t*>(dq));
+  hipLaunchKernelGGL(dq_kernel, grid, dim3(128), 0, s, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<const uint16_t*>(d_o), ld, row_ptr, col_idx, row_split, n_rows, N,
+                     nb, c2, sc, static_cast<uint16_t*>(dq), part_q);
   BSA_HIP_CHECK_LAUNCH();
+  if (max_ch > 1) {
+    hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<uint32_t>(n_rows)), dim3(256), 0, s,
+                       col_split, row_split, part_kv, part_q, N, nb, sc,
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                       static_cast<uint16_t*>(dq));
+    BSA_HIP_CHECK_LAUNCH();
+  }
   return BSA_OK;
 }

@@ -396,8 +396,10 @@ BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* 
  * scale <= 0 selects 1/sqrt(D).  Accumulation in fp32, P and dS rounded to bf16 as
  * MFMA operands; no atomics on the gradients, so results are deterministic.
  * workspace: device, bsa_backward_workspace_bytes(B, H, N, block, nnz) bytes, 16-byte
- * aligned; it holds (LSE log2 e, delta) per query row and the transposed CSR, and
- * needs no initial contents.
+ * aligned; it holds (LSE log2 e, delta) per query row, the transposed CSR, the split
+ * of key columns and CSR rows longer than the chunk length (twice the mean row
+ * length, at least 16) into chunks, and the chunks' fp32 partial gradients (bounded
+ * by 2 nnz / chunk + 1 slots of 48 KiB); it needs no initial contents.
  * Supported: D = 64, block = 64, nb <= 1024.
  * Errors: INVALID_ARG (null or misaligned pointer, bad size, NaN scale),
  * UNSUPPORTED (D, block, nb), CAPACITY (workspace too small), HIP.

@@ -212,8 +212,21 @@ def test_import_does_not_open_the_library():
 
 def test_backward_workspace_bytes():
     L = bsa.lib
-    # (LSE log2 e, delta) per row, then col_ptr [B*H*nb + 1], then row_idx [nnz]; 256-B rounding
-    assert L.bsa_backward_workspace_bytes(1, 2, 512, 64, 100) == 8 * 1024 + 256 + 512
-    assert L.bsa_backward_workspace_bytes(2, 24, 4224, 64, 31968) == \
-        8 * 202752 + 12800 + 128000
+
+    def r256(x):
+        return (x + 255) // 256 * 256
+
+    def want(B, H, N, nnz):
+        # (LSE log2 e, delta) per row, col_ptr [B*H*nb + 1], row_idx [nnz], the column
+        # and row splits (int2 [B*H*nb] each), the slot counters, then the partial
+        # slots: chunk = max(16, 2 * ceil(nnz / rows)), 2 nnz / chunk + 1 slots of
+        # fp32 [dK | dV] (32 KiB) and as many of dQ (16 KiB); 256-byte rounding.
+        nrow = B * H * (-(-N // 64))
+        chunk = max(16, 2 * (-(-nnz // nrow)))
+        cap = 2 * nnz // chunk + 1
+        return (r256(8 * B * H * N) + r256(4 * (nrow + 1)) + r256(4 * nnz) + 2 * r256(8 * nrow)
+                + 256 + cap * 32768 + cap * 16384)
+
+    assert L.bsa_backward_workspace_bytes(1, 2, 512, 64, 100) == want(1, 2, 512, 100) == 648704
+    assert L.bsa_backward_workspace_bytes(2, 24, 4224, 64, 31968) == want(2, 24, 4224, 31968)
     assert L.bsa_backward_workspace_bytes(0, 2, 512, 64, 100) == 0

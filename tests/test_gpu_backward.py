@@ -95,6 +95,29 @@ def test_backward_dense_and_deterministic():
     assert all(np.array_equal(a, b) for a, b in zip(got, again))
 
 
+@pytest.mark.parametrize("N,H", [(2000, 2), (4050, 1)])
+def test_backward_split_rows_and_columns(N, H):
+    """Rows and key columns longer than the chunk length (twice the mean row length, at
+    least 16) are cut into chunks whose fp32 partials are summed in chunk order: query
+    block 0 lists every key block and every row lists key block 0 (2 and 4 chunks at
+    nb = 32 and 64), the rest is the diagonal and its right neighbour; ragged N; a
+    repeat call gives the same bits."""
+    bsa = need_gpu()
+    print(f"case N={N} H={H}", flush=True)
+    B, D, block = 1, 64, 64
+    nb = -(-N // block)
+    q, k, v = W.gaussian_qkv(300 + N, B, H, N, D)
+    do = W.gaussian_qkv(400 + N, B, H, N, D)[0]
+    cols = [list(range(nb)) if r % nb == 0 else sorted({0, r % nb, min(r % nb + 1, nb - 1)})
+            for r in range(B * H * nb)]
+    rp, ci = csr_from_cols(cols)
+    got = run(bsa, q, k, v, do, rp, ci)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / 8.0, do)
+    compare(got, want)
+    again = run(bsa, q, k, v, do, rp, ci)
+    assert all(np.array_equal(a, b) for a, b in zip(got, again))
+
+
 def test_backward_t2i_sampled_heads():
     """The t2i workload at full size (B2 H24 N4224, its static mask); the oracle on two
     heads (each head's gradients depend on that head only)."""
