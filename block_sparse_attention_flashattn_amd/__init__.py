@@ -64,7 +64,8 @@ _SIGS = {
     "bsa_csr_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "bsa_residual": (_i32, [_vp, _vp, _vp, _i64, _vp]),
     "bsa_compensate": (_i32, [_vp, _vp, _vp, _i64, _vp]),
-    "bsa_query_groups": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "bsa_query_groups_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "bsa_query_groups": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "bsa_token_mass": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
     "bsa_select_tokens": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "bsa_gather_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
@@ -76,7 +77,7 @@ _SIGS = {
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class BsaError(RuntimeError):
@@ -572,14 +573,17 @@ class AnchorReuse:
         return compensate(o, self.r, out=o)
 
 
-def query_groups(q: torch.Tensor, C: int) -> torch.Tensor:
+def query_groups(q: torch.Tensor, C: int, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Tile-aligned query groups -> int32 [B,H,N/C,C] (token indices, ascending per group)."""
     B, H, N, D = _check_qkv(q)
     if N % C:
         raise ValueError("N must be a multiple of the group size")
     groups = torch.empty((B, H, N // C, C), dtype=torch.int32, device=q.device)
-    _check(lib.bsa_query_groups(_t_ptr(q), B, H, N, D, C, _t_ptr(groups),
-                                _stream_ptr(q.device)), "bsa_query_groups")
+    need = int(lib.bsa_query_groups_workspace_bytes(B, H, N, D, C))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_query_groups(_t_ptr(q), B, H, N, D, C, _t_ptr(groups), _t_ptr(workspace),
+                                workspace.numel(), _stream_ptr(q.device)), "bsa_query_groups")
     return groups
 
 

@@ -13,14 +13,17 @@
 // is cut into floor(g/2)*C and the rest, smallest projections (ties to the lower
 // token) first, groups numbered depth first; a token's mass for a group is the
 // dense attention probability summed over the group's queries.
+#include <algorithm>
+#include <mutex>
+
 #include "common.h"
+#include "tile.h"
 
 namespace bsa {
 namespace {
 
 constexpr int kPowerIters = 8;
 constexpr int kMaxTokens = 8192;  // tokens per head handled by the sorts (LDS)
-constexpr int kMaxGroups = kMaxTokens / 64;  // group sizes are 64 or 128
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
@@ -54,152 +57,375 @@ __device__ void bitonic(uint64_t* keys, int n, int max_size) {
   __syncthreads();
 }
 
-// One workgroup per head.  `perm` (the output, [N]) holds the current order of the
-// head's tokens; segments of whole groups are split level by level in place, so
-// the final segments come out in depth-first order.
+// ---------------------------------------------------------------------------
+// Query groups, one launch pair per level of the split tree.  A segment of g
+// groups (g > 1) at depth l becomes (s, g/2) and (s + g/2, g - g/2) at depth
+// l + 1; its tokens occupy perm[s C, (s + g) C) of the head, so every segment of
+// one depth can be split at the same time, each by its own workgroup.  The
+// principal direction comes from the segment's scatter matrix
+// M = sum (x - mu)(x - mu)^T (power iteration v <- M v / |M v|, the same map as
+// X_c^T (X_c v) on the centred rows): large segments get M from fp32 partials of
+// 512-token slices (many workgroups), combined in slice order with the
+// parallel-variance update, small ones compute it in the splitting workgroup.
+
+constexpr int kPart = 512;        // tokens per slice of a partial scatter matrix
+constexpr int kDirectMax = 1024;  // segments up to this size compute M themselves
+
+// Segment (s, g) of node b at depth `level` of the split tree of G groups;
+// g = 0 if the node does not exist (an ancestor was a single group).
+__device__ __forceinline__ void node_segment(int G, int level, int b, int& s, int& g) {
+  s = 0;
+  g = G;
+  for (int l = level - 1; l >= 0; --l) {
+    if (g <= 1) {
+      g = 0;
+      return;
+    }
+    const int gl = g >> 1;
+    if ((b >> l) & 1) {
+      s += gl;
+      g -= gl;
+    } else {
+      g = gl;
+    }
+  }
+}
+
+// Scatter-matrix blocks of one thread: HD = 64, a 4x4 block (rows a0.., columns
+// b0..); HD = 128, four 4x4 blocks (rows a0.., columns b0 + 32 k).
 template <int HD>
-__global__ __launch_bounds__(kThreads) void group_kernel(const uint16_t* __restrict__ Q, int32_t N,
-                                                         int32_t C, int32_t* __restrict__ groups) {
-  constexpr int RG = kThreads / HD;  // row groups of the dimension-parallel sums
-  __shared__ uint64_t keys[kMaxTokens];
-  __shared__ float red[RG][HD];
-  __shared__ float mu[HD], v[HD];
-  __shared__ int32_t seg_s[2 * kMaxGroups], seg_g[2 * kMaxGroups];  // list, then the next
-  __shared__ int32_t nseg_sh;
-  __shared__ float norm_sh;
-  float* y = reinterpret_cast<float*>(keys);  // row dot products (reuses the key area)
+struct ScatterBlock {
+  static constexpr int NB = HD == 64 ? 1 : 4;
+  f32x4 m[NB][4];
+  int a0, b0;
+  __device__ void init(int tid) {
+    a0 = HD == 64 ? (tid >> 4) * 4 : (tid >> 3) * 4;
+    b0 = HD == 64 ? (tid & 15) * 4 : (tid & 7) * 4;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m[k][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ int col(int k) const { return b0 + 32 * k; }
+};
+
+// Mean and scatter matrix of the tokens ids[0, n) (LDS) of one head (rows of q):
+// mu (LDS, HD floats) and this thread's blocks of M.  One pass over the rows,
+// shifted by the first row x0 (fp32 differences of bf16 values are exact):
+// S1 = sum (x - x0), S2 = sum (x - x0)(x - x0)^T, mu = x0 + S1 / n,
+// M = S2 - S1 S1^T / n.  xs: LDS for 64 shifted fp32 rows; red: LDS
+// [256 / HD][HD]; x0s: LDS, HD floats.  All threads of the workgroup call it.
+template <int HD>
+__device__ void slice_stats(const uint16_t* __restrict__ q, const int32_t* ids, int n, float* xs,
+                            float (*red)[HD], float* x0s, float* mu, ScatterBlock<HD>& sb) {
+  constexpr int RG = kThreads / HD;
+  constexpr int CH = HD / 8;  // 16-byte chunks per row
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
-  const uint16_t* q = Q + size_t(bh) * N * HD;
-  int32_t* perm = groups + size_t(bh) * N;
-  const int G = N / C;
-  for (int r = tid; r < N; r += kThreads) perm[r] = r;
-  if (tid == 0) {
-    seg_s[0] = 0;
-    seg_g[0] = G;
-    nseg_sh = 1;
+  const int d = tid % HD, rg = tid / HD;
+  if (tid < HD) x0s[tid] = n > 0 ? bf2f(q[size_t(ids[0]) * HD + tid]) : 0.f;
+  __syncthreads();
+  sb.init(tid);
+  float s1 = 0.f;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    for (int e = tid; e < 64 * CH; e += kThreads) {
+      const int r = e / CH, c = e % CH;
+      const int j = j0 + r;
+      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+      if (j < n) {
+        const v4u w = *reinterpret_cast<const v4u*>(q + size_t(ids[j]) * HD + 8 * c);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float e0 = __uint_as_float(w[x] << 16), e1 = __uint_as_float(w[x] & 0xffff0000u);
+          const int dd = 8 * c + 2 * x;
+          if (x < 2) {
+            lo[2 * x] = e0 - x0s[dd];
+            lo[2 * x + 1] = e1 - x0s[dd + 1];
+          } else {
+            hi[2 * x - 4] = e0 - x0s[dd];
+            hi[2 * x - 3] = e1 - x0s[dd + 1];
+          }
+        }
+      }
+      *reinterpret_cast<f32x4*>(xs + r * HD + 8 * c) = lo;
+      *reinterpret_cast<f32x4*>(xs + r * HD + 8 * c + 4) = hi;
+    }
+    __syncthreads();
+    const int rows = min(64, n - j0);
+    for (int r = rg; r < rows; r += RG) s1 += xs[r * HD + d];
+    for (int r = 0; r < rows; ++r) {
+      const f32x4 xa = *reinterpret_cast<const f32x4*>(xs + r * HD + sb.a0);
+#pragma unroll
+      for (int k = 0; k < ScatterBlock<HD>::NB; ++k) {
+        const f32x4 xb = *reinterpret_cast<const f32x4*>(xs + r * HD + sb.col(k));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sb.m[k][i] += xa[i] * xb;
+      }
+    }
+    __syncthreads();
+  }
+  red[rg][d] = s1;
+  __syncthreads();
+  if (tid < HD) {
+    float t = 0.f;
+    for (int k = 0; k < RG; ++k) t += red[k][tid];
+    red[0][tid] = t;  // S1
+    mu[tid] = n > 0 ? x0s[tid] + t / float(n) : 0.f;
   }
   __syncthreads();
-  for (;;) {
-    const int nseg = nseg_sh;
-    bool any = false;
-    for (int s = 0; s < nseg; ++s) any |= seg_g[s] > 1;
-    if (!any) break;
+  const float inv = n > 0 ? 1.f / float(n) : 0.f;
+  const f32x4 sa = *reinterpret_cast<const f32x4*>(&red[0][0] + sb.a0);
+#pragma unroll
+  for (int k = 0; k < ScatterBlock<HD>::NB; ++k) {
+    const f32x4 sbk = *reinterpret_cast<const f32x4*>(&red[0][0] + sb.col(k));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sb.m[k][i] -= (sa[i] * inv) * sbk;
+  }
+  __syncthreads();
+}
+
+// Identity order of every head's tokens.
+__global__ __launch_bounds__(kThreads) void perm_init_kernel(int32_t N, int32_t* __restrict__ perm) {
+  const int bh = blockIdx.y;
+  for (int r = blockIdx.x * kThreads + threadIdx.x; r < N; r += gridDim.x * kThreads)
+    perm[size_t(bh) * N + r] = r;
+}
+
+// Partial (n, mu, M) of slice p of the segment of node b at depth `level`:
+// grid (2^level * P, B*H); floats per partial 1 + HD + HD^2.
+template <int HD>
+__global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restrict__ Q, int32_t N,
+                                                         int32_t C, int32_t level, int32_t P,
+                                                         const int32_t* __restrict__ perm,
+                                                         float* __restrict__ part) {
+  __shared__ __align__(16) float xs[64 * HD];
+  __shared__ __align__(16) float red[kThreads / HD][HD];
+  __shared__ float mu[HD], x0s[HD];
+  __shared__ int32_t ids[kPart];
+  const int bh = blockIdx.y;
+  const int b = blockIdx.x / P, p = blockIdx.x - b * P;
+  int s, g;
+  node_segment(N / C, level, b, s, g);
+  if (g <= 1) return;
+  const int n = g * C;
+  const int L = (n + P - 1) / P;
+  const int lo = min(p * L, n), hi = min(lo + L, n);
+  const uint16_t* q = Q + size_t(bh) * N * HD;
+  const int32_t* idx = perm + size_t(bh) * N + size_t(s) * C + lo;
+  for (int j = threadIdx.x; j < hi - lo; j += kThreads) ids[j] = idx[j];
+  __syncthreads();
+  ScatterBlock<HD> sb;
+  slice_stats<HD>(q, ids, hi - lo, xs, red, x0s, mu, sb);
+  constexpr int F = 1 + HD + HD * HD;
+  float* out = part + ((size_t(bh) << level) * P + size_t(b) * P + p) * F;
+  const int tid = threadIdx.x;
+  if (tid == 0) out[0] = float(hi - lo);
+  if (tid < HD) out[1 + tid] = mu[tid];
+  float* M = out + 1 + HD;
+#pragma unroll
+  for (int k = 0; k < ScatterBlock<HD>::NB; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) M[(sb.a0 + i) * HD + sb.col(k) + j] = sb.m[k][i][j];
+}
+
+// w = M v for a scatter matrix held in ScatterBlocks (M symmetric, each thread
+// its blocks): per-thread partial rows, summed over the lanes that share a row
+// block (16 consecutive lanes at HD = 64, 8 at HD = 128), into w (LDS, HD floats).
+template <int HD>
+__device__ void scatter_matvec(const ScatterBlock<HD>& sb, const float* v, float* w) {
+  f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < ScatterBlock<HD>::NB; ++k) {
+    const f32x4 vb = *reinterpret_cast<const f32x4*>(v + sb.col(k));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      part[i] += sb.m[k][i][0] * vb[0] + sb.m[k][i][1] * vb[1] + sb.m[k][i][2] * vb[2] +
+                 sb.m[k][i][3] * vb[3];
+  }
+  constexpr int span = HD == 64 ? 16 : 8;
+#pragma unroll
+  for (int off = 1; off < span; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], off);
+  if ((threadIdx.x & (span - 1)) == 0) *reinterpret_cast<f32x4*>(w + sb.a0) = part;
+}
+
+// Euclidean norm of x[0, HD) (LDS), computed by wavefront 0 and left in *out.
+template <int HD>
+__device__ void norm_w0(const float* x, float* out) {
+  if (threadIdx.x < 64) {
+    float s2 = 0.f;
+#pragma unroll
+    for (int h = 0; h < HD / 64; ++h) s2 += x[64 * h + threadIdx.x] * x[64 * h + threadIdx.x];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
+    if (threadIdx.x == 0) *out = sqrtf(s2);
+  }
+}
+
+// Split of the segment of node b at depth `level` (grid (2^level, B*H)): its
+// scatter matrix (from the P partials in slice order, or computed here when
+// P == 1; either way held in registers, ScatterBlock), the principal direction,
+// the projections, and the segment's tokens rewritten in ascending (projection,
+// token) order, so that the first floor(g/2) C of them form the left child.
+// Dynamic LDS: the keys of the level's largest segment (and the row staging).
+template <int HD>
+__global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restrict__ Q, int32_t N,
+                                                         int32_t C, int32_t level, int32_t P,
+                                                         int32_t key_words,
+                                                         const float* __restrict__ part,
+                                                         int32_t* __restrict__ perm) {
+  extern __shared__ __align__(16) uint64_t keys[];  // 16-byte aligned: xs takes 16-byte reads
+  __shared__ __align__(16) float red[kThreads / HD][HD];
+  __shared__ float x0s[HD];
+  __shared__ __align__(16) float mu[HD];
+  __shared__ __align__(16) float v[HD];
+  __shared__ __align__(16) float dl[HD];
+  __shared__ float norm_sh, nacc_sh;
+  float* xs = reinterpret_cast<float*>(keys);  // staging of slice_stats (before the keys)
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.y, b = blockIdx.x;
+  int s, g;
+  node_segment(N / C, level, b, s, g);
+  if (g <= 1) return;
+  const int n = g * C, s0 = s * C;
+  const uint16_t* q = Q + size_t(bh) * N * HD;
+  int32_t* idx = perm + size_t(bh) * N + s0;
+  int npad = 1;
+  while (npad < n) npad <<= 1;
+  // The segment's tokens, after the key (and staging) area.
+  int32_t* ids = reinterpret_cast<int32_t*>(keys) + 2 * key_words;
+  for (int j = tid; j < n; j += kThreads) ids[j] = idx[j];
+  __syncthreads();
+  constexpr int F = 1 + HD + HD * HD;
+  ScatterBlock<HD> sb;
+  if (P <= 1) {
+    slice_stats<HD>(q, ids, n, xs, red, x0s, mu, sb);
+  } else {
+    // (n, mu, M) <- (n, mu, M) + partial: delta = mu_p - mu, M += M_p +
+    // n n_p / (n + n_p) delta delta^T, mu += delta n_p / (n + n_p).
+    sb.init(tid);
+    const float* pp = part + ((size_t(bh) << level) * P + size_t(b) * P) * F;
+    if (tid < HD) mu[tid] = 0.f;
+    if (tid == 0) nacc_sh = 0.f;
     __syncthreads();
-    // New segment list written after the splits (at most doubling).
-    int out_n = 0;
-    for (int s = 0; s < nseg; ++s) {
-      const int s0 = seg_s[s] * C, g = seg_g[s], n = g * C;
-      if (g > 1) {
-        const int32_t* idx = perm + s0;
-        // mean
-        {
-          const int d = tid % HD, rg = tid / HD;
-          float acc = 0.f;
-          for (int j = rg; j < n; j += RG) acc += bf2f(q[size_t(idx[j]) * HD + d]);
-          red[rg][d] = acc;
-          __syncthreads();
-          if (tid < HD) {
-            float m = 0.f;
-            for (int k = 0; k < RG; ++k) m += red[k][tid];
-            mu[tid] = m / float(n);
-            v[tid] = 1.f + float(tid) / float(HD);
-          }
-          __syncthreads();
-          if (tid == 0) {
-            float s2 = 0.f;
-            for (int k = 0; k < HD; ++k) s2 += v[k] * v[k];
-            norm_sh = sqrtf(s2);
-          }
-          __syncthreads();
-          if (tid < HD) v[tid] /= norm_sh;
-          __syncthreads();
-        }
-        for (int it = 0; it < kPowerIters; ++it) {
-          for (int j = tid; j < n; j += kThreads) {
-            const uint16_t* row = q + size_t(idx[j]) * HD;
-            float a = 0.f;
-            for (int k = 0; k < HD; ++k) a += (bf2f(row[k]) - mu[k]) * v[k];
-            y[j] = a;
-          }
-          __syncthreads();
-          {
-            const int d = tid % HD, rg = tid / HD;
-            float acc = 0.f;
-            for (int j = rg; j < n; j += RG) acc += (bf2f(q[size_t(idx[j]) * HD + d]) - mu[d]) * y[j];
-            red[rg][d] = acc;
-          }
-          __syncthreads();
-          if (tid < HD) {
-            float w = 0.f;
-            for (int k = 0; k < RG; ++k) w += red[k][tid];
-            red[0][tid] = w;
-          }
-          __syncthreads();
-          if (tid == 0) {
-            float s2 = 0.f;
-            for (int k = 0; k < HD; ++k) s2 += red[0][k] * red[0][k];
-            norm_sh = sqrtf(s2);
-          }
-          __syncthreads();
-          const float nrm = norm_sh;
-          if (nrm == 0.f) break;  // uniform: every thread reads the same value
-          if (tid < HD) v[tid] = red[0][tid] / nrm;
-          __syncthreads();
-        }
-        // projections -> sort keys (projection ascending, then token ascending)
-        int npad = 1;
-        while (npad < n) npad <<= 1;
-        for (int j = tid; j < npad; j += kThreads) {
-          if (j < n) {
-            const uint16_t* row = q + size_t(idx[j]) * HD;
-            float a = 0.f;
-            for (int k = 0; k < HD; ++k) a += (bf2f(row[k]) - mu[k]) * v[k];
-            keys[j] = (uint64_t(ordered(a)) << 32) | uint32_t(idx[j]);
-          } else {
-            keys[j] = ~0ull;
-          }
-        }
-        bitonic(keys, npad, npad);
-        for (int j = tid; j < n; j += kThreads) perm[s0 + j] = static_cast<int32_t>(keys[j] & 0xffffffffu);
+    for (int p = 0; p < P; ++p) {
+      const float* src = pp + size_t(p) * F;
+      const float na = nacc_sh, np = src[0];
+      const float nt = na + np;
+      if (np > 0.f) {  // uniform
+        if (tid < HD) dl[tid] = src[1 + tid] - mu[tid];
         __syncthreads();
-        const int gl = g / 2;
-        if (tid == 0) {
-          seg_s[nseg + out_n] = seg_s[s];
-          seg_g[nseg + out_n] = gl;
-          seg_s[nseg + out_n + 1] = seg_s[s] + gl;
-          seg_g[nseg + out_n + 1] = g - gl;
+        const float f = na * np / nt;
+        const f32x4 da = *reinterpret_cast<const f32x4*>(dl + sb.a0);
+#pragma unroll
+        for (int k = 0; k < ScatterBlock<HD>::NB; ++k) {
+          const f32x4 db = *reinterpret_cast<const f32x4*>(dl + sb.col(k));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 mp =
+                *reinterpret_cast<const f32x4*>(src + 1 + HD + (sb.a0 + i) * HD + sb.col(k));
+            sb.m[k][i] += mp + (f * da[i]) * db;
+          }
         }
-        out_n += 2;
-      } else {
-        if (tid == 0) {
-          seg_s[nseg + out_n] = seg_s[s];
-          seg_g[nseg + out_n] = 1;
-        }
-        out_n += 1;
+        __syncthreads();
+        if (tid < HD) mu[tid] += dl[tid] * (np / nt);
+        if (tid == 0) nacc_sh = nt;
       }
       __syncthreads();
     }
-    // Move the new list to the front (out_n <= kMaxGroups <= kThreads).
-    int a = 0, b = 0;
-    if (tid < out_n) {
-      a = seg_s[nseg + tid];
-      b = seg_g[nseg + tid];
-    }
+  }
+  __syncthreads();
+  // Power iteration from u[d] = 1 + d / HD.
+  if (tid < HD) v[tid] = 1.f + float(tid) / float(HD);
+  __syncthreads();
+  norm_w0<HD>(v, &norm_sh);
+  __syncthreads();
+  if (tid < HD) v[tid] /= norm_sh;
+  __syncthreads();
+  float* w = &red[0][0];
+  for (int it = 0; it < kPowerIters; ++it) {
+    scatter_matvec<HD>(sb, v, w);
     __syncthreads();
-    if (tid < out_n) {
-      seg_s[tid] = a;
-      seg_g[tid] = b;
-    }
-    if (tid == 0) nseg_sh = out_n;
+    norm_w0<HD>(w, &norm_sh);
+    __syncthreads();
+    const float nrm = norm_sh;
+    if (nrm == 0.f) break;  // uniform
+    if (tid < HD) v[tid] = w[tid] / nrm;
     __syncthreads();
   }
-  // Every group's tokens ascending: bitonic stages up to C sort each aligned run.
+  // Projections -> keys (projection ascending, then token ascending).
+  for (int j = tid; j < npad; j += kThreads) {
+    if (j < n) {
+      const int t = ids[j];
+      const uint16_t* row = q + size_t(t) * HD;
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < HD / 8; ++c) {
+        const v4u x = *reinterpret_cast<const v4u*>(row + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = 8 * c + 2 * e;
+          a += (__uint_as_float(x[e] << 16) - mu[d]) * v[d];
+          a += (__uint_as_float(x[e] & 0xffff0000u) - mu[d + 1]) * v[d + 1];
+        }
+      }
+      keys[j] = (uint64_t(ordered(a)) << 32) | uint32_t(t);
+    } else {
+      keys[j] = ~0ull;
+    }
+  }
+  bitonic(keys, npad, npad);
+  for (int j = tid; j < n; j += kThreads) idx[j] = static_cast<int32_t>(keys[j] & 0xffffffffu);
+}
+
+// 64-bit words of split_kernel's key (and row staging) area for segments of up
+// to nmax tokens; the segment's token list follows it (npad int32).
+inline int split_key_words(int nmax, int D) {
   int npad = 1;
-  while (npad < N) npad <<= 1;
-  for (int j = tid; j < npad; j += kThreads) keys[j] = j < N ? uint64_t(uint32_t(perm[j])) : ~0ull;
-  bitonic(keys, npad, C);
-  for (int j = tid; j < N; j += kThreads) perm[j] = static_cast<int32_t>(keys[j] & 0xffffffffu);
+  while (npad < nmax) npad <<= 1;
+  return std::max(npad, 64 * D * 4 / 8);
+}
+inline size_t split_lds_bytes(int nmax, int D) {
+  int npad = 1;
+  while (npad < nmax) npad <<= 1;
+  return size_t(split_key_words(nmax, D)) * 8 + size_t(npad) * 4;
+}
+
+// Every group's tokens ascending: grid (G, B*H).
+__global__ __launch_bounds__(kThreads) void group_sort_kernel(int32_t N, int32_t C,
+                                                              int32_t* __restrict__ perm) {
+  __shared__ uint64_t keys[128];
+  int32_t* grp = perm + size_t(blockIdx.y) * N + size_t(blockIdx.x) * C;
+  for (int j = threadIdx.x; j < C; j += kThreads) keys[j] = uint32_t(grp[j]);
+  bitonic(keys, C, C);
+  for (int j = threadIdx.x; j < C; j += kThreads) grp[j] = static_cast<int32_t>(keys[j]);
+}
+
+// Levels of the split tree that have a segment of more than one group, the
+// slice count of each (1: the split workgroup computes M itself), and the
+// partial floats the largest level needs.
+struct GroupLevels {
+  int depth = 0;
+  int P[32] = {};
+  size_t part_floats = 0;
+};
+
+inline GroupLevels group_levels(int32_t BH, int32_t N, int32_t D, int32_t C) {
+  GroupLevels L;
+  const int G = N / C;
+  for (int l = 0; l < 31; ++l) {
+    const int gmax = (G + (1 << l) - 1) >> l;  // the largest segment at depth l
+    if (gmax <= 1) break;
+    const int nmax = gmax * C;
+    L.P[l] = nmax > kDirectMax ? (nmax + kPart - 1) / kPart : 1;
+    if (L.P[l] > 1)
+      L.part_floats = std::max(L.part_floats, size_t(BH) * (size_t(1) << l) * size_t(L.P[l]) *
+                                                  size_t(1 + D + D * D));
+    L.depth = l + 1;
+  }
+  return L;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -295,20 +521,68 @@ __global__ __launch_bounds__(kThreads) void select_tokens_kernel(const float* __
 }  // namespace
 }  // namespace bsa
 
+extern "C" BSA_API size_t bsa_query_groups_workspace_bytes(int32_t B, int32_t H, int32_t N,
+                                                          int32_t D, int32_t C) {
+  using namespace bsa;
+  if (B < 1 || H < 1 || N < 1 || (C != 64 && C != 128) || (D != 64 && D != 128) || N % C)
+    return 0;
+  return std::max<size_t>(256, group_levels(B * H, N, D, C).part_floats * sizeof(float));
+}
+
 extern "C" BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t H, int32_t N,
                                                int32_t D, int32_t C, int32_t* groups_out,
+                                               void* workspace, size_t workspace_bytes,
                                                void* stream) {
   using namespace bsa;
-  if (!q || !groups_out || B < 1 || H < 1 || N < 1 || C < 1) return BSA_ERR_INVALID_ARG;
-  if (N % C != 0) return BSA_ERR_INVALID_ARG;
+  if (!q || !groups_out || !workspace || B < 1 || H < 1 || N < 1 || C < 1)
+    return BSA_ERR_INVALID_ARG;
+  if (N % C != 0 || !aligned16(q) || !aligned16(workspace)) return BSA_ERR_INVALID_ARG;
   if (N > kMaxTokens || (C != 64 && C != 128) || (D != 64 && D != 128)) return BSA_ERR_UNSUPPORTED;
+  if (int64_t(B) * H > 65535) return BSA_ERR_UNSUPPORTED;
+  if (workspace_bytes < bsa_query_groups_workspace_bytes(B, H, N, D, C)) return BSA_ERR_CAPACITY;
+  const GroupLevels L = group_levels(B * H, N, D, C);
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    const int big = int(split_lds_bytes(kMaxTokens, 128));
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<64>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, big);
+    if (attr == hipSuccess)
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<128>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, big);
+  });
+  if (attr != hipSuccess) return BSA_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D == 64)
-    hipLaunchKernelGGL(group_kernel<64>, dim3(B * H), dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(q), N, C, groups_out);
-  else
-    hipLaunchKernelGGL(group_kernel<128>, dim3(B * H), dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(q), N, C, groups_out);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  float* part = static_cast<float*>(workspace);
+  const uint32_t bh = static_cast<uint32_t>(B * H);
+  hipLaunchKernelGGL(perm_init_kernel, dim3((N + kThreads - 1) / kThreads, bh), dim3(kThreads), 0,
+                     s, N, groups_out);
+  BSA_HIP_CHECK_LAUNCH();
+  for (int l = 0; l < L.depth; ++l) {
+    const uint32_t nodes = 1u << l;
+    const int P = L.P[l];
+    if (P > 1) {
+      if (D == 64)
+        hipLaunchKernelGGL(stats_kernel<64>, dim3(nodes * P, bh), dim3(kThreads), 0, s, qq, N, C,
+                           l, P, groups_out, part);
+      else
+        hipLaunchKernelGGL(stats_kernel<128>, dim3(nodes * P, bh), dim3(kThreads), 0, s, qq, N, C,
+                           l, P, groups_out, part);
+      BSA_HIP_CHECK_LAUNCH();
+    }
+    const int gmax = (N / C + int(nodes) - 1) / int(nodes);
+    const size_t lds = split_lds_bytes(gmax * C, D);
+    const int kw = split_key_words(gmax * C, D);
+    if (D == 64)
+      hipLaunchKernelGGL(split_kernel<64>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C, l, P,
+                         kw, part, groups_out);
+    else
+      hipLaunchKernelGGL(split_kernel<128>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C, l,
+                         P, kw, part, groups_out);
+    BSA_HIP_CHECK_LAUNCH();
+  }
+  hipLaunchKernelGGL(group_sort_kernel, dim3(N / C, bh), dim3(kThreads), 0, s, N, C, groups_out);
   BSA_HIP_CHECK_LAUNCH();
   return BSA_OK;
 }

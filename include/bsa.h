@@ -51,7 +51,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 8
+#define BSA_ABI_VERSION 9
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -339,7 +339,12 @@ BSA_API bsa_status bsa_compensate(const void* o_sparse, const void* r, void* o_o
  *   u[d] = 1 + d/D, fp32) and cut into floor(g/2)*C and the rest, smallest
  *   projections first (ties to the lower token), recursively; groups are
  *   numbered depth first.  C in {64, 128}, N a multiple of C and at most 8192, D
- *   in {64, 128}.
+ *   in {64, 128}, B*H at most 65535.  One level of the split tree per launch pair;
+ *   the principal direction is iterated on the segment's scatter matrix
+ *   sum (x - mu)(x - mu)^T (the same map as X_c^T X_c on the centred rows), which
+ *   segments above 1024 tokens assemble from fp32 partials of 512-token slices.
+ *   workspace: device, bsa_query_groups_workspace_bytes(B, H, N, D, C) bytes,
+ *   16-byte aligned, no initial contents (the partials of one level at a time).
  * bsa_token_mass: mass_out fp32 [B,H,N/C,N]: for group g and token c, the sum over
  *   the group's queries t of exp(scale q_t.k_c - lse[t]) (with the dense LSE: the
  *   dense attention probability mass of token c for the group).  Queries with a
@@ -348,8 +353,11 @@ BSA_API bsa_status bsa_compensate(const void* o_sparse, const void* r, void* o_o
  *   largest mass (ties to the lower token), ascending.  N at most 8192, 0 <= k <= N.
  * Errors: INVALID_ARG, UNSUPPORTED (sizes above), HIP.
  */
+BSA_API size_t bsa_query_groups_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D,
+                                                int32_t C);
 BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t H, int32_t N, int32_t D,
-                                    int32_t C, int32_t* groups_out, void* stream);
+                                    int32_t C, int32_t* groups_out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 BSA_API bsa_status bsa_token_mass(const void* q, const void* k, const float* lse,
                                   const int32_t* groups, int32_t B, int32_t H, int32_t N,
                                   int32_t D, int32_t C, float scale, float* mass_out,
