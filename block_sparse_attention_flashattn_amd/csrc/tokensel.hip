@@ -126,13 +126,29 @@ __device__ void slice_stats(const uint16_t* __restrict__ q, const int32_t* ids, 
   __syncthreads();
   sb.init(tid);
   float s1 = 0.f;
+  // The 16-byte chunks this thread moves per batch of 64 rows, the next batch's
+  // in flight while the current one is used.
+  constexpr int PT = 64 * CH / kThreads;
+  v4u pre[PT];
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + kThreads * u;
+      const int j = j0 + e / CH;
+      pre[u] = j < n ? *reinterpret_cast<const v4u*>(q + size_t(ids[j]) * HD + 8 * (e % CH))
+                     : v4u{0u, 0u, 0u, 0u};
+    }
+  };
+  fetch(0);
   for (int j0 = 0; j0 < n; j0 += 64) {
-    for (int e = tid; e < 64 * CH; e += kThreads) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + kThreads * u;
       const int r = e / CH, c = e % CH;
       const int j = j0 + r;
       f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
       if (j < n) {
-        const v4u w = *reinterpret_cast<const v4u*>(q + size_t(ids[j]) * HD + 8 * c);
+        const v4u w = pre[u];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const float e0 = __uint_as_float(w[x] << 16), e1 = __uint_as_float(w[x] & 0xffff0000u);
@@ -150,6 +166,7 @@ __device__ void slice_stats(const uint16_t* __restrict__ q, const int32_t* ids, 
       *reinterpret_cast<f32x4*>(xs + r * HD + 8 * c + 4) = hi;
     }
     __syncthreads();
+    if (j0 + 64 < n) fetch(j0 + 64);
     const int rows = min(64, n - j0);
     for (int r = rg; r < rows; r += RG) s1 += xs[r * HD + d];
     for (int r = 0; r < rows; ++r) {
@@ -264,12 +281,32 @@ __device__ void norm_w0(const float* x, float* out) {
   }
 }
 
+// Exclusive prefix sum over the workgroup's threads (one value each, thread
+// order): a shuffle scan in each wavefront, then the wavefront totals through
+// tmp (kThreads / 64 ints of LDS).  All threads call it.
+__device__ int block_excl_scan(int x, int32_t* tmp) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int k = 0; k < w; ++k) base += tmp[k];
+  __syncthreads();  // tmp is free for the next call
+  return base + incl - x;
+}
+
 // Split of the segment of node b at depth `level` (grid (2^level, B*H)): its
 // scatter matrix (from the P partials in slice order, or computed here when
 // P == 1; either way held in registers, ScatterBlock), the principal direction,
-// the projections, and the segment's tokens rewritten in ascending (projection,
-// token) order, so that the first floor(g/2) C of them form the left child.
-// Dynamic LDS: the keys of the level's largest segment (and the row staging).
+// the projections, and the segment's tokens rewritten so that the floor(g/2) C
+// smallest (projection, token) keys come first (the left child), each side in
+// its previous order.  Dynamic LDS: the keys of the level's largest segment
+// (and the row staging), then its token list.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restrict__ Q, int32_t N,
                                                          int32_t C, int32_t level, int32_t P,
@@ -283,6 +320,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
   __shared__ __align__(16) float v[HD];
   __shared__ __align__(16) float dl[HD];
   __shared__ float norm_sh, nacc_sh;
+  __shared__ int32_t scan_sh[kThreads], sel_sh[3];
+  __shared__ uint64_t pivot_sh;
   float* xs = reinterpret_cast<float*>(keys);  // staging of slice_stats (before the keys)
   const int tid = threadIdx.x;
   const int bh = blockIdx.y, b = blockIdx.x;
@@ -292,8 +331,6 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
   const int n = g * C, s0 = s * C;
   const uint16_t* q = Q + size_t(bh) * N * HD;
   int32_t* idx = perm + size_t(bh) * N + s0;
-  int npad = 1;
-  while (npad < n) npad <<= 1;
   // The segment's tokens, after the key (and staging) area.
   int32_t* ids = reinterpret_cast<int32_t*>(keys) + 2 * key_words;
   for (int j = tid; j < n; j += kThreads) ids[j] = idx[j];
@@ -355,42 +392,79 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
     if (tid < HD) v[tid] = w[tid] / nrm;
     __syncthreads();
   }
-  // Projections -> keys (projection ascending, then token ascending).
-  for (int j = tid; j < npad; j += kThreads) {
-    if (j < n) {
-      const int t = ids[j];
-      const uint16_t* row = q + size_t(t) * HD;
-      float a = 0.f;
+  // Projections -> keys (projection ascending, then token ascending); thread
+  // tid owns the contiguous keys [tid per, (tid + 1) per).
+  const int per = (n + kThreads - 1) / kThreads;
+  const int jlo = min(tid * per, n), jhi = min(jlo + per, n);
+  for (int j = jlo; j < jhi; ++j) {
+    const int t = ids[j];
+    const uint16_t* row = q + size_t(t) * HD;
+    float a = 0.f;
 #pragma unroll
-      for (int c = 0; c < HD / 8; ++c) {
-        const v4u x = *reinterpret_cast<const v4u*>(row + 8 * c);
+    for (int c = 0; c < HD / 8; ++c) {
+      const v4u x = *reinterpret_cast<const v4u*>(row + 8 * c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = 8 * c + 2 * e;
-          a += (__uint_as_float(x[e] << 16) - mu[d]) * v[d];
-          a += (__uint_as_float(x[e] & 0xffff0000u) - mu[d + 1]) * v[d + 1];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int d = 8 * c + 2 * e;
+        a += (__uint_as_float(x[e] << 16) - mu[d]) * v[d];
+        a += (__uint_as_float(x[e] & 0xffff0000u) - mu[d + 1]) * v[d + 1];
       }
-      keys[j] = (uint64_t(ordered(a)) << 32) | uint32_t(t);
-    } else {
-      keys[j] = ~0ull;
     }
+    keys[j] = (uint64_t(ordered(a)) << 32) | uint32_t(t);
   }
-  bitonic(keys, npad, npad);
-  for (int j = tid; j < n; j += kThreads) idx[j] = static_cast<int32_t>(keys[j] & 0xffffffffu);
+  // The left child is the k = floor(g/2) C smallest keys (keys are distinct: the
+  // token is part of them).  Radix select of the k-th smallest key, 8 bits at a
+  // time from the top, then a stable partition: smaller keys to the front in
+  // their current order, the rest after them.
+  int32_t* hist = reinterpret_cast<int32_t*>(&red[0][0]);  // 256 bins (red holds >= 256 floats)
+  uint64_t prefix = 0, mask = 0;
+  int want = (g >> 1) * C;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int j = jlo; j < jhi; ++j)
+      if ((keys[j] & mask) == prefix) atomicAdd(&hist[(keys[j] >> shift) & 255], 1);
+    __syncthreads();
+    const int cnt = hist[tid];
+    const int excl = block_excl_scan(cnt, scan_sh);
+    if (excl <= want && want < excl + cnt) {
+      sel_sh[0] = tid;
+      sel_sh[1] = want - excl;
+      sel_sh[2] = cnt;
+    }
+    __syncthreads();
+    prefix |= uint64_t(sel_sh[0]) << shift;
+    mask |= uint64_t(255) << shift;
+    want = sel_sh[1];
+    const int left = sel_sh[2];
+    __syncthreads();
+    if (left == 1) break;  // uniform: one candidate key has this prefix
+  }
+  // The pivot: the one key with the selected prefix (the k-th smallest).
+  for (int j = jlo; j < jhi; ++j)
+    if ((keys[j] & mask) == prefix) pivot_sh = keys[j];
+  __syncthreads();
+  const uint64_t pivot = pivot_sh;
+  int nl = 0;
+  for (int j = jlo; j < jhi; ++j) nl += keys[j] < pivot ? 1 : 0;
+  const int kleft = (g >> 1) * C;
+  int pl = block_excl_scan(nl, scan_sh);  // left slots before this thread
+  int pr = kleft + (jlo - pl);             // right slots before this thread
+  for (int j = jlo; j < jhi; ++j) {
+    const uint64_t key = keys[j];
+    const int32_t t = static_cast<int32_t>(key & 0xffffffffu);
+    if (key < pivot)
+      idx[pl++] = t;
+    else
+      idx[pr++] = t;
+  }
 }
 
 // 64-bit words of split_kernel's key (and row staging) area for segments of up
-// to nmax tokens; the segment's token list follows it (npad int32).
-inline int split_key_words(int nmax, int D) {
-  int npad = 1;
-  while (npad < nmax) npad <<= 1;
-  return std::max(npad, 64 * D * 4 / 8);
-}
+// to nmax tokens; the segment's token list follows it (nmax int32).
+inline int split_key_words(int nmax, int D) { return std::max((nmax + 1) & ~1, 64 * D * 4 / 8); }
 inline size_t split_lds_bytes(int nmax, int D) {
-  int npad = 1;
-  while (npad < nmax) npad <<= 1;
-  return size_t(split_key_words(nmax, D)) * 8 + size_t(npad) * 4;
+  return size_t(split_key_words(nmax, D)) * 8 + size_t(nmax) * 4;
 }
 
 // Every group's tokens ascending: grid (G, B*H).
@@ -497,25 +571,70 @@ __global__ __launch_bounds__(256) void token_mass_kernel(const uint16_t* __restr
 }
 
 // Top-k tokens of one group's mass row (largest mass, ties to the lower token),
-// ascending: one workgroup per row, two bitonic sorts in LDS.
+// ascending: one workgroup per row.  Keys (~ordered(mass), token) are distinct and
+// ascend with the wanted order; thread tid holds the keys of tokens
+// [tid per, (tid + 1) per) in registers.  A radix select (8 bits at a time from
+// the top) finds the k-th smallest key; the keys below it are the chosen tokens,
+// written in token order by a workgroup scan of the per-thread counts.
+constexpr int kSelPer = kMaxTokens / kThreads;  // keys per thread at most
+
 __global__ __launch_bounds__(kThreads) void select_tokens_kernel(const float* __restrict__ mass,
                                                                  int32_t N, int32_t k,
                                                                  int32_t* __restrict__ tokens) {
-  __shared__ uint64_t keys[kMaxTokens];
+  __shared__ int32_t hist[256], scan_sh[kThreads / 64], sel_sh[3];
+  __shared__ uint64_t pivot_sh;
+  const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const float* m = mass + size_t(row) * N;
-  int npad = 1;
-  while (npad < N) npad <<= 1;
-  for (int j = threadIdx.x; j < npad; j += kThreads)
-    keys[j] = j < N ? (uint64_t(~ordered(m[j])) << 32) | uint32_t(j) : ~0ull;
-  bitonic(keys, npad, npad);
-  int kpad = 1;
-  while (kpad < k) kpad <<= 1;
-  // The k chosen tokens, by index: each entry is rewritten by the thread that reads it.
-  for (int j = threadIdx.x; j < kpad; j += kThreads)
-    keys[j] = j < k ? (keys[j] & 0xffffffffu) : ~0ull;
-  bitonic(keys, kpad, kpad);
-  for (int j = threadIdx.x; j < k; j += kThreads) tokens[size_t(row) * k + j] = static_cast<int32_t>(keys[j]);
+  int32_t* out = tokens + size_t(row) * k;
+  const int per = (N + kThreads - 1) / kThreads;
+  const int jlo = min(tid * per, N), jhi = min(jlo + per, N);
+  uint64_t key[kSelPer];
+#pragma unroll
+  for (int u = 0; u < kSelPer; ++u) {
+    const int j = jlo + u;
+    key[u] = (u < per && j < jhi) ? (uint64_t(~ordered(m[j])) << 32) | uint32_t(j) : ~0ull;
+  }
+  auto valid = [&](int u) { return u < per && jlo + u < jhi; };
+  uint64_t pivot = ~0ull;  // k == N: every key is below no pivot; take them all
+  if (k < N) {
+    uint64_t prefix = 0, mask = 0;
+    int want = k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kSelPer; ++u)
+        if (valid(u) && (key[u] & mask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255], 1);
+      __syncthreads();
+      const int cnt = hist[tid];
+      const int excl = block_excl_scan(cnt, scan_sh);
+      if (excl <= want && want < excl + cnt) {
+        sel_sh[0] = tid;
+        sel_sh[1] = want - excl;
+        sel_sh[2] = cnt;
+      }
+      __syncthreads();
+      prefix |= uint64_t(sel_sh[0]) << shift;
+      mask |= uint64_t(255) << shift;
+      want = sel_sh[1];
+      const int left = sel_sh[2];
+      __syncthreads();
+      if (left == 1) break;  // uniform
+    }
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u)
+      if (valid(u) && (key[u] & mask) == prefix) pivot_sh = key[u];
+    __syncthreads();
+    pivot = pivot_sh;
+  }
+  int nl = 0;
+#pragma unroll
+  for (int u = 0; u < kSelPer; ++u) nl += (valid(u) && (k >= N || key[u] < pivot)) ? 1 : 0;
+  int pos = block_excl_scan(nl, scan_sh);
+#pragma unroll
+  for (int u = 0; u < kSelPer; ++u)
+    if (valid(u) && (k >= N || key[u] < pivot)) out[pos++] = jlo + u;
 }
 
 }  // namespace
