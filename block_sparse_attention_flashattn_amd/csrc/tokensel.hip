@@ -511,7 +511,8 @@ __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Token mass of one group: one workgroup (four wavefronts) per (group, 128 keys);
+// Token mass of one group: one workgroup (four wavefronts) per (group, slice of
+// the key tiles of 128 keys);
 // S = Q K^T with the group's queries as MFMA rows (gathered by index): lane
 // (kl, hh) holds, for key kl of its 32, the queries 8(e/4) + 4hh + (e%4) of a
 // 32-query slice, so summing over the group's queries is a sum over the lane's
@@ -551,23 +552,39 @@ __global__ __launch_bounds__(256) void token_mass_kernel(const uint16_t* __restr
       lq[s][e] = (l > -INFINITY && l < INFINITY) ? l * 1.4426950408889634f : INFINITY;
     }
   }
-  const int key = blockIdx.y * 128 + 32 * wave + kl;
-  bf16x8 kf[NC];
+  // Key tiles blockIdx.y, blockIdx.y + gridDim.y, ...: the group's query
+  // fragments and LSEs stay in registers; the next tile's K rows are in flight
+  // while this one is used.
+  const int n_tiles = (N + 127) / 128;
+  auto fetch = [&](int kt, bf16x8 (&kf)[NC]) {
+    const int key = kt * 128 + 32 * wave + kl;
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    kf[c] = load16(kr, key < N ? static_cast<uint32_t>(key * HD + 16 * c + 8 * hh) * 2u : hbytes);
-  float acc = 0.f;
+    for (int c = 0; c < NC; ++c)
+      kf[c] = load16(kr, key < N ? static_cast<uint32_t>(key * HD + 16 * c + 8 * hh) * 2u : hbytes);
+  };
+  bf16x8 kf[NC], kn[NC];
+  int kt = blockIdx.y;
+  if (kt < n_tiles) fetch(kt, kf);
+  for (; kt < n_tiles; kt += gridDim.y) {
+    if (kt + int(gridDim.y) < n_tiles) fetch(kt + gridDim.y, kn);
+    float acc = 0.f;
 #pragma unroll
-  for (int s = 0; s < QS; ++s) {
-    f32x16 sv = {};
+    for (int s = 0; s < QS; ++s) {
+      f32x16 sv = {};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s][c], kf[c], sv, 0, 0, 0);
+      for (int c = 0; c < NC; ++c)
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s][c], kf[c], sv, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc += __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -lq[s][e]));
+      for (int e = 0; e < 16; ++e) acc += __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -lq[s][e]));
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc),
+                                                     false, false);
+    const float other = __uint_as_float(hh ? sw[0] : sw[1]);
+    const int key = kt * 128 + 32 * wave + kl;
+    if (hh == 0 && key < N) mass[size_t(row) * N + key] = acc + other;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kf[c] = kn[c];
   }
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-  const float other = __uint_as_float(hh ? sw[0] : sw[1]);
-  if (hh == 0 && key < N) mass[size_t(row) * N + key] = acc + other;
 }
 
 // Top-k tokens of one group's mass row (largest mass, ties to the lower token),
@@ -719,7 +736,9 @@ extern "C" BSA_API bsa_status bsa_token_mass(const void* q, const void* k, const
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
   const float sl2 = sc * 1.4426950408889634f;
   const int32_t G = N / C;
-  const dim3 grid(B * H * G, (N + 127) / 128);
+  // Four key-tile slices per group: the group's queries are gathered once per
+  // workgroup and reused over a quarter of the keys.
+  const dim3 grid(B * H * G, std::min(4, (N + 127) / 128));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
