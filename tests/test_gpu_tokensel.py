@@ -33,9 +33,11 @@ def dense_lse(bsa, q, k, block):
 
 
 @pytest.mark.parametrize("G,C,D", [(1, 64, 64), (2, 64, 64), (3, 64, 64), (5, 64, 128),
-                                   (8, 64, 64), (6, 128, 64)])
+                                   (8, 64, 64), (6, 128, 64), (40, 64, 128), (66, 64, 64)])
 def test_query_groups_recover_separated_clusters(G, C, D):
-    """Far-apart clusters leave no near-tie at any cut: the GPU groups are the oracle's."""
+    """Far-apart clusters leave no near-tie at any cut: the GPU groups are the oracle's.
+    The two largest cases split segments above 1024 tokens, whose scatter matrices come
+    from 512-token slice partials."""
     bsa = need_gpu()
     print(f"case G={G} C={C} D={D}", flush=True)
     q = clustered_q(G * 10 + D, G, C, D)
