@@ -72,32 +72,52 @@ template <int HD>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ Pq,
                                                     const float* __restrict__ Pk, int32_t nb,
                                                     float* __restrict__ S) {
-  __shared__ float sq[32][HD + 1];
-  __shared__ float sk[32][HD + 1];
+  // A 32 x 32 tile of one head's scores per workgroup; thread (ti, tj) computes the
+  // 2 x 2 block of rows 2ti, 2ti+1 and columns 2tj, 2tj+1, four dimensions per
+  // step from 16-byte LDS reads (rows padded by 4 floats: 16-byte aligned, and
+  // the 16 threads of a row group read 16 different bank groups).
+  constexpr int LD = HD + 4;
+  __shared__ __align__(16) float sq[32 * LD];
+  __shared__ __align__(16) float sk[32 * LD];
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * 32;
   const int i0 = blockIdx.y * 32;
   const size_t bh = blockIdx.z;
-  for (int x = tid; x < 32 * HD; x += 256) {
-    const int rr = x / HD;
-    const int d = x - rr * HD;
-    sq[rr][d] = (i0 + rr < nb) ? Pq[(bh * nb + i0 + rr) * HD + d] : 0.f;
-    sk[rr][d] = (j0 + rr < nb) ? Pk[(bh * nb + j0 + rr) * HD + d] : 0.f;
+  for (int x = tid; x < 32 * HD / 4; x += 256) {
+    const int rr = x / (HD / 4);
+    const int d = 4 * (x - rr * (HD / 4));
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(sq + rr * LD + d) =
+        (i0 + rr < nb) ? *reinterpret_cast<const f32x4*>(Pq + (bh * nb + i0 + rr) * HD + d) : z;
+    *reinterpret_cast<f32x4*>(sk + rr * LD + d) =
+        (j0 + rr < nb) ? *reinterpret_cast<const f32x4*>(Pk + (bh * nb + j0 + rr) * HD + d) : z;
   }
   __syncthreads();
-  const int ti = tid >> 3;
-  const int tj = tid & 7;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int d = 0; d < HD; ++d) {
-    const float a = sq[ti][d];
+  const int ti = tid >> 4;
+  const int tj = tid & 15;
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll 4
+  for (int d = 0; d < HD; d += 4) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(sq + (2 * ti) * LD + d);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(sq + (2 * ti + 1) * LD + d);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(sk + (2 * tj) * LD + d);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(sk + (2 * tj + 1) * LD + d);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] = fmaf(a, sk[tj + 8 * m][d], acc[m]);
+    for (int e = 0; e < 4; ++e) {
+      acc[0][0] = fmaf(a0[e], b0[e], acc[0][0]);
+      acc[0][1] = fmaf(a0[e], b1[e], acc[0][1]);
+      acc[1][0] = fmaf(a1[e], b0[e], acc[1][0]);
+      acc[1][1] = fmaf(a1[e], b1[e], acc[1][1]);
+    }
   }
-  if (i0 + ti < nb) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int j = j0 + tj + 8 * m;
-      if (j < nb) S[(bh * nb + i0 + ti) * nb + j] = acc[m];
+  for (int m = 0; m < 2; ++m) {
+    const int i = i0 + 2 * ti + m;
+    if (i >= nb) continue;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int j = j0 + 2 * tj + n;
+      if (j < nb) S[(bh * nb + i) * nb + j] = acc[m][n];
     }
   }
 }
