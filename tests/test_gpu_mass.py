@@ -117,3 +117,25 @@ def test_block_oracle_keeps_at_least_the_mean_pool_mass():
     assert np.all(kept_gpu >= kept_best - 1e-4 * w.block)
     got = bsa.csr_mass(mass, rp, ci_o).cpu().numpy()
     np.testing.assert_allclose(got, kept_gpu, rtol=2e-4, atol=1e-5)
+
+
+def test_block_mass_t2i_sampled_heads():
+    """The t2i workload at full size (B2 H24 N4224 D64, block 64), as the benchmark runs
+    it: the dense LSE from the forward over the all-ones CSR, then the block masses of
+    every head on the GPU; the oracle on two heads (a head's masses depend on that head
+    only), and every row sums to its block's query count."""
+    bsa = need_gpu()
+    w = W.make("t2i")
+    q, k, _ = w.tensors()
+    qd, kd = q.cuda(), k.cuda()
+    lse = dense_lse(bsa, qd, kd, w.block)
+    mass = bsa.block_mass(qd, kd, lse, w.block)
+    torch.cuda.synchronize()
+    got = mass.cpu().numpy().astype(np.float64)
+    for b, h in ((0, 3), (1, 20)):
+        ref = OM.block_mass(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], w.block,
+                            1.0 / np.sqrt(w.D))[0, 0]
+        err = np.abs(got[b, h] - ref)
+        print(f"head ({b},{h}): max abs {err.max():.3e}", flush=True)
+        assert np.all(err <= 1e-4 * ref + 2e-6)
+    np.testing.assert_allclose(got.sum(-1), float(w.block), rtol=2e-4)
