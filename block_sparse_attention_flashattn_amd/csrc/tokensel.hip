@@ -23,7 +23,7 @@ namespace bsa {
 namespace {
 
 constexpr int kPowerIters = 8;
-constexpr int kMaxTokens = 8192;  // tokens per head handled by the sorts (LDS)
+constexpr int kMaxTokens = 8192;  // tokens per head (LDS key and token lists, register key arrays)
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
