@@ -71,25 +71,14 @@ __device__ void bitonic(uint64_t* keys, int n, int max_size) {
 constexpr int kPart = 512;        // tokens per slice of a partial scatter matrix
 constexpr int kDirectMax = 1024;  // segments up to this size compute M themselves
 
-// Segment (s, g) of node b at depth `level` of the split tree of G groups;
-// g = 0 if the node does not exist (an ancestor was a single group).
-__device__ __forceinline__ void node_segment(int G, int level, int b, int& s, int& g) {
-  s = 0;
-  g = G;
-  for (int l = level - 1; l >= 0; --l) {
-    if (g <= 1) {
-      g = 0;
-      return;
-    }
-    const int gl = g >> 1;
-    if ((b >> l) & 1) {
-      s += gl;
-      g -= gl;
-    } else {
-      g = gl;
-    }
-  }
-}
+// The segments of one depth of the split tree that still hold more than one
+// group, left to right (passed by value: a launch covers exactly these).
+constexpr int kMaxNodes = 128;
+struct NodeList {
+  int32_t n;
+  int32_t s[kMaxNodes];  // first group
+  int32_t g[kMaxNodes];  // groups
+};
 
 // Scatter-matrix blocks of one thread: HD = 64, a 4x4 block (rows a0.., columns
 // b0..); HD = 128, four 4x4 blocks (rows a0.., columns b0 + 32 k).
@@ -207,11 +196,11 @@ __global__ __launch_bounds__(kThreads) void perm_init_kernel(int32_t N, int32_t*
     perm[size_t(bh) * N + r] = r;
 }
 
-// Partial (n, mu, M) of slice p of the segment of node b at depth `level`:
-// grid (2^level * P, B*H); floats per partial 1 + HD + HD^2.
+// Partial (n, mu, M) of slice p of the segment of node b of the depth's list:
+// grid (nodes * P, B*H); floats per partial 1 + HD + HD^2.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restrict__ Q, int32_t N,
-                                                         int32_t C, int32_t level, int32_t P,
+                                                         int32_t C, NodeList nodes, int32_t P,
                                                          const int32_t* __restrict__ perm,
                                                          float* __restrict__ part) {
   __shared__ __align__(16) float xs[64 * HD];
@@ -220,9 +209,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
   __shared__ int32_t ids[kPart];
   const int bh = blockIdx.y;
   const int b = blockIdx.x / P, p = blockIdx.x - b * P;
-  int s, g;
-  node_segment(N / C, level, b, s, g);
-  if (g <= 1) return;
+  const int s = nodes.s[b], g = nodes.g[b];
   const int n = g * C;
   const int L = (n + P - 1) / P;
   const int lo = min(p * L, n), hi = min(lo + L, n);
@@ -233,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
   ScatterBlock<HD> sb;
   slice_stats<HD>(q, ids, hi - lo, xs, red, x0s, mu, sb);
   constexpr int F = 1 + HD + HD * HD;
-  float* out = part + ((size_t(bh) << level) * P + size_t(b) * P + p) * F;
+  float* out = part + ((size_t(bh) * nodes.n + b) * P + p) * F;
   const int tid = threadIdx.x;
   if (tid == 0) out[0] = float(hi - lo);
   if (tid < HD) out[1 + tid] = mu[tid];
@@ -300,7 +287,7 @@ __device__ int block_excl_scan(int x, int32_t* tmp) {
   return base + incl - x;
 }
 
-// Split of the segment of node b at depth `level` (grid (2^level, B*H)): its
+// Split of the segment of node b of the depth's list (grid (nodes, B*H)): its
 // scatter matrix (from the P partials in slice order, or computed here when
 // P == 1; either way held in registers, ScatterBlock), the principal direction,
 // the projections, and the segment's tokens rewritten so that the floor(g/2) C
@@ -309,7 +296,7 @@ __device__ int block_excl_scan(int x, int32_t* tmp) {
 // (and the row staging), then its token list.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restrict__ Q, int32_t N,
-                                                         int32_t C, int32_t level, int32_t P,
+                                                         int32_t C, NodeList nodes, int32_t P,
                                                          int32_t key_words,
                                                          const float* __restrict__ part,
                                                          int32_t* __restrict__ perm) {
@@ -325,9 +312,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
   float* xs = reinterpret_cast<float*>(keys);  // staging of slice_stats (before the keys)
   const int tid = threadIdx.x;
   const int bh = blockIdx.y, b = blockIdx.x;
-  int s, g;
-  node_segment(N / C, level, b, s, g);
-  if (g <= 1) return;
+  const int s = nodes.s[b], g = nodes.g[b];
   const int n = g * C, s0 = s * C;
   const uint16_t* q = Q + size_t(bh) * N * HD;
   int32_t* idx = perm + size_t(bh) * N + s0;
@@ -343,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
     // (n, mu, M) <- (n, mu, M) + partial: delta = mu_p - mu, M += M_p +
     // n n_p / (n + n_p) delta delta^T, mu += delta n_p / (n + n_p).
     sb.init(tid);
-    const float* pp = part + ((size_t(bh) << level) * P + size_t(b) * P) * F;
+    const float* pp = part + ((size_t(bh) * nodes.n + b) * P) * F;
     if (tid < HD) mu[tid] = 0.f;
     if (tid == 0) nacc_sh = 0.f;
     __syncthreads();
@@ -695,28 +680,52 @@ extern "C" BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t
   hipLaunchKernelGGL(perm_init_kernel, dim3((N + kThreads - 1) / kThreads, bh), dim3(kThreads), 0,
                      s, N, groups_out);
   BSA_HIP_CHECK_LAUNCH();
-  for (int l = 0; l < L.depth; ++l) {
-    const uint32_t nodes = 1u << l;
+  // The split tree level by level: only the segments that still hold more than
+  // one group are launched (the last level of t2i has 2 of 64 possible nodes).
+  NodeList cur{};
+  cur.n = 0;
+  if (N / C > 1) {
+    cur.n = 1;
+    cur.s[0] = 0;
+    cur.g[0] = N / C;
+  }
+  for (int l = 0; cur.n > 0; ++l) {
+    const uint32_t nodes = static_cast<uint32_t>(cur.n);
+    int gmax = 0;
+    for (int x = 0; x < cur.n; ++x) gmax = std::max(gmax, cur.g[x]);
     const int P = L.P[l];
     if (P > 1) {
       if (D == 64)
         hipLaunchKernelGGL(stats_kernel<64>, dim3(nodes * P, bh), dim3(kThreads), 0, s, qq, N, C,
-                           l, P, groups_out, part);
+                           cur, P, groups_out, part);
       else
         hipLaunchKernelGGL(stats_kernel<128>, dim3(nodes * P, bh), dim3(kThreads), 0, s, qq, N, C,
-                           l, P, groups_out, part);
+                           cur, P, groups_out, part);
       BSA_HIP_CHECK_LAUNCH();
     }
-    const int gmax = (N / C + int(nodes) - 1) / int(nodes);
     const size_t lds = split_lds_bytes(gmax * C, D);
     const int kw = split_key_words(gmax * C, D);
     if (D == 64)
-      hipLaunchKernelGGL(split_kernel<64>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C, l, P,
-                         kw, part, groups_out);
-    else
-      hipLaunchKernelGGL(split_kernel<128>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C, l,
+      hipLaunchKernelGGL(split_kernel<64>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C, cur,
                          P, kw, part, groups_out);
+    else
+      hipLaunchKernelGGL(split_kernel<128>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C,
+                         cur, P, kw, part, groups_out);
     BSA_HIP_CHECK_LAUNCH();
+    NodeList nxt{};
+    nxt.n = 0;
+    for (int x = 0; x < cur.n; ++x) {
+      const int gl = cur.g[x] / 2, gr = cur.g[x] - gl;
+      if (gl > 1) {
+        nxt.s[nxt.n] = cur.s[x];
+        nxt.g[nxt.n++] = gl;
+      }
+      if (gr > 1) {
+        nxt.s[nxt.n] = cur.s[x] + gl;
+        nxt.g[nxt.n++] = gr;
+      }
+    }
+    cur = nxt;
   }
   hipLaunchKernelGGL(group_sort_kernel, dim3(N / C, bh), dim3(kThreads), 0, s, N, C, groups_out);
   BSA_HIP_CHECK_LAUNCH();
