@@ -128,13 +128,38 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// A 64-bit value moved between lanes by a DPP pattern (both halves).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(v & 0xffffffffu), static_cast<int>(v & 0xffffffffu), CTRL, 0xf, 0xf, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(v >> 32), static_cast<int>(v >> 32), CTRL, 0xf, 0xf, false));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Maximum of a 64-bit value over the wavefront, in every lane, without LDS:
+// DPP exchanges within each 16-lane row (lane ^ 1, lane ^ 2, mirror within 8,
+// mirror within 16), then v_permlane16_swap (the other row of a 32-lane half)
+// and v_permlane32_swap (the other half).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v & 0xffffffffu), off));
-    const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), off));
-    const uint64_t o = (uint64_t(hi) << 32) | lo;
-    v = o > v ? o : v;
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<0xb1>(v));   // quad_perm [1, 0, 3, 2]
+  v = mx(v, dpp_u64<0x4e>(v));   // quad_perm [2, 3, 0, 1]
+  v = mx(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = mx(v, dpp_u64<0x140>(v));  // row_mirror
+  const bool odd_row = (threadIdx.x & 16) != 0, upper = (threadIdx.x & 32) != 0;
+  {
+    const uint32_t lo = static_cast<uint32_t>(v & 0xffffffffu), hi = static_cast<uint32_t>(v >> 32);
+    const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    v = mx(v, (uint64_t(odd_row ? sh[0] : sh[1]) << 32) | (odd_row ? sl[0] : sl[1]));
+  }
+  {
+    const uint32_t lo = static_cast<uint32_t>(v & 0xffffffffu), hi = static_cast<uint32_t>(v >> 32);
+    const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    v = mx(v, (uint64_t(upper ? sh[0] : sh[1]) << 32) | (upper ? sl[0] : sl[1]));
   }
   return v;
 }
