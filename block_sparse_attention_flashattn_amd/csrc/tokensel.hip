@@ -233,6 +233,34 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
       for (int j = 0; j < 4; ++j) M[(sb.a0 + i) * HD + sb.col(k) + j] = sb.m[k][i][j];
 }
 
+// Sums over lane groups without LDS, every lane of the group receiving the sum:
+// DPP exchanges inside a 16-lane row (lane ^ 1, lane ^ 2, mirror within 8,
+// mirror within 16), then v_permlane16_swap / v_permlane32_swap across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf,
+                                                    0xf, false));
+}
+__device__ __forceinline__ float row_sum8(float v) {
+  v += dpp_f32<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v = row_sum8(v);
+  v += dpp_f32<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v += __uint_as_float((threadIdx.x & 16) ? s16[0] : s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v += __uint_as_float((threadIdx.x & 32) ? s32[0] : s32[1]);
+  return v;
+}
+
 // w = M v for a scatter matrix held in ScatterBlocks (M symmetric, each thread
 // its blocks): per-thread partial rows, summed over the lanes that share a row
 // block (16 consecutive lanes at HD = 64, 8 at HD = 128), into w (LDS, HD floats).
@@ -249,9 +277,7 @@ __device__ void scatter_matvec(const ScatterBlock<HD>& sb, const float* v, float
   }
   constexpr int span = HD == 64 ? 16 : 8;
 #pragma unroll
-  for (int off = 1; off < span; off <<= 1)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], off);
+  for (int i = 0; i < 4; ++i) part[i] = span == 16 ? row_sum16(part[i]) : row_sum8(part[i]);
   if ((threadIdx.x & (span - 1)) == 0) *reinterpret_cast<f32x4*>(w + sb.a0) = part;
 }
 
@@ -262,8 +288,7 @@ __device__ void norm_w0(const float* x, float* out) {
     float s2 = 0.f;
 #pragma unroll
     for (int h = 0; h < HD / 64; ++h) s2 += x[64 * h + threadIdx.x] * x[64 * h + threadIdx.x];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
+    s2 = wave_sum(s2);
     if (threadIdx.x == 0) *out = sqrtf(s2);
   }
 }
