@@ -98,93 +98,128 @@ struct ScatterBlock {
   __device__ int col(int k) const { return b0 + 32 * k; }
 };
 
+// LDS bytes slice_stats needs: the shifted rows of one 64-row batch as high and
+// low bf16 halves, the scatter matrix, and per-thread partial row sums.
+constexpr int stats_lds_bytes(int HD) { return 2 * 64 * HD * 2 + HD * HD * 4 + kThreads * 8 * 4; }
+
 // Mean and scatter matrix of the tokens ids[0, n) (LDS) of one head (rows of q):
-// mu (LDS, HD floats) and this thread's blocks of M.  One pass over the rows,
-// shifted by the first row x0 (fp32 differences of bf16 values are exact):
-// S1 = sum (x - x0), S2 = sum (x - x0)(x - x0)^T, mu = x0 + S1 / n,
-// M = S2 - S1 S1^T / n.  xs: LDS for 64 shifted fp32 rows; red: LDS
-// [256 / HD][HD]; x0s: LDS, HD floats.  All threads of the workgroup call it.
+// mu (LDS, HD floats) and this thread's blocks of M.  The rows are shifted by
+// the first row x0 (fp32 differences of bf16 values are exact) and split into
+// bf16 halves, v = hi + lo; S2 = sum (x - x0)(x - x0)^T accumulates on bf16
+// MFMA (hi hi^T + hi lo^T + lo hi^T, fp32 accumulation: the dropped lo lo^T and
+// the rounding of lo are ~2^-16 of each term), both operands read transposed
+// from the staged rows (ds_read_b64_tr_b16).  S1 = sum (x - x0) in fp32,
+// mu = x0 + S1 / n, M = S2 - S1 S1^T / n.  ws: stats_lds_bytes(HD) of LDS,
+// 16-byte aligned; x0s: HD floats of LDS.  All threads of the workgroup call it.
 template <int HD>
-__device__ void slice_stats(const uint16_t* __restrict__ q, const int32_t* ids, int n, float* xs,
-                            float (*red)[HD], float* x0s, float* mu, ScatterBlock<HD>& sb) {
-  constexpr int RG = kThreads / HD;
-  constexpr int CH = HD / 8;  // 16-byte chunks per row
-  const int tid = threadIdx.x;
-  const int d = tid % HD, rg = tid / HD;
+__device__ void slice_stats(const uint16_t* __restrict__ q, const int32_t* ids, int n, uint8_t* ws,
+                            float* x0s, float* mu, ScatterBlock<HD>& sb) {
+  constexpr int ROWB = HD * 2, CH = HD / 8, TILE = 64 * ROWB;
+  constexpr int PT = 64 * CH / kThreads;  // 16-byte chunks per thread and batch
+  constexpr int NTL = HD == 64 ? 1 : 4;   // 32x32 output tiles per wavefront
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, hh = lane >> 5;
+  float* Mbuf = reinterpret_cast<float*>(ws + 2 * TILE);
+  float* s1p = Mbuf + HD * HD;
+  const uint32_t hiA = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)ws));
+  const uint32_t loA = hiA + TILE;
   if (tid < HD) x0s[tid] = n > 0 ? bf2f(q[size_t(ids[0]) * HD + tid]) : 0.f;
   __syncthreads();
-  sb.init(tid);
-  float s1 = 0.f;
-  // The 16-byte chunks this thread moves per batch of 64 rows, the next batch's
-  // in flight while the current one is used.
-  constexpr int PT = 64 * CH / kThreads;
+  // Thread tid's chunks always sit in column chunk tid % CH (kThreads % CH == 0).
+  const int cc = tid % CH;
+  float s1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x16 acc[NTL];
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) acc[t] = f32x16{};
+  const int ab = HD == 64 ? (wave >> 1) : wave;  // row block (a) of this wave's tiles
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   v4u pre[PT];
   auto fetch = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int e = tid + kThreads * u;
-      const int j = j0 + e / CH;
-      pre[u] = j < n ? *reinterpret_cast<const v4u*>(q + size_t(ids[j]) * HD + 8 * (e % CH))
+      const int j = j0 + (tid + kThreads * u) / CH;
+      pre[u] = j < n ? *reinterpret_cast<const v4u*>(q + size_t(ids[j]) * HD + 8 * cc)
                      : v4u{0u, 0u, 0u, 0u};
     }
+  };
+  // Operand [32 columns x 16 rows] of the staged tile at LDS address base,
+  // columns 32 blk .. +31, rows 16 c2 .. +15 (the transposing read).
+  auto opnd = [&](uint32_t base, int blk, int c2) -> bf16x8 {
+    const int col = 32 * blk + tr_col;
+    const v4s lo = lds_read_tr(base + swz<ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
+    const v4s hi = lds_read_tr(base + swz<ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   fetch(0);
   for (int j0 = 0; j0 < n; j0 += 64) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int e = tid + kThreads * u;
-      const int r = e / CH, c = e % CH;
-      const int j = j0 + r;
-      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-      if (j < n) {
-        const v4u w = pre[u];
+      const int r = (tid + kThreads * u) / CH;
+      const bool ok = j0 + r < n;
+      bf16x8 vh, vl;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float e0 = __uint_as_float(w[x] << 16), e1 = __uint_as_float(w[x] & 0xffff0000u);
-          const int dd = 8 * c + 2 * x;
-          if (x < 2) {
-            lo[2 * x] = e0 - x0s[dd];
-            lo[2 * x + 1] = e1 - x0s[dd + 1];
-          } else {
-            hi[2 * x - 4] = e0 - x0s[dd];
-            hi[2 * x - 3] = e1 - x0s[dd + 1];
-          }
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t w = pre[u][x];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int e = 2 * x + y;
+          const float v = ok ? __uint_as_float(y ? (w & 0xffff0000u) : (w << 16)) - x0s[8 * cc + e]
+                             : 0.f;
+          s1[e] += v;
+          const __bf16 h = static_cast<__bf16>(v);
+          vh[e] = h;
+          vl[e] = static_cast<__bf16>(v - static_cast<float>(h));
         }
       }
-      *reinterpret_cast<f32x4*>(xs + r * HD + 8 * c) = lo;
-      *reinterpret_cast<f32x4*>(xs + r * HD + 8 * c + 4) = hi;
+      *reinterpret_cast<BSA_LDS bf16x8*>(static_cast<uintptr_t>(hiA + swz<ROWB>(r, cc))) = vh;
+      *reinterpret_cast<BSA_LDS bf16x8*>(static_cast<uintptr_t>(loA + swz<ROWB>(r, cc))) = vl;
     }
     __syncthreads();
     if (j0 + 64 < n) fetch(j0 + 64);
-    const int rows = min(64, n - j0);
-    for (int r = rg; r < rows; r += RG) s1 += xs[r * HD + d];
-    for (int r = 0; r < rows; ++r) {
-      const f32x4 xa = *reinterpret_cast<const f32x4*>(xs + r * HD + sb.a0);
 #pragma unroll
-      for (int k = 0; k < ScatterBlock<HD>::NB; ++k) {
-        const f32x4 xb = *reinterpret_cast<const f32x4*>(xs + r * HD + sb.col(k));
+    for (int c2 = 0; c2 < 4; ++c2) {
+      const bf16x8 aH = opnd(hiA, ab, c2), aL = opnd(loA, ab, c2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sb.m[k][i] += xa[i] * xb;
+      for (int t = 0; t < NTL; ++t) {
+        const int bb = HD == 64 ? (wave & 1) : t;
+        const bf16x8 bH = opnd(hiA, bb, c2), bL = opnd(loA, bb, c2);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bH, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bL, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL, bH, acc[t], 0, 0, 0);
       }
     }
     __syncthreads();
   }
-  red[rg][d] = s1;
+  // Tiles to LDS: lane (ql, hh) holds rows 32 ab + 8(e/4) + 4hh + e%4, column 32 bb + ql.
+#pragma unroll
+  for (int t = 0; t < NTL; ++t) {
+    const int bb = HD == 64 ? (wave & 1) : t;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      Mbuf[(32 * ab + 8 * (e >> 2) + 4 * hh + (e & 3)) * HD + 32 * bb + ql] = acc[t][e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s1p[tid * 8 + e] = s1[e];
   __syncthreads();
+  float S1 = 0.f;
   if (tid < HD) {
-    float t = 0.f;
-    for (int k = 0; k < RG; ++k) t += red[k][tid];
-    red[0][tid] = t;  // S1
-    mu[tid] = n > 0 ? x0s[tid] + t / float(n) : 0.f;
+    for (int t = tid / 8; t < kThreads; t += CH) S1 += s1p[t * 8 + (tid & 7)];
+    mu[tid] = n > 0 ? x0s[tid] + S1 / float(n) : 0.f;
   }
   __syncthreads();
+  if (tid < HD) s1p[tid] = S1;
+  __syncthreads();
   const float inv = n > 0 ? 1.f / float(n) : 0.f;
-  const f32x4 sa = *reinterpret_cast<const f32x4*>(&red[0][0] + sb.a0);
+  sb.init(tid);
+  const f32x4 sa = *reinterpret_cast<const f32x4*>(s1p + sb.a0);
 #pragma unroll
   for (int k = 0; k < ScatterBlock<HD>::NB; ++k) {
-    const f32x4 sbk = *reinterpret_cast<const f32x4*>(&red[0][0] + sb.col(k));
+    const f32x4 sbk = *reinterpret_cast<const f32x4*>(s1p + sb.col(k));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sb.m[k][i] -= (sa[i] * inv) * sbk;
+    for (int i = 0; i < 4; ++i)
+      sb.m[k][i] = *reinterpret_cast<const f32x4*>(Mbuf + (sb.a0 + i) * HD + sb.col(k)) -
+                   (sa[i] * inv) * sbk;
   }
   __syncthreads();
 }
@@ -203,10 +238,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
                                                          int32_t C, NodeList nodes, int32_t P,
                                                          const int32_t* __restrict__ perm,
                                                          float* __restrict__ part) {
-  __shared__ __align__(16) float xs[64 * HD];
-  __shared__ __align__(16) float red[kThreads / HD][HD];
+  extern __shared__ __align__(16) uint8_t sws[];  // stats_lds_bytes(HD), then the token list
   __shared__ float mu[HD], x0s[HD];
-  __shared__ int32_t ids[kPart];
+  int32_t* ids = reinterpret_cast<int32_t*>(sws + stats_lds_bytes(HD));
   const int bh = blockIdx.y;
   const int b = blockIdx.x / P, p = blockIdx.x - b * P;
   const int s = nodes.s[b], g = nodes.g[b];
@@ -218,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
   for (int j = threadIdx.x; j < hi - lo; j += kThreads) ids[j] = idx[j];
   __syncthreads();
   ScatterBlock<HD> sb;
-  slice_stats<HD>(q, ids, hi - lo, xs, red, x0s, mu, sb);
+  slice_stats<HD>(q, ids, hi - lo, sws, x0s, mu, sb);
   constexpr int F = 1 + HD + HD * HD;
   float* out = part + ((size_t(bh) * nodes.n + b) * P + p) * F;
   const int tid = threadIdx.x;
@@ -325,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
                                                          int32_t key_words,
                                                          const float* __restrict__ part,
                                                          int32_t* __restrict__ perm) {
-  extern __shared__ __align__(16) uint64_t keys[];  // 16-byte aligned: xs takes 16-byte reads
+  extern __shared__ __align__(16) uint64_t keys[];  // 16-byte aligned: slice_stats stages rows here
   __shared__ __align__(16) float red[kThreads / HD][HD];
   __shared__ float x0s[HD];
   __shared__ __align__(16) float mu[HD];
@@ -334,7 +368,6 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
   __shared__ float norm_sh, nacc_sh;
   __shared__ int32_t scan_sh[kThreads], sel_sh[3];
   __shared__ uint64_t pivot_sh;
-  float* xs = reinterpret_cast<float*>(keys);  // staging of slice_stats (before the keys)
   const int tid = threadIdx.x;
   const int bh = blockIdx.y, b = blockIdx.x;
   const int s = nodes.s[b], g = nodes.g[b];
@@ -348,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
   constexpr int F = 1 + HD + HD * HD;
   ScatterBlock<HD> sb;
   if (P <= 1) {
-    slice_stats<HD>(q, ids, n, xs, red, x0s, mu, sb);
+    slice_stats<HD>(q, ids, n, reinterpret_cast<uint8_t*>(keys), x0s, mu, sb);
   } else {
     // (n, mu, M) <- (n, mu, M) + partial: delta = mu_p - mu, M += M_p +
     // n n_p / (n + n_p) delta delta^T, mu += delta n_p / (n + n_p).
@@ -472,7 +505,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
 
 // 64-bit words of split_kernel's key (and row staging) area for segments of up
 // to nmax tokens; the segment's token list follows it (nmax int32).
-inline int split_key_words(int nmax, int D) { return std::max((nmax + 1) & ~1, 64 * D * 4 / 8); }
+inline int split_key_words(int nmax, int D) {
+  return std::max((nmax + 1) & ~1, stats_lds_bytes(D) / 8);
+}
 inline size_t split_lds_bytes(int nmax, int D) {
   return size_t(split_key_words(nmax, D)) * 8 + size_t(nmax) * 4;
 }
@@ -696,6 +731,11 @@ extern "C" BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t
     if (attr == hipSuccess)
       attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<128>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, big);
+    for (const void* f : {reinterpret_cast<const void*>(&stats_kernel<64>),
+                          reinterpret_cast<const void*>(&stats_kernel<128>)})
+      if (attr == hipSuccess)
+        attr = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   stats_lds_bytes(128) + kPart * 4);
   });
   if (attr != hipSuccess) return BSA_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -721,11 +761,11 @@ extern "C" BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t
     const int P = L.P[l];
     if (P > 1) {
       if (D == 64)
-        hipLaunchKernelGGL(stats_kernel<64>, dim3(nodes * P, bh), dim3(kThreads), 0, s, qq, N, C,
-                           cur, P, groups_out, part);
+        hipLaunchKernelGGL(stats_kernel<64>, dim3(nodes * P, bh), dim3(kThreads),
+                           stats_lds_bytes(64) + kPart * 4, s, qq, N, C, cur, P, groups_out, part);
       else
-        hipLaunchKernelGGL(stats_kernel<128>, dim3(nodes * P, bh), dim3(kThreads), 0, s, qq, N, C,
-                           cur, P, groups_out, part);
+        hipLaunchKernelGGL(stats_kernel<128>, dim3(nodes * P, bh), dim3(kThreads),
+                           stats_lds_bytes(128) + kPart * 4, s, qq, N, C, cur, P, groups_out, part);
       BSA_HIP_CHECK_LAUNCH();
     }
     const size_t lds = split_lds_bytes(gmax * C, D);
