@@ -99,8 +99,10 @@ struct ScatterBlock {
 };
 
 // LDS bytes slice_stats needs: the shifted rows of one 64-row batch as high and
-// low bf16 halves, the scatter matrix, and per-thread partial row sums.
-constexpr int stats_lds_bytes(int HD) { return 2 * 64 * HD * 2 + HD * HD * 4 + kThreads * 8 * 4; }
+// low bf16 halves (later the scatter matrix, in the same bytes), then per-thread
+// partial row sums.
+constexpr int stats_mat_bytes(int HD) { return 4 * 64 * HD > 4 * HD * HD ? 4 * 64 * HD : 4 * HD * HD; }
+constexpr int stats_lds_bytes(int HD) { return stats_mat_bytes(HD) + kThreads * 8 * 4; }
 
 // Mean and scatter matrix of the tokens ids[0, n) (LDS) of one head (rows of q):
 // mu (LDS, HD floats) and this thread's blocks of M.  The rows are shifted by
@@ -119,8 +121,8 @@ __device__ void slice_stats(const uint16_t* __restrict__ q, const int32_t* ids, 
   constexpr int NTL = HD == 64 ? 1 : 4;   // 32x32 output tiles per wavefront
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  float* Mbuf = reinterpret_cast<float*>(ws + 2 * TILE);
-  float* s1p = Mbuf + HD * HD;
+  float* Mbuf = reinterpret_cast<float*>(ws);  // after the last batch
+  float* s1p = reinterpret_cast<float*>(ws + stats_mat_bytes(HD));
   const uint32_t hiA = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)ws));
   const uint32_t loA = hiA + TILE;
   if (tid < HD) x0s[tid] = n > 0 ? bf2f(q[size_t(ids[0]) * HD + tid]) : 0.f;
@@ -295,11 +297,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// w = M v for a scatter matrix held in ScatterBlocks (M symmetric, each thread
+// w = scale M v for a scatter matrix held in ScatterBlocks (M symmetric, each thread
 // its blocks): per-thread partial rows, summed over the lanes that share a row
 // block (16 consecutive lanes at HD = 64, 8 at HD = 128), into w (LDS, HD floats).
 template <int HD>
-__device__ void scatter_matvec(const ScatterBlock<HD>& sb, const float* v, float* w) {
+__device__ void scatter_matvec(const ScatterBlock<HD>& sb, const float* v, float* w, float scale) {
   f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < ScatterBlock<HD>::NB; ++k) {
@@ -311,7 +313,7 @@ __device__ void scatter_matvec(const ScatterBlock<HD>& sb, const float* v, float
   }
   constexpr int span = HD == 64 ? 16 : 8;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[i] = span == 16 ? row_sum16(part[i]) : row_sum8(part[i]);
+  for (int i = 0; i < 4; ++i) part[i] = (span == 16 ? row_sum16(part[i]) : row_sum8(part[i])) * scale;
   if ((threadIdx.x & (span - 1)) == 0) *reinterpret_cast<f32x4*>(w + sb.a0) = part;
 }
 
@@ -353,7 +355,7 @@ __device__ int block_excl_scan(int x, int32_t* tmp) {
 // smallest (projection, token) keys come first (the left child), each side in
 // its previous order.  Dynamic LDS: the keys of the level's largest segment
 // (and the row staging), then its token list.
-template <int HD>
+template <int HD, bool WIDE>
 __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restrict__ Q, int32_t N,
                                                          int32_t C, NodeList nodes, int32_t P,
                                                          int32_t key_words,
@@ -417,43 +419,113 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const uint16_t* __restr
     }
   }
   __syncthreads();
-  // Power iteration from u[d] = 1 + d / HD.
-  if (tid < HD) v[tid] = 1.f + float(tid) / float(HD);
-  __syncthreads();
-  norm_w0<HD>(v, &norm_sh);
-  __syncthreads();
-  if (tid < HD) v[tid] /= norm_sh;
-  __syncthreads();
-  float* w = &red[0][0];
-  for (int it = 0; it < kPowerIters; ++it) {
-    scatter_matvec<HD>(sb, v, w);
-    __syncthreads();
-    norm_w0<HD>(w, &norm_sh);
-    __syncthreads();
-    const float nrm = norm_sh;
-    if (nrm == 0.f) break;  // uniform
-    if (tid < HD) v[tid] = w[tid] / nrm;
-    __syncthreads();
+  // Power iteration from u[d] = 1 + d / HD on M / trace(M) (spectral norm at
+  // most 1: no overflow, and eight steps shrink v by at most (HD)^-8), one
+  // barrier per step; the direction is normalised once at the end.  trace(M) = 0
+  // (every row equal) or M u = 0 keeps u.
+  {
+    float dsum = 0.f;
+    bool diag = false;
+#pragma unroll
+    for (int k = 0; k < ScatterBlock<HD>::NB; ++k)
+      if (sb.a0 == sb.col(k)) {
+        dsum = sb.m[k][0][0] + sb.m[k][1][1] + sb.m[k][2][2] + sb.m[k][3][3];
+        diag = true;
+      }
+    if (diag) dl[sb.a0 / 4] = dsum;  // one thread per 4-row block
   }
-  // Projections -> keys (projection ascending, then token ascending); thread
-  // tid owns the contiguous keys [tid per, (tid + 1) per).
-  const int per = (n + kThreads - 1) / kThreads;
-  const int jlo = min(tid * per, n), jhi = min(jlo + per, n);
-  for (int j = jlo; j < jhi; ++j) {
-    const int t = ids[j];
-    const uint16_t* row = q + size_t(t) * HD;
+  float* w = &red[0][0];  // two HD-float buffers, used in turn
+  if (tid < HD) w[tid] = 1.f + float(tid) / float(HD);
+  __syncthreads();
+  float tr = 0.f;
+#pragma unroll 8
+  for (int i = 0; i < HD / 4; ++i) tr += dl[i];
+  const float inv_tr = tr > 1e-30f ? 1.f / tr : 0.f;
+  int cur = 0;
+  if (inv_tr > 0.f) {
+#pragma unroll 1
+    for (int it = 0; it < kPowerIters; ++it) {
+      scatter_matvec<HD>(sb, w + cur * HD, w + (cur ^ 1) * HD, inv_tr);
+      cur ^= 1;
+      __syncthreads();
+    }
+  }
+  norm_w0<HD>(w + cur * HD, &norm_sh);
+  __syncthreads();
+  if (tid < HD) v[tid] = norm_sh > 0.f ? w[cur * HD + tid] / norm_sh : 1.f + float(tid) / float(HD);
+  __syncthreads();
+  // Projections -> keys (projection ascending, then token ascending).  WIDE
+  // (segments split from slice partials, few workgroups): tokens strided over
+  // the threads, two rows in flight per thread; otherwise (many workgroups,
+  // where occupancy matters) each thread's own keys one row at a time.
+  // Afterwards thread tid owns the contiguous keys [tid per, (tid + 1) per).
+  auto proj = [&](const v4u* x) {
     float a = 0.f;
 #pragma unroll
-    for (int c = 0; c < HD / 8; ++c) {
-      const v4u x = *reinterpret_cast<const v4u*>(row + 8 * c);
+    for (int c = 0; c < HD / 8; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d = 8 * c + 2 * e;
-        a += (__uint_as_float(x[e] << 16) - mu[d]) * v[d];
-        a += (__uint_as_float(x[e] & 0xffff0000u) - mu[d + 1]) * v[d + 1];
+        a += (__uint_as_float(x[c][e] << 16) - mu[d]) * v[d];
+        a += (__uint_as_float(x[c][e] & 0xffff0000u) - mu[d + 1]) * v[d + 1];
+      }
+    return a;
+  };
+  const int per = (n + kThreads - 1) / kThreads;
+  const int jlo = min(tid * per, n), jhi = min(jlo + per, n);
+  if constexpr (WIDE) {
+    for (int j = tid; j < n; j += 2 * kThreads) {
+      const int j2 = j + kThreads;
+      const int t = ids[j], t2 = j2 < n ? ids[j2] : t;
+      v4u x[HD / 8], x2[HD / 8];
+#pragma unroll
+      for (int c = 0; c < HD / 8; ++c) {
+        x[c] = *reinterpret_cast<const v4u*>(q + size_t(t) * HD + 8 * c);
+        x2[c] = *reinterpret_cast<const v4u*>(q + size_t(t2) * HD + 8 * c);
+      }
+      keys[j] = (uint64_t(ordered(proj(x))) << 32) | uint32_t(t);
+      if (j2 < n) keys[j2] = (uint64_t(ordered(proj(x2))) << 32) | uint32_t(t2);
+    }
+    __syncthreads();
+  } else {
+    // Eight lanes per row (lane part c8 holds dimensions [HD/8 c8, +HD/8)), four
+    // rows per lane octet in flight; the octet's partial dots meet by DPP.
+    constexpr int DP = HD / 8, U = 4;
+    const int c8 = tid & 7, slot = tid >> 3;
+    float mv[DP], vv[DP];
+#pragma unroll
+    for (int e = 0; e < DP; ++e) {
+      mv[e] = mu[DP * c8 + e];
+      vv[e] = v[DP * c8 + e];
+    }
+    for (int j0 = slot; j0 < n; j0 += U * (kThreads / 8)) {
+      v4u x[U][DP / 8];
+      int t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * (kThreads / 8);
+        t[u] = ids[j < n ? j : j0];
+#pragma unroll
+        for (int c = 0; c < DP / 8; ++c)
+          x[u][c] = *reinterpret_cast<const v4u*>(q + size_t(t[u]) * HD + DP * c8 + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < DP / 8; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int d = 8 * c + 2 * e;
+            a += (__uint_as_float(x[u][c][e] << 16) - mv[d]) * vv[d];
+            a += (__uint_as_float(x[u][c][e] & 0xffff0000u) - mv[d + 1]) * vv[d + 1];
+          }
+        a = row_sum8(a);
+        const int j = j0 + u * (kThreads / 8);
+        if (c8 == 0 && j < n) keys[j] = (uint64_t(ordered(a)) << 32) | uint32_t(t[u]);
       }
     }
-    keys[j] = (uint64_t(ordered(a)) << 32) | uint32_t(t);
+    __syncthreads();
   }
   // The left child is the k = floor(g/2) C smallest keys (keys are distinct: the
   // token is part of them).  Radix select of the k-th smallest key, 8 bits at a
@@ -726,11 +798,12 @@ extern "C" BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
     const int big = int(split_lds_bytes(kMaxTokens, 128));
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<64>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    if (attr == hipSuccess)
-      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<128>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, big);
+    for (const void* f : {reinterpret_cast<const void*>(&split_kernel<64, false>),
+                          reinterpret_cast<const void*>(&split_kernel<64, true>),
+                          reinterpret_cast<const void*>(&split_kernel<128, false>),
+                          reinterpret_cast<const void*>(&split_kernel<128, true>)})
+      if (attr == hipSuccess)
+        attr = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, big);
     for (const void* f : {reinterpret_cast<const void*>(&stats_kernel<64>),
                           reinterpret_cast<const void*>(&stats_kernel<128>)})
       if (attr == hipSuccess)
@@ -770,12 +843,10 @@ extern "C" BSA_API bsa_status bsa_query_groups(const void* q, int32_t B, int32_t
     }
     const size_t lds = split_lds_bytes(gmax * C, D);
     const int kw = split_key_words(gmax * C, D);
-    if (D == 64)
-      hipLaunchKernelGGL(split_kernel<64>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C, cur,
-                         P, kw, part, groups_out);
-    else
-      hipLaunchKernelGGL(split_kernel<128>, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C,
-                         cur, P, kw, part, groups_out);
+    auto* split = D == 64 ? (P > 1 ? split_kernel<64, true> : split_kernel<64, false>)
+                          : (P > 1 ? split_kernel<128, true> : split_kernel<128, false>);
+    hipLaunchKernelGGL(split, dim3(nodes, bh), dim3(kThreads), lds, s, qq, N, C, cur, P, kw, part,
+                       groups_out);
     BSA_HIP_CHECK_LAUNCH();
     NodeList nxt{};
     nxt.n = 0;
