@@ -707,7 +707,7 @@ __global__ __launch_bounds__(256) void token_mass_kernel(const uint16_t* __restr
 // Top-k tokens of one group's mass row (largest mass, ties to the lower token),
 // ascending: one workgroup per row.  Keys (~ordered(mass), token) are distinct and
 // ascend with the wanted order; thread tid holds the keys of tokens
-// [tid per, (tid + 1) per) in registers.  A radix select (8 bits at a time from
+// [tid per, (tid + 1) per) in registers.  A radix select (11 bits at a time from
 // the top) finds the k-th smallest key; the keys below it are the chosen tokens,
 // written in token order by a workgroup scan of the per-thread counts.
 constexpr int kSelPer = kMaxTokens / kThreads;  // keys per thread at most
@@ -715,7 +715,8 @@ constexpr int kSelPer = kMaxTokens / kThreads;  // keys per thread at most
 __global__ __launch_bounds__(kThreads) void select_tokens_kernel(const float* __restrict__ mass,
                                                                  int32_t N, int32_t k,
                                                                  int32_t* __restrict__ tokens) {
-  __shared__ int32_t hist[256], scan_sh[kThreads / 64], sel_sh[3];
+  constexpr int kBits = 11, kBins = 1 << kBits, kPerT = kBins / kThreads;
+  __shared__ int32_t hist[kBins], scan_sh[kThreads / 64], sel_sh[3];
   __shared__ uint64_t pivot_sh;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -723,34 +724,62 @@ __global__ __launch_bounds__(kThreads) void select_tokens_kernel(const float* __
   int32_t* out = tokens + size_t(row) * k;
   const int per = (N + kThreads - 1) / kThreads;
   const int jlo = min(tid * per, N), jhi = min(jlo + per, N);
-  uint64_t key[kSelPer];
+  // The high word of each key in registers; the low word is the token, jlo + u.
+  // Buffer loads (an out-of-range offset reads zero without touching memory) so
+  // that all of a thread's loads are in flight together.
+  const __amdgpu_buffer_rsrc_t mr = rsrc(m, static_cast<uint32_t>(N) * 4u);
+  uint32_t kh[kSelPer];
 #pragma unroll
   for (int u = 0; u < kSelPer; ++u) {
     const int j = jlo + u;
-    key[u] = (u < per && j < jhi) ? (uint64_t(~ordered(m[j])) << 32) | uint32_t(j) : ~0ull;
+    kh[u] = __builtin_amdgcn_raw_buffer_load_b32(
+        mr, static_cast<uint32_t>(u < per && j < jhi ? j : N) * 4u, 0, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their first use
+#pragma unroll
+  for (int u = 0; u < kSelPer; ++u)
+    kh[u] = u < per && jlo + u < jhi ? ~ordered(__uint_as_float(kh[u])) : ~0u;
   auto valid = [&](int u) { return u < per && jlo + u < jhi; };
+  auto keyof = [&](int u) { return (uint64_t(kh[u]) << 32) | uint32_t(jlo + u); };
   uint64_t pivot = ~0ull;  // k == N: every key is below no pivot; take them all
   if (k < N) {
+    // 11-bit digits from the top (bits [53, 64), [42, 53), ...): the first digit
+    // holds the mass's exponent and three mantissa bits, which spreads the LDS
+    // histogram's atomics over many more bins than a byte of exponent would.
     uint64_t prefix = 0, mask = 0;
     int want = k;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+    for (int top = 64; top > 0; top -= kBits) {
+      const int shift = top > kBits ? top - kBits : 0;
+      const uint32_t dmask = (1u << (top - shift)) - 1u;
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) hist[kPerT * tid + i] = 0;
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < kSelPer; ++u)
-        if (valid(u) && (key[u] & mask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255], 1);
+        if (valid(u) && (keyof(u) & mask) == prefix)
+          atomicAdd(&hist[uint32_t(keyof(u) >> shift) & dmask], 1);
       __syncthreads();
-      const int cnt = hist[tid];
-      const int excl = block_excl_scan(cnt, scan_sh);
+      int c[kPerT], cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) {
+        c[i] = hist[kPerT * tid + i];
+        cnt += c[i];
+      }
+      int excl = block_excl_scan(cnt, scan_sh);
       if (excl <= want && want < excl + cnt) {
-        sel_sh[0] = tid;
-        sel_sh[1] = want - excl;
-        sel_sh[2] = cnt;
+#pragma unroll
+        for (int i = 0; i < kPerT; ++i) {
+          if (excl <= want && want < excl + c[i]) {
+            sel_sh[0] = kPerT * tid + i;
+            sel_sh[1] = want - excl;
+            sel_sh[2] = c[i];
+          }
+          excl += c[i];
+        }
       }
       __syncthreads();
       prefix |= uint64_t(sel_sh[0]) << shift;
-      mask |= uint64_t(255) << shift;
+      mask |= uint64_t(dmask) << shift;
       want = sel_sh[1];
       const int left = sel_sh[2];
       __syncthreads();
@@ -758,17 +787,17 @@ __global__ __launch_bounds__(kThreads) void select_tokens_kernel(const float* __
     }
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u)
-      if (valid(u) && (key[u] & mask) == prefix) pivot_sh = key[u];
+      if (valid(u) && (keyof(u) & mask) == prefix) pivot_sh = keyof(u);
     __syncthreads();
     pivot = pivot_sh;
   }
   int nl = 0;
 #pragma unroll
-  for (int u = 0; u < kSelPer; ++u) nl += (valid(u) && (k >= N || key[u] < pivot)) ? 1 : 0;
+  for (int u = 0; u < kSelPer; ++u) nl += (valid(u) && (k >= N || keyof(u) < pivot)) ? 1 : 0;
   int pos = block_excl_scan(nl, scan_sh);
 #pragma unroll
   for (int u = 0; u < kSelPer; ++u)
-    if (valid(u) && (k >= N || key[u] < pivot)) out[pos++] = jlo + u;
+    if (valid(u) && (k >= N || keyof(u) < pivot)) out[pos++] = jlo + u;
 }
 
 }  // namespace
