@@ -185,6 +185,21 @@ __global__ __launch_bounds__(256) void select_kernel(
       prior ? prior + (prior_per_head ? size_t(bh) * nb * nb : size_t(0)) + size_t(i) * nb
             : nullptr;
   const float* srow = S ? S + (size_t(bh) * nb + i) * nb : nullptr;
+  // The row's prior bytes and scores, every load in flight at once: buffer loads
+  // past the row (or from an absent prior or score matrix, a zero-size range)
+  // read zero without touching memory.
+  const __amdgpu_buffer_rsrc_t prr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(pr), static_cast<short>(0), pr ? nb : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(srow), static_cast<short>(0), srow ? nb * 4 : 0, 0x00020000);
+  uint32_t pv[CM], sv[CM];
+#pragma unroll
+  for (int c = 0; c < CM; ++c) {
+    const uint32_t j = static_cast<uint32_t>(min(lane + 64 * c, nb));
+    pv[c] = __builtin_amdgcn_raw_buffer_load_b8(prr, j, 0, 0);
+    sv[c] = __builtin_amdgcn_raw_buffer_load_b32(sr, j * 4u, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their first use
   const int nnz = row_ptr[n_rows];
   const int start = row_ptr[r];
   const int cnt = row_ptr[r + 1] - start;
@@ -199,11 +214,11 @@ __global__ __launch_bounds__(256) void select_kernel(
 #pragma unroll
   for (int c = 0; c < CM; ++c) {
     const int j = lane + 64 * c;
-    const bool in = j < nb && ((pr && pr[j]) || (force_diag && j == i));
+    const bool in = j < nb && (pv[c] != 0 || (force_diag && j == i));
     insel[c] = in;
     chosen[c] = false;
     key[c] = (j < nb && !in && srow)
-                 ? ((uint64_t(ordered_bits(srow[j])) << 32) | (0xffffffffu - uint32_t(j)))
+                 ? ((uint64_t(ordered_bits(__uint_as_float(sv[c]))) << 32) | (0xffffffffu - uint32_t(j)))
                  : 0ull;
     nsel += __popcll(__ballot(in));
   }
