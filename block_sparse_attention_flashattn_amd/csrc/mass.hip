@@ -141,23 +141,28 @@ __global__ __launch_bounds__(256) void mass_kernel(const uint16_t* __restrict__ 
   }
 }
 
-// One thread per CSR row: the mass of its listed blocks, in list order.
+// One wavefront per CSR row: the mass of its listed blocks (each lane sums every
+// 64th entry of the row, then the lanes' sums are added by shuffles), so a row's
+// column and mass loads are all in flight at once.
 __global__ __launch_bounds__(256) void csr_mass_kernel(const float* __restrict__ mass,
                                                        int32_t n_rows, int32_t nb,
                                                        const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ col_idx,
                                                        float* __restrict__ out) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_rows) return;
   const int nnz = row_ptr[n_rows];
   const int b = min(max(row_ptr[r], 0), nnz);
   const int e = min(max(row_ptr[r + 1], b), nnz);
   float s = 0.f;
-  for (int c = b; c < e; ++c) {
+  for (int c = b + lane; c < e; c += 64) {
     const int j = col_idx[c];
     if (j >= 0 && j < nb) s += mass[size_t(r) * nb + j];
   }
-  out[r] = s;
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d);
+  if (lane == 0) out[r] = s;
 }
 
 template <int BLK, int HD>
@@ -205,7 +210,7 @@ extern "C" BSA_API bsa_status bsa_csr_mass(const float* mass, int32_t n_rows, in
                                            const int32_t* row_ptr, const int32_t* col_idx,
                                            float* out, void* stream) {
   if (!mass || !row_ptr || !col_idx || !out || n_rows < 1 || nb < 1) return BSA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(bsa::csr_mass_kernel, dim3((n_rows + 255) / 256), dim3(256), 0,
+  hipLaunchKernelGGL(bsa::csr_mass_kernel, dim3((n_rows + 3) / 4), dim3(256), 0,
                      static_cast<hipStream_t>(stream), mass, n_rows, nb, row_ptr, col_idx, out);
   BSA_HIP_CHECK_LAUNCH();
   return BSA_OK;
