@@ -653,8 +653,12 @@ __global__ __launch_bounds__(256) void token_mass_kernel(const uint16_t* __restr
   const uint32_t hbytes = static_cast<uint32_t>(N) * HD * 2u;
   const __amdgpu_buffer_rsrc_t qr = rsrc(Q + head, hbytes);
   const __amdgpu_buffer_rsrc_t kr = rsrc(K + head, hbytes);
+  // Each lane loads its own query's row fragments and LSE (one index load and
+  // one LSE load per slice, all in flight together); the LSEs of the queries a
+  // lane's accumulator rows hold then come from the lanes that loaded them.
   bf16x8 qf[QS][NC];
   float lq[QS][16];
+  float lown[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s) {
     const int t = ids[32 * s + kl];
@@ -662,13 +666,13 @@ __global__ __launch_bounds__(256) void token_mass_kernel(const uint16_t* __restr
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       qf[s][c] = load16(qr, ok ? static_cast<uint32_t>(t * HD + 16 * c + 8 * hh) * 2u : hbytes);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int te = ids[32 * s + 8 * (e >> 2) + 4 * hh + (e & 3)];
-      const float l = (te >= 0 && te < N) ? lse[size_t(bh) * N + te] : -INFINITY;
-      lq[s][e] = (l > -INFINITY && l < INFINITY) ? l * 1.4426950408889634f : INFINITY;
-    }
+    const float l = ok ? lse[size_t(bh) * N + t] : -INFINITY;
+    lown[s] = (l > -INFINITY && l < INFINITY) ? l * 1.4426950408889634f : INFINITY;
   }
+#pragma unroll
+  for (int s = 0; s < QS; ++s)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lq[s][e] = __shfl(lown[s], 8 * (e >> 2) + 4 * hh + (e & 3));
   // Key tiles blockIdx.y, blockIdx.y + gridDim.y, ...: the group's query
   // fragments and LSEs stay in registers; the next tile's K rows are in flight
   // while this one is used.
@@ -679,11 +683,16 @@ __global__ __launch_bounds__(256) void token_mass_kernel(const uint16_t* __restr
     for (int c = 0; c < NC; ++c)
       kf[c] = load16(kr, key < N ? static_cast<uint32_t>(key * HD + 16 * c + 8 * hh) * 2u : hbytes);
   };
+  // No branch around the prefetch or the store: tiles past the end read zeros
+  // (out-of-range offsets) and the dropped lanes store past the row's end, so the
+  // waits for this tile's K never also wait for the next tile's loads.
+  const __amdgpu_buffer_rsrc_t mrow =
+      rsrc(mass + size_t(row) * N, static_cast<uint32_t>(N) * 4u);
   bf16x8 kf[NC], kn[NC];
   int kt = blockIdx.y;
-  if (kt < n_tiles) fetch(kt, kf);
+  fetch(kt, kf);
   for (; kt < n_tiles; kt += gridDim.y) {
-    if (kt + int(gridDim.y) < n_tiles) fetch(kt + gridDim.y, kn);
+    fetch(kt + gridDim.y, kn);
     float acc = 0.f;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
@@ -698,7 +707,9 @@ __global__ __launch_bounds__(256) void token_mass_kernel(const uint16_t* __restr
                                                      false, false);
     const float other = __uint_as_float(hh ? sw[0] : sw[1]);
     const int key = kt * 128 + 32 * wave + kl;
-    if (hh == 0 && key < N) mass[size_t(row) * N + key] = acc + other;
+    __builtin_amdgcn_raw_buffer_store_b32(
+        __float_as_uint(acc + other), mrow,
+        static_cast<uint32_t>(hh == 0 && key < N ? key : N) * 4u, 0, 0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) kf[c] = kn[c];
   }
