@@ -921,9 +921,14 @@ extern "C" BSA_API bsa_status bsa_token_mass(const void* q, const void* k, const
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
   const float sl2 = sc * 1.4426950408889634f;
   const int32_t G = N / C;
-  // Four key-tile slices per group: the group's queries are gathered once per
-  // workgroup and reused over a quarter of the keys.
-  const dim3 grid(B * H * G, std::min(4, (N + 127) / 128));
+  // Key-tile slices per group: the group's queries are gathered once per
+  // workgroup and reused over its slice of the keys.  About 6144 workgroups in
+  // all (t2i, 3168 groups: two slices) balance that gather against filling the
+  // chip; at most four slices.
+  const int64_t n_groups = int64_t(B) * H * G;
+  const int64_t slices = std::min<int64_t>(std::min(4, (N + 127) / 128),
+                                           std::max<int64_t>(1, (6144 + n_groups / 2) / n_groups));
+  const dim3 grid(static_cast<uint32_t>(n_groups), static_cast<uint32_t>(slices));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);

@@ -217,3 +217,29 @@ def test_gather_forward_rejects_unsupported():
     q64 = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         bsa.gather_forward(q64, q64, q64, g[..., :32].contiguous(), t)
+
+
+def test_token_mass_t2i_sampled_heads():
+    """The t2i workload at full size (B2 H24 N4224 D64, 66 groups of 64 per head, the
+    launch that splits each group's keys into two slices), seeded random groups, the LSE
+    of the dense forward; the oracle on two heads (a head's masses depend on that head
+    only), and every group's masses sum to its query count."""
+    bsa = need_gpu()
+    w = W.make("t2i")
+    q, k, _ = w.tensors()
+    qd, kd = q.cuda(), k.cuda()
+    B, H, N, C = w.B, w.H, w.N, 64
+    G = N // C
+    rng = np.random.default_rng(4224)
+    groups = np.stack([np.sort(rng.permutation(N).reshape(G, C), axis=-1)
+                       for _ in range(B * H)]).reshape(B, H, G, C).astype(np.int32)
+    lse = dense_lse(bsa, qd, kd, 64)
+    mass = bsa.token_mass(qd, kd, lse, torch.from_numpy(groups).cuda())
+    torch.cuda.synchronize()
+    got = mass.cpu().numpy().astype(np.float64)
+    for b, h in ((0, 3), (1, 20)):
+        want = OT.token_mass(q[b, h], k[b, h], groups[b, h], 1.0 / np.sqrt(w.D))
+        err = np.abs(got[b, h] - want)
+        print(f"head ({b},{h}): max abs {err.max():.3e}", flush=True)
+        assert np.all(err <= 2e-4 * want + 1e-6), err.max()
+    np.testing.assert_allclose(got.sum(-1), C, rtol=2e-4)
