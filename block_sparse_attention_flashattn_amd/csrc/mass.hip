@@ -82,19 +82,31 @@ __global__ __launch_bounds__(256) void mass_kernel(const uint16_t* __restrict__ 
     lq[g] = (l > -INFINITY && l < INFINITY) ? l * 1.4426950408889634f : INFINITY;
   }
 
+  // The next step's K rows are requested before this step computes; steps past
+  // the workgroup's blocks read zeros (out-of-range offsets), so no load sits
+  // behind a branch and its own wait.
+  auto fetch = [&](int t, bf16x8* dst) {
+    const int jj = t * JPS + jsub;
+    const int kbase = (j0 + jj) * BLK + 32 * kg;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      dst[c] = load16(kr, t < NS && jj < jn
+                              ? static_cast<uint32_t>((kbase + ql) * HD + 16 * c + 8 * hh) * 2u
+                              : hbytes);
+  };
+  bf16x8 kbuf[2][NC];
+  fetch(0, kbuf[0]);
   float part[QB][NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
+    fetch(t + 1, kbuf[(t + 1) & 1]);
 #pragma unroll
     for (int b = 0; b < QB; ++b) part[b][t] = 0.f;
     const int jj = t * JPS + jsub;
     if (jj < jn) {
       const int j = j0 + jj;
       const int kbase = j * BLK + 32 * kg;
-      bf16x8 kf[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        kf[c] = load16(kr, static_cast<uint32_t>((kbase + ql) * HD + 16 * c + 8 * hh) * 2u);
+      const bf16x8* kf = kbuf[t & 1];
       const bool full = kbase + 32 <= N;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
