@@ -18,12 +18,15 @@ __device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
 // Issued as inline assembly so that the compiler's wait-count bookkeeping,
 // which cannot tell LDS ring stages apart, does not drain the ring before
 // every LDS read; the waits for these loads are the explicit vmcnt below.
-// M0 (the LDS destination) is saved and restored inside the statement.
+// M0 (the LDS destination) is saved and restored inside the statement; an
+// LDS-DMA load needs one wait state after the SALU write of M0 (the compiler
+// does not insert it for inline assembly), hence the s_nop.
 __device__ __forceinline__ void dma16(v4i desc, uint32_t voff, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)

@@ -782,7 +782,13 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
   // with M = max_c m_c, O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c and
   // LSE = (M + log2 L) ln 2.  Lane (ql, hh) owns query 32 kh + ql, columns
   // 32 hh .. +31.  Returns the number of stores issued.
+  //
+  // Ordering: a chunk's partial stores use the device-coherent cache policy
+  // and complete (vmcnt) before its relaxed count-in, which is the release
+  // side; the wave whose count-in completes the row acquires (agent scope)
+  // before it reads the other chunks' partials.
   auto merge_group = [&](int m) -> int {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (lane == 0)
       __hip_atomic_store(mctr + 2 * m + kh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int r = ld_uniform(merges, 3 * size_t(m));
@@ -1750,3 +1756,4 @@ extern "C" BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, c
   BSA_HIP_CHECK_LAUNCH();
   return BSA_OK;
 }
+
