@@ -33,7 +33,7 @@ __all__ = [
     "forward_workspace_bytes", "build_mask", "build_mask_status", "schedule", "forward",
     "block_mass", "select_by_mass", "csr_mass", "block_oracle", "residual", "compensate",
     "AnchorReuse", "query_groups", "token_mass", "select_tokens", "gather_forward",
-    "backward", "backward_workspace_bytes",
+    "backward", "backward_workspace_bytes", "forward_noalloc", "FORWARD_NOALLOC_MAX_BYTES",
     "Plan", "Work", "n_blocks", "default_max_tiles",
 ]
 
@@ -59,6 +59,8 @@ _SIGS = {
     "bsa_forward_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "bsa_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                            _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "bsa_forward_noalloc": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                   _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "bsa_block_mass": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
     "bsa_select_by_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "bsa_csr_mass": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -77,7 +79,7 @@ _SIGS = {
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class BsaError(RuntimeError):
@@ -421,6 +423,32 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx,
                            _t_ptr(lse) if return_lse else None, _t_ptr(ws), wsb,
                            _stream_ptr(dev)), "bsa_forward")
     return out, (lse if return_lse else None)
+
+
+# Workspace bytes bsa_forward_noalloc serves (BSA_FORWARD_NOALLOC_MAX_BYTES in bsa.h).
+FORWARD_NOALLOC_MAX_BYTES = 16 << 20
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                    col_idx: torch.Tensor, block: int, out: torch.Tensor, lse: Optional[torch.Tensor],
+                    scale: Optional[float] = None, work: Optional["Work"] = None):
+    """bsa_forward_noalloc: the forward without a caller workspace (the library's static
+    device array serves a work list's counters and partials).  Every argument must already
+    be on the device: this wrapper converts and allocates nothing, it only passes pointers."""
+    B, H, N, D = _check_qkv(q, k, v)
+    for t in (row_ptr, col_idx) + (() if work is None else (work.work,)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("row_ptr, col_idx and the work list must be int32 device tensors")
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    s = -1.0 if scale is None else float(scale)
+    wp, ni, nm, ns = (None, 0, 0, 0) if work is None else (
+        _t_ptr(work.work), work.n_items, work.n_merges, work.n_slots)
+    _check(lib.bsa_forward_noalloc(_t_ptr(q), _t_ptr(k), _t_ptr(v), B, H, N, D, block,
+                                   _t_ptr(row_ptr), _t_ptr(col_idx), wp, ni, nm, ns, s,
+                                   _t_ptr(out), _t_ptr(lse), _stream_ptr(q.device)),
+           "bsa_forward_noalloc")
+    return out, lse
 
 
 def block_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, block: int,

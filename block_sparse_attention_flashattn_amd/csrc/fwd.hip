@@ -1757,3 +1757,79 @@ extern "C" BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, c
   return BSA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the work-list workspace lives in a static device
+// array instead of a caller buffer.
+namespace bsa {
+namespace {
+
+// Largest workspace bsa_forward_noalloc serves: the item counters (256 KiB),
+// the merge counters and the partial results of cut rows.
+constexpr size_t kNoAllocScratchBytes = BSA_FORWARD_NOALLOC_MAX_BYTES;
+static_assert(kNoAllocScratchBytes == (size_t(16) << 20), "header and library agree");
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` per device, taken once per device with that
+// device current (the host-side name of the array is not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+bsa_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return BSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
+// Zeroes the item counters (one per group, kCounterStride apart) and the
+// merge counters that follow them.
+__global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* __restrict__ ctr,
+                                                             int32_t n_merge_ints) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < BSA_MAX_GROUPS) ctr[size_t(t) * kCounterStride] = 0;
+  int32_t* mctr = ctr + kCounterBytes / sizeof(int32_t);
+  if (t < n_merge_ints) mctr[t] = 0;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" BSA_API bsa_status bsa_forward_noalloc(const void* q, const void* k, const void* v,
+                                                  int32_t B, int32_t H, int32_t N, int32_t D,
+                                                  int32_t block, const int32_t* row_ptr_dev,
+                                                  const int32_t* col_idx_dev,
+                                                  const int32_t* work_dev, int32_t n_items,
+                                                  int32_t n_merges, int32_t n_slots, float scale,
+                                                  void* o, float* lse, void* stream) {
+  using namespace bsa;
+  if (!work_dev)
+    return bsa_forward(q, k, v, B, H, N, D, block, row_ptr_dev, col_idx_dev, nullptr, 0, 0, 0,
+                       scale, o, lse, nullptr, 0, stream);
+  if (n_slots < 0 || D < 1 || block < 1) return BSA_ERR_INVALID_ARG;
+  const size_t need = bsa_forward_workspace_bytes(n_slots, D, block);
+  if (need == 0 || need > kNoAllocScratchBytes) return BSA_ERR_CAPACITY;
+  // Argument checks before anything is enqueued (bsa_forward repeats them).
+  if (!q || !k || !v || !o || !row_ptr_dev || !col_idx_dev) return BSA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || n_items < 0 || n_merges < 0) return BSA_ERR_INVALID_ARG;
+  if (!supported_shape(D, block)) return BSA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const bsa_status st = scratch_of_current_device(&ws);
+  if (st != BSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t n_merge_ints = static_cast<int32_t>(merge_counter_bytes(n_slots) / sizeof(int32_t));
+  const int32_t n_clear = n_merge_ints > BSA_MAX_GROUPS ? n_merge_ints : BSA_MAX_GROUPS;
+  hipLaunchKernelGGL(clear_counters_kernel, dim3((n_clear + 255) / 256), dim3(256), 0, s,
+                     static_cast<int32_t*>(ws), n_merge_ints);
+  BSA_HIP_CHECK_LAUNCH();
+  return bsa_forward(q, k, v, B, H, N, D, block, row_ptr_dev, col_idx_dev, work_dev, n_items,
+                     n_merges, n_slots, scale, o, lse, ws, kNoAllocScratchBytes, stream);
+}

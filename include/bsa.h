@@ -21,7 +21,8 @@
  *   - Supported: D in {64, 128}, b in {64, 128}, 1 <= N, nb <= 1024.
  *   - Ownership: the caller allocates every buffer (device buffers with
  *     hipMalloc or torch, host buffers anywhere); the library allocates no
- *     memory and keeps no state.  Device work is enqueued on `stream`
+ *     memory and keeps no state (bsa_forward_noalloc aside: its static device
+ *     array and that array's address per device).  Device work is enqueued on `stream`
  *     (a hipStream_t passed as void*; NULL = the null stream) and is
  *     asynchronous: the library never synchronises.
  *   - Errors: every entry point returns a bsa_status; invalid arguments are
@@ -51,7 +52,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 9
+#define BSA_ABI_VERSION 10
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -251,6 +252,32 @@ BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v, int3
                                const int32_t* work_dev, int32_t n_items, int32_t n_merges,
                                int32_t n_slots, float scale, void* o, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and arguments as bsa_forward, without the workspace.  With
+ * a work list, the workspace bsa_forward would take (item and merge counters,
+ * partial results of cut rows) lives in a static device array of
+ * BSA_FORWARD_NOALLOC_MAX_BYTES that each GPU the library runs on holds until
+ * the process ends; its device address is taken once per device, on the
+ * first call with that device current.  Every call first clears the counters
+ * (a small kernel on `stream`, no memset), then runs bsa_forward on it.
+ * Calls on one GPU share the array: calls that may overlap (different
+ * streams without ordering) race and must not be issued.  Without a work
+ * list no workspace is used at all.  Nothing is allocated, no library routine
+ * that allocates is called.
+ * Errors: those of bsa_forward; CAPACITY when bsa_forward_workspace_bytes(
+ * n_slots, D, block) exceeds BSA_FORWARD_NOALLOC_MAX_BYTES; HIP if the array's
+ * address cannot be taken.
+ */
+#define BSA_FORWARD_NOALLOC_MAX_BYTES (16u << 20)
+BSA_API bsa_status bsa_forward_noalloc(const void* q, const void* k, const void* v, int32_t B,
+                                       int32_t H, int32_t N, int32_t D, int32_t block,
+                                       const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
+                                       const int32_t* work_dev, int32_t n_items,
+                                       int32_t n_merges, int32_t n_slots, float scale, void* o,
+                                       float* lse, void* stream);
 
 /*
  * Exact attention mass per block pair (device, async): the second pass of
