@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: block-sparse attention on the text-to-image workload, one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload t2i] [--no-cpu] [--extra]
+    python bench.py [--steps K] [--warmup W] [--workload t2i] [--no-cpu] [--no-extra]
 
 Workload (default "t2i"): batch 2, 24 heads, N = 4224 (128 text + 4096 image
 tokens), head_dim 64, block 64, static modality prior (text dense, image
@@ -81,12 +81,101 @@ def traffic_for(fwd_sha):
 
 def cpu_baseline(w, q, k, v, row_ptr, col_idx, budget_s=10.0):
     """Time the fp64 oracle head by head until `budget_s` seconds of CPU work are spent."""
-    from oracle import attention as OA
     try:
         from threadpoolctl import threadpool_info
         threads = max([i["num_threads"] for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = os.cpu_count() or 1
+    heads, flops, dt = oracle_seconds(w, q, k, v, row_ptr, col_idx, budget_s)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{heads} of {w.B * w.H} heads (all {w.nb} query blocks each) of the {w.name} "
+                      f"workload, fp64 numpy masked softmax, {dt:.1f} s"}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def graph_ms(fn, reps, stream):
+    """Mean time of one call among `reps` back-to-back calls captured in one HIP graph
+    (HIP events on `stream` around the replay; one untimed replay uploads the graph)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def linear_fit(x, y):
+    """Least-squares t = intercept + slope * x, with R^2."""
+    x, y = np.asarray(x, float), np.asarray(y, float)
+    slope, icpt = np.polyfit(x, y, 1)
+    ss = np.sum((y - y.mean()) ** 2)
+    r2 = 1.0 - np.sum((y - (slope * x + icpt)) ** 2) / ss if ss > 0 else 1.0
+    return float(slope), float(icpt), float(r2)
+
+
+def sample_clock_mhz(keep_busy, seconds=1.5):
+    """Shader clock while `keep_busy()` (a graph replay loop) runs: the current level of
+    /sys/class/drm/card*/device/pp_dpm_sclk, sampled from a second thread.  Returns
+    {"samples", "mean_mhz", "min_mhz", "max_mhz", "source"} or None when unreadable."""
+    import glob
+    import re
+    import threading
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return None
+    vals, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            for p in paths:
+                try:
+                    with open(p) as f:
+                        for line in f:
+                            if line.rstrip().endswith("*"):
+                                m = re.search(r"(\d+)\s*[Mm]hz", line)
+                                if m:
+                                    vals.append(int(m.group(1)))
+                except OSError:
+                    pass
+            time.sleep(0.005)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        keep_busy()
+    stop.set()
+    th.join()
+    if not vals:
+        return None
+    busy = [v for v in vals if v > 0]
+    return {"samples": len(vals), "mean_mhz": float(np.mean(busy)), "min_mhz": int(min(busy)),
+            "max_mhz": int(max(busy)), "source": "pp_dpm_sclk current level"}
+
+
+def oracle_seconds(w, q, k, v, row_ptr, col_idx, budget_s):
+    """fp64 oracle over whole heads of workload w until `budget_s` elapsed:
+    (heads done, active FLOPs done, seconds)."""
+    from oracle import attention as OA
     q64, k64, v64 = (x.float().numpy().astype(np.float64) for x in (q, k, v))
     nb = w.nb
     heads, flops, t0 = 0, 0.0, time.perf_counter()
@@ -97,11 +186,7 @@ def cpu_baseline(w, q, k, v, row_ptr, col_idx, budget_s=10.0):
         sub_rp = row_ptr[heads * nb:(heads + 1) * nb + 1] - lo
         flops += active_flops(sub_rp, col_idx[lo:hi], w.N, w.D, w.block, nb)
         heads += 1
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads (all {nb} query blocks each) of the {w.name} "
-                      f"workload, fp64 numpy masked softmax, {dt:.1f} s"}
+    return heads, flops, time.perf_counter() - t0
 
 
 def main():
@@ -112,8 +197,8 @@ def main():
     ap.add_argument("--workload", default="t2i")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--extra", action="store_true",
-                    help="also time the all-ones (dense) CSR and a density sweep")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the metric, its roofline and the CPU baseline (for profiling runs)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run 10 device-to-device copies of this many MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a copy of known size) and exit")
@@ -255,125 +340,178 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "cu_count": torch.cuda.get_device_properties(0).multi_processor_count,
     }
-    # Exact block selection at this workload's density (two passes: dense LSE, then the
-    # block mass; the block oracle keeps the most mass per row), timed per kernel, and
-    # the mass and output error of this workload's CSR against it.
-    rp_all = torch.arange(n_rows + 1, dtype=torch.int32, device=dev) * nb
-    ci_all = torch.arange(nb, dtype=torch.int32, device=dev).repeat(n_rows)
-    o_dense = torch.empty_like(qd)
-    lse_dense = torch.empty_like(lse)
-    dense_once_ms = time_launches(lambda: bsa.forward(qd, kd, vd, rp_all, ci_all, w.block,
-                                                      out=o_dense, lse=lse_dense), n=5)
-    mass = bsa.block_mass(qd, kd, lse_dense, w.block)
-    mass_ms = time_launches(lambda: bsa.block_mass(qd, kd, lse_dense, w.block), n=10)
-    ci_or = bsa.select_by_mass(mass, plan.row_ptr)
-    select_ms = time_launches(lambda: bsa.select_by_mass(mass, plan.row_ptr, check=False,
-                                                                  nnz=plan.nnz), n=10)
-    kept_csr = bsa.csr_mass(mass, plan.row_ptr, col_idx[:plan.nnz]).double().sum().item()
-    kept_or = bsa.csr_mass(mass, plan.row_ptr, ci_or).double().sum().item()
-    o_or = torch.empty_like(qd)
-    bsa.forward(qd, kd, vd, plan.row_ptr, ci_or, w.block, out=o_or, lse=None, return_lse=False)
-    bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, work=plan, out=o, lse=lse)
-    torch.cuda.synchronize()
-    n_q = w.B * w.H * w.N
-    def rel_err(a):
-        d = (a.float() - o_dense.float()).norm().item()
-        return d / max(o_dense.float().norm().item(), 1e-30)
-    mass_flops = 2.0 * w.B * w.H * float(w.N) * float(w.N) * w.D   # the QK^T products
-    extra["block_oracle"] = {
-        "dense_forward_ms": dense_once_ms, "block_mass_ms": mass_ms, "select_ms": select_ms,
-        "block_mass_tflops": mass_flops / (mass_ms * 1e-3) / 1e12,
-        "block_mass_scores_per_ns": w.B * w.H * float(w.N) ** 2 / (mass_ms * 1e6),
-        "mean_kept_mass_csr": kept_csr / n_q, "mean_kept_mass_oracle": kept_or / n_q,
-        "rel_err_vs_dense_csr": rel_err(o), "rel_err_vs_dense_oracle": rel_err(o_or),
-    }
-
-    # Residual compensation at reuse steps: the two elementwise passes (memory-bound: two
-    # bf16 reads and one bf16 write per element) and the anchor and reuse steps.
-    r_buf = torch.empty_like(qd)
-    n_el = o.numel()
-    res_ms = time_launches(lambda: bsa.residual(o_dense, o, out=r_buf), n=20)
-    o_c = torch.empty_like(qd)
-    comp_ms = time_launches(lambda: bsa.compensate(o, r_buf, out=o_c), n=20)
-    ar = bsa.AnchorReuse(w.block)
-    anchor_ms = time_launches(lambda: ar.anchor(qd, kd, vd, plan.row_ptr, col_idx, work=plan), n=5)
-    reuse_ms = time_launches(lambda: ar.reuse(qd, kd, vd, out=o_c), n=20)
-    extra["residual_compensation"] = {
-        "residual_ms": res_ms, "compensate_ms": comp_ms,
-        "compensate_gbps": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9,
-        "compensate_frac_of_hbm_peak": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "anchor_step_ms": anchor_ms, "reuse_step_ms": reuse_ms,
-    }
-
-    # Token-level selection at the same density: tile-aligned query groups of 64, token
-    # mass per group from the dense LSE, the top T tokens per group, and the gathered
-    # forward; the kept mass and the output error next to the block CSR's.
-    if w.D == 64 and w.N % 64 == 0:
-        T = int(round(plan.nnz / (n_rows * nb) * w.N))
-        groups = bsa.query_groups(qd, 64)
-        grp_ms = time_launches(lambda: bsa.query_groups(qd, 64), n=5)
-        tmass = bsa.token_mass(qd, kd, lse_dense, groups)
-        tmass_ms = time_launches(lambda: bsa.token_mass(qd, kd, lse_dense, groups), n=10)
-        toks = bsa.select_tokens(tmass, T)
-        sel_tok_ms = time_launches(lambda: bsa.select_tokens(tmass, T), n=10)
-        o_g = torch.zeros_like(qd)
-        bsa.gather_forward(qd, kd, vd, groups, toks, out=o_g, return_lse=False)
-        gather_ms = time_launches(lambda: bsa.gather_forward(qd, kd, vd, groups, toks, out=o_g,
-                                                             return_lse=False), n=20)
-        kept_tok = torch.gather(tmass, 3, toks.long()).double().sum().item()
-        n_groups = groups.shape[0] * groups.shape[1] * groups.shape[2]
-        gather_flops = 4.0 * n_groups * 64 * T * w.D
-        extra["token_selection"] = {
-            "tokens_per_group": T, "groups": n_groups,
-            "query_groups_ms": grp_ms, "token_mass_ms": tmass_ms, "select_tokens_ms": sel_tok_ms,
-            "gather_forward_ms": gather_ms,
-            "gather_forward_tflops": gather_flops / (gather_ms * 1e-3) / 1e12,
-            "mean_kept_mass_tokens": kept_tok / n_q, "mean_kept_mass_csr": kept_csr / n_q,
-            "rel_err_vs_dense_tokens": rel_err(o_g), "rel_err_vs_dense_csr": rel_err(o),
+    if not args.no_extra:
+        # Exact block selection at this workload's density (two passes: dense LSE, then the
+        # block mass; the block oracle keeps the most mass per row), timed per kernel, and
+        # the mass and output error of this workload's CSR against it.
+        rp_all = torch.arange(n_rows + 1, dtype=torch.int32, device=dev) * nb
+        ci_all = torch.arange(nb, dtype=torch.int32, device=dev).repeat(n_rows)
+        o_dense = torch.empty_like(qd)
+        lse_dense = torch.empty_like(lse)
+        dense_once_ms = time_launches(lambda: bsa.forward(qd, kd, vd, rp_all, ci_all, w.block,
+                                                          out=o_dense, lse=lse_dense), n=5)
+        mass = bsa.block_mass(qd, kd, lse_dense, w.block)
+        mass_ms = time_launches(lambda: bsa.block_mass(qd, kd, lse_dense, w.block), n=10)
+        ci_or = bsa.select_by_mass(mass, plan.row_ptr)
+        select_ms = time_launches(lambda: bsa.select_by_mass(mass, plan.row_ptr, check=False,
+                                                                      nnz=plan.nnz), n=10)
+        kept_csr = bsa.csr_mass(mass, plan.row_ptr, col_idx[:plan.nnz]).double().sum().item()
+        kept_or = bsa.csr_mass(mass, plan.row_ptr, ci_or).double().sum().item()
+        o_or = torch.empty_like(qd)
+        bsa.forward(qd, kd, vd, plan.row_ptr, ci_or, w.block, out=o_or, lse=None, return_lse=False)
+        bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, work=plan, out=o, lse=lse)
+        torch.cuda.synchronize()
+        n_q = w.B * w.H * w.N
+        def rel_err(a):
+            d = (a.float() - o_dense.float()).norm().item()
+            return d / max(o_dense.float().norm().item(), 1e-30)
+        mass_flops = 2.0 * w.B * w.H * float(w.N) * float(w.N) * w.D   # the QK^T products
+        extra["block_oracle"] = {
+            "dense_forward_ms": dense_once_ms, "block_mass_ms": mass_ms, "select_ms": select_ms,
+            "block_mass_tflops": mass_flops / (mass_ms * 1e-3) / 1e12,
+            "block_mass_scores_per_ns": w.B * w.H * float(w.N) ** 2 / (mass_ms * 1e6),
+            "mean_kept_mass_csr": kept_csr / n_q, "mean_kept_mass_oracle": kept_or / n_q,
+            "rel_err_vs_dense_csr": rel_err(o), "rel_err_vs_dense_oracle": rel_err(o_or),
         }
 
-    # Backward over the same CSR (block 64, D 64): dQ, dK, dV from the forward's O and LSE
-    # for a seeded N(0,1) incoming gradient; 10 * q_valid * k_valid * D FLOPs per active
-    # pair (the five products S, dP, dV, dS K, dS^T Q), all four launches in the timing.
-    if w.D == 64 and w.block == 64:
-        g = torch.Generator("cpu").manual_seed(1000 + w.N)
-        do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
-        bws = torch.empty(max(bsa.backward_workspace_bytes(w.B, w.H, w.N, w.block, plan.nnz),
-                              256), dtype=torch.uint8, device=dev)
-        bsa.backward(qd, kd, vd, o, lse, do, plan.row_ptr, col_idx[:plan.nnz], w.block,
-                     workspace=bws)
-        bwd_ms = time_launches(lambda: bsa.backward(qd, kd, vd, o, lse, do, plan.row_ptr,
-                                                    col_idx[:plan.nnz], w.block,
-                                                    workspace=bws), n=20)
-        bwd_flops = 2.5 * flops
-        extra["backward"] = {
-            "backward_ms": bwd_ms, "active_gflop": bwd_flops / 1e9,
-            "tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
-            "frac_of_bf16_peak": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        # Residual compensation at reuse steps: the two elementwise passes (memory-bound: two
+        # bf16 reads and one bf16 write per element) and the anchor and reuse steps.
+        r_buf = torch.empty_like(qd)
+        n_el = o.numel()
+        res_ms = time_launches(lambda: bsa.residual(o_dense, o, out=r_buf), n=20)
+        o_c = torch.empty_like(qd)
+        comp_ms = time_launches(lambda: bsa.compensate(o, r_buf, out=o_c), n=20)
+        ar = bsa.AnchorReuse(w.block)
+        anchor_ms = time_launches(lambda: ar.anchor(qd, kd, vd, plan.row_ptr, col_idx, work=plan), n=5)
+        reuse_ms = time_launches(lambda: ar.reuse(qd, kd, vd, out=o_c), n=20)
+        extra["residual_compensation"] = {
+            "residual_ms": res_ms, "compensate_ms": comp_ms,
+            "compensate_gbps": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9,
+            "compensate_frac_of_hbm_peak": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "anchor_step_ms": anchor_ms, "reuse_step_ms": reuse_ms,
         }
 
-    if args.extra:
-        rp1 =(np.arange(n_rows + 1) * nb).astype(np.int32)
-        ci1 = torch.from_numpy(np.tile(np.arange(nb, dtype=np.int32), n_rows)).to(dev)
-        rp1d = torch.from_numpy(rp1).to(dev)
-        dense_ms = time_launches(lambda: bsa.forward(qd, kd, vd, rp1d, ci1, w.block, out=o, lse=lse))
-        dense_flops = active_flops(rp1, ci1.cpu().numpy(), w.N, w.D, w.block, nb)
-        extra["dense_ms"] = dense_ms
-        extra["dense_tflops"] = dense_flops / (dense_ms * 1e-3) / 1e12
-        extra["speedup_vs_dense"] = dense_ms / fwd_ms
-        sweep = []
+        # Token-level selection at the same density: tile-aligned query groups of 64, token
+        # mass per group from the dense LSE, the top T tokens per group, and the gathered
+        # forward; the kept mass and the output error next to the block CSR's.
+        if w.D == 64 and w.N % 64 == 0:
+            T = int(round(plan.nnz / (n_rows * nb) * w.N))
+            groups = bsa.query_groups(qd, 64)
+            grp_ms = time_launches(lambda: bsa.query_groups(qd, 64), n=5)
+            tmass = bsa.token_mass(qd, kd, lse_dense, groups)
+            tmass_ms = time_launches(lambda: bsa.token_mass(qd, kd, lse_dense, groups), n=10)
+            toks = bsa.select_tokens(tmass, T)
+            sel_tok_ms = time_launches(lambda: bsa.select_tokens(tmass, T), n=10)
+            o_g = torch.zeros_like(qd)
+            bsa.gather_forward(qd, kd, vd, groups, toks, out=o_g, return_lse=False)
+            gather_ms = time_launches(lambda: bsa.gather_forward(qd, kd, vd, groups, toks, out=o_g,
+                                                                 return_lse=False), n=20)
+            kept_tok = torch.gather(tmass, 3, toks.long()).double().sum().item()
+            n_groups = groups.shape[0] * groups.shape[1] * groups.shape[2]
+            gather_flops = 4.0 * n_groups * 64 * T * w.D
+            extra["token_selection"] = {
+                "tokens_per_group": T, "groups": n_groups,
+                "query_groups_ms": grp_ms, "token_mass_ms": tmass_ms, "select_tokens_ms": sel_tok_ms,
+                "gather_forward_ms": gather_ms,
+                "gather_forward_tflops": gather_flops / (gather_ms * 1e-3) / 1e12,
+                "mean_kept_mass_tokens": kept_tok / n_q, "mean_kept_mass_csr": kept_csr / n_q,
+                "rel_err_vs_dense_tokens": rel_err(o_g), "rel_err_vs_dense_csr": rel_err(o),
+            }
+
+        # Backward over the same CSR (block 64, D 64): dQ, dK, dV from the forward's O and LSE
+        # for a seeded N(0,1) incoming gradient; 10 * q_valid * k_valid * D FLOPs per active
+        # pair (the five products S, dP, dV, dS K, dS^T Q), all four launches in the timing.
+        if w.D == 64 and w.block == 64:
+            g = torch.Generator("cpu").manual_seed(1000 + w.N)
+            do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+            bws = torch.empty(max(bsa.backward_workspace_bytes(w.B, w.H, w.N, w.block, plan.nnz),
+                                  256), dtype=torch.uint8, device=dev)
+            bsa.backward(qd, kd, vd, o, lse, do, plan.row_ptr, col_idx[:plan.nnz], w.block,
+                         workspace=bws)
+            bwd_ms = time_launches(lambda: bsa.backward(qd, kd, vd, o, lse, do, plan.row_ptr,
+                                                        col_idx[:plan.nnz], w.block,
+                                                        workspace=bws), n=20)
+            bwd_flops = 2.5 * flops
+            extra["backward"] = {
+                "backward_ms": bwd_ms, "active_gflop": bwd_flops / 1e9,
+                "tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+                "frac_of_bf16_peak": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            }
+
+        # Dense attention at the same shape: this kernel on the all-ones CSR (its own work
+        # list), graph-timed like the forward.
+        p_dense = bsa.Plan.create(w.B, w.H, w.N, w.D, w.block, 1.0, None, None, True, dev)
+        ci_all_h = np.tile(np.arange(nb, dtype=np.int32), n_rows)
+        dense_ms = graph_ms(lambda: bsa.forward(qd, kd, vd, p_dense.row_ptr, ci_all, w.block,
+                                                work=p_dense, out=o_dense, lse=lse_dense),
+                            20, stream)
+        dense_flops = active_flops(p_dense.row_ptr_host, ci_all_h, w.N, w.D, w.block, nb)
+        extra["dense"] = {"kernel_on_all_ones_csr_ms": dense_ms,
+                          "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+                          "frac_of_bf16_peak": dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                          "speedup_of_sparse_vs_dense": dense_ms / fwd_ms,
+                          "density_ratio": n_rows * nb / plan.nnz, "timed_as_graph": True}
+        # Density scaling (BSA-DiT §1.2, §2.1: work falls with the kept fraction of blocks):
+        # mean-pool top-k masks on this shape at six densities, plus this workload's own
+        # mask; time against active block pairs, with a least-squares line.
+        points = [{"mask": w.note, "density": plan.nnz / (n_rows * nb), "nnz": plan.nnz,
+                   "fwd_ms": fwd_ms}]
         for d in (0.05, 0.10, 0.15, 0.25, 0.50, 1.0):
             p2 = bsa.Plan.create(w.B, w.H, w.N, w.D, w.block, d, None, None, True, dev)
-            rp2, ci2 = bsa.build_mask(qd, kd, w.block, plan=p2)
-            t = time_launches(lambda: bsa.forward(qd, kd, vd, rp2, ci2, w.block, work=p2,
-                                                  out=o, lse=lse))
-            sweep.append({"density": p2.nnz / (n_rows * nb), "nnz": p2.nnz, "fwd_ms": t})
-        x = np.array([s["nnz"] for s in sweep], float)
-        y = np.array([s["fwd_ms"] for s in sweep])
-        slope, icpt = np.polyfit(x, y, 1)
-        r2 = 1 - np.sum((y - (slope * x + icpt)) ** 2) / np.sum((y - y.mean()) ** 2)
-        extra["density_sweep"] = sweep
-        extra["linear_fit"] = {"ms_per_1k_blocks": slope * 1e3, "intercept_ms": icpt, "r2": r2}
+            ci2 = torch.empty(max(p2.nnz, 1), dtype=torch.int32, device=dev)
+            bsa.build_mask(qd, kd, w.block, plan=p2, col_idx=ci2)
+            t = graph_ms(lambda: bsa.forward(qd, kd, vd, p2.row_ptr, ci2, w.block, work=p2,
+                                             out=o_c, lse=lse_dense), 30, stream)
+            points.append({"mask": f"mean-pool top-k {d:.0%}", "density": p2.nnz / (n_rows * nb),
+                           "nnz": p2.nnz, "fwd_ms": t})
+        slope, icpt, r2 = linear_fit([x["nnz"] for x in points], [x["fwd_ms"] for x in points])
+        extra["density_sweep"] = {
+            "points": points,
+            "fit": {"ms_per_1k_blocks": slope * 1e3, "intercept_ms": icpt, "r2": r2,
+                    "intercept_frac_of_workload_time": icpt / fwd_ms},
+        }
+        # Shader clock under this load, next to the rated one the peak assumes.
+        clk = sample_clock_mhz(lambda: fwd_graph.replay() if fwd_graph is not None else None)
+        extra["clock"] = {"rated_mhz": 2400, "measured": clk,
+                          "peak_bf16_tflops_at_measured": (PEAK_BF16_TFLOPS * clk["mean_mhz"] / 2400.0
+                                                            if clk else None)}
+        # The other configurations (parity cases, not the metric): forward and builder per
+        # call, graph-timed, and the fp64 CPU oracle on the same inputs and CSR.
+        others = {}
+        for name in ("tiny", "dynamic", "video", "ragged", "ragged_twin"):
+            wc = W.make(name)
+            qc, kc, vc = wc.tensors()
+            pc = bsa.Plan.create(wc.B, wc.H, wc.N, wc.D, wc.block, wc.density, wc.prior(),
+                                 wc.budgets(), wc.force_diag, dev)
+            qcd, kcd, vcd = qc.to(dev), kc.to(dev), vc.to(dev)
+            cic = torch.empty(max(pc.nnz, 1), dtype=torch.int32, device=dev)
+            bsa.build_mask(qcd, kcd, wc.block, plan=pc, col_idx=cic)
+            occ = torch.empty_like(qcd)
+            lcc = torch.empty((wc.B, wc.H, wc.N), dtype=torch.float32, device=dev)
+            reps = 200 if name == "tiny" else 20
+            f_ms = graph_ms(lambda: bsa.forward(qcd, kcd, vcd, pc.row_ptr, cic, wc.block,
+                                                work=pc, out=occ, lse=lcc), reps, stream)
+            b_ms = graph_ms(lambda: bsa.build_mask(qcd, kcd, wc.block, plan=pc, col_idx=cic),
+                            reps, stream)
+            torch.cuda.synchronize()
+            cic_h = cic.cpu().numpy()[:pc.nnz]
+            nbc, rows_c = wc.nb, wc.B * wc.H * wc.nb
+            fl = active_flops(pc.row_ptr_host, cic_h, wc.N, wc.D, wc.block, nbc)
+            entry = {"shape": f"B{wc.B} H{wc.H} N{wc.N} D{wc.D} b{wc.block}",
+                     "density": pc.nnz / (rows_c * nbc), "active_gflop": fl / 1e9,
+                     "forward_ms": f_ms, "forward_tflops": fl / (f_ms * 1e-3) / 1e12,
+                     "forward_frac_of_bf16_peak": fl / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "kernel": fwd_kernel_name(wc.block, wc.D), "build_mask_ms": b_ms}
+            if not args.no_cpu:
+                heads, cfl, dt = oracle_seconds(wc, qc, kc, vc, pc.row_ptr_host, cic_h,
+                                                args.cpu_seconds)
+                entry["cpu_oracle"] = {"tflops": cfl / dt / 1e12, "seconds": dt,
+                                       "heads": f"{heads} of {wc.B * wc.H}",
+                                       "gpu_over_cpu": (fl / (f_ms * 1e-3)) / (cfl / dt)}
+            others[name] = entry
+            del qcd, kcd, vcd, occ, lcc, cic
+            torch.cuda.empty_cache()
+        extra["other_configs"] = others
 
     out = {
         "metric": METRIC,

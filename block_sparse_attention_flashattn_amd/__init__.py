@@ -213,13 +213,16 @@ def work_plan(row_ptr, max_tiles: int = 0, nb: int = 0, n_groups: int = 1):
     return work[:used].copy(), ni.value, nm.value, ns.value
 
 
-def validate_csr_host(row_ptr, col_idx, nb: int, strict: bool = True) -> int:
-    """-1 if the CSR is well formed, else the first offending row."""
+def validate_csr_host(row_ptr, col_idx, nb: int, strict=True) -> int:
+    """-1 if the CSR is well formed, else the first offending row.  strict: True (or 1)
+    strictly ascending rows, "distinct" (or 2) distinct columns in any order, False (0)
+    columns in range only."""
     rp = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
     ci = np.ascontiguousarray(np.asarray(col_idx), dtype=np.int32)
+    mode = 2 if strict == "distinct" or strict == 2 else int(bool(strict))
     bad = ctypes.c_int64(-1)
     lib.bsa_validate_csr_host(_np_ptr(rp), _np_ptr(ci) if ci.size else None, rp.shape[0] - 1,
-                              nb, int(bool(strict)), ctypes.byref(bad))
+                              nb, mode, ctypes.byref(bad))
     return int(bad.value)
 
 

@@ -174,13 +174,21 @@ extern "C" BSA_API bsa_status bsa_validate_csr_host(const int32_t* row_ptr,
     if (bad_row) *bad_row = 0;
     return BSA_ERR_INVALID_ARG;
   }
+  // strict == 2: a column already seen in this row carries the row's stamp.
+  std::vector<int32_t> seen(strict == 2 ? size_t(nb) : 0, -1);
   for (int32_t r = 0; r < n_rows; ++r) {
     const int32_t a = row_ptr[r], b = row_ptr[r + 1];
     bool ok = b >= a && (b == a || col_idx != nullptr);
     for (int32_t t = a; ok && t < b; ++t) {
       const int32_t c = col_idx[t];
-      if (c < 0 || c >= nb) ok = false;
-      if (strict && t > a && col_idx[t - 1] >= c) ok = false;
+      if (c < 0 || c >= nb) {
+        ok = false;
+      } else if (strict == 2) {
+        if (seen[size_t(c)] == r) ok = false;
+        seen[size_t(c)] = r;
+      } else if (strict && t > a && col_idx[t - 1] >= c) {
+        ok = false;
+      }
     }
     if (!ok) {
       if (bad_row) *bad_row = r;

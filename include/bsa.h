@@ -15,8 +15,11 @@
  *     computed nor stored, its missing keys are masked out.
  *   - CSR row r = (bi*H + h)*nb + i lists the KV blocks that query block i of
  *     head (bi, h) attends to: row_ptr int32 [B*H*nb + 1], col_idx int32 [nnz],
- *     nnz = row_ptr[B*H*nb].  Columns of a row are in [0, nb); the mask builder
- *     writes them strictly ascending (the forward does not need any order).
+ *     nnz = row_ptr[B*H*nb].  Columns of a row are in [0, nb) and distinct: a
+ *     block is either active or not (BSA-DiT §4.1, §4.3), while the forward
+ *     would count the keys of a repeated column twice.  The mask builder writes
+ *     them strictly ascending; the forward needs no order.
+ *     bsa_validate_csr_host checks both (strict = 1) or distinctness alone (2).
  *   - LSE: fp32 [B, H, N], natural log, including the softmax scale.
  *   - Supported: D in {64, 128}, b in {64, 128}, 1 <= N, nb <= 1024.
  *   - Ownership: the caller allocates every buffer (device buffers with
@@ -134,7 +137,8 @@ BSA_API bsa_status bsa_work_plan_host(const int32_t* row_ptr, int32_t n_rows, in
 
 /*
  * Structural CSR check (host, synchronous): row_ptr[0] == 0, non-decreasing,
- * every column in [0, nb), and (if strict != 0) strictly ascending per row.
+ * every column in [0, nb); strict == 1: also strictly ascending per row (which
+ * implies distinct); strict == 2: distinct per row, in any order.
  * On failure returns INVALID_ARG and writes the first offending row to
  * *bad_row (if non-NULL); on success *bad_row = -1.
  */

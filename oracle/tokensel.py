@@ -35,7 +35,7 @@ import numpy as np
 from . import attention as A
 from . import mass as M
 
-__all__ = ["POWER_ITERS", "principal_direction", "median_split_groups", "token_mass",
+__all__ = ["POWER_ITERS", "start_vector", "principal_direction", "median_split_groups", "token_mass",
            "select_tokens", "gathered_attention"]
 
 POWER_ITERS = 8
@@ -47,13 +47,19 @@ def _as64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def principal_direction(x: np.ndarray, iters: int = POWER_ITERS) -> np.ndarray:
-    """Unit vector after `iters` power-iteration steps v <- X^T (X v) / |.| on the centred
-    rows X of x, from u[d] = 1 + d / D."""
+def start_vector(D: int) -> np.ndarray:
+    """The power iteration's start vector u[d] = 1 + d / D (not normalised)."""
+    return 1.0 + np.arange(D) / D
+
+
+def principal_direction(x: np.ndarray, iters: int | None = None) -> np.ndarray:
+    """Unit vector after `iters` (default POWER_ITERS) power-iteration steps
+    v <- X^T (X v) / |.| on the centred rows X of x, from start_vector(D)."""
+    iters = POWER_ITERS if iters is None else iters
     xc = x - x.mean(axis=0)
     D = x.shape[1]
-    v = 1.0 + np.arange(D) / D
-    v /= np.linalg.norm(v)
+    v = start_vector(D)
+    v = v / np.linalg.norm(v)
     for _ in range(iters):
         w = xc.T @ (xc @ v)
         n = np.linalg.norm(w)
@@ -63,7 +69,7 @@ def principal_direction(x: np.ndarray, iters: int = POWER_ITERS) -> np.ndarray:
     return v
 
 
-def median_split_groups(x, C: int, iters: int = POWER_ITERS) -> np.ndarray:
+def median_split_groups(x, C: int, iters: int | None = None) -> np.ndarray:
     """Groups [N / C, C] of token indices (each row ascending) for queries x [N, D];
     N must be a multiple of C."""
     x = _as64(x)

@@ -168,6 +168,11 @@ def test_validate_csr_host():
     assert bsa.validate_csr_host(rp, np.array([0, 4, 1, 2, 3]), 4) == 0      # column out of range
     assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 1, 3]), 4) == 2      # not ascending
     assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 1, 3]), 4, strict=False) == -1
+    # distinct columns in any order (a repeated column would count twice in the forward)
+    assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 1, 3]), 4, strict="distinct") == -1
+    assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 1, 2]), 4, strict="distinct") == 2
+    assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 2, 3]), 4, strict="distinct") == 2
+    assert bsa.validate_csr_host(rp, np.array([0, 3, 2, 2, 3]), 4, strict=False) == -1
     assert bsa.validate_csr_host(np.array([0, 2, 1], np.int32), np.array([0, 1]), 4) == 1
 
 

@@ -1,9 +1,10 @@
 """Full-size workloads in the launch configuration the benchmark times.
 
 The builder is compared row by row with the oracle builder (bit-exact where the
-fp64 top-k gap exceeds 1e-4); the forward is compared with the attention oracle
-on sampled CSR rows, the oracle being fed the GPU's own CSR so that attention
-parity does not depend on how ties were broken.
+fp64 top-k gap exceeds 1e-4); the forward is compared element by element with the
+attention oracle on every CSR row of the benchmark workload (t2i) and on every cut
+row plus at least 100 others of the rest, the oracle being fed the GPU's own CSR
+so that attention parity does not depend on how ties were broken.
 """
 import numpy as np
 import pytest
@@ -46,15 +47,18 @@ def test_full_config(name):
     print(f"csr rows exact {exact} tie-excused {loose}; nnz {plan.nnz} "
           f"density {plan.nnz / (w.B * w.H * nb * nb):.4f}", flush=True)
 
-    rows = sample_rows(plan.row_ptr_host, nb, n_rows, 12, seed=len(name))
+    # Rows compared with the oracle: every row of the benchmark workload (t2i); for the
+    # others every row the work list cuts into chunks plus at least 100 more (the longest,
+    # the shortest, each head's partial last block, random ones).
+    ni, nm = plan.work.n_items, plan.work.n_merges
+    cut = plan.work.work.cpu().numpy()[4 * ni:4 * ni + 3 * nm].reshape(-1, 3)[:, 0]
+    if name == "t2i":
+        rows = list(range(n_rows))
+    else:
+        rows = sorted(set(sample_rows(plan.row_ptr_host, nb, n_rows, 100, seed=len(name)))
+                      | set(cut.tolist()))
+        assert len(rows) >= 100
     O, L = OA.block_sparse_attention(q, k, v, plan.row_ptr_host, ci_h, w.block, w.scale, rows=rows)
     stats = compare_attention(o, lse, O, L, token_rows(rows, nb, w.block, w.N, w.H))
-    print(f"attention on {len(rows)} rows: {stats}; work items {plan.work.n_items}, "
-          f"cut rows {plan.work.n_merges} (max_tiles {plan.work.max_tiles})", flush=True)
-    if plan.work.n_merges:
-        ni, nm = plan.work.n_items, plan.work.n_merges
-        cut = plan.work.work.cpu().numpy()[4 * ni:4 * ni + 3 * nm].reshape(-1, 3)[:, 0]
-        rows2 = sorted(set(cut[:6].tolist()))
-        O2, L2 = OA.block_sparse_attention(q, k, v, plan.row_ptr_host, ci_h, w.block, w.scale,
-                                           rows=rows2)
-        print("cut rows:", compare_attention(o, lse, O2, L2, token_rows(rows2, nb, w.block, w.N, w.H)))
+    print(f"attention on {len(rows)} of {n_rows} rows ({len(cut)} cut rows among them): "
+          f"{stats}; work items {ni} (max_tiles {plan.work.max_tiles})", flush=True)

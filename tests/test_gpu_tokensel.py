@@ -49,25 +49,67 @@ def test_query_groups_recover_separated_clusters(G, C, D):
         assert np.array_equal(got[0, h], want)
 
 
-def test_query_groups_random_are_valid_and_as_tight():
-    """Random queries of a full t2i head length: a partition into tile-sized ascending
-    groups whose within-group scatter matches the oracle's to 1 % (cuts near the median
-    may go either way in fp32)."""
+# Per-split tolerance on projections (relative to the segment's largest |projection|).
+# The GPU forms the scatter matrix in fp32 from bf16 hi/lo products (relative error near
+# 2^-16 per product), runs the eight power-iteration steps and the projections in fp32;
+# through eight steps that moves the direction by well under 1e-4 relative, so projections
+# of the GPU and of the fp64 oracle differ by less than 1e-3 of the largest one.
+SPLIT_EPS = 1e-3
+
+
+def check_splits(x, groups, C, eps_rel=SPLIT_EPS):
+    """Walk the GPU's split tree (groups numbered depth first, first part first): for every
+    segment of g > 1 groups, project its tokens on the oracle's fp64 principal direction of
+    that segment; every token the GPU put left must project at most eps above every token it
+    put right, and where the oracle's cut has a gap above 2 eps the two cuts are the same.
+    Returns (splits checked exactly, splits within the tolerance only)."""
+    exact = loose = 0
+
+    def rec(s, g):
+        nonlocal exact, loose
+        if g == 1:
+            return
+        toks = np.concatenate(groups[s:s + g])
+        sub = x[toks]
+        p = (sub - sub.mean(0)) @ OT.principal_direction(sub)
+        gl = g // 2
+        nl = gl * C
+        left = np.isin(toks, np.concatenate(groups[s:s + gl]))
+        eps = eps_rel * np.abs(p).max()
+        assert p[left].max() <= p[~left].min() + eps, (s, g, p[left].max(), p[~left].min())
+        ps = np.sort(p)
+        if ps[nl] - ps[nl - 1] > 2 * eps:
+            assert np.array_equal(np.sort(toks[np.lexsort((toks, p))[:nl]]), np.sort(toks[left]))
+            exact += 1
+        else:
+            loose += 1
+        rec(s, gl)
+        rec(s + gl, g - gl)
+
+    rec(0, len(groups))
+    return exact, loose
+
+
+@pytest.mark.parametrize("N,C,D,H", [(4224, 64, 64, 2), (2048, 128, 128, 1), (8192, 64, 128, 1)])
+def test_query_groups_random_split_by_split(N, C, D, H):
+    """Random queries at full head lengths (t2i, and lengths whose top segments are split
+    from 512-token slice partials): a partition into tile-sized ascending groups, checked
+    split by split against the oracle's fp64 direction of the same segment (see
+    check_splits); exact wherever the median has a gap above the fp32 tolerance."""
     bsa = need_gpu()
-    N, C, D = 4224, 64, 64
-    q, _, _ = W.gaussian_qkv(77, 1, 2, N, D)
+    print(f"case N={N} C={C} D={D}", flush=True)
+    q, _, _ = W.gaussian_qkv(77 + N, 1, H, N, D)
     groups = bsa.query_groups(q.cuda(), C)
     torch.cuda.synchronize()
     got = groups.cpu().numpy()
-    for h in range(2):
+    for h in range(H):
         x = q[0, h].float().numpy().astype(np.float64)
         g = got[0, h]
         assert sorted(g.ravel().tolist()) == list(range(N))
         assert all((np.diff(r) > 0).all() for r in g)
-        want = OT.median_split_groups(x, C)
-        scat = lambda gs: sum(((x[r] - x[r].mean(0)) ** 2).sum() for r in gs)
-        print(f"head {h}: scatter gpu {scat(g):.1f} oracle {scat(want):.1f}", flush=True)
-        assert abs(scat(g) - scat(want)) <= 0.01 * scat(want)
+        exact, loose = check_splits(x, g, C)
+        print(f"head {h}: {exact} splits exact, {loose} within tolerance", flush=True)
+        assert exact + loose == N // C - 1
 
 
 @pytest.mark.parametrize("C,D,N", [(64, 64, 1024), (64, 128, 512), (128, 64, 768)])

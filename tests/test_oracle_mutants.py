@@ -260,6 +260,7 @@ TOK_PINS = [
     (TT.test_token_mass_conservation_and_block_sums, ()),
     (TT.test_select_tokens_hand, ()),
     (TT.test_gathered_attention_reduces_to_dense_and_block_sparse, ()),
+    (TT.test_power_iteration_hand_golden, ()),
 ]
 
 
@@ -274,7 +275,22 @@ def test_unmodified_tokensel_oracle_passes():
 def test_tok_mutant_direction_is_a_fixed_axis(monkeypatch):
     """Projecting on the first coordinate instead of the principal direction."""
     monkeypatch.setattr(Tk, "principal_direction",
-                        lambda x, iters=8: np.eye(x.shape[1])[0])
+                        lambda x, iters=None: np.eye(x.shape[1])[0])
+    assert any_tok_pin_fails()
+
+
+@pytest.mark.parametrize("iters", [7, 9])
+def test_tok_mutant_power_iteration_count(monkeypatch, iters):
+    monkeypatch.setattr(Tk, "POWER_ITERS", iters)
+    assert any_tok_pin_fails()
+
+
+@pytest.mark.parametrize("start", ["ones", "d_over_D_minus_1", "descending"])
+def test_tok_mutant_start_vector(monkeypatch, start):
+    f = {"ones": lambda D: np.ones(D),
+         "d_over_D_minus_1": lambda D: 1.0 + np.arange(D) / max(D - 1, 1),
+         "descending": lambda D: 1.0 + np.arange(D)[::-1] / D}[start]
+    monkeypatch.setattr(Tk, "start_vector", f)
     assert any_tok_pin_fails()
 
 

@@ -8,6 +8,7 @@ import pytest
 from oracle import attention as A
 from oracle import mass as M
 from oracle import tokensel as T
+from conftest import load_golden
 
 
 def test_principal_direction_is_the_top_eigenvector():
@@ -99,3 +100,16 @@ def test_gathered_attention_reduces_to_dense_and_block_sparse():
         o, l = T.gathered_attention(q, k, v, g[None], t[None], 0.3)
         np.testing.assert_allclose(o[g], Ob[0, 0, g], atol=1e-12)
         np.testing.assert_allclose(l[g], Lb[0, 0, g], atol=1e-12)
+
+
+def test_power_iteration_hand_golden():
+    """tests/golden/query_groups_hand.json (worked by hand): 2-D points in +/- pairs whose
+    scatter matrix is diag(490, 392); from u = (1, 1.5) the direction after k steps has
+    tan = 1.5 * 0.8^k, and the single median split depends on k being 8 and on the start."""
+    g = load_golden("query_groups_hand.json")
+    half = np.array(g["half_points"], dtype=np.float64)
+    x = np.empty((2 * len(half), 2))
+    x[0::2], x[1::2] = half, -half
+    v = T.principal_direction(x)
+    assert abs(v[1] / v[0] - g["tan_theta_after_8"]) < 1e-12
+    assert T.median_split_groups(x, g["C"]).tolist() == g["groups"]
