@@ -184,6 +184,7 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
   const int hh = lane >> 5;      // which half of the k / row dimension the lane feeds
   const uint32_t head_bytes = static_cast<uint32_t>(size_t(N) * C::ROWB);
   const int nnz = ld_uniform(row_ptr, n_rows);
+  const int32_t* col_src = nnz > 0 ? col_idx : row_ptr;  // valid for index 0
 
   // Work item k -> (row, first column position, column count, slot); row = -1
   // when k is past the end.  Everything here is wavefront-uniform.
@@ -214,8 +215,12 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
   };
 
   // This wave's share of a stage: DPW loads of 64 chunks; waves [0, NW/2) fill
-  // the K tile, the others the V tile.  doff = source offset of the chunk that
-  // lands at this lane's (swizzled) LDS position.
+  // the K tile, the others the V tile.  Load i brings the chunk that lands at
+  // this lane's (swizzled) LDS position of segment i; its source offset lies
+  // at least 1024 i bytes into the tile (segment i holds tile rows at or past
+  // 1024 i / ROWB), so doff[i] = source offset - 1024 (i % 4) >= 0 serves the
+  // four-load groups of dma16x4.
+  static_assert(C::DPW % 4 == 0, "loads go in groups of four");
   const bool loads_v = wave >= C::NW / 2;
   uint32_t doff[C::DPW];
 #pragma unroll
@@ -223,7 +228,8 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const int g = (wave * C::DPW + i) * 64 + lane - (loads_v ? BLK * C::CPR : 0);
     const int row = g / C::CPR;
     const int pos = g - row * C::CPR;
-    doff[i] = uint32_t(row) * C::ROWB + uint32_t((pos ^ chunk_swizzle<C::ROWB>(row)) << 4);
+    doff[i] = uint32_t(row) * C::ROWB + uint32_t((pos ^ chunk_swizzle<C::ROWB>(row)) << 4) -
+              uint32_t(i & 3) * 1024u;
   }
 
   // This wave's K or V buffer descriptor for the head of CSR row `row`
@@ -243,7 +249,9 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const uint32_t tb = (j >= 0 && j < nb) ? uint32_t(j) * C::TILEB : head_bytes;
     const uint32_t l0 = lds_wave + uint32_t(st) * C::STAGEB;
 #pragma unroll
-    for (int i = 0; i < C::DPW; ++i) dma16(desc, tb + doff[i], l0 + uint32_t(i) * 1024u);
+    for (int i = 0; i < C::DPW; i += 4)
+      dma16x4(desc, tb + doff[i], tb + doff[i + 1], tb + doff[i + 2], tb + doff[i + 3],
+              l0 + uint32_t(i) * 1024u);
   };
 
   // Query fragment of the item on CSR row `row` (B operand of S^T = K Q^T):
@@ -334,9 +342,11 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       // the barrier).  The tiles issued after the current one are the only
       // loads allowed in flight; the barrier then makes every wave's part of
       // the current tile visible and frees the stage computed one step ago.
+      // (The column load is unconditional, from a valid dummy entry past the
+      // stream, so that the wave waits for it only at the barrier.)
       bool in_next;
       const int src = inflight < C::NSTAGE ? stream_src(u + inflight, in_next) : -1;
-      const int jn = src >= 0 ? ld_uniform(col_idx, src) : -1;
+      const int jn = ld_uniform(col_src, src >= 0 ? src : 0);
       if (inflight > 1)
         wait_vm(C::DPW);
       else
@@ -348,17 +358,49 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
       const int valid = static_cast<int>(vq & 0xffu);
 
       // S^T tile: lane (ql, hh) holds keys key0 + 8(i/4) + 4hh + (i%4) of query ql.
+      // A subtile's K operands are all read before its MFMAs (one LDS round
+      // trip, not one per MFMA).
       const f32x16 zero = {};
       f32x16 s[C::NKT];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt) {
         const int key = (kh * C::NKT + kt) * 32 + ql;
+        bf16x8 ka[C::NDC];
 #pragma unroll
-        for (int c = 0; c < C::NDC; ++c) {
-          const bf16x8 a = lds_read16(ks + swz<C::ROWB>(key, 2 * c + hh));
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? zero : s[kt], 0, 0,
-                                                          0);
+        for (int c = 0; c < C::NDC; ++c) ka[c] = lds_read16(ks + swz<C::ROWB>(key, 2 * c + hh));
+#pragma unroll
+        for (int c = 0; c < C::NDC; ++c)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], c == 0 ? zero : s[kt], 0,
+                                                          0, 0);
+      }
+
+      // V^T operands of O^T += V^T P^T.  For the 16-key step kb, V^T rows
+      // d = 32u + (lane % 32) need keys kb + 4hh + e and kb + 8 + 4hh + e
+      // (e = 0..3): lane t of each 16-lane block points at key row t / 4 and
+      // columns 4 (t % 4) .. +3 of its block's 16 d values, and the transposing
+      // read returns to every lane the four keys of its own d column.  When
+      // they fit in the registers the K operands held, all are read here and
+      // land while the softmax runs; otherwise one key subtile's at a time.
+      constexpr bool kEarlyV = C::NKT * C::NDT <= 4;
+      const int tr_row = 4 * hh + ((lane & 15) >> 2);
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      v4s vlo[C::NKT][2][C::NDT], vhi[C::NKT][2][C::NDT];
+      auto read_v = [&](int kt) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int kb = (kh * C::NKT + kt) * 32 + 16 * c2;
+#pragma unroll
+          for (int u2 = 0; u2 < C::NDT; ++u2) {
+            const int col = 32 * u2 + tr_col;
+            vlo[kt][c2][u2] = lds_read_tr(vs + swz<C::ROWB>(kb + tr_row, col >> 3) + (col & 7) * 2);
+            vhi[kt][c2][u2] =
+                lds_read_tr(vs + swz<C::ROWB>(kb + 8 + tr_row, col >> 3) + (col & 7) * 2);
+          }
         }
+      };
+      if (kEarlyV) {
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt) read_v(kt);
       }
       if (__builtin_expect(valid < BLK, 0)) {
 #pragma unroll
@@ -407,29 +449,20 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
         }
       l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-      // O^T += V^T P^T.  For the 16-key step kb, V^T rows d = 32u + (lane % 32)
-      // need keys kb + 4hh + e and kb + 8 + 4hh + e (e = 0..3): lane t of each
-      // 16-lane block points at key row t / 4 and columns 4 (t % 4) .. +3 of its
-      // block's 16 d values, and the transposing read returns to every lane the
-      // four keys of its own d column.
-      const int tr_row = 4 * hh + ((lane & 15) >> 2);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      // O^T += V^T P^T.
 #pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
+      for (int kt = 0; kt < C::NKT; ++kt) {
+        if (!kEarlyV) read_v(kt);
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int kb = (kh * C::NKT + kt) * 32 + 16 * c2;
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
           for (int u2 = 0; u2 < C::NDT; ++u2) {
-            const int col = 32 * u2 + tr_col;
-            const v4s lo = lds_read_tr(vs + swz<C::ROWB>(kb + tr_row, col >> 3) + (col & 7) * 2);
-            const v4s hi =
-                lds_read_tr(vs + swz<C::ROWB>(kb + 8 + tr_row, col >> 3) + (col & 7) * 2);
             const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                bf16x8, __builtin_shufflevector(vlo[kt][c2][u2], vhi[kt][c2][u2], 0, 1, 2, 3, 4,
+                                                5, 6, 7));
             acc[u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c2], acc[u2], 0, 0, 0);
           }
-        }
+      }
 
       // Retire the tile.
       st_cur = st_cur + 1 == C::NSTAGE ? 0 : st_cur + 1;
