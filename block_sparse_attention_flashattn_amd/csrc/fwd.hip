@@ -160,6 +160,11 @@ struct ItemSource {
 // accumulator is rescaled; probabilities then stay below 2^8 before the final
 // division, well inside fp32 and bf16 range.
 constexpr float kRescaleSlack = 8.0f;
+// Largest lane-partial row sum of one tile's probabilities (each taken against
+// the running max as it stands) accepted without raising the max: every such
+// probability is then below 2^20, so the accumulators stay far inside fp32
+// range and the bf16 operand keeps its relative precision.
+constexpr float kSumCap = 1048576.0f;
 
 
 
@@ -411,43 +416,52 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
             if (kv >= valid) s[kt][i] = -INFINITY;
           }
       }
-      float mx = -INFINITY;
+      // Probabilities against the running max as it stands.  The tile's max
+      // is needed only when a probability could leave the safe range, which
+      // some lane's partial row sum shows (above kSumCap, or not finite), or
+      // while a row has no max yet; then each row's max is raised to the
+      // tile's, its state rescaled and the tile's probabilities recomputed.
+      // Row sums in four independent chains (no long serial add dependency).
+      float lt;
+      bf16x8 pb[C::NKT][2];
+      auto probs = [&]() {
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float ls[4];
 #pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
+        for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-      mx = fmaxf(mx, other_half(mx));
-      const float mt = mx * sl2;
-      // Lazy rescale: only when some row's max grew by more than the slack.
-      // A row's first finite max is adopted without touching its (zero) state.
-      const bool need = mt > m_run + kRescaleSlack;
-      const bool rescale = need && m_run != -INFINITY;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(rescale) != 0, 0)) {
-        const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_use));
+            if (kt == 0 && i < 4)
+              ls[i] = p;
+            else
+              ls[i & 3] += p;
+            pb[kt][i >> 3][i & 7] = static_cast<__bf16>(p);
+          }
+        lt = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      };
+      probs();
+      if (__builtin_expect(
+              __builtin_amdgcn_ballot_w64(!(lt <= kSumCap) || m_run == -INFINITY) != 0, 0)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+        mx = fmaxf(mx, other_half(mx));
+        const float mt = mx * sl2;
+        const bool up = mt > m_run;
+        // A row's first finite max is adopted without touching its (zero) state.
+        const float alpha = (up && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
         l_run *= alpha;
 #pragma unroll
         for (int u2 = 0; u2 < C::NDT; ++u2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[u2][i] *= alpha;
+        m_run = up ? mt : m_run;
+        probs();
       }
-      m_run = need ? mt : m_run;
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-      // Row sums in four independent chains (no long serial add dependency).
-      float ls[4];
-      bf16x8 pb[C::NKT][2];
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_use));
-          if (kt == 0 && i < 4)
-            ls[i] = p;
-          else
-            ls[i & 3] += p;
-          pb[kt][i >> 3][i & 7] = static_cast<__bf16>(p);
-        }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      l_run += lt;
 
       // O^T += V^T P^T.
 #pragma unroll
