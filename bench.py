@@ -389,6 +389,8 @@ def main():
             "compensate_gbps": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9,
             "compensate_frac_of_hbm_peak": 3 * 2 * n_el / (comp_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "anchor_step_ms": anchor_ms, "reuse_step_ms": reuse_ms,
+            "reuse_adds_residual_in_forward_epilogue": True,
+            "reuse_step_over_forward": reuse_ms / fwd_ms_eager,
         }
 
         # Token-level selection at the same density: tile-aligned query groups of 64, token

@@ -59,6 +59,8 @@ _SIGS = {
     "bsa_forward_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "bsa_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                            _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "bsa_forward_compensated": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                        _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bsa_forward_noalloc": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                    _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
     "bsa_block_mass": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
@@ -79,7 +81,7 @@ _SIGS = {
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 
 class BsaError(RuntimeError):
@@ -389,11 +391,14 @@ def schedule(row_ptr: torch.Tensor, max_len: int) -> Work:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx, block: int,
             scale: Optional[float] = None, work=None, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+            lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+            residual: Optional[torch.Tensor] = None):
     """Block-sparse attention forward -> (O bf16 [B,H,N,D], LSE fp32 [B,H,N] or None).
 
     `work` is a `Work`, a `Plan` (its work list is used) or None (one workgroup
-    per row, natural order).
+    per row, natural order).  With `residual` (bf16 [B,H,N,D], not overlapping
+    `out`), O = attention + residual, summed in fp32 and rounded once
+    (bsa_forward_compensated); LSE stays the attention's.
     """
     B, H, N, D = _check_qkv(q, k, v)
     dev = q.device
@@ -421,10 +426,21 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr, col_idx,
         wp, ni, nm, ns = _t_ptr(work.work), work.n_items, work.n_merges, work.n_slots
         ws = work.workspace
         wsb = 0 if ws is None else ws.numel()
-    _check(lib.bsa_forward(_t_ptr(q), _t_ptr(k), _t_ptr(v), B, H, N, D, block, _t_ptr(row_ptr),
-                           _t_ptr(col_idx), wp, ni, nm, ns, s, _t_ptr(out),
-                           _t_ptr(lse) if return_lse else None, _t_ptr(ws), wsb,
-                           _stream_ptr(dev)), "bsa_forward")
+    if residual is None:
+        _check(lib.bsa_forward(_t_ptr(q), _t_ptr(k), _t_ptr(v), B, H, N, D, block,
+                               _t_ptr(row_ptr), _t_ptr(col_idx), wp, ni, nm, ns, s, _t_ptr(out),
+                               _t_ptr(lse) if return_lse else None, _t_ptr(ws), wsb,
+                               _stream_ptr(dev)), "bsa_forward")
+    else:
+        if not isinstance(residual, torch.Tensor) or residual.dtype != torch.bfloat16 \
+                or not residual.is_contiguous() or residual.shape != q.shape \
+                or residual.device != dev:
+            raise ValueError("residual must be a contiguous bf16 [B,H,N,D] tensor on the device")
+        _check(lib.bsa_forward_compensated(_t_ptr(q), _t_ptr(k), _t_ptr(v), B, H, N, D, block,
+                                           _t_ptr(row_ptr), _t_ptr(col_idx), wp, ni, nm, ns, s,
+                                           _t_ptr(residual), _t_ptr(out),
+                                           _t_ptr(lse) if return_lse else None, _t_ptr(ws), wsb,
+                                           _stream_ptr(dev)), "bsa_forward_compensated")
     return out, (lse if return_lse else None)
 
 
@@ -575,7 +591,7 @@ class AnchorReuse:
     `anchor(q, k, v, row_ptr, col_idx, work=None)` runs the dense and the sparse
     forward, keeps the CSR (and work list) and the residual R = O_dense - O_sparse,
     and returns the dense output.  `reuse(q, k, v)` runs the sparse forward with
-    the kept CSR and returns O_sparse + R.
+    the kept CSR and R added in its epilogue (bsa_forward_compensated): O_sparse + R.
     """
 
     def __init__(self, block: int, scale: Optional[float] = None):
@@ -600,8 +616,8 @@ class AnchorReuse:
         if self.r is None:
             raise RuntimeError("reuse() before anchor()")
         o, _ = forward(q, k, v, self.row_ptr, self.col_idx, self.block, scale=self.scale,
-                       work=self.work, out=out, return_lse=False)
-        return compensate(o, self.r, out=o)
+                       work=self.work, out=out, return_lse=False, residual=self.r)
+        return o
 
 
 def query_groups(q: torch.Tensor, C: int, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -168,13 +168,15 @@ constexpr float kSumCap = 1048576.0f;
 
 
 
-template <int BLK, int HD>
+// RES: O = attention + R (a residual added before O is rounded).
+template <int BLK, int HD, bool RES>
 __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
     int32_t n_merges, int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr) {
+    float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr,
+    const uint16_t* __restrict__ R) {
   using C = FwdCfg<BLK, HD>;
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
@@ -552,14 +554,21 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
         const size_t head = size_t(bh) * size_t(N) * HD;
         const float inv = l_half > 0.f ? 1.f / l_half : 0.f;
         uint16_t* orow = O + head + size_t(qrow) * HD;
+        // With a residual, O = attention + R, summed in fp32, rounded once.
+        const uint16_t* rrow = RES ? R + head + size_t(qrow) * HD : nullptr;
 #pragma unroll
         for (int u = 0; u < C::NDT; ++u)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int d0 = 32 * u + 8 * g + 4 * hh;
-            const uint32_t w0 = pack_bf16x2(acc[u][4 * g + 0] * inv, acc[u][4 * g + 1] * inv);
-            const uint32_t w1 = pack_bf16x2(acc[u][4 * g + 2] * inv, acc[u][4 * g + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+            f32x4 y = f32x4{acc[u][4 * g + 0], acc[u][4 * g + 1], acc[u][4 * g + 2],
+                            acc[u][4 * g + 3]} * inv;
+            if (RES) {
+              const uint2 rv = *reinterpret_cast<const uint2*>(rrow + d0);
+              y += f32x4{bf16_lo(rv.x), bf16_hi(rv.x), bf16_lo(rv.y), bf16_hi(rv.y)};
+            }
+            *reinterpret_cast<uint2*>(orow + d0) =
+                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
           }
         if (hh == 0 && LSE != nullptr) {
           LSE[size_t(bh) * N + qrow] =
@@ -617,13 +626,14 @@ struct Wide {
   static_assert(2 * 16 * 4 * 64 == STAGEB, "one query group's accumulator fills a stage");
 };
 
+template <bool RES>
 __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
     int32_t n_merges, int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
     float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr, int32_t n_slots,
-    int32_t* __restrict__ mctr) {
+    int32_t* __restrict__ mctr, const uint16_t* __restrict__ R) {
   using W = Wide;
   constexpr int BLK = W::BLK, HD = W::HD;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -885,11 +895,22 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const __amdgpu_buffer_rsrc_t orsc = make_rsrc(O + size_t(bh) * size_t(N) * HD, head_bytes);
     const uint32_t ob = uint32_t(qrow) * W::ROWB + uint32_t(32 * hh) * 2u;
+    // O = attention (+ R, summed in fp32), rounded once to bf16.
+    v4u rr[4];
+    if (RES) {
+      const __amdgpu_buffer_rsrc_t rrsc = make_rsrc(R + size_t(bh) * size_t(N) * HD, head_bytes);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rr[j] = __builtin_amdgcn_raw_buffer_load_b128(rrsc, ob + 16u * j, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 x = o[2 * j], y = o[2 * j + 1];
-      const v4u w = v4u{pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv),
-                        pack_bf16x2(y[0] * inv, y[1] * inv), pack_bf16x2(y[2] * inv, y[3] * inv)};
+      f32x4 x = o[2 * j] * inv, y = o[2 * j + 1] * inv;
+      if (RES) {
+        x += f32x4{bf16_lo(rr[j][0]), bf16_hi(rr[j][0]), bf16_lo(rr[j][1]), bf16_hi(rr[j][1])};
+        y += f32x4{bf16_lo(rr[j][2]), bf16_hi(rr[j][2]), bf16_lo(rr[j][3]), bf16_hi(rr[j][3])};
+      }
+      const v4u w = v4u{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
+                        pack_bf16x2(y[2], y[3])};
       __builtin_amdgcn_raw_buffer_store_b128(w, orsc, ob + 16u * j, 0, 0);
     }
     if (LSE == nullptr) return 4;
@@ -1069,6 +1090,21 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       wait_vm(8);
     else
       wait_vm(0);
+    // With a residual, the part this wave adds (its query group kh, the columns
+    // its lanes finalise; rows past N read as zeros) is loaded now and lands
+    // during the exchange.  Chunks of cut rows add it when they are combined.
+    const bool add_r = RES && cur_row >= 0 && cur_slot < 0;
+    v2u rres[2][4];
+    if (add_r) {
+      const __amdgpu_buffer_rsrc_t rrsc = make_rsrc(R + size_t(cur_bh) * size_t(N) * HD, head_bytes);
+      const uint32_t rrow = uint32_t((cur_row - cur_bh * nb) * BLK + kh * 32 + ql) * W::ROWB;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          rres[u][g4] = __builtin_amdgcn_raw_buffer_load_b64(
+              rrsc, rrow + uint32_t(32 * u + 8 * g4 + 4 * hh) * 2u, 0, 0);
+    }
     // The previous epilogue's partial stores are complete: count them in.
     int rel_m = -1, rel_old = 0;
     if (rel_slot >= 0) {
@@ -1155,6 +1191,22 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
         const __amdgpu_buffer_rsrc_t orsc =
             make_rsrc(O + size_t(bh) * size_t(N) * HD, head_bytes);
         const uint32_t orow = uint32_t(qrow) * W::ROWB;
+        // O = attention (+ R, summed in fp32), rounded once to bf16.
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[u][i] *= inv;
+        if (add_r) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              o[u][4 * g4 + 0] += bf16_lo(rres[u][g4][0]);
+              o[u][4 * g4 + 1] += bf16_hi(rres[u][g4][0]);
+              o[u][4 * g4 + 2] += bf16_lo(rres[u][g4][1]);
+              o[u][4 * g4 + 3] += bf16_hi(rres[u][g4][1]);
+            }
+        }
         // Lane (ql, hh) holds columns 32u + 8g4 + 4hh .. +3.  Swapping the odd-g4
         // pieces of the lower half-wave with the even-g4 pieces of the upper one
         // leaves every lane 8 contiguous columns (32u + 16p + 8hh .. +7), so four
@@ -1164,10 +1216,10 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
 #pragma unroll
           for (int pq = 0; pq < 2; ++pq) {
             const int ge = 2 * pq, go2 = 2 * pq + 1;
-            const uint32_t e0 = pack_bf16x2(o[u][4 * ge + 0] * inv, o[u][4 * ge + 1] * inv);
-            const uint32_t e1 = pack_bf16x2(o[u][4 * ge + 2] * inv, o[u][4 * ge + 3] * inv);
-            const uint32_t d0v = pack_bf16x2(o[u][4 * go2 + 0] * inv, o[u][4 * go2 + 1] * inv);
-            const uint32_t d1v = pack_bf16x2(o[u][4 * go2 + 2] * inv, o[u][4 * go2 + 3] * inv);
+            const uint32_t e0 = pack_bf16x2(o[u][4 * ge + 0], o[u][4 * ge + 1]);
+            const uint32_t e1 = pack_bf16x2(o[u][4 * ge + 2], o[u][4 * ge + 3]);
+            const uint32_t d0v = pack_bf16x2(o[u][4 * go2 + 0], o[u][4 * go2 + 1]);
+            const uint32_t d1v = pack_bf16x2(o[u][4 * go2 + 2], o[u][4 * go2 + 3]);
             // swap(X, Y): the upper lanes of the first result get the lower
             // lanes' Y, the lower lanes of the second result the upper lanes'
             // X.  Lower lanes need the upper half's even piece, upper lanes the
@@ -1547,13 +1599,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void g
 constexpr int kMergeThreads = 256;
 constexpr int kUnroll = 8;
 
-template <int BLK, int HD>
+template <int BLK, int HD, bool RES>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* __restrict__ merges,
                                                               const float* __restrict__ part,
                                                               int32_t N, int32_t nb,
                                                               int32_t n_rows,
                                                               uint16_t* __restrict__ O,
-                                                              float* __restrict__ LSE) {
+                                                              float* __restrict__ LSE,
+                                                              const uint16_t* __restrict__ R) {
   constexpr int D4 = HD / 4;
   constexpr int WG_PER_ROW = BLK * D4 / kMergeThreads;
   constexpr size_t SLOT = size_t(BLK) * (HD + 2);
@@ -1606,15 +1659,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* __r
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const size_t head = size_t(bh) * size_t(N) * HD;
+  f32x4 y = o * inv;
+  if (RES) {  // O = attention + R, summed in fp32, rounded once
+    const uint2 rv = *reinterpret_cast<const uint2*>(R + head + size_t(qrow) * HD + d);
+    y += f32x4{bf16_lo(rv.x), bf16_hi(rv.x), bf16_lo(rv.y), bf16_hi(rv.y)};
+  }
   *reinterpret_cast<uint2*>(O + head + size_t(qrow) * HD + d) =
-      make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+      make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
   if (d == 0 && LSE != nullptr)
     LSE[size_t(bh) * N + qrow] =
         L > 0.f ? (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-// Resident workgroups of fwd_kernel<BLK, HD> on the current device (cached).
-template <int BLK, int HD>
+// Resident workgroups of fwd_kernel<BLK, HD, RES> on the current device (cached).
+template <int BLK, int HD, bool RES>
 int resident_workgroups() {
   using C = FwdCfg<BLK, HD>;
   static std::once_flag once;
@@ -1625,7 +1683,7 @@ int resident_workgroups() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&fwd_kernel<BLK, HD>), C::NT,
+            &per_cu, reinterpret_cast<const void*>(&fwd_kernel<BLK, HD, RES>), C::NT,
             C::LDS_BYTES) != hipSuccess)
       return;
     n = cus * (per_cu > 0 ? per_cu : 1);
@@ -1643,6 +1701,7 @@ int32_t launch_grid(int32_t items, int resident, bool queued) {
   return g;
 }
 
+template <bool RES>
 int resident_wide_workgroups() {
   static std::once_flag once;
   static int n = 0;
@@ -1652,7 +1711,7 @@ int resident_wide_workgroups() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&fwd_wide_kernel), Wide::NT,
+            &per_cu, reinterpret_cast<const void*>(&fwd_wide_kernel<RES>), Wide::NT,
             Wide::LDS_BYTES) != hipSuccess)
       return;
     n = cus * (per_cu > 0 ? per_cu : 1);
@@ -1660,65 +1719,67 @@ int resident_wide_workgroups() {
   return n;
 }
 
+template <bool RES>
 bsa_status launch_wide(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
                        int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
                        const int32_t* work, int32_t n_items, int32_t n_merges, int32_t n_slots,
                        float sl2, void* o, float* lse, float* part, int32_t* ctr, int32_t* mctr,
-                       hipStream_t stream) {
+                       const void* r, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_wide_kernel),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_wide_kernel<RES>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                static_cast<int>(Wide::LDS_BYTES));
   });
   if (attr != hipSuccess) return BSA_ERR_HIP;
   const int32_t items = work ? n_items : n_rows;
-  const int resident = resident_wide_workgroups();
+  const int resident = resident_wide_workgroups<RES>();
   if (resident <= 0) return BSA_ERR_HIP;
   const int32_t grid = launch_grid(items, resident, work != nullptr);
   if (grid > 0) {
-    hipLaunchKernelGGL(fwd_wide_kernel, dim3(grid), dim3(Wide::NT), Wide::LDS_BYTES, stream,
+    hipLaunchKernelGGL(fwd_wide_kernel<RES>, dim3(grid), dim3(Wide::NT), Wide::LDS_BYTES, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, n_merges,
                        N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr,
-                       work ? n_slots : 0, mctr);
+                       work ? n_slots : 0, mctr, static_cast<const uint16_t*>(r));
     BSA_HIP_CHECK_LAUNCH();
   }
   return BSA_OK;
 }
 
-template <int BLK, int HD>
+template <int BLK, int HD, bool RES>
 bsa_status launch_fwd(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
                       int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
                       const int32_t* work, int32_t n_items, int32_t n_merges, float sl2, void* o,
-                      float* lse, float* part, int32_t* ctr, hipStream_t stream) {
+                      float* lse, float* part, int32_t* ctr, const void* r, hipStream_t stream) {
   using C = FwdCfg<BLK, HD>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<BLK, HD>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<BLK, HD, RES>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                static_cast<int>(C::LDS_BYTES));
   });
   if (attr != hipSuccess) return BSA_ERR_HIP;
   const int32_t items = work ? n_items : n_rows;
-  const int resident = resident_workgroups<BLK, HD>();
+  const int resident = resident_workgroups<BLK, HD, RES>();
   if (resident <= 0) return BSA_ERR_HIP;
   const int32_t grid = launch_grid(items, resident, work != nullptr);
   if (grid > 0) {
-    hipLaunchKernelGGL((fwd_kernel<BLK, HD>), dim3(grid), dim3(C::NT), C::LDS_BYTES, stream,
+    hipLaunchKernelGGL((fwd_kernel<BLK, HD, RES>), dim3(grid), dim3(C::NT), C::LDS_BYTES, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, n_merges,
-                       N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr);
+                       N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr,
+                       static_cast<const uint16_t*>(r));
     BSA_HIP_CHECK_LAUNCH();
   }
   if (work && n_merges > 0) {
     constexpr int wg_per_row = BLK * (HD / 4) / kMergeThreads;
-    hipLaunchKernelGGL((merge_kernel<BLK, HD>), dim3(n_merges * wg_per_row), dim3(kMergeThreads),
+    hipLaunchKernelGGL((merge_kernel<BLK, HD, RES>), dim3(n_merges * wg_per_row), dim3(kMergeThreads),
                        0, stream,
                        work + 4 * size_t(n_items), part, N, nb, n_rows,
-                       static_cast<uint16_t*>(o), lse);
+                       static_cast<uint16_t*>(o), lse, static_cast<const uint16_t*>(r));
     BSA_HIP_CHECK_LAUNCH();
   }
   return BSA_OK;
@@ -1734,19 +1795,20 @@ extern "C" BSA_API size_t bsa_forward_workspace_bytes(int32_t n_slots, int32_t D
          size_t(n_slots) * size_t(block) * size_t(D + 2) * sizeof(float);
 }
 
-extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v,
-                                          int32_t B, int32_t H, int32_t N, int32_t D,
-                                          int32_t block, const int32_t* row_ptr_dev,
-                                          const int32_t* col_idx_dev, const int32_t* work_dev,
-                                          int32_t n_items, int32_t n_merges, int32_t n_slots,
-                                          float scale, void* o, float* lse, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
-  using namespace bsa;
+namespace bsa {
+namespace {
+// The forward with an optional residual r added before O is rounded.
+bsa_status forward_impl(const void* q, const void* k, const void* v, int32_t B, int32_t H,
+                        int32_t N, int32_t D, int32_t block, const int32_t* row_ptr_dev,
+                        const int32_t* col_idx_dev, const int32_t* work_dev, int32_t n_items,
+                        int32_t n_merges, int32_t n_slots, float scale, const void* r, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !row_ptr_dev || !col_idx_dev) return BSA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return BSA_ERR_INVALID_ARG;
   if (!supported_shape(D, block)) return BSA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return BSA_ERR_INVALID_ARG;
+  if (r != nullptr && !aligned16(r)) return BSA_ERR_INVALID_ARG;
   if (!(scale == scale)) return BSA_ERR_INVALID_ARG;
   const int32_t nb = n_blocks(N, block);
   // Buffer offsets inside one head are 32-bit: keep a head plus one tile below 2^31 bytes.
@@ -1774,14 +1836,50 @@ extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const vo
                          : nullptr;
 #define BSA_FWD_ARGS                                                                            \
   q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items, n_merges, sl2, o, lse, \
-      part, ctr, s
+      part, ctr, r, s
+  const bool res = r != nullptr;
   if (block == 64 && D == 64)
-    return launch_wide(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items,
-                       n_merges, n_slots, sl2, o, lse, part, ctr, mctr, s);
-  if (block == 64 && D == 128) return launch_fwd<64, 128>(BSA_FWD_ARGS);
-  if (block == 128 && D == 64) return launch_fwd<128, 64>(BSA_FWD_ARGS);
-  return launch_fwd<128, 128>(BSA_FWD_ARGS);
+    return res ? launch_wide<true>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev,
+                                   n_items, n_merges, n_slots, sl2, o, lse, part, ctr, mctr, r, s)
+               : launch_wide<false>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev,
+                                    n_items, n_merges, n_slots, sl2, o, lse, part, ctr, mctr, r,
+                                    s);
+  if (block == 64 && D == 128)
+    return res ? launch_fwd<64, 128, true>(BSA_FWD_ARGS) : launch_fwd<64, 128, false>(BSA_FWD_ARGS);
+  if (block == 128 && D == 64)
+    return res ? launch_fwd<128, 64, true>(BSA_FWD_ARGS) : launch_fwd<128, 64, false>(BSA_FWD_ARGS);
+  return res ? launch_fwd<128, 128, true>(BSA_FWD_ARGS) : launch_fwd<128, 128, false>(BSA_FWD_ARGS);
 #undef BSA_FWD_ARGS
+}
+}  // namespace
+}  // namespace bsa
+
+extern "C" BSA_API bsa_status bsa_forward(const void* q, const void* k, const void* v,
+                                          int32_t B, int32_t H, int32_t N, int32_t D,
+                                          int32_t block, const int32_t* row_ptr_dev,
+                                          const int32_t* col_idx_dev, const int32_t* work_dev,
+                                          int32_t n_items, int32_t n_merges, int32_t n_slots,
+                                          float scale, void* o, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return bsa::forward_impl(q, k, v, B, H, N, D, block, row_ptr_dev, col_idx_dev, work_dev,
+                           n_items, n_merges, n_slots, scale, nullptr, o, lse, workspace,
+                           workspace_bytes, stream);
+}
+
+extern "C" BSA_API bsa_status bsa_forward_compensated(
+    const void* q, const void* k, const void* v, int32_t B, int32_t H, int32_t N, int32_t D,
+    int32_t block, const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
+    const int32_t* work_dev, int32_t n_items, int32_t n_merges, int32_t n_slots, float scale,
+    const void* r, void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (r == nullptr) return BSA_ERR_INVALID_ARG;
+  // r and o must not overlap (r is read while other rows of o are written).
+  const size_t bytes = size_t(B > 0 ? B : 0) * size_t(H > 0 ? H : 0) * size_t(N > 0 ? N : 0) *
+                       size_t(D > 0 ? D : 0) * 2;
+  const uintptr_t rb = reinterpret_cast<uintptr_t>(r), ob = reinterpret_cast<uintptr_t>(o);
+  if (o != nullptr && rb < ob + bytes && ob < rb + bytes) return BSA_ERR_INVALID_ARG;
+  return bsa::forward_impl(q, k, v, B, H, N, D, block, row_ptr_dev, col_idx_dev, work_dev,
+                           n_items, n_merges, n_slots, scale, r, o, lse, workspace,
+                           workspace_bytes, stream);
 }
 
 extern "C" BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* v,

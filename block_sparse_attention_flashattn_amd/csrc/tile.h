@@ -8,6 +8,7 @@ namespace bsa {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define BSA_LDS __attribute__((address_space(3)))
 
@@ -42,6 +43,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const uint16_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
   return uint32_t(lo) | (uint32_t(hi) << 16);
 }
+
+// The two bf16 values packed in a 32-bit word, widened to fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,

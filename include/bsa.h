@@ -55,7 +55,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 10
+#define BSA_ABI_VERSION 11
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -355,6 +355,26 @@ BSA_API bsa_status bsa_residual(const void* o_dense, const void* o_sparse, void*
                                 void* stream);
 BSA_API bsa_status bsa_compensate(const void* o_sparse, const void* r, void* o_out, int64_t n,
                                   void* stream);
+
+/*
+ * bsa_forward with the residual added in its epilogue (device, async): the
+ * reuse step of the same section (sparse output plus the cached residual) in
+ * one pass instead of bsa_forward followed by bsa_compensate.
+ *   O[bi,h,a,:] = round_bf16(attention_fp32[bi,h,a,:] + r[bi,h,a,:]), the sum
+ *   formed in fp32 from the unrounded attention output and r, rounded once to
+ *   bf16 (nearest even); LSE is the attention's, as in bsa_forward.
+ *   r   bf16 [B,H,N,D] device, 16-byte aligned (e.g. bsa_residual's output),
+ *       not overlapping o.
+ * Every other argument, the work list and workspace rules and the errors are
+ * bsa_forward's; INVALID_ARG also for r NULL, misaligned or overlapping o.
+ */
+BSA_API bsa_status bsa_forward_compensated(const void* q, const void* k, const void* v,
+                                           int32_t B, int32_t H, int32_t N, int32_t D,
+                                           int32_t block, const int32_t* row_ptr_dev,
+                                           const int32_t* col_idx_dev, const int32_t* work_dev,
+                                           int32_t n_items, int32_t n_merges, int32_t n_slots,
+                                           float scale, const void* r, void* o, float* lse,
+                                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Token-level KV selection with tile-aligned query groups (device, async).  Page

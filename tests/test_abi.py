@@ -33,7 +33,7 @@ def test_status_strings_and_version():
     assert bsa.status_string(-1) == "BSA_ERR_INVALID_ARG"
     assert bsa.status_string(-5) == "BSA_ERR_PLAN_MISMATCH"
     assert bsa.status_string(-99) == "BSA_ERR_UNKNOWN"
-    assert bsa.abi_version() == bsa.ABI_VERSION == 10
+    assert bsa.abi_version() == bsa.ABI_VERSION == 11
 
 
 def test_budget_matches_oracle():

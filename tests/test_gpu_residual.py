@@ -67,3 +67,59 @@ def test_anchor_reuse_matches_oracle(block, D):
         assert err.max() <= 3e-2 and err.mean() <= 3e-3
         if t > 0:
             assert np.linalg.norm(got - od) < 0.5 * np.linalg.norm(os_ - od)
+
+
+def _rand_csr(rng, rows, nb, p):
+    cols = []
+    for r in range(rows):
+        m = rng.random(nb) < p
+        m[r % nb] = True
+        cols.append(np.flatnonzero(m))
+    rp = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    return rp, np.concatenate(cols).astype(np.int32)
+
+
+@pytest.mark.parametrize("block,D,max_tiles", [(64, 64, 0), (64, 64, 2), (64, 128, 0),
+                                               (64, 128, 2), (128, 64, 2), (128, 128, 0)])
+def test_forward_compensated_matches_oracle(block, D, max_tiles):
+    """bsa_forward_compensated: O = attention + R formed in fp32 and rounded once, for
+    every kernel (64 x 64 and the general one) with and without cut rows (combined in
+    the kernel or by the merge pass): the oracle's attention plus R within the forward's
+    tolerance, the same LSE bits as bsa_forward, and with R = 0 the same O bits."""
+    from oracle import attention as OA
+    bsa = need_gpu()
+    print(f"case block={block} D={D} max_tiles={max_tiles}", flush=True)
+    B, H, N = 1, 3, 6 * block - 19
+    nb = -(-N // block)
+    rng = np.random.default_rng(block * 7 + D + max_tiles)
+    rp, ci = _rand_csr(rng, B * H * nb, nb, 0.6)
+    q, k, v = W.gaussian_qkv(500 + block + D, B, H, N, D)
+    r = (torch.randn(B, H, N, D, generator=torch.Generator("cpu").manual_seed(9)) * 0.3
+         ).to(torch.bfloat16)
+    qd, kd, vd, rd = q.cuda(), k.cuda(), v.cuda(), r.cuda()
+    work = bsa.Work.from_host(rp, D, block, max_tiles, "cuda", nb=nb, n_groups=2) \
+        if max_tiles else None
+    if work is not None:
+        assert work.n_merges > 0
+    o0, l0 = bsa.forward(qd, kd, vd, rp, ci, block, work=work)
+    o1, l1 = bsa.forward(qd, kd, vd, rp, ci, block, work=work, residual=rd)
+    oz, lz = bsa.forward(qd, kd, vd, rp, ci, block, work=work, residual=torch.zeros_like(rd))
+    torch.cuda.synchronize()
+    assert torch.equal(l0, l1) and torch.equal(l0, lz)
+    assert torch.equal(o0, oz)
+    O, _ = OA.block_sparse_attention(q, k, v, rp, ci, block, 1.0 / np.sqrt(D))
+    want = O + r.float().numpy().astype(np.float64)
+    err = np.abs(o1.float().cpu().numpy().astype(np.float64) - want)
+    print(f"max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_forward_compensated_rejects_overlap():
+    bsa = need_gpu()
+    B, H, N, D, block = 1, 1, 128, 64, 64
+    q = torch.zeros(B, H, N, D, dtype=torch.bfloat16, device="cuda")
+    rp = np.array([0, 1, 2], np.int32)
+    ci = np.array([0, 1], np.int32)
+    out = torch.empty_like(q)
+    with pytest.raises(bsa.BsaError):
+        bsa.forward(q, q, q, rp, ci, block, out=out, residual=out)
