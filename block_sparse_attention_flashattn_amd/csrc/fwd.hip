@@ -170,7 +170,7 @@ constexpr float kSumCap = 1048576.0f;
 
 // RES: O = attention + R (a residual added before O is rounded).
 template <int BLK, int HD, bool RES>
-__global__ __launch_bounds__(4 * BLK) void fwd_kernel(
+__global__ __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
@@ -418,11 +418,12 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
             if (kv >= valid) s[kt][i] = -INFINITY;
           }
       }
-      // Probabilities against the running max as it stands.  The tile's max
-      // is needed only when a probability could leave the safe range, which
-      // some lane's partial row sum shows (above kSumCap, or not finite), or
-      // while a row has no max yet; then each row's max is raised to the
-      // tile's, its state rescaled and the tile's probabilities recomputed.
+      // Probabilities against the running max as it stands.  Past a row's
+      // first tile the tile's max is needed only when a probability could
+      // leave the safe range, which some lane's partial row sum shows (above
+      // kSumCap, or not finite), or while a row has no max yet; then each
+      // row's max is raised to the tile's, its state rescaled and the tile's
+      // probabilities recomputed.  The first tile takes its max up front.
       // Row sums in four independent chains (no long serial add dependency).
       float lt;
       bf16x8 pb[C::NKT][2];
@@ -442,9 +443,7 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
           }
         lt = (ls[0] + ls[1]) + (ls[2] + ls[3]);
       };
-      probs();
-      if (__builtin_expect(
-              __builtin_amdgcn_ballot_w64(!(lt <= kSumCap) || m_run == -INFINITY) != 0, 0)) {
+      auto raise_max = [&]() {
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
@@ -461,6 +460,13 @@ __global__ __launch_bounds__(4 * BLK) void fwd_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[u2][i] *= alpha;
         m_run = up ? mt : m_run;
+      };
+      if (u == 0) raise_max();
+      probs();
+      if (u != 0 &&
+          __builtin_expect(
+              __builtin_amdgcn_ballot_w64(!(lt <= kSumCap) || m_run == -INFINITY) != 0, 0)) {
+        raise_max();
         probs();
       }
       l_run += lt;
