@@ -1605,6 +1605,222 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void g
 constexpr int kMergeThreads = 256;
 constexpr int kUnroll = 8;
 
+// Gathered attention at head dim 128 (same page and section as gather_kernel).
+// One workgroup of four wavefronts per (head, group of 64 queries): wave w owns
+// query group w % 2 (32 of the group's queries) and key half w / 2 (keys
+// 32 (w / 2) .. +31 of every 64-token tile).  The tile's 64 K and V rows are
+// gathered by token index into registers one tile ahead (every lane moves
+// eight 16-byte chunks: rows 4 (w + 4 s) + lane / 16, s = 0..3, of K and of V)
+// and written to LDS, swizzled, in two stages; one barrier per tile makes the
+// rows visible and frees the other stage.  The compute is the block forward's
+// at D = 128: S^T = K Q^T with the K operands from LDS, the online softmax,
+// O^T += V^T P^T with V^T read transposed; the key halves meet at the end
+// through LDS and O, LSE are written at the group's token positions.
+struct Gather128 {
+  static constexpr int HD = 128, ROWB = 256, TILEB = 64 * ROWB;  // 16 KiB
+  static constexpr int STAGEB = 2 * TILEB;                         // K tile, V tile
+  static constexpr size_t LDS_BYTES = 2 * STAGEB + 2 * 64 * 2 * 4;  // + m, l exchange
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gather128_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ groups,
+    const int32_t* __restrict__ tokens, int32_t T, int32_t N, int32_t G, float sl2,
+    uint16_t* __restrict__ O, float* __restrict__ LSE) {
+  using GC = Gather128;
+  constexpr int HD = GC::HD, ROWB = GC::ROWB;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
+  float* ml = reinterpret_cast<float*>(smem + 2 * size_t(GC::STAGEB));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qg = wave & 1, kh = wave >> 1;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int row = blockIdx.x;
+  const int bh = row / G;
+  const int32_t* ids = groups + size_t(row) * 64;
+  const int32_t* toks = tokens + size_t(row) * T;
+  const uint32_t hbytes = static_cast<uint32_t>(N) * ROWB;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, hbytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, hbytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, hbytes);
+
+  // Query fragments (B operand of S^T = K Q^T): d = 16c + 8hh .. +7 of query
+  // ids[32 qg + ql]; a query outside [0, N) reads zeros.
+  bf16x8 qf[8];
+  {
+    const int t = ids[32 * qg + ql];
+    const uint32_t base = (t >= 0 && t < N) ? uint32_t(t) * ROWB : hbytes;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                             qr, base + uint32_t(32 * c + 16 * hh), 0, 0));
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+
+  // Token at list position idx, or -1 past the list or outside [0, N).
+  auto tok_at = [&](int idx) {
+    const int t = idx < T ? toks[idx] : -1;
+    return (t >= 0 && t < N) ? t : -1;
+  };
+  // This lane's chunks of tile tt: K and V rows 4 (wave + 4 sg) + lane / 16
+  // (sg = 0..3: the 16 1-KiB segments of a tile over the four waves), chunk
+  // lane % 16 of each row's LDS position, from source chunk
+  // (lane % 16) ^ swizzle(row).  ltok: the lane's token of the tile (lane l
+  // holds position l).
+  v4u kx[4], vx[4];
+  auto load_rows = [&](int ltok) {
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+      const int r = 4 * (wave + 4 * sg) + (lane >> 4);
+      const int t = __builtin_amdgcn_ds_bpermute(r << 2, ltok);
+      const uint32_t src = t >= 0 ? uint32_t(t) * ROWB + uint32_t(((lane & 15) ^
+                                        chunk_swizzle<ROWB>(r)) << 4)
+                                  : hbytes;
+      kx[sg] = __builtin_amdgcn_raw_buffer_load_b128(kr, src, 0, 0);
+      vx[sg] = __builtin_amdgcn_raw_buffer_load_b128(vr, src, 0, 0);
+    }
+  };
+  auto store_rows = [&](int st) {
+    const uint32_t kb = lds0 + uint32_t(st) * GC::STAGEB;
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+      const uint32_t off = uint32_t(wave + 4 * sg) * 1024u + uint32_t(lane) * 16u;
+      *reinterpret_cast<BSA_LDS v4u*>(static_cast<uintptr_t>(kb + off)) = kx[sg];
+      *reinterpret_cast<BSA_LDS v4u*>(static_cast<uintptr_t>(kb + GC::TILEB + off)) = vx[sg];
+    }
+  };
+
+  const int ntiles = (T + 63) / 64;
+  int ltok = tok_at(lane);
+  load_rows(ltok);
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int st = tt & 1;
+    // Keys of this wave's half that exist (bit j: key 32 kh + j of the tile).
+    const uint32_t kvalid =
+        static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(ltok >= 0) >> (32 * kh));
+    store_rows(st);  // the other waves finished reading this stage (tile tt - 2)
+    if (tt + 1 < ntiles) {
+      ltok = tok_at(64 * (tt + 1) + lane);
+      load_rows(ltok);
+    }
+    __syncthreads();  // tile tt is in LDS; every wave is done with tile tt - 1
+    const uint32_t ks = lds0 + uint32_t(st) * GC::STAGEB, vs = ks + GC::TILEB;
+    const int key = 32 * kh + ql;
+    bf16x8 ka[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ka[c] = lds_read16(ks + swz<ROWB>(key, 2 * c + hh));
+    const f32x16 zero = {};
+    f32x16 sv = zero;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], c == 0 ? zero : sv, 0, 0, 0);
+    v4s vlo[2][4], vhi[2][4];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const int kb = 32 * kh + 16 * c2;
+        const int col = 32 * u2 + tr_col;
+        vlo[c2][u2] = lds_read_tr(vs + swz<ROWB>(kb + tr_row, col >> 3) + (col & 7) * 2);
+        vhi[c2][u2] = lds_read_tr(vs + swz<ROWB>(kb + 8 + tr_row, col >> 3) + (col & 7) * 2);
+      }
+    // register i: key 8(i/4) + 4hh + (i%4) of this half; missing keys get -inf
+    if (kvalid != 0xffffffffu) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!((kvalid >> (8 * (i >> 2) + 4 * hh + (i & 3))) & 1u)) sv[i] = -INFINITY;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+    mx = fmaxf(mx, other_half(mx));
+    const float mt = fmaxf(m_run, mx * sl2);
+    const float alpha = m_run == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - mt);
+    l_run *= alpha;
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[u2][i] *= alpha;
+    m_run = mt;
+    const float m_use = mt == -INFINITY ? 0.f : mt;
+    bf16x8 pb[2];
+    float ls[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -m_use));
+      if (i < 4)
+        ls[i] = p;
+      else
+        ls[i & 3] += p;
+      pb[i >> 3][i & 7] = static_cast<__bf16>(p);
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(vlo[c2][u2], vhi[c2][u2], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c2], acc[u2], 0, 0, 0);
+      }
+  }
+
+  // Key-half merge through stage 0 (every wave is past its last tile's reads
+  // once all have arrived): wave (qg, 1) sends its state, wave (qg, 0) combines
+  // and writes the group's rows.
+  const float l_half = l_run + other_half(l_run);
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(smem) + size_t(qg) * 64 * 4 * 16;
+  if (kh == 1) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(mg + ((u * 4 + g4) * 64 + lane) * 4) =
+            f32x4{acc[u][4 * g4], acc[u][4 * g4 + 1], acc[u][4 * g4 + 2], acc[u][4 * g4 + 3]};
+    ml[(qg * 2) * 64 + lane] = m_run;
+    ml[(qg * 2 + 1) * 64 + lane] = l_half;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = ml[(qg * 2) * 64 + lane];
+    const float l1 = ml[(qg * 2 + 1) * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    const float l = l_half * a0 + l1 * a1;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int t = ids[32 * qg + ql];
+    if (t >= 0 && t < N) {
+      uint16_t* orow = O + head + size_t(t) * HD;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(mg + ((u * 4 + g4) * 64 + lane) * 4);
+          const int d = 32 * u + 8 * g4 + 4 * hh;
+          const uint32_t w0 = pack_bf16x2((acc[u][4 * g4] * a0 + o1[0] * a1) * inv,
+                                          (acc[u][4 * g4 + 1] * a0 + o1[1] * a1) * inv);
+          const uint32_t w1 = pack_bf16x2((acc[u][4 * g4 + 2] * a0 + o1[2] * a1) * inv,
+                                          (acc[u][4 * g4 + 3] * a0 + o1[3] * a1) * inv);
+          *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
+        }
+      if (LSE != nullptr && hh == 0)
+        LSE[size_t(bh) * N + t] =
+            l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+}
+
 template <int BLK, int HD, bool RES>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int32_t* __restrict__ merges,
                                                               const float* __restrict__ part,
@@ -1896,10 +2112,26 @@ extern "C" BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, c
   using namespace bsa;
   if (!q || !k || !v || !o || !groups || (!tokens && T > 0)) return BSA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || G < 1 || T < 0 || !(scale == scale)) return BSA_ERR_INVALID_ARG;
-  if (D != 64) return BSA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return BSA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BSA_ERR_INVALID_ARG;
   if (int64_t(N) * D * 2 >= (int64_t(1) << 31) || int64_t(B) * H * G > INT32_MAX) return BSA_ERR_UNSUPPORTED;
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
+  if (D == 128) {
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gather128_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(Gather128::LDS_BYTES));
+    });
+    if (attr != hipSuccess) return BSA_ERR_HIP;
+    hipLaunchKernelGGL(gather128_kernel, dim3(B * H * G), dim3(256), Gather128::LDS_BYTES,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), groups,
+                       tokens, T, N, G, sc * 1.4426950408889634f, static_cast<uint16_t*>(o), lse);
+    BSA_HIP_CHECK_LAUNCH();
+    return BSA_OK;
+  }
   hipLaunchKernelGGL(gather_kernel, dim3(B * H * G), dim3(128), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), groups, tokens, T, N, G,

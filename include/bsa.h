@@ -421,7 +421,7 @@ BSA_API bsa_status bsa_select_tokens(const float* mass, int32_t n_rows, int32_t 
  * the selected KV tokens of a query group are gathered by index, not repacked into
  * blocks, and the group's queries attend to exactly those tokens.
  *
- * q, k, v: bf16 [B,H,N,D], D = 64, 16-byte aligned.  groups: int32 [B,H,G,64], the
+ * q, k, v: bf16 [B,H,N,D], D = 64 or 128, 16-byte aligned.  groups: int32 [B,H,G,64], the
  * token positions of each group's 64 queries (as bsa_query_groups writes them with
  * C = 64).  tokens: int32 [B,H,G,T], the KV tokens of each group (as
  * bsa_select_tokens writes them); a list must not repeat a token (a repeat counts
@@ -432,7 +432,7 @@ BSA_API bsa_status bsa_select_tokens(const float* mass, int32_t n_rows, int32_t 
  * lse = -inf.  Rows of o and lse that no group names are not written.  scale <= 0
  * selects 1/sqrt(D); lse may be NULL.
  * Errors: INVALID_ARG (null or misaligned pointer, non-positive sizes, NaN scale),
- * UNSUPPORTED (D != 64, N*D*2 >= 2^31), HIP.
+ * UNSUPPORTED (D not 64 or 128, N*D*2 >= 2^31), HIP.
  */
 BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* v, int32_t B,
                                       int32_t H, int32_t N, int32_t D, const int32_t* groups,

@@ -169,22 +169,44 @@ def check_rows(o, lse, O, L, rows):
         assert np.abs(lse[rows][fin] - L[rows][fin]).max() <= LSE_ABS
 
 
-@pytest.mark.parametrize("N,T", [(512, 100), (512, 64), (1024, 1), (1024, 33), (1024, 640),
-                                 (320, 320)])
-def test_gather_forward_matches_oracle(N, T):
+@pytest.mark.parametrize("N,T,D", [(512, 100, 64), (512, 64, 64), (1024, 1, 64), (1024, 33, 64),
+                                   (1024, 640, 64), (320, 320, 64), (512, 100, 128),
+                                   (512, 64, 128), (1024, 1, 128), (1024, 33, 128),
+                                   (1024, 640, 128), (320, 320, 128)])
+def test_gather_forward_matches_oracle(N, T, D):
     """Oracle groups (median split) and seeded token lists: ragged last tiles, a tile half
-    with no key, one token, every token."""
+    with no key, one token, every token; both head dims."""
     bsa = need_gpu()
-    print(f"case N={N} T={T}", flush=True)
-    B, H, D = 1, 2, 64
-    q, k, v = W.gaussian_qkv(N + T, B, H, N, D)
+    print(f"case N={N} T={T} D={D}", flush=True)
+    B, H = 1, 2
+    q, k, v = W.gaussian_qkv(N + T + D, B, H, N, D)
     G = N // 64
     groups = np.stack([OT.median_split_groups(q[0, h].float().numpy(), 64) for h in range(H)])
     tokens = np.stack([random_lists(7 * h + T, G, N, T) for h in range(H)])
     o, lse = run_gather(bsa, q, k, v, groups[None].astype(np.int32), tokens[None])
     for h in range(H):
-        O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[h], tokens[h], 1 / 8.0)
+        O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[h], tokens[h],
+                                     1 / np.sqrt(D))
         check_rows(o[0, h], lse[0, h], O, L, np.arange(N))
+
+
+def test_gather_forward_d128_long_head_sampled():
+    """A dynamic-config head at D = 128 (N = 8192, 128 groups, 820 tokens each, about
+    10 %); the oracle on every thirteenth group."""
+    bsa = need_gpu()
+    B, H, N, D, T = 1, 2, 8192, 128, 820
+    q, k, v = W.gaussian_qkv(8192 + 128, B, H, N, D)
+    G = N // 64
+    rng = np.random.default_rng(6)
+    groups = np.stack([rng.permutation(N).reshape(G, 64) for _ in range(H)]).astype(np.int32)
+    groups.sort(axis=-1)
+    tokens = np.stack([random_lists(11 + h, G, N, T) for h in range(H)])
+    o, lse = run_gather(bsa, q, k, v, groups[None], tokens[None])
+    for h in range(H):
+        for g in range(0, G, 13):
+            O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[h, g:g + 1],
+                                         tokens[h, g:g + 1], 1 / np.sqrt(D))
+            check_rows(o[0, h], lse[0, h], O, L, groups[h, g])
 
 
 def test_gather_forward_t2i_head_length_sampled():
@@ -206,10 +228,11 @@ def test_gather_forward_t2i_head_length_sampled():
             check_rows(o[0, h], lse[0, h], O, L, groups[h, g])
 
 
-def test_gather_forward_skips_out_of_range_entries():
+@pytest.mark.parametrize("D", [64, 128])
+def test_gather_forward_skips_out_of_range_entries(D):
     """Token entries outside [0, N) are skipped; so are group slots outside [0, N)."""
     bsa = need_gpu()
-    B, H, N, D, T = 1, 1, 256, 64, 90
+    B, H, N, T = 1, 1, 256, 90
     q, k, v = W.gaussian_qkv(31, B, H, N, D)
     G = N // 64
     groups = np.arange(N, dtype=np.int32).reshape(G, 64)
@@ -224,16 +247,17 @@ def test_gather_forward_skips_out_of_range_entries():
     for g in range(G):
         keep = bad_t[g][(bad_t[g] >= 0) & (bad_t[g] < N)]
         O, L = OT.gathered_attention(q[0, 0], k[0, 0], v[0, 0], groups[g:g + 1], keep[None],
-                                     1 / 8.0)
+                                     1 / np.sqrt(D))
         rows = bad_g[g][bad_g[g] >= 0]
         check_rows(o[0, 0], lse[0, 0], O, L, rows)
     assert (o[0, 0, 64 + 5] == 3.0).all() and np.isneginf(lse[0, 0, 64 + 5])
 
 
-def test_gather_forward_empty_lists_and_unnamed_rows():
+@pytest.mark.parametrize("D", [64, 128])
+def test_gather_forward_empty_lists_and_unnamed_rows(D):
     """T = 0: every named row gets O = 0 and LSE = -inf; rows no group names keep `out`."""
     bsa = need_gpu()
-    B, H, N, D = 1, 2, 384, 64
+    B, H, N = 1, 2, 384
     q, k, v = W.gaussian_qkv(8, B, H, N, D)
     groups = np.arange(128, dtype=np.int32).reshape(1, 1, 2, 64).repeat(H, 1)
     out = torch.full((B, H, N, D), -2.0, dtype=torch.bfloat16, device="cuda")
@@ -245,17 +269,18 @@ def test_gather_forward_empty_lists_and_unnamed_rows():
     o, lse = run_gather(bsa, q, k, v, groups, tokens, out=out)
     assert (o[:, :, 128:] == -2.0).all()
     for h in range(H):
-        O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[0, h], tokens[0, h], 1 / 8.0)
+        O, L = OT.gathered_attention(q[0, h], k[0, h], v[0, h], groups[0, h], tokens[0, h],
+                                     1 / np.sqrt(D))
         check_rows(o[0, h], lse[0, h], O, L, np.arange(128))
 
 
 def test_gather_forward_rejects_unsupported():
     bsa = need_gpu()
-    q = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 1, 128, 96), dtype=torch.bfloat16, device="cuda")
     g = torch.zeros((1, 1, 2, 64), dtype=torch.int32, device="cuda")
     t = torch.zeros((1, 1, 2, 8), dtype=torch.int32, device="cuda")
     with pytest.raises(bsa.BsaError):
-        bsa.gather_forward(q, q, q, g, t)
+        bsa.gather_forward(q, q, q, g, t)        # head dim 96 is not supported
     q64 = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         bsa.gather_forward(q64, q64, q64, g[..., :32].contiguous(), t)
