@@ -426,7 +426,7 @@ def main():
         if w.D == 64 and w.block == 64:
             g = torch.Generator("cpu").manual_seed(1000 + w.N)
             do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
-            bws = torch.empty(max(bsa.backward_workspace_bytes(w.B, w.H, w.N, w.block, plan.nnz),
+            bws = torch.empty(max(bsa.backward_workspace_bytes(w.B, w.H, w.N, w.D, w.block, plan.nnz),
                                   256), dtype=torch.uint8, device=dev)
             bsa.backward(qd, kd, vd, o, lse, do, plan.row_ptr, col_idx[:plan.nnz], w.block,
                          workspace=bws)

@@ -74,14 +74,14 @@ _SIGS = {
     "bsa_select_tokens": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "bsa_gather_forward": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
                                   _f32, _vp, _vp, _vp]),
-    "bsa_backward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i64]),
+    "bsa_backward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64]),
     "bsa_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                             _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
 # BSA_ABI_VERSION of include/bsa.h that these signatures and work-list layouts follow.
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 
 class BsaError(RuntimeError):
@@ -694,8 +694,8 @@ def gather_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, groups: to
     return out, lse
 
 
-def backward_workspace_bytes(B: int, H: int, N: int, block: int, nnz: int) -> int:
-    return int(lib.bsa_backward_workspace_bytes(B, H, N, block, int(nnz)))
+def backward_workspace_bytes(B: int, H: int, N: int, D: int, block: int, nnz: int) -> int:
+    return int(lib.bsa_backward_workspace_bytes(B, H, N, D, block, int(nnz)))
 
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
@@ -710,7 +710,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     rp = _dev_i32(row_ptr, q.device)
     ci = _dev_i32(col_idx, q.device)
     nnz = ci.numel()                 # an upper bound of row_ptr[-1]
-    need = backward_workspace_bytes(B, H, N, block, nnz)
+    need = backward_workspace_bytes(B, H, N, D, block, nnz)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

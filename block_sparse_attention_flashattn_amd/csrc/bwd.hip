@@ -31,8 +31,6 @@ namespace bsa {
 namespace {
 
 constexpr int kBB = 64;     // block (query block = key block)
-constexpr int kBD = 64;     // head dimension
-constexpr int kRB = 128;    // bytes of one bf16 row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDqStages = 2;  // K/V ring depth of the dQ kernel
 
@@ -56,25 +54,26 @@ __device__ __forceinline__ float dot8(v4u a, v4u b) {
 }
 
 // Per query row t: (LSE_t * log2(e), delta_t); rows with LSE = -inf (no active key)
-// get +inf so that every probability of the row is exp2(-inf) = 0.  Eight lanes
+// get +inf so that every probability of the row is exp2(-inf) = 0.  HD / 8 lanes
 // per row, 16 bytes each.  Also clears the two partial-slot counters.
+template <int HD>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ O,
                                                    const uint16_t* __restrict__ dO,
                                                    const float* __restrict__ LSE, int64_t rows,
                                                    float2* __restrict__ out,
                                                    int32_t* __restrict__ slot_ctr) {
   if (blockIdx.x == 0 && threadIdx.x < 2) slot_ctr[threadIdx.x] = 0;  // read by transpose
-  const int64_t t = (int64_t(blockIdx.x) * 256 + threadIdx.x) >> 3;
-  const int c = threadIdx.x & 7;
+  constexpr int LPR = HD / 8;  // lanes per row
+  const int64_t t = (int64_t(blockIdx.x) * 256 + threadIdx.x) / LPR;
+  const int c = threadIdx.x & (LPR - 1);
   float acc = 0.f;
   if (t < rows) {
-    const v4u a = *reinterpret_cast<const v4u*>(O + t * kBD + 8 * c);
-    const v4u b = *reinterpret_cast<const v4u*>(dO + t * kBD + 8 * c);
+    const v4u a = *reinterpret_cast<const v4u*>(O + t * HD + 8 * c);
+    const v4u b = *reinterpret_cast<const v4u*>(dO + t * HD + 8 * c);
     acc = dot8(a, b);
   }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
   if (c == 0 && t < rows) {
     const float l = LSE[t];
     out[t] = make_float2(l > -INFINITY ? l * kLog2e : INFINITY, acc);
@@ -104,12 +103,31 @@ __device__ __forceinline__ v4i uniform_desc(const void* base, uint32_t bytes) {
   return d;
 }
 
-// Source offsets of the 16-byte chunks a lane moves in dma_half: segments 0, 2
-// (ve) and 1, 3 (vo) of a 32-row half tile, so that they land swizzled.
-__device__ __forceinline__ void dma_offsets(int lane, uint32_t& ve, uint32_t& vo) {
-  const int r0 = lane >> 3, p = lane & 7;
-  ve = uint32_t(r0) * kRB + uint32_t((p ^ chunk_swizzle<kRB>(r0)) << 4);
-  vo = uint32_t(r0) * kRB + uint32_t((p ^ chunk_swizzle<kRB>(8 + r0)) << 4);
+// A 32-row half tile (rows h0 .. h0 + 31 of a 64-row tile of RB-byte rows) is
+// HALF_SEGS 1-KiB segments; lane l of segment s moves the 16-byte chunk that
+// lands at its swizzled LDS position: row h0 + s * 1024 / RB + l / (RB / 16),
+// position l % (RB / 16).  off[s] is its source offset from the half's first
+// row, less 1024 (s % 4) (>= 0: segment s starts s KiB into the half), as
+// dma16x4 takes it.
+template <int RB>
+__device__ __forceinline__ void half_offsets(int lane, int h0, uint32_t (&off)[RB / 32]) {
+  constexpr int CPR = RB / 16, RPS = 1024 / RB;
+#pragma unroll
+  for (int s = 0; s < RB / 32; ++s) {
+    const int r = s * RPS + lane / CPR, p = lane % CPR;
+    off[s] = uint32_t(r) * RB + uint32_t((p ^ chunk_swizzle<RB>(h0 + r)) << 4) -
+             uint32_t(s & 3) * 1024u;
+  }
+}
+// The half tile at source offset tb of `desc` into LDS at dst (its segments
+// consecutive), from half_offsets.
+template <int RB>
+__device__ __forceinline__ void dma_half_tile(v4i desc, const uint32_t (&off)[RB / 32],
+                                              uint32_t tb, uint32_t dst) {
+#pragma unroll
+  for (int s = 0; s < RB / 32; s += 4)
+    dma16x4(desc, tb + off[s], tb + off[s + 1], tb + off[s + 2], tb + off[s + 3],
+            dst + uint32_t(s) * 1024u);
 }
 
 // The entries idx[e] of a CSR range [e0, e1) a workgroup walks in order, 64 at a
@@ -278,7 +296,18 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
 // dS = P (dP - delta), and dV^T += dO^T P, dK^T += Q^T dS with dO^T, Q^T read
 // transposed from LDS.  An unsplit column writes bf16 dK, dV; a chunk of a
 // split one writes its fp32 sums (dK unscaled) to partial slot `slot + chunk`.
-__global__ __launch_bounds__(128) void dkdv_kernel(
+// At HD = 128 the two stages take 65 KiB of LDS: two workgroups per CU, one
+// wave per SIMD, which may then use the whole register file.
+template <int HD>
+struct DkdvCfg {
+  static constexpr int RB = HD * 2, NDC = HD / 16, NDT = HD / 32;
+  static constexpr uint32_t kTile = kBB * RB, kHalf = kTile / 2, kLd = kBB * 8;
+  static constexpr uint32_t kStage = 2 * kTile + kLd;
+  static constexpr size_t LDS_BYTES = 2 * size_t(kStage);
+};
+
+template <int HD>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 2 : 1))) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ ld,
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
@@ -286,9 +315,11 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part) {
   // Two stages of (Q tile, dO tile, per-row (LSE log2 e, delta)) of one query
   // block, each wave streaming its 32-row halves by LDS DMA one block ahead.
-  constexpr uint32_t kTile = kBB * kRB, kHalf = kTile / 2, kLd = kBB * 8;
-  constexpr uint32_t kStage = 2 * kTile + kLd;
-  __shared__ __align__(16) uint8_t smem[2 * kStage];
+  using C = DkdvCfg<HD>;
+  constexpr int RB = C::RB, NDC = C::NDC, NDT = C::NDT;
+  constexpr uint32_t kTile = C::kTile, kHalf = C::kHalf, kLd = C::kLd, kStage = C::kStage;
+  constexpr int kLoads = 2 * (RB / 32) + 1;  // tile loads one stage takes per wave
+  extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,31 +331,31 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
   const int nch = slot < 0 ? 1 : __builtin_amdgcn_readfirstlane(sp.y);
   if (ch >= nch) return;
   const int bh = r / nb, j = r - bh * nb;
-  const size_t head = size_t(bh) * size_t(N) * kBD;
-  const uint32_t hbytes = static_cast<uint32_t>(N) * kRB;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+  const uint32_t hbytes = static_cast<uint32_t>(N) * RB;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, hbytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, hbytes);
   const v4i qd = uniform_desc(Q + head, hbytes), dd = uniform_desc(dO + head, hbytes);
   // (LSE log2 e, delta) of the head's rows; rows past N read zeros, which is
   // harmless: their Q and dO rows are zeros too, so they add exactly nothing.
   const v4i ldd = uniform_desc(ld + size_t(bh) * N, static_cast<uint32_t>(N) * 8u);
-  uint32_t ve, vo;
-  dma_offsets(lane, ve, vo);
+  uint32_t hoff[RB / 32];
+  half_offsets<RB>(lane, 32 * w, hoff);
   const int key = kBB * j + 32 * w + ql;
   const bool key_ok = key < N;
-  bf16x8 kf[4], vf[4];
+  bf16x8 kf[NDC], vf[NDC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t off = uint32_t(key) * kRB + uint32_t(32 * c + 16 * hh);
+  for (int c = 0; c < NDC; ++c) {
+    const uint32_t off = uint32_t(key) * RB + uint32_t(32 * c + 16 * hh);
     kf[c] = __builtin_bit_cast(bf16x8, load16(kr, off));
     vf[c] = __builtin_bit_cast(bf16x8, load16(vr, off));
   }
   // Complete these loads before the DMA-pipelined loop.
 #pragma unroll
-  for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(kf[c]), "v"(vf[c]));
-  f32x16 dk[2], dv[2];
+  for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(kf[c]), "v"(vf[c]));
+  f32x16 dk[NDT], dv[NDT];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NDT; ++u)
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       dk[u][x] = 0.f;
@@ -338,14 +369,14 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
   const int e1 = c0 + int(int64_t(c1 - c0) * (ch + 1) / nch);
   IndexWindow rows;
   rows.init(row_idx, e0, e1, lane);
-  // This wave's halves of query block i into stage st (9 loads); a block outside
-  // [0, nb) reads past the buffers, i.e. zeros.
+  // This wave's halves of query block i into stage st (kLoads loads); a block
+  // outside [0, nb) reads past the buffers, i.e. zeros.
   auto issue = [&](int i, int st) {
     const bool ok = i >= 0 && i < nb;
     const uint32_t tb = ok ? uint32_t(i) * kTile + uint32_t(w) * kHalf : hbytes;
     const uint32_t sb = lds0 + uint32_t(st) * kStage;
-    dma_half(qd, ve + tb, vo + tb, sb + uint32_t(w) * kHalf);
-    dma_half(dd, ve + tb, vo + tb, sb + kTile + uint32_t(w) * kHalf);
+    dma_half_tile<RB>(qd, hoff, tb, sb + uint32_t(w) * kHalf);
+    dma_half_tile<RB>(dd, hoff, tb, sb + kTile + uint32_t(w) * kHalf);
     const uint32_t lo = ok ? uint32_t(kBB * i + 32 * w) * 8u + 4u * uint32_t(lane)
                            : static_cast<uint32_t>(N) * 8u;
     dma4(ldd, lo, sb + 2 * kTile + uint32_t(w) * (kLd / 2));
@@ -358,7 +389,7 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
     if (e + 1 < e1) {
       i_next = rows.at(e + 1, lane);
       issue(i_next, st ^ 1);
-      wait_vm_n(9);
+      wait_vm_n(kLoads);
     } else {
       wait_vm(0);
     }
@@ -371,9 +402,9 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
       const f32x16 zero = {};
       f32x16 s, dp;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 qa = lds_read16(qs + swz<kRB>(32 * g + ql, 2 * c + hh));
-        const bf16x8 da = lds_read16(dss + swz<kRB>(32 * g + ql, 2 * c + hh));
+      for (int c = 0; c < NDC; ++c) {
+        const bf16x8 qa = lds_read16(qs + swz<RB>(32 * g + ql, 2 * c + hh));
+        const bf16x8 da = lds_read16(dss + swz<RB>(32 * g + ql, 2 * c + hh));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], c == 0 ? zero : s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[c], c == 0 ? zero : dp, 0, 0, 0);
       }
@@ -398,14 +429,14 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NDT; ++u) {
           const int col = 32 * u + tr_col;
           const int r_lo = 32 * g + 16 * k2 + tr_row;
           const uint32_t clo = (col & 7) * 2;
-          const v4s dlo = lds_read_tr(dss + swz<kRB>(r_lo, col >> 3) + clo);
-          const v4s dhi = lds_read_tr(dss + swz<kRB>(r_lo + 8, col >> 3) + clo);
-          const v4s qlo = lds_read_tr(qs + swz<kRB>(r_lo, col >> 3) + clo);
-          const v4s qhi = lds_read_tr(qs + swz<kRB>(r_lo + 8, col >> 3) + clo);
+          const v4s dlo = lds_read_tr(dss + swz<RB>(r_lo, col >> 3) + clo);
+          const v4s dhi = lds_read_tr(dss + swz<RB>(r_lo + 8, col >> 3) + clo);
+          const v4s qlo = lds_read_tr(qs + swz<RB>(r_lo, col >> 3) + clo);
+          const v4s qhi = lds_read_tr(qs + swz<RB>(r_lo + 8, col >> 3) + clo);
           const bf16x8 ad = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
           const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
           dv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pb[k2], dv[u], 0, 0, 0);
@@ -416,10 +447,10 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
   // register e of dv[u], dk[u]: dimension 32u + 8(e/4) + 4hh + e%4 of key `key`
   if (nch > 1) {
     // [dK | dV] of the block's 64 keys, row-major, fp32; keys past N hold zeros
-    float* pk = part + size_t(slot + ch) * (2 * kBB * kBD) + size_t(32 * w + ql) * kBD;
-    float* pv = pk + kBB * kBD;
+    float* pk = part + size_t(slot + ch) * (2 * kBB * HD) + size_t(32 * w + ql) * HD;
+    float* pv = pk + kBB * HD;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NDT; ++u)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * u + 8 * g4 + 4 * hh;
@@ -429,10 +460,10 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
             f32x4{dv[u][4 * g4], dv[u][4 * g4 + 1], dv[u][4 * g4 + 2], dv[u][4 * g4 + 3]};
       }
   } else if (key_ok) {
-    uint16_t* vrow = dV + head + size_t(key) * kBD;
-    uint16_t* krow = dK + head + size_t(key) * kBD;
+    uint16_t* vrow = dV + head + size_t(key) * HD;
+    uint16_t* krow = dK + head + size_t(key) * HD;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NDT; ++u)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * u + 8 * g4 + 4 * hh;
@@ -453,17 +484,29 @@ __global__ __launch_bounds__(128) void dkdv_kernel(
 // delta), and dQ^T += K^T dS^T with K^T read transposed from the wave's LDS
 // area.  The two key halves are summed through LDS at the end; an unsplit row
 // writes bf16 dQ, a chunk of a split one its fp32 sum (unscaled) to partial
-// slot `slot + chunk`.
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dq_kernel(
+// slot `slot + chunk`.  At HD = 128 the rings take 64 KiB and the registers
+// exceed half the file: one wave per SIMD.
+template <int HD>
+struct DqCfg {
+  static constexpr int RB = HD * 2;
+  static constexpr uint32_t kHalf = 32 * RB, kStage = 2 * kHalf;
+  static constexpr size_t LDS_BYTES = 2 * size_t(kDqStages) * kStage;
+};
+
+template <int HD>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 2 : 1))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ ld,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int2* __restrict__ row_split, int32_t n_rows, int32_t N, int32_t nb, float c2,
     float scale, uint16_t* __restrict__ dQ, float* __restrict__ part) {
-  // Per wave: a ring of kDqStages stages of its 32 key rows of K and of V
-  // (4 KiB each per stage), streamed by LDS DMA kDqStages - 1 key blocks ahead;
-  // no barrier in the loop.
-  __shared__ __align__(16) uint8_t smem[2 * kDqStages * 2 * 32 * kRB];
+  // Per wave: a ring of kDqStages stages of its 32 key rows of K and of V,
+  // streamed by LDS DMA kDqStages - 1 key blocks ahead; no barrier in the loop.
+  using C = DqCfg<HD>;
+  constexpr int RB = C::RB, NDC = HD / 16, NDT = HD / 32;
+  constexpr uint32_t kHalf = C::kHalf, kStage = C::kStage;
+  constexpr int kLoads = 2 * (RB / 32);  // tile loads one stage takes per wave
+  extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
   const int lane = threadIdx.x & 63;
   const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -475,23 +518,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int nch = slot < 0 ? 1 : __builtin_amdgcn_readfirstlane(sp.y);
   if (ch >= nch) return;
   const int bh = r / nb, i = r - bh * nb;
-  const size_t head = size_t(bh) * size_t(N) * kBD;
-  const uint32_t hbytes = static_cast<uint32_t>(N) * kRB;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+  const uint32_t hbytes = static_cast<uint32_t>(N) * RB;
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, hbytes);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(dO + head, hbytes);
   const v4i kd = uniform_desc(K + head, hbytes), vd = uniform_desc(V + head, hbytes);
-  constexpr uint32_t kHalf = 32 * kRB, kStage = 2 * kHalf;
   const uint32_t ring = lds0 + uint32_t(kh) * (kDqStages * kStage);
-  uint32_t ve, vo;
-  dma_offsets(lane, ve, vo);
-  bf16x8 qf[2][4], df[2][4];
+  uint32_t hoff[RB / 32];
+  half_offsets<RB>(lane, 32 * kh, hoff);
+  bf16x8 qf[2][NDC], df[2][NDC];
   float L[2], Dl[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int t = kBB * i + 32 * g + ql;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t off = uint32_t(t) * kRB + uint32_t(32 * c + 16 * hh);
+    for (int c = 0; c < NDC; ++c) {
+      const uint32_t off = uint32_t(t) * RB + uint32_t(32 * c + 16 * hh);
       qf[g][c] = __builtin_bit_cast(bf16x8, load16(qr, off));
       df[g][c] = __builtin_bit_cast(bf16x8, load16(dr, off));
     }
@@ -504,14 +546,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qf[g][c]), "v"(df[g][c]));
+    for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(qf[g][c]), "v"(df[g][c]));
     asm volatile("" ::"v"(L[g]), "v"(Dl[g]));
   }
-  f32x16 acc[2][2];
+  f32x16 acc[2][NDT];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NDT; ++u)
 #pragma unroll
       for (int x = 0; x < 16; ++x) acc[g][u][x] = 0.f;
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
@@ -526,13 +568,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   // outside [0, nb) reads past the buffers, i.e. zeros.
   auto issue = [&](int j, int st) {
     const bool ok = j >= 0 && j < nb;
-    const uint32_t tb = ok ? uint32_t(j) * (kBB * kRB) + uint32_t(kh) * kHalf : hbytes;
+    const uint32_t tb = ok ? uint32_t(j) * (kBB * RB) + uint32_t(kh) * kHalf : hbytes;
     const uint32_t dst = ring + uint32_t(st) * kStage;
-    dma_kv_half(kd, vd, ve + tb, vo + tb, dst, dst + kHalf);
+    dma_half_tile<RB>(kd, hoff, tb, dst);
+    dma_half_tile<RB>(vd, hoff, tb, dst + kHalf);
   };
   // Blocks e0 .. e0 + kDqStages - 2 go first; at step e, block e + kDqStages - 1
   // goes into the stage block e - 1 used (its reads are complete), then the
-  // wait leaves the younger blocks (8 loads each) in flight.
+  // wait leaves the younger blocks (kLoads loads each) in flight.
   int jq[kDqStages];
 #pragma unroll
   for (int x = 0; x < kDqStages - 1; ++x) {
@@ -553,15 +596,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         if (x == sa) jq[x] = ja;
       issue(ja, sa);
     }
-    wait_vm_n(8 * (min(ahead, e1 - 1) - e));
+    wait_vm_n(kLoads * (min(ahead, e1 - 1) - e));
     if (j < 0 || j >= nb) continue;
     const int kbase = kBB * j + 32 * kh;  // first key of this wave's half
     const uint32_t ks = ring + uint32_t(st) * kStage, vs = ks + kHalf;
-    bf16x8 va[4], ka[4];
+    bf16x8 va[NDC], ka[NDC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      va[c] = lds_read16(vs + swz<kRB>(ql, 2 * c + hh));
-      ka[c] = lds_read16(ks + swz<kRB>(ql, 2 * c + hh));
+    for (int c = 0; c < NDC; ++c) {
+      va[c] = lds_read16(vs + swz<RB>(ql, 2 * c + hh));
+      ka[c] = lds_read16(ks + swz<RB>(ql, 2 * c + hh));
     }
     bf16x8 sb[2][2];
 #pragma unroll
@@ -569,7 +612,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
       const f32x16 zero = {};
       f32x16 s, dp;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NDC; ++c) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], df[g][c], c == 0 ? zero : dp, 0, 0, 0);
       }
@@ -585,11 +628,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NDT; ++u) {
         const int col = 32 * u + tr_col;
         const uint32_t clo = (col & 7) * 2;
-        const v4s lo = lds_read_tr(ks + swz<kRB>(16 * k2 + tr_row, col >> 3) + clo);
-        const v4s hi = lds_read_tr(ks + swz<kRB>(16 * k2 + 8 + tr_row, col >> 3) + clo);
+        const v4s lo = lds_read_tr(ks + swz<RB>(16 * k2 + tr_row, col >> 3) + clo);
+        const v4s hi = lds_read_tr(ks + swz<RB>(16 * k2 + 8 + tr_row, col >> 3) + clo);
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int g = 0; g < 2; ++g)
@@ -599,23 +642,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   // Key-half sum: wave kh finishes query group kh and hands group 1 - kh over.
   // Exchange through the rings (each wave's own is free once its loop ends).
   float* xo = reinterpret_cast<float*>(smem);
-  auto send = [&](const f32x16 (&a)[2]) {
+  auto send = [&](const f32x16 (&a)[NDT]) {
     float* dst = xo + size_t(kh) * (kDqStages * kStage / 4);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NDT; ++u)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<f32x4*>(dst + ((u * 4 + g4) * 64 + lane) * 4) =
             f32x4{a[u][4 * g4], a[u][4 * g4 + 1], a[u][4 * g4 + 2], a[u][4 * g4 + 3]};
   };
-  auto finish = [&](const f32x16 (&a)[2]) {
+  auto finish = [&](const f32x16 (&a)[NDT]) {
     const int t = kBB * i + 32 * kh + ql;
     const float* src = xo + size_t(1 - kh) * (kDqStages * kStage / 4);
     if (nch > 1) {
       // dQ of the block's 64 queries, row-major, fp32 (queries past N too)
-      float* pq = part + size_t(slot + ch) * (kBB * kBD) + size_t(32 * kh + ql) * kBD;
+      float* pq = part + size_t(slot + ch) * (kBB * HD) + size_t(32 * kh + ql) * HD;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < NDT; ++u)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + ((u * 4 + g4) * 64 + lane) * 4);
@@ -627,9 +670,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
       return;
     }
     if (t >= N) return;
-    uint16_t* qrow = dQ + head + size_t(t) * kBD;
+    uint16_t* qrow = dQ + head + size_t(t) * HD;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NDT; ++u)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + ((u * 4 + g4) * 64 + lane) * 4);
@@ -654,6 +697,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
 // dK (times scale) and dV of key column r, and dQ (times scale) of CSR row r
 // (r = bh nb + block).  Rows past N are not stored.  Unsplit blocks were
 // written by the gradient kernels.
+template <int HD>
 __global__ __launch_bounds__(256) void reduce_kernel(const int2* __restrict__ col_split,
                                                      const int2* __restrict__ row_split,
                                                      const float* __restrict__ part_kv,
@@ -664,24 +708,25 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int2* __restrict__ co
                                                      uint16_t* __restrict__ dQ) {
   const int r = blockIdx.x;
   const int bh = r / nb, blk = r - bh * nb;
-  const size_t head = size_t(bh) * size_t(N) * kBD;
+  const size_t head = size_t(bh) * size_t(N) * HD;
   const int tid = threadIdx.x;
+  constexpr int kIters = kBB * HD / 4 / 256;
   auto store4 = [&](uint16_t* T, int e, f32x4 x, float f) {
-    const int t = kBB * blk + (e >> 6);
+    const int t = kBB * blk + e / HD;
     if (t >= N) return;
-    *reinterpret_cast<uint2*>(T + head + size_t(t) * kBD + (e & 63)) =
+    *reinterpret_cast<uint2*>(T + head + size_t(t) * HD + (e % HD)) =
         make_uint2(pack_bf16x2(f * x[0], f * x[1]), pack_bf16x2(f * x[2], f * x[3]));
   };
   const int2 sk = col_split[r];
   if (sk.x >= 0 && sk.y > 1) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int e = 4 * (tid + 256 * x);  // element of the 64 x 64 block
+    for (int x = 0; x < kIters; ++x) {
+      const int e = 4 * (tid + 256 * x);  // element of the 64 x HD block
       f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
       for (int c = 0; c < sk.y; ++c) {
-        const float* p = part_kv + size_t(sk.x + c) * (2 * kBB * kBD);
+        const float* p = part_kv + size_t(sk.x + c) * (2 * kBB * HD);
         a += *reinterpret_cast<const f32x4*>(p + e);
-        b += *reinterpret_cast<const f32x4*>(p + kBB * kBD + e);
+        b += *reinterpret_cast<const f32x4*>(p + kBB * HD + e);
       }
       store4(dK, e, a, scale);
       store4(dV, e, b, 1.f);
@@ -690,11 +735,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int2* __restrict__ co
   const int2 sq = row_split[r];
   if (sq.x >= 0 && sq.y > 1) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < kIters; ++x) {
       const int e = 4 * (tid + 256 * x);
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
       for (int c = 0; c < sq.y; ++c)
-        a += *reinterpret_cast<const f32x4*>(part_q + size_t(sq.x + c) * (kBB * kBD) + e);
+        a += *reinterpret_cast<const f32x4*>(part_q + size_t(sq.x + c) * (kBB * HD) + e);
       store4(dQ, e, a, scale);
     }
   }
@@ -717,7 +762,7 @@ struct BwdLayout {
   size_t ld, col_ptr, row_idx, col_split, row_split, ctr, part_kv, part_q, total;
 };
 
-BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t block, int64_t nnz) {
+BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, int64_t nnz) {
   BwdLayout L{};
   const size_t rows = size_t(B) * H * N;
   const size_t nrow = size_t(B) * H * n_blocks(N, block);
@@ -729,20 +774,96 @@ BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t block, int64_t nnz
   L.col_split = o; o += round256(nrow * sizeof(int2));
   L.row_split = o; o += round256(nrow * sizeof(int2));
   L.ctr = o;       o += 256;
-  L.part_kv = o;   o += round256(size_t(cap) * 2 * kBB * kBD * sizeof(float));
-  L.part_q = o;    o += round256(size_t(cap) * kBB * kBD * sizeof(float));
+  L.part_kv = o;   o += round256(size_t(cap) * 2 * kBB * size_t(D) * sizeof(float));
+  L.part_q = o;    o += round256(size_t(cap) * kBB * size_t(D) * sizeof(float));
   L.total = o;
   return L;
+}
+
+// The five launches for head dim HD (see the top of the file).
+template <int HD>
+bsa_status launch_backward(const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, int32_t B, int32_t H, int32_t N,
+                           int32_t block, const int32_t* row_ptr, const int32_t* col_idx,
+                           int64_t nnz, float sc, void* dq, void* dk, void* dv, uint8_t* ws,
+                           hipStream_t s) {
+  const int32_t nb = n_blocks(N, block);
+  const int64_t rows = int64_t(B) * H * N;
+  const int32_t n_heads = B * H;
+  const int32_t n_rows = n_heads * nb;
+  const int32_t chunk = chunk_len(nnz, n_rows);
+  const int32_t max_ch = std::max(1, (nb + chunk - 1) / chunk);
+  const int64_t cap = slot_cap(nnz, chunk);
+  if (int64_t(n_rows) * max_ch > INT32_MAX || cap > INT32_MAX) return BSA_ERR_UNSUPPORTED;
+  const BwdLayout lay = bwd_layout(B, H, N, HD, block, nnz);
+  float2* ld = reinterpret_cast<float2*>(ws + lay.ld);
+  int32_t* col_ptr = reinterpret_cast<int32_t*>(ws + lay.col_ptr);
+  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + lay.row_idx);
+  int2* col_split = reinterpret_cast<int2*>(ws + lay.col_split);
+  int2* row_split = reinterpret_cast<int2*>(ws + lay.row_split);
+  int32_t* ctr = reinterpret_cast<int32_t*>(ws + lay.ctr);
+  float* part_kv = reinterpret_cast<float*>(ws + lay.part_kv);
+  float* part_q = reinterpret_cast<float*>(ws + lay.part_q);
+
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&transpose_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kMaxBlocks * (kMaxBlocks / 32) * 4);
+    if (attr == hipSuccess)
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dkdv_kernel<HD>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(DkdvCfg<HD>::LDS_BYTES));
+    if (attr == hipSuccess)
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dq_kernel<HD>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(DqCfg<HD>::LDS_BYTES));
+  });
+  if (attr != hipSuccess) return BSA_ERR_HIP;
+
+  constexpr int kLpr = HD / 8;  // prep lanes per row
+  hipLaunchKernelGGL(prep_kernel<HD>, dim3(static_cast<uint32_t>((rows * kLpr + 255) / 256)),
+                     dim3(256), 0, s, static_cast<const uint16_t*>(o),
+                     static_cast<const uint16_t*>(d_o), lse, rows, ld, ctr);
+  BSA_HIP_CHECK_LAUNCH();
+  const size_t bits_bytes = size_t(nb) * ((nb + 31) / 32) * 4;
+  hipLaunchKernelGGL(transpose_kernel, dim3(n_heads), dim3(256), bits_bytes, s, row_ptr, col_idx,
+                     nb, n_heads, col_ptr, row_idx, chunk, max_ch, ctr, static_cast<int32_t>(cap),
+                     static_cast<int32_t>(cap), col_split, row_split);
+  BSA_HIP_CHECK_LAUNCH();
+  const float c2 = sc * kLog2e;
+  const dim3 grid(static_cast<uint32_t>(n_rows * max_ch));
+  hipLaunchKernelGGL(dkdv_kernel<HD>, grid, dim3(128), DkdvCfg<HD>::LDS_BYTES, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
+                     col_ptr, row_idx, col_split, n_rows, N, nb, c2, sc,
+                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), part_kv);
+  BSA_HIP_CHECK_LAUNCH();
+  hipLaunchKernelGGL(dq_kernel<HD>, grid, dim3(128), DqCfg<HD>::LDS_BYTES, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
+                     row_ptr, col_idx, row_split, n_rows, N, nb, c2, sc,
+                     static_cast<uint16_t*>(dq), part_q);
+  BSA_HIP_CHECK_LAUNCH();
+  if (max_ch > 1) {
+    hipLaunchKernelGGL(reduce_kernel<HD>, dim3(static_cast<uint32_t>(n_rows)), dim3(256), 0, s,
+                       col_split, row_split, part_kv, part_q, N, nb, sc,
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                       static_cast<uint16_t*>(dq));
+    BSA_HIP_CHECK_LAUNCH();
+  }
+  return BSA_OK;
 }
 
 }  // namespace
 }  // namespace bsa
 
-extern "C" BSA_API size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t N,
+extern "C" BSA_API size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D,
                                                       int32_t block, int64_t nnz) {
   using namespace bsa;
-  if (B < 1 || H < 1 || N < 1 || block < 1 || nnz < 0) return 0;
-  return bwd_layout(B, H, N, block, nnz).total;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || block < 1 || nnz < 0) return 0;
+  return bwd_layout(B, H, N, D, block, nnz).total;
 }
 
 extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const void* v,
@@ -757,72 +878,22 @@ extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const v
       !dv || !workspace)
     return BSA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || nnz < 0 || !(scale == scale)) return BSA_ERR_INVALID_ARG;
-  if (D != kBD || block != kBB) return BSA_ERR_UNSUPPORTED;
+  if ((D != 64 && D != 128) || block != kBB) return BSA_ERR_UNSUPPORTED;
   const int32_t nb = n_blocks(N, block);
-  if (nb > kMaxBlocks || int64_t(N) * kRB >= (int64_t(1) << 31) || nnz > INT32_MAX ||
+  if (nb > kMaxBlocks || int64_t(N) * D * 2 >= (int64_t(1) << 31) || nnz > INT32_MAX ||
       int64_t(B) * H * nb > INT32_MAX)
     return BSA_ERR_UNSUPPORTED;
   for (const void* p : {q, k, v, o, d_o, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv), static_cast<const void*>(workspace)})
     if (!aligned16(p)) return BSA_ERR_INVALID_ARG;
-  if (workspace_bytes < bsa_backward_workspace_bytes(B, H, N, block, nnz)) return BSA_ERR_CAPACITY;
-  const int64_t rows = int64_t(B) * H * N;
-  const int32_t n_heads = B * H;
-  const int32_t n_rows = n_heads * nb;
-  const int32_t chunk = chunk_len(nnz, n_rows);
-  const int32_t max_ch = std::max(1, (nb + chunk - 1) / chunk);
-  const int64_t cap = slot_cap(nnz, chunk);
-  if (int64_t(n_rows) * max_ch > INT32_MAX || cap > INT32_MAX) return BSA_ERR_UNSUPPORTED;
-  const BwdLayout lay = bwd_layout(B, H, N, block, nnz);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float2* ld = reinterpret_cast<float2*>(ws + lay.ld);
-  int32_t* col_ptr = reinterpret_cast<int32_t*>(ws + lay.col_ptr);
-  int32_t* row_idx = reinterpret_cast<int32_t*>(ws + lay.row_idx);
-  int2* col_split = reinterpret_cast<int2*>(ws + lay.col_split);
-  int2* row_split = reinterpret_cast<int2*>(ws + lay.row_split);
-  int32_t* ctr = reinterpret_cast<int32_t*>(ws + lay.ctr);
-  float* part_kv = reinterpret_cast<float*>(ws + lay.part_kv);
-  float* part_q = reinterpret_cast<float*>(ws + lay.part_q);
+  if (workspace_bytes < bsa_backward_workspace_bytes(B, H, N, D, block, nnz))
+    return BSA_ERR_CAPACITY;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
-
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&transpose_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               kMaxBlocks * (kMaxBlocks / 32) * 4);
-  });
-  if (attr != hipSuccess) return BSA_ERR_HIP;
-
-  hipLaunchKernelGGL(prep_kernel, dim3(static_cast<uint32_t>((rows * 8 + 255) / 256)), dim3(256),
-                     0, s, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(d_o), lse,
-                     rows, ld, ctr);
-  BSA_HIP_CHECK_LAUNCH();
-  const size_t bits_bytes = size_t(nb) * ((nb + 31) / 32) * 4;
-  hipLaunchKernelGGL(transpose_kernel, dim3(n_heads), dim3(256), bits_bytes, s, row_ptr, col_idx,
-                     nb, n_heads, col_ptr, row_idx, chunk, max_ch, ctr, static_cast<int32_t>(cap),
-                     static_cast<int32_t>(cap), col_split, row_split);
-  BSA_HIP_CHECK_LAUNCH();
-  const float c2 = sc * kLog2e;
-  const dim3 grid(static_cast<uint32_t>(n_rows * max_ch));
-  hipLaunchKernelGGL(dkdv_kernel, grid, dim3(128), 0, s, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                     static_cast<const uint16_t*>(d_o), ld, col_ptr, row_idx, col_split, n_rows,
-                     N, nb, c2, sc, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
-                     part_kv);
-  BSA_HIP_CHECK_LAUNCH();
-  hipLaunchKernelGGL(dq_kernel, grid, dim3(128), 0, s, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                     static_cast<const uint16_t*>(d_o), ld, row_ptr, col_idx, row_split, n_rows, N,
-                     nb, c2, sc, static_cast<uint16_t*>(dq), part_q);
-  BSA_HIP_CHECK_LAUNCH();
-  if (max_ch > 1) {
-    hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<uint32_t>(n_rows)), dim3(256), 0, s,
-                       col_split, row_split, part_kv, part_q, N, nb, sc,
-                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
-                       static_cast<uint16_t*>(dq));
-    BSA_HIP_CHECK_LAUNCH();
-  }
-  return BSA_OK;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (D == 64)
+    return launch_backward<64>(q, k, v, o, d_o, lse, B, H, N, block, row_ptr, col_idx, nnz, sc,
+                               dq, dk, dv, ws, s);
+  return launch_backward<128>(q, k, v, o, d_o, lse, B, H, N, block, row_ptr, col_idx, nnz, sc,
+                              dq, dk, dv, ws, s);
 }

@@ -55,7 +55,7 @@ typedef int32_t bsa_status;
 BSA_API const char* bsa_status_string(bsa_status s);
 
 /* ABI version of this header (incremented on any signature change). */
-#define BSA_ABI_VERSION 11
+#define BSA_ABI_VERSION 12
 
 /* Largest number of item groups a work list may have (see bsa_work_plan_host). */
 #define BSA_MAX_GROUPS 64
@@ -454,17 +454,17 @@ BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* 
  * are ignored.  nnz: an upper bound of row_ptr[B*H*nb] (sizes the workspace).
  * scale <= 0 selects 1/sqrt(D).  Accumulation in fp32, P and dS rounded to bf16 as
  * MFMA operands; no atomics on the gradients, so results are deterministic.
- * workspace: device, bsa_backward_workspace_bytes(B, H, N, block, nnz) bytes, 16-byte
+ * workspace: device, bsa_backward_workspace_bytes(B, H, N, D, block, nnz) bytes, 16-byte
  * aligned; it holds (LSE log2 e, delta) per query row, the transposed CSR, the split
  * of key columns and CSR rows longer than the chunk length (twice the mean row
  * length, at least 16) into chunks, and the chunks' fp32 partial gradients (bounded
- * by 2 nnz / chunk + 1 slots of 48 KiB); it needs no initial contents.
- * Supported: D = 64, block = 64, nb <= 1024.
+ * by 2 nnz / chunk + 1 slots of 768 D bytes); it needs no initial contents.
+ * Supported: D = 64 or 128, block = 64, nb <= 1024.
  * Errors: INVALID_ARG (null or misaligned pointer, bad size, NaN scale),
  * UNSUPPORTED (D, block, nb), CAPACITY (workspace too small), HIP.
  */
-BSA_API size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t block,
-                                            int64_t nnz);
+BSA_API size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D,
+                                            int32_t block, int64_t nnz);
 BSA_API bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o,
                                 const void* d_o, const float* lse, int32_t B, int32_t H,
                                 int32_t N, int32_t D, int32_t block, const int32_t* row_ptr,

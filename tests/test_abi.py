@@ -33,7 +33,7 @@ def test_status_strings_and_version():
     assert bsa.status_string(-1) == "BSA_ERR_INVALID_ARG"
     assert bsa.status_string(-5) == "BSA_ERR_PLAN_MISMATCH"
     assert bsa.status_string(-99) == "BSA_ERR_UNKNOWN"
-    assert bsa.abi_version() == bsa.ABI_VERSION == 11
+    assert bsa.abi_version() == bsa.ABI_VERSION == 12
 
 
 def test_budget_matches_oracle():
@@ -221,17 +221,22 @@ def test_backward_workspace_bytes():
     def r256(x):
         return (x + 255) // 256 * 256
 
-    def want(B, H, N, nnz):
+    def want(B, H, N, D, nnz):
         # (LSE log2 e, delta) per row, col_ptr [B*H*nb + 1], row_idx [nnz], the column
         # and row splits (int2 [B*H*nb] each), the slot counters, then the partial
         # slots: chunk = max(16, 2 * ceil(nnz / rows)), 2 nnz / chunk + 1 slots of
-        # fp32 [dK | dV] (32 KiB) and as many of dQ (16 KiB); 256-byte rounding.
+        # fp32 [dK | dV] (2 x 64 x D x 4 bytes) and as many of dQ (64 x D x 4 bytes);
+        # 256-byte rounding.
         nrow = B * H * (-(-N // 64))
         chunk = max(16, 2 * (-(-nnz // nrow)))
         cap = 2 * nnz // chunk + 1
         return (r256(8 * B * H * N) + r256(4 * (nrow + 1)) + r256(4 * nnz) + 2 * r256(8 * nrow)
-                + 256 + cap * 32768 + cap * 16384)
+                + 256 + cap * 512 * D + cap * 256 * D)
 
-    assert L.bsa_backward_workspace_bytes(1, 2, 512, 64, 100) == want(1, 2, 512, 100) == 648704
-    assert L.bsa_backward_workspace_bytes(2, 24, 4224, 64, 31968) == want(2, 24, 4224, 31968)
-    assert L.bsa_backward_workspace_bytes(0, 2, 512, 64, 100) == 0
+    assert L.bsa_backward_workspace_bytes(1, 2, 512, 64, 64, 100) == want(1, 2, 512, 64, 100) \
+        == 648704
+    assert L.bsa_backward_workspace_bytes(2, 24, 4224, 64, 64, 31968) == \
+        want(2, 24, 4224, 64, 31968)
+    assert L.bsa_backward_workspace_bytes(1, 16, 8192, 128, 64, 26624) == \
+        want(1, 16, 8192, 128, 26624)
+    assert L.bsa_backward_workspace_bytes(0, 2, 512, 64, 64, 100) == 0

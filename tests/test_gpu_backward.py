@@ -42,12 +42,15 @@ def compare(got, want, names=("dq", "dk", "dv")):
         assert err.max() <= MAX_REL * scale and err.mean() <= MEAN_REL * scale, n
 
 
-@pytest.mark.parametrize("N,p,seed", [(512, 0.5, 0), (245, 0.6, 1), (64, 1.0, 2), (1000, 0.3, 3)])
-def test_backward_matches_oracle(N, p, seed):
-    """Random CSR (diagonal kept), ragged last blocks, one row left empty."""
+@pytest.mark.parametrize("N,p,seed,D", [(512, 0.5, 0, 64), (245, 0.6, 1, 64), (64, 1.0, 2, 64),
+                                        (1000, 0.3, 3, 64), (512, 0.5, 4, 128),
+                                        (245, 0.6, 5, 128), (64, 1.0, 6, 128),
+                                        (1000, 0.3, 7, 128)])
+def test_backward_matches_oracle(N, p, seed, D):
+    """Random CSR (diagonal kept), ragged last blocks, one row left empty; both head dims."""
     bsa = need_gpu()
-    print(f"case N={N} p={p}", flush=True)
-    B, H, D, block = 1, 2, 64, 64
+    print(f"case N={N} p={p} D={D}", flush=True)
+    B, H, block = 1, 2, 64
     nb = -(-N // block)
     q, k, v = W.gaussian_qkv(100 + seed, B, H, N, D)
     do = W.gaussian_qkv(200 + seed, B, H, N, D)[0]
@@ -58,7 +61,7 @@ def test_backward_matches_oracle(N, p, seed):
         cols[1] = []
     rp, ci = csr_from_cols(cols)
     got = run(bsa, q, k, v, do, rp, ci)
-    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / 8.0, do)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / np.sqrt(D), do)
     compare(got, want)
     if nb > 1:
         assert np.all(got[0][0, 0, 64:128] == 0.0)       # the empty row's dQ
@@ -80,31 +83,32 @@ def test_backward_unlisted_block_and_out_of_range_columns():
     assert np.all(got[1][0, 0, 192:256] == 0.0) and np.all(got[2][0, 0, 192:256] == 0.0)
 
 
-def test_backward_dense_and_deterministic():
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_dense_and_deterministic(D):
     """All-ones CSR (every key block listed by every row); two calls give the same bits."""
     bsa = need_gpu()
-    B, H, N, D, block = 2, 2, 320, 64, 64
+    B, H, N, block = 2, 2, 320, 64
     nb = N // block
     q, k, v = W.gaussian_qkv(9, B, H, N, D)
     do = W.gaussian_qkv(10, B, H, N, D)[0]
     rp, ci = csr_from_cols([list(range(nb))] * (B * H * nb))
     got = run(bsa, q, k, v, do, rp, ci)
-    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / 8.0, do)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / np.sqrt(D), do)
     compare(got, want)
     again = run(bsa, q, k, v, do, rp, ci)
     assert all(np.array_equal(a, b) for a, b in zip(got, again))
 
 
-@pytest.mark.parametrize("N,H", [(2000, 2), (4050, 1)])
-def test_backward_split_rows_and_columns(N, H):
+@pytest.mark.parametrize("N,H,D", [(2000, 2, 64), (4050, 1, 64), (2000, 1, 128)])
+def test_backward_split_rows_and_columns(N, H, D):
     """Rows and key columns longer than the chunk length (twice the mean row length, at
     least 16) are cut into chunks whose fp32 partials are summed in chunk order: query
     block 0 lists every key block and every row lists key block 0 (2 and 4 chunks at
     nb = 32 and 64), the rest is the diagonal and its right neighbour; ragged N; a
     repeat call gives the same bits."""
     bsa = need_gpu()
-    print(f"case N={N} H={H}", flush=True)
-    B, D, block = 1, 64, 64
+    print(f"case N={N} H={H} D={D}", flush=True)
+    B, block = 1, 64
     nb = -(-N // block)
     q, k, v = W.gaussian_qkv(300 + N, B, H, N, D)
     do = W.gaussian_qkv(400 + N, B, H, N, D)[0]
@@ -112,10 +116,33 @@ def test_backward_split_rows_and_columns(N, H):
             for r in range(B * H * nb)]
     rp, ci = csr_from_cols(cols)
     got = run(bsa, q, k, v, do, rp, ci)
-    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / 8.0, do)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / np.sqrt(D), do)
     compare(got, want)
     again = run(bsa, q, k, v, do, rp, ci)
     assert all(np.array_equal(a, b) for a, b in zip(got, again))
+
+
+def test_backward_dynamic_config_sampled_head():
+    """The dynamic config's shape at D = 128 (B1 H16 N8192, block 64, 10 % top-k density
+    built on the GPU); the oracle on one head."""
+    bsa = need_gpu()
+    w = W.make("dynamic")
+    q, k, v = w.tensors()
+    do = W.gaussian_qkv(w.seed + 2000, w.B, w.H, w.N, w.D)[0]
+    qd, kd = q.cuda(), k.cuda()
+    plan = bsa.Plan.create(w.B, w.H, w.N, w.D, w.block, w.density, w.prior(), w.budgets(),
+                           w.force_diag, "cuda")
+    rp_d, ci_d = bsa.build_mask(qd, kd, w.block, plan=plan)
+    torch.cuda.synchronize()
+    rp, ci = rp_d.cpu().numpy(), ci_d.cpu().numpy()
+    got = run(bsa, q, k, v, do, rp, ci, w.block)
+    nb = w.nb
+    h = 5
+    sub_rp = (rp[h * nb:(h + 1) * nb + 1] - rp[h * nb]).astype(np.int32)
+    sub_ci = ci[rp[h * nb]:rp[(h + 1) * nb]]
+    want = OB.block_sparse_backward(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], sub_rp, sub_ci,
+                                    w.block, 1 / np.sqrt(w.D), do[:, h:h + 1])
+    compare([g[:, h:h + 1] for g in got], want)
 
 
 def test_backward_t2i_sampled_heads():
@@ -142,7 +169,7 @@ def test_backward_t2i_sampled_heads():
 
 def test_backward_rejects_unsupported():
     bsa = need_gpu()
-    q = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 1, 128, 96), dtype=torch.bfloat16, device="cuda")   # head dim 96
     lse = torch.zeros((1, 1, 128), dtype=torch.float32, device="cuda")
     rp = np.array([0, 1, 2], np.int32)
     ci = np.array([0, 1], np.int32)
