@@ -780,6 +780,39 @@ BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, 
   return L;
 }
 
+// A 128-block CSR as the 64-block CSR of the same mask: query block i of 128
+// rows is query blocks 2i and 2i + 1 of 64 rows (the second only if it starts
+// before N), key block j is key blocks 2j and 2j + 1.  CSR row r = bh nb128 + i
+// owns entries [4 rp[r], 4 rp[r + 1]) of the result: the first half for row
+// 2i of head bh, the second for row 2i + 1, whose columns are (2j, 2j + 1) for
+// every listed j in order; when row 2i + 1 does not exist, row 2i's range also
+// takes the second half, filled with -1 (a column the backward ignores), and
+// so does a column 2j + 1 past the last 64-block.  One workgroup per row.
+__global__ __launch_bounds__(64) void refine_kernel(const int32_t* __restrict__ rp,
+                                                   const int32_t* __restrict__ ci, int32_t nb128,
+                                                   int32_t nb64, int32_t n_rows,
+                                                   int32_t* __restrict__ rp64,
+                                                   int32_t* __restrict__ ci64) {
+  const int r = blockIdx.x;
+  const int bh = r / nb128, i = r - bh * nb128;
+  const int b = rp[r], len = rp[r + 1] - b;
+  const bool second = 2 * i + 1 < nb64;
+  const int r64 = bh * nb64 + 2 * i;
+  if (threadIdx.x == 0) {
+    rp64[r64] = 4 * b;
+    if (second) rp64[r64 + 1] = 4 * b + 2 * len;
+    if (r == n_rows - 1) rp64[bh * nb64 + nb64] = 4 * rp[n_rows];
+  }
+  for (int m = threadIdx.x; m < len; m += 64) {
+    const int j = ci[b + m];
+    const int c0 = 2 * j, c1 = (j >= 0 && 2 * j + 1 < nb64) ? 2 * j + 1 : -1;
+    ci64[4 * b + 2 * m] = c0;
+    ci64[4 * b + 2 * m + 1] = c1;
+    ci64[4 * b + 2 * len + 2 * m] = second ? c0 : -1;
+    ci64[4 * b + 2 * len + 2 * m + 1] = second ? c1 : -1;
+  }
+}
+
 // The five launches for head dim HD (see the top of the file).
 template <int HD>
 bsa_status launch_backward(const void* q, const void* k, const void* v, const void* o,
@@ -863,7 +896,12 @@ extern "C" BSA_API size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int
                                                       int32_t block, int64_t nnz) {
   using namespace bsa;
   if (B < 1 || H < 1 || N < 1 || D < 1 || block < 1 || nnz < 0) return 0;
-  return bwd_layout(B, H, N, D, block, nnz).total;
+  if (block != 2 * kBB) return bwd_layout(B, H, N, D, block, nnz).total;
+  // Block 128: the 64-block CSR of the same mask first, then the block-64
+  // workspace for its (at most 4 nnz) entries.
+  const size_t rows64 = size_t(B) * H * n_blocks(N, kBB);
+  return round256((rows64 + 1) * sizeof(int32_t)) + round256(size_t(4 * nnz) * sizeof(int32_t)) +
+         bwd_layout(B, H, N, D, kBB, 4 * nnz).total;
 }
 
 extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const void* v,
@@ -878,9 +916,9 @@ extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const v
       !dv || !workspace)
     return BSA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || nnz < 0 || !(scale == scale)) return BSA_ERR_INVALID_ARG;
-  if ((D != 64 && D != 128) || block != kBB) return BSA_ERR_UNSUPPORTED;
-  const int32_t nb = n_blocks(N, block);
-  if (nb > kMaxBlocks || int64_t(N) * D * 2 >= (int64_t(1) << 31) || nnz > INT32_MAX ||
+  if ((D != 64 && D != 128) || (block != kBB && block != 2 * kBB)) return BSA_ERR_UNSUPPORTED;
+  const int32_t nb = n_blocks(N, kBB);  // 64-row blocks (a block-128 CSR is refined)
+  if (nb > kMaxBlocks || int64_t(N) * D * 2 >= (int64_t(1) << 31) || 4 * nnz > INT32_MAX ||
       int64_t(B) * H * nb > INT32_MAX)
     return BSA_ERR_UNSUPPORTED;
   for (const void* p : {q, k, v, o, d_o, static_cast<const void*>(dq), static_cast<const void*>(dk),
@@ -891,6 +929,20 @@ extern "C" BSA_API bsa_status bsa_backward(const void* q, const void* k, const v
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = scale > 0.f ? scale : 1.f / sqrtf(static_cast<float>(D));
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (block == 2 * kBB) {
+    const int32_t nb128 = n_blocks(N, block), rows128 = B * H * nb128;
+    int32_t* rp64 = reinterpret_cast<int32_t*>(ws);
+    const size_t rp_bytes = round256((size_t(B) * H * nb + 1) * sizeof(int32_t));
+    int32_t* ci64 = reinterpret_cast<int32_t*>(ws + rp_bytes);
+    hipLaunchKernelGGL(refine_kernel, dim3(static_cast<uint32_t>(rows128)), dim3(64), 0, s,
+                       row_ptr, col_idx, nb128, nb, rows128, rp64, ci64);
+    BSA_HIP_CHECK_LAUNCH();
+    row_ptr = rp64;
+    col_idx = ci64;
+    nnz *= 4;
+    block = kBB;
+    ws += rp_bytes + round256(size_t(nnz) * sizeof(int32_t));
+  }
   if (D == 64)
     return launch_backward<64>(q, k, v, o, d_o, lse, B, H, N, block, row_ptr, col_idx, nnz, sc,
                                dq, dk, dv, ws, s);

@@ -458,8 +458,11 @@ BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* 
  * aligned; it holds (LSE log2 e, delta) per query row, the transposed CSR, the split
  * of key columns and CSR rows longer than the chunk length (twice the mean row
  * length, at least 16) into chunks, and the chunks' fp32 partial gradients (bounded
- * by 2 nnz / chunk + 1 slots of 768 D bytes); it needs no initial contents.
- * Supported: D = 64 or 128, block = 64, nb <= 1024.
+ * by 2 nnz / chunk + 1 slots of 768 D bytes); it needs no initial contents.  With
+ * block = 128 the CSR is first refined to the 64-block CSR of the same mask (query
+ * block i is query blocks 2i, 2i + 1 and key block j key blocks 2j, 2j + 1; at most
+ * 4 nnz entries, held in the workspace), and the rest works on that.
+ * Supported: D = 64 or 128, block = 64 or 128, ceil(N / 64) <= 1024.
  * Errors: INVALID_ARG (null or misaligned pointer, bad size, NaN scale),
  * UNSUPPORTED (D, block, nb), CAPACITY (workspace too small), HIP.
  */

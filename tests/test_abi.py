@@ -240,3 +240,7 @@ def test_backward_workspace_bytes():
     assert L.bsa_backward_workspace_bytes(1, 16, 8192, 128, 64, 26624) == \
         want(1, 16, 8192, 128, 26624)
     assert L.bsa_backward_workspace_bytes(0, 2, 512, 64, 64, 100) == 0
+    # block 128: the refined 64-block CSR (row pointers, 4 nnz columns) first
+    nrow64 = 2 * 24 * (-(-32000 // 64))
+    assert L.bsa_backward_workspace_bytes(2, 24, 32000, 128, 128, 5000) == \
+        r256(4 * (nrow64 + 1)) + r256(4 * 4 * 5000) + want(2, 24, 32000, 128, 4 * 5000)

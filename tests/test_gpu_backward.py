@@ -122,6 +122,32 @@ def test_backward_split_rows_and_columns(N, H, D):
     assert all(np.array_equal(a, b) for a, b in zip(got, again))
 
 
+@pytest.mark.parametrize("N,D", [(500, 64), (320, 64), (256, 128), (320, 128), (4000, 128)])
+def test_backward_block128_matches_oracle(N, D):
+    """Block 128 (refined to the 64-block CSR of the same mask): ragged N with and
+    without a last 64-row half block (N % 128 of 116 and 64), uneven row lengths, one
+    row left empty; the oracle works on the 128-block CSR directly."""
+    bsa = need_gpu()
+    print(f"case N={N} D={D}", flush=True)
+    B, H, block = 1, 2, 128
+    nb = -(-N // block)
+    q, k, v = W.gaussian_qkv(700 + N + D, B, H, N, D)
+    do = W.gaussian_qkv(800 + N + D, B, H, N, D)[0]
+    rng = np.random.default_rng(N + D)
+    cols = [sorted(set(rng.choice(nb, rng.integers(1, nb + 1), replace=False).tolist())
+                   | {r % nb}) for r in range(B * H * nb)]
+    if nb > 1:
+        cols[1] = []
+    rp, ci = csr_from_cols(cols)
+    got = run(bsa, q, k, v, do, rp, ci, block)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / np.sqrt(D), do)
+    compare(got, want)
+    if nb > 1:
+        assert np.all(got[0][0, 0, 128:256] == 0.0)      # the empty row's dQ
+    again = run(bsa, q, k, v, do, rp, ci, block)
+    assert all(np.array_equal(a, b) for a, b in zip(got, again))
+
+
 def test_backward_dynamic_config_sampled_head():
     """The dynamic config's shape at D = 128 (B1 H16 N8192, block 64, 10 % top-k density
     built on the GPU); the oracle on one head."""
