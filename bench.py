@@ -391,7 +391,13 @@ def main():
             "anchor_step_ms": anchor_ms, "reuse_step_ms": reuse_ms,
             "reuse_adds_residual_in_forward_epilogue": True,
             "reuse_step_over_forward": reuse_ms / fwd_ms_eager,
+            # The compensated forward alone, graph-timed like the forward.
+            "compensated_forward_graph_ms": graph_ms(
+                lambda: bsa.forward(qd, kd, vd, plan.row_ptr, col_idx, w.block, work=plan,
+                                    out=o_c, lse=lse_dense, residual=r_buf), 30, stream),
         }
+        extra["residual_compensation"]["compensated_over_forward_graph"] = (
+            extra["residual_compensation"]["compensated_forward_graph_ms"] / fwd_ms)
 
         # Token-level selection at the same density: tile-aligned query groups of 64, token
         # mass per group from the dense LSE, the top T tokens per group, and the gathered
@@ -420,10 +426,10 @@ def main():
                 "rel_err_vs_dense_tokens": rel_err(o_g), "rel_err_vs_dense_csr": rel_err(o),
             }
 
-        # Backward over the same CSR (block 64, D 64): dQ, dK, dV from the forward's O and LSE
-        # for a seeded N(0,1) incoming gradient; 10 * q_valid * k_valid * D FLOPs per active
-        # pair (the five products S, dP, dV, dS K, dS^T Q), all four launches in the timing.
-        if w.D == 64 and w.block == 64:
+        # Backward over the same CSR: dQ, dK, dV from the forward's O and LSE for a seeded
+        # N(0,1) incoming gradient; 10 * q_valid * k_valid * D FLOPs per active pair (the
+        # five products S, dP, dV, dS K, dS^T Q), all launches in the timing.
+        if True:
             g = torch.Generator("cpu").manual_seed(1000 + w.N)
             do = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
             bws = torch.empty(max(bsa.backward_workspace_bytes(w.B, w.H, w.N, w.D, w.block, plan.nnz),
@@ -495,6 +501,16 @@ def main():
                                                 work=pc, out=occ, lse=lcc), reps, stream)
             b_ms = graph_ms(lambda: bsa.build_mask(qcd, kcd, wc.block, plan=pc, col_idx=cic),
                             reps, stream)
+            # The backward on the same CSR (a block-128 CSR is refined to 64-row blocks
+            # inside it), eagerly timed like the t2i one.
+            gc = torch.Generator("cpu").manual_seed(1000 + wc.N)
+            doc = torch.randn(qcd.shape, generator=gc, dtype=torch.float32).to(torch.bfloat16).to(dev)
+            bwsc = torch.empty(max(bsa.backward_workspace_bytes(wc.B, wc.H, wc.N, wc.D, wc.block,
+                                                                pc.nnz), 256),
+                               dtype=torch.uint8, device=dev)
+            bk_ms = time_launches(lambda: bsa.backward(qcd, kcd, vcd, occ, lcc, doc, pc.row_ptr,
+                                                       cic[:pc.nnz], wc.block, workspace=bwsc),
+                                  n=5 if name != "tiny" else 50)
             torch.cuda.synchronize()
             cic_h = cic.cpu().numpy()[:pc.nnz]
             nbc, rows_c = wc.nb, wc.B * wc.H * wc.nb
@@ -503,7 +519,10 @@ def main():
                      "density": pc.nnz / (rows_c * nbc), "active_gflop": fl / 1e9,
                      "forward_ms": f_ms, "forward_tflops": fl / (f_ms * 1e-3) / 1e12,
                      "forward_frac_of_bf16_peak": fl / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                     "kernel": fwd_kernel_name(wc.block, wc.D), "build_mask_ms": b_ms}
+                     "kernel": fwd_kernel_name(wc.block, wc.D), "build_mask_ms": b_ms,
+                     "backward_ms": bk_ms,
+                     "backward_tflops": 2.5 * fl / (bk_ms * 1e-3) / 1e12,
+                     "backward_frac_of_bf16_peak": 2.5 * fl / (bk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
             if not args.no_cpu:
                 heads, cfl, dt = oracle_seconds(wc, qc, kc, vc, pc.row_ptr_host, cic_h,
                                                 args.cpu_seconds)
@@ -511,7 +530,7 @@ def main():
                                        "heads": f"{heads} of {wc.B * wc.H}",
                                        "gpu_over_cpu": (fl / (f_ms * 1e-3)) / (cfl / dt)}
             others[name] = entry
-            del qcd, kcd, vcd, occ, lcc, cic
+            del qcd, kcd, vcd, occ, lcc, cic, doc, bwsc
             torch.cuda.empty_cache()
         extra["other_configs"] = others
 
