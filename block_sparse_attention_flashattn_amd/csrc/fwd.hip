@@ -633,7 +633,7 @@ struct Wide {
 };
 
 template <bool RES>
-__global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
+__global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) void fwd_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
@@ -708,16 +708,21 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     return d;
   };
 
+  // Count of this wave's vector-memory operations (loads into LDS, stores,
+  // claims) in issue order.  Operations retire in order, so an operation
+  // issued when the count read `stamp` is complete once seq - stamp younger
+  // ones remain outstanding.  Operations left out of the count only make a
+  // wait stricter.
+  int seq = 0;
   // This wave's half of the query tile of CSR row `row` into the staging area.
-  // q_newest: no tile load has been issued since (the epilogue's wait for the
-  // staged tile must then not leave the newest loads in flight).
-  bool q_newest = false;
+  int q_stamp = 0;
   auto stage_q = [&](int row, int bh) {
     if (row < 0) return;
-    q_newest = true;
     const int qb = row - bh * nb;
     const uint32_t tb = uint32_t(qb) * (BLK * W::ROWB) + uint32_t(kh) * W::HALFB;
     dma_half(head_desc(Q, row, bh), ve + tb, vo + tb, qarea + uint32_t(kh) * W::HALFB);
+    seq += 4;
+    q_stamp = seq;
   };
   // Query fragments (B operand of S^T = K Q^T) from the staging area: lane
   // holds d = 16c + 8hh .. +7 of query row 32g + ql.
@@ -764,56 +769,47 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     load_item(nn_k, nn_row, nn_c0, nn_cnt, nn_slot);
   };
 
-  // Column position of stream tile p (counted from the current item's first
-  // tile), or -1 past the next item.
-  auto stream_src = [&](int p, bool& in_next) -> int {
-    in_next = p >= cur_cnt;
-    const int pn = p - cur_cnt;
-    return !in_next ? cur_c0 + p : (pn < nxt_cnt ? nxt_c0 + pn : -1);
-  };
 
-  int st_cur = 0;     // ring stage of the tile being computed
-  int vm_after = 0;   // operations issued after the current tile before the loop
-  int pending = 0;    // tiles issued beyond the current one (0 or 1)
-  int pf = 0;         // stream position of the next tile to issue
-  int valid_pf = 0;   // valid keys of the prefetched tile
-  // Issue stream tile `pf` (column j) into stage st; returns its valid key count.
-  auto issue = [&](int j, bool in_next, int st) -> int {
+  // K and V stream as half tiles through the wave's two-stage ring, K one tile
+  // further ahead than V, so that the scores of tile u + 1 are formed while the
+  // softmax of tile u runs and the matrix cores and the vector ALU of the
+  // wavefront overlap.  Position p of the current item (p = cur_cnt: the next
+  // item's first tile) uses stage (ib + p) & 1 of both the K and the V half of
+  // the ring.  k_last and v_last are the issue stamps of the latest K and V
+  // loads.
+  int ib = 0, k_last = 0, v_last = 0;
+  auto valid_of = [&](int j) -> int { return (j >= 0 && j < nb) ? min(BLK, N - j * BLK) : 0; };
+  auto issue = [&](v4i d, int j, int p, bool is_v) {
     const bool ok = j >= 0 && j < nb;
     const uint32_t tb = ok ? uint32_t(j) * (BLK * W::ROWB) + uint32_t(kh) * W::HALFB : head_bytes;
-    const uint32_t dst = ring + uint32_t(st) * W::STAGEB;
-    if (in_next)
-      dma_kv_half(kd_nxt, vd_nxt, ve + tb, vo + tb, dst, dst + W::HALFB);
+    dma_half(d, ve + tb, vo + tb,
+             ring + uint32_t((ib + p) & 1) * W::STAGEB + (is_v ? uint32_t(W::HALFB) : 0u));
+    seq += 4;
+    if (is_v)
+      v_last = seq;
     else
-      dma_kv_half(kd_cur, vd_cur, ve + tb, vo + tb, dst, dst + W::HALFB);
-    q_newest = false;
-    ++pf;
-    return ok ? min(BLK, N - j * BLK) : 0;
+      k_last = seq;
   };
+  // Column of the next item's first tile, or -1.
+  auto first_of_next = [&]() -> int { return nxt_cnt > 0 ? ld_uniform(col_idx, nxt_c0) : -1; };
 
-  // Start-up: the first query tile and the first K/V tile load together.
+  // Start-up: the first query tile and the first item's first K and V tiles.
   bf16x8 qf[2][4];
   stage_q(cur_row, cur_bh);
-  int valid_cur = 0;
-  {
-    bool in_next;
-    const int src = stream_src(0, in_next);
-    if (src >= 0) {
-      valid_cur = issue(ld_uniform(col_idx, src), in_next, 0);
-      pending = 1;  // counts the current tile until the loop takes it
-    }
+  if (cur_cnt > 0) {
+    const int j0 = ld_uniform(col_idx, cur_c0);
+    issue(kd_cur, j0, 0, false);
+    issue(vd_cur, j0, 0, true);
   }
-  if (pending)
-    wait_vm(8);
-  else
-    wait_vm(0);
+  wait_vm_n(seq - q_stamp);
   lds_barrier();
   read_q(qf);
   lds_barrier();
   stage_q(nxt_row, nxt_bh);
+
   // Chunk partials and their merge.  A wave's partial stores (agent-scope
-  // coherent) are known complete one epilogue later, where the wait for the
-  // query tile covers them (after the last item: at once, by a full wait).
+  // coherent) are known complete one epilogue later, where that epilogue's
+  // first wait covers them (after the last item: at once, by a full wait).
   // The wave then counts its query group of that chunk in; the wave whose
   // count-in completes the number of chunks combines the group's partials of
   // every chunk of the row and clears the count.  The count-in's result is
@@ -821,6 +817,7 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
   // is left in flight into the loop (the compiler's wait bookkeeping would
   // then drain the tile prefetch there).
   int rel_slot = -1;  // chunk whose partial this wave stored, not yet counted in
+  int st_stamp = 0;   // issue stamp after the latest epilogue's stores
   const int32_t* slot_merge =
       work ? work + 4 * size_t(n_items) + 3 * size_t(n_merges) + 2 + src.ng : nullptr;
   const int32_t* merges = work ? work + 4 * size_t(n_items) : nullptr;
@@ -868,11 +865,15 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     f32x4 o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < nc; c0 += 4) {
-      f32x4 a[4][8];
-      float mc[4], lc[4];
+    // Chunks are read kMB at a time (their loads in flight together); the
+    // batch is kept small so that the merge does not set the kernel's
+    // register budget.
+    constexpr int kMB = 2;
+    for (int c0 = 0; c0 < nc; c0 += kMB) {
+      f32x4 a[kMB][8];
+      float mc[kMB], lc[kMB];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < kMB; ++t) {
         // Chunks past the row's last read past the range: zeros, weight 0.
         const uint32_t cb = uint32_t(c0 + t) * kSlotFloats * 4u;
         mc[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
@@ -885,7 +886,7 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
               f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, cb + qoff + 16u * j, 0, kAgentScope));
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < kMB; ++t) {
         if (c0 + t >= nc) break;
         const float mn = fmaxf(M, mc[t]);
         const float wo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
@@ -928,21 +929,81 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     return 5;
   };
 
-  // Column of stream tile `pf`, looked up one step before it is issued.
-  int j_pf = 0;
-  bool has_pf = false, pf_next = false;
-  auto lookup = [&]() {
-    const int src = stream_src(pf, pf_next);
-    has_pf = src >= 0;
-    j_pf = has_pf ? ld_uniform(col_idx, src) : 0;
+  // Lane position of the transposing V^T reads: for the 16-key step c2, V^T
+  // rows d = 32u + (lane % 32) need keys 16c2 + 4hh + e and 16c2 + 8 + 4hh + e
+  // (e = 0..3): lane t of each 16-lane block points at key row t / 4 and
+  // columns 4 (t % 4) .. +3 of its block's 16 d values, and the transposing
+  // read returns to every lane the four keys of its own d.  V^T rows 16..31 of
+  // a tile (the second 16-key step) sit 2048 bytes past rows 0..15 and
+  // swizzle alike.
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t koff[4], voff[4];  // lane offsets of the K and V^T reads within a stage
+#pragma unroll
+  for (int c = 0; c < 4; ++c) koff[c] = swz<W::ROWB>(ql, 2 * c + hh);
+#pragma unroll
+  for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+      const int col = 32 * u2 + tr_col;
+      voff[2 * u2 + hl] = W::HALFB + swz<W::ROWB>(8 * hl + tr_row, col >> 3) + (col & 7) * 2;
+    }
+  auto stage_at = [&](int p) -> uint32_t { return ring + uint32_t((ib + p) & 1) * W::STAGEB; };
+  auto read_k = [&](uint32_t st, bf16x8 (&ka)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ka[c] = lds_read16(st + koff[c]);
   };
-  lookup();
+  auto read_v = [&](uint32_t st, v4s (&vlo)[2][2], v4s (&vhi)[2][2]) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        vlo[c2][u2] = lds_read_tr(st + voff[2 * u2] + 2048u * c2);
+        vhi[c2][u2] = lds_read_tr(st + voff[2 * u2 + 1] + 2048u * c2);
+      }
+  };
+  // S^T of query group g: lane (ql, hh) holds keys 8(i/4) + 4hh + (i%4) (of
+  // this half) of query 32g + ql.
+  auto scores_g = [&](int g, const bf16x8 (&ka)[4], f32x16& s) {
+    const f32x16 zero = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s, 0, 0, 0);
+  };
+  // Keys at or past the tile's valid count score -inf (both groups).  Lane
+  // element i is key 32kh + 4hh + o_i of the tile, o_i = 8(i/4) + (i%4); bit o
+  // of `bad` marks offsets at or past the valid count, and min(s, +-inf) keeps
+  // or drops the score without per-element compare masks.
+  auto mask = [&](f32x16 (&s)[2], int valid) {
+    const int lim = valid - (32 * kh + 4 * hh);
+    const uint32_t bad = lim <= 0 ? 0xffffffffu : (lim >= 32 ? 0u : (0xffffffffu << lim));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int o = 8 * (i >> 2) + (i & 3);
+      const float cap = __uint_as_float(0x7f800000u | (((bad >> o) & 1u) << 31));
+      s[0][i] = __builtin_fminf(s[0][i], cap);
+      s[1][i] = __builtin_fminf(s[1][i], cap);
+    }
+  };
+  // Row maxima of a score tile in log2 units (both key halves of the wave).
+  auto tile_max = [&](const f32x16 (&s)[2], float (&mt)[2]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float mx = vmax(s[g][0], s[g][1]);
+#pragma unroll
+      for (int i = 2; i < 16; ++i) mx = vmax(mx, s[g][i]);
+      // The other half-wave holds the other 16 keys of the same queries.
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mt[g] = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+    }
+  };
 
   for (;;) {
     // ---- one item ---------------------------------------------------------
     float m_run[2] = {kNoMax, kNoMax};  // running max of scale*log2(e)*s
-    float l_run[2] = {0.f, 0.f};              // lane-partial running sums
-    f32x16 acc[2][2];                          // [query group][d half]
+    float l_run[2] = {0.f, 0.f};        // lane-partial running sums
+    f32x16 acc[2][2];                   // [query group][d half]
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -950,92 +1011,12 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[g][u][i] = 0.f;
 
-    for (int u = 0; u < cur_cnt; ++u) {
-      // Tile u was issued one step ago (or at the item transition).  Issue the
-      // next stream tile into the other stage, which this wave finished
-      // reading in the previous step, then wait for tile u only.
-      if (queue && kh == 0 && claim_out && !nn_known && u == cur_cnt - 1) resolve_claim();
-      // Tile u is complete once at most `allowed` younger operations are
-      // outstanding: the tile issued now and, at an item's first step, the
-      // previous epilogue's stores, a claim and the query staging, all issued
-      // after tile u (vector memory operations retire in order).
-      int allowed = vm_after;
-      vm_after = 0;
-      pending = 0;
-      if (has_pf) {
-        valid_pf = issue(j_pf, pf_next, st_cur ^ 1);
-        pending = 1;
-        lookup();
-        allowed += 8;
-      }
-      wait_vm_n(allowed);
-      const uint32_t ks = ring + uint32_t(st_cur) * W::STAGEB;
-      const uint32_t vs = ks + W::HALFB;
-
-      // The four K operands are read up front (one round trip instead of
-      // four).  The eight V^T halves are issued between the S MFMAs, whose
-      // issue they then hide, and land while the softmax runs.  For the 16-key
-      // step c2, V^T rows d = 32u + (lane % 32) need keys 16c2 + 4hh + e and
-      // 16c2 + 8 + 4hh + e (e = 0..3): lane t of each 16-lane block points at
-      // key row t / 4 and columns 4 (t % 4) .. +3 of its block's 16 d values,
-      // and the transposing read returns to every lane the four keys of its
-      // own d.
-      bf16x8 ka[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ka[c] = lds_read16(ks + swz<W::ROWB>(ql, 2 * c + hh));
-      __builtin_amdgcn_sched_barrier(0);
-
-      // S^T tiles: lane (ql, hh) holds keys 8(i/4) + 4hh + (i%4) (of this
-      // half) of query 32g + ql.
-      const f32x16 zero = {};
-      f32x16 s[2];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-          s[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s[g], 0,
-                                                         0, 0);
-      const int tr_row = 4 * hh + ((lane & 15) >> 2);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      v4s vlo[2][2], vhi[2][2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int u2 = 0; u2 < 2; ++u2) {
-          const int col = 32 * u2 + tr_col;
-          vlo[c2][u2] = lds_read_tr(vs + swz<W::ROWB>(16 * c2 + tr_row, col >> 3) + (col & 7) * 2);
-          vhi[c2][u2] =
-              lds_read_tr(vs + swz<W::ROWB>(16 * c2 + 8 + tr_row, col >> 3) + (col & 7) * 2);
-        }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
-      if (__builtin_expect(valid_cur < BLK, 0)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kv = 32 * kh + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (kv >= valid_cur) {
-            s[0][i] = -INFINITY;
-            s[1][i] = -INFINITY;
-          }
-        }
-      }
-      // Lazy rescale: only when some row's max grew by more than the slack;
-      // a row's first finite max is adopted without touching its zero state.
-      float mt[2];
+    // Lazy rescale: only when some row's max grew by more than the slack; a
+    // row's first finite max is adopted without touching its zero state.
+    auto adopt_max = [&](const float (&mt)[2]) {
       bool need[2], rescale[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        float mx = vmax(s[g][0], s[g][1]);
-#pragma unroll
-        for (int i = 2; i < 16; ++i) mx = vmax(mx, s[g][i]);
-        // The other half-wave holds the other 16 keys of the same queries.
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                         false, false);
-        mx = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        mt[g] = mx * sl2;
         need[g] = mt[g] > m_run[g] + kRescaleSlack;
         rescale[g] = need[g] && m_run[g] != kNoMax;
       }
@@ -1052,27 +1033,53 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       }
 #pragma unroll
       for (int g = 0; g < 2; ++g) m_run[g] = need[g] ? mt[g] : m_run[g];
-
-      // P in bf16 only as the MFMA operand; the row sums add the fp32 values,
-      // in four independent chains.
-      bf16x8 pb[2][2];
+    };
+    // Softmax numerators of query group g: P in bf16 only as the MFMA operand;
+    // the row sum adds the fp32 values in four independent chains.
+    auto probs_g = [&](int g, const f32x16& s, bf16x8 (&pb)[2]) {
+      float ls[4];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        float ls[4];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[g][i], sl2, -m_run[g]));
-          if (i < 4)
-            ls[i] = p;
-          else
-            ls[i & 3] += p;
-          pb[g][i >> 3][i & 7] = static_cast<__bf16>(p);
-        }
-        l_run[g] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -m_run[g]));
+        if (i < 4)
+          ls[i] = p;
+        else
+          ls[i & 3] += p;
+        pb[i >> 3][i & 7] = static_cast<__bf16>(p);
       }
-
-      // O^T += V^T P^T, one V^T operand per 16-key step and d half, shared by
-      // both query groups.
+      l_run[g] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    // Query group g: the softmax numerators of tile u (scores sc) interleaved
+    // with the four MFMAs of tile u + 1's scores (into sn), a quarter of the
+    // vector work after each, so that both run at once.
+    auto phase = [&](int g, const bf16x8 (&ka)[4], const f32x16& sc, f32x16& sn, bf16x8 (&pb)[2]) {
+      const f32x16 zero = {};
+      float p[16];
+      float ls[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : sn, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * c + e;
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -m_run[g]));
+          if (c == 0)
+            ls[e] = p[i];
+          else
+            ls[e] += p[i];
+        }
+        if (c & 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[c >> 1][e] = static_cast<__bf16>(p[8 * (c >> 1) + e]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // its share of the softmax
+      }
+      l_run[g] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    // O^T += V^T P^T, one V^T operand per 16-key step and d half, shared by both
+    // query groups.
+    auto pv = [&](const v4s (&vlo)[2][2], const v4s (&vhi)[2][2], const bf16x8 (&pb)[2][2]) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
@@ -1083,19 +1090,128 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
           for (int g = 0; g < 2; ++g)
             acc[g][u2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][c2], acc[g][u2], 0, 0, 0);
         }
+    };
 
-      st_cur ^= 1;
-      valid_cur = valid_pf;
+    const int cnt = cur_cnt;
+    const int j0n = first_of_next();
+    // Columns of positions u + 1 (its V is issued in step u and its scores
+    // formed there) and u + 2 (its K is issued in step u), looked up one step
+    // early.
+    int jv = cnt > 1 ? ld_uniform(col_idx, cur_c0 + 1) : 0;
+    int jk = cnt > 2 ? ld_uniform(col_idx, cur_c0 + 2) : j0n;
+    // Row maxima of the tile whose scores are held (mt) are adopted at the
+    // start of the step that runs its softmax; a tile with keys past N
+    // (valid count vs < BLK, only the last block of a head) has its scores
+    // masked and its maxima recomputed first.  Before the step's own loads,
+    // the latest are V(u) and K(u + 1).
+    float mt[2];
+    int vs = BLK;  // valid keys of the tile whose scores are held
+    auto settle = [&](f32x16 (&sc)[2]) {
+      if (__builtin_expect(vs < BLK, 0)) {
+        mask(sc, vs);
+        tile_max(sc, mt);
+      }
+      adopt_max(mt);
+    };
+    // One pipelined step: softmax and P V of tile u (scores in sc), scores and
+    // unmasked maxima of tile u + 1 (< cnt) into sn.  Three phases, each
+    // pairing matrix work with independent vector work: (A) group 0's softmax
+    // with group 0's next scores, (B) the same for group 1, (C) P V with the
+    // next row maxima.
+    auto step = [&](int u, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      // Wave 0 reads the claim for the item after next where the only loads
+      // in flight are the ones this step waits for anyway.
+      if (queue && kh == 0 && claim_out && !nn_known && u + 2 == cnt) resolve_claim();
+      settle(sc);
+      issue(vd_cur, jv, u + 1, true);
+      int issued = 4;
+      if (u + 2 < cnt) {
+        issue(kd_cur, jk, u + 2, false);
+        issued = 8;
+      } else if (jk >= 0) {  // the next item's first tile
+        issue(kd_nxt, jk, u + 2, false);
+        issued = 8;
+      }
+      vs = valid_of(jv);
+      jv = jk;
+      jk = u + 3 < cnt ? ld_uniform(col_idx, cur_c0 + u + 3) : j0n;
+      wait_vm_n(issued);
+      bf16x8 ka[4];
+      v4s vlo[2][2], vhi[2][2];
+      bf16x8 pb[2][2];
+      read_k(stage_at(u + 1), ka);
+      read_v(stage_at(u), vlo, vhi);
+      __builtin_amdgcn_sched_barrier(0);
+      phase(0, ka, sc[0], sn[0], pb[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      phase(1, ka, sc[1], sn[1], pb[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(vlo, vhi, pb);
+      tile_max(sn, mt);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one P V MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // row max of the next tile
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Item start: K(0) and V(0) were issued with the previous item (or at
+    // start-up).  Issue K(1), which is the next item's first tile when this
+    // item has one tile; an item without tiles issues the next item's first
+    // K and V.
+    const int k0_stamp = k_last;
+    if (cnt > 1)
+      issue(kd_cur, jv, 1, false);
+    else if (j0n >= 0) {
+      issue(kd_nxt, j0n, cnt, false);
+      if (cnt == 0) issue(vd_nxt, j0n, 0, true);
+    }
+    if (cnt > 0) {
+      f32x16 sa[2], sb[2];
+      // Prologue: the scores of the first tile and their maxima.
+      {
+        vs = valid_of(ld_uniform(col_idx, cur_c0));
+        wait_vm_n(seq - k0_stamp);
+        bf16x8 ka[4];
+        read_k(stage_at(0), ka);
+        scores_g(0, ka, sa[0]);
+        scores_g(1, ka, sa[1]);
+        tile_max(sa, mt);
+      }
+      // Pipelined steps u = 0 .. cnt - 2, two per trip so that the score tiles
+      // alternate between sa and sb without copies.
+      int u = 0;
+      while (u + 2 < cnt) {
+        step(u, sa, sb);
+        step(u + 1, sb, sa);
+        u += 2;
+      }
+      if (u + 1 < cnt) {
+        step(u, sa, sb);
+        ++u;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) sa[g] = sb[g];
+      }
+      // The last tile: its softmax and P V; the next item's first V follows
+      // its first K.
+      settle(sa);
+      if (queue && kh == 0 && claim_out && !nn_known) resolve_claim();
+      const int v_stamp = v_last;
+      if (j0n >= 0) issue(vd_nxt, j0n, cnt, true);
+      wait_vm_n(seq - v_stamp);
+      v4s vlo[2][2], vhi[2][2];
+      bf16x8 pb[2][2];
+      read_v(stage_at(cnt - 1), vlo, vhi);
+      probs_g(0, sa[0], pb[0]);
+      probs_g(1, sa[1], pb[1]);
+      pv(vlo, vhi, pb);
     }
 
     // ---- epilogue -----------------------------------------------------------
-    // The next item's query tile: this wave's half is complete once only the
-    // prefetched tile may be outstanding, provided that tile was issued after
-    // the query tile (not so when an item without tiles follows start-up).
-    if (pending && !q_newest)
-      wait_vm(8);
-    else
-      wait_vm(0);
+    // The next item's query tile (this wave's half) and the previous
+    // epilogue's partial stores, if any, are complete.
+    wait_vm_n(seq - (rel_slot >= 0 ? max(q_stamp, st_stamp) : q_stamp));
     // With a residual, the part this wave adds (its query group kh, the columns
     // its lanes finalise; rows past N read as zeros) is loaded now and lands
     // during the exchange.  Chunks of cut rows add it when they are combined.
@@ -1112,12 +1228,16 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
               rrsc, rrow + uint32_t(32 * u + 8 * g4 + 4 * hh) * 2u, 0, 0);
     }
     // The previous epilogue's partial stores are complete: count them in.
-    int rel_m = -1, rel_old = 0;
+    // (Only after a chunk of a cut row.  The count is read at once, on that
+    // path alone: a wait for a memory result drains every load issued before
+    // it, the next item's first tiles included, so the common path has none.)
+    int mg_a = -1;
     if (rel_slot >= 0) {
-      rel_m = merge_of(rel_slot);
-      if (rel_m >= 0) rel_old = count_in(rel_m);
+      const int m = merge_of(rel_slot);
+      if (m >= 0 && completes(m, __builtin_amdgcn_readfirstlane(count_in(m)))) mg_a = m;
       rel_slot = -1;
     }
+    mg_a = __builtin_amdgcn_readfirstlane(mg_a);
     const bool more = k_nxt >= 0;
     lds_barrier();  // both halves of the staged query tile are in LDS
     if (more) read_q(qf);
@@ -1127,9 +1247,10 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     lds_barrier();  // the staging area is free for the exchange of m and l
 
     // Wave kh finalises query group kh; it sends its state of group 1 - kh
-    // through its own last-computed stage, and m, l through the staging area.
+    // through the stage of its own ring that held the item's last tile (the
+    // other holds the next item's first), and m, l through the staging area.
     // (Branches on kh keep every register array index a compile-time constant.)
-    const int st_free = st_cur ^ 1;
+    const int st_free = (ib + cur_cnt + 1) & 1;
     float* xml = reinterpret_cast<float*>(smem + 2 * size_t(W::RINGB));
     auto send = [&](const f32x16 (&a)[2], float m, float l) {
       float* xo = reinterpret_cast<float*>(smem + size_t(kh) * W::RINGB +
@@ -1279,14 +1400,7 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     } else {
       k_nn = src.stat(round);
     }
-    // The count-in's result, before this epilogue's stores (the wait then
-    // covers only the prefetched tile and the count-in).
-    int mg_a = -1, mg_b = -1;
-    {
-      const int old = __builtin_amdgcn_readfirstlane(rel_old);  // on every path
-      if (rel_m >= 0 && completes(rel_m, old)) mg_a = rel_m;
-    }
-    mg_a = __builtin_amdgcn_readfirstlane(mg_a);
+    int mg_b = -1;
     if (kh == 0)
       finish(acc[0], m_run[0], l_half[0]);
     else
@@ -1316,13 +1430,15 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
       merge_stores += merge_group(m);
     }
     merge_stores = __builtin_amdgcn_readfirstlane(merge_stores);
+    seq += n_stores + merge_stores;
+    st_stamp = seq;
 
     // ---- advance to the next item ------------------------------------------
     k_cur = k_nxt;
     k_nxt = k_nn;
     ++round;
     if (k_cur < 0) break;
-    pf -= cur_cnt;
+    ib = (ib + cur_cnt) & 1;
     cur_row = nxt_row;
     cur_c0 = nxt_c0;
     cur_cnt = nxt_cnt;
@@ -1345,28 +1461,13 @@ __global__ __launch_bounds__(Wide::NT) void fwd_wide_kernel(
     nn_row = -1;
     nn_c0 = nn_cnt = 0;
     nn_slot = -1;
-    if (claim_out && kh == 0 && lane == 0) ticket = src.claim(ctr);
+    if (claim_out && kh == 0) {
+      if (lane == 0) ticket = src.claim(ctr);
+      seq += 1;
+    }
     kd_nxt = head_desc(K, nxt_row, nxt_bh);
     vd_nxt = head_desc(V, nxt_row, nxt_bh);
     stage_q(nxt_row, nxt_bh);
-    // Operations issued after the prefetched first tile of the new item: the
-    // epilogue's stores, this wave's claim and the query staging.
-    vm_after = pending ? n_stores + merge_stores + ((claim_out && kh == 0) ? 1 : 0) +
-                             (nxt_row >= 0 ? 4 : 0)
-                       : 0;
-    // The looked-up column, if any, lies in the old next item, which is now
-    // the current one; a lookup that ran past it is redone now that the item
-    // after it is known.
-    if (has_pf)
-      pf_next = false;
-    else
-      lookup();
-    if (!pending && cur_cnt > 0) {
-      // Nothing was prefetched for the new item (its predecessor had no tile
-      // to look ahead to): issue its first tile now.
-      valid_cur = issue(j_pf, pf_next, st_cur);
-      lookup();
-    }
   }
   wait_vm(0);  // no load may still target LDS when the workgroup retires
 }
