@@ -318,7 +318,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   using C = DkdvCfg<HD>;
   constexpr int RB = C::RB, NDC = C::NDC, NDT = C::NDT;
   constexpr uint32_t kTile = C::kTile, kHalf = C::kHalf, kLd = C::kLd, kStage = C::kStage;
-  constexpr int kLoads = 2 * (RB / 32) + 1;  // tile loads one stage takes per wave
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
   const int tid = threadIdx.x, lane = tid & 63;
@@ -369,7 +368,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   const int e1 = c0 + int(int64_t(c1 - c0) * (ch + 1) / nch);
   IndexWindow rows;
   rows.init(row_idx, e0, e1, lane);
-  // This wave's halves of query block i into stage st (kLoads loads); a block
+  // This wave's halves of query block i into stage st; a block
   // outside [0, nb) reads past the buffers, i.e. zeros.
   auto issue = [&](int i, int st) {
     const bool ok = i >= 0 && i < nb;
@@ -385,15 +384,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   if (e0 < e1) issue(i_next, 0);
   for (int e = e0, st = 0; e < e1; ++e, st ^= 1) {
     const int i = i_next;
-    lds_barrier();  // both waves are done reading the other stage (block e-1)
+    // Only block e is in flight: this wave's halves of it have landed once
+    // the wait returns.  After the barrier both waves' halves are in LDS and
+    // both waves are done reading block e-1, whose stage then takes block e+1.
+    wait_vm(0);
+    lds_barrier();
     if (e + 1 < e1) {
       i_next = rows.at(e + 1, lane);
       issue(i_next, st ^ 1);
-      wait_vm_n(kLoads);
-    } else {
-      wait_vm(0);
     }
-    lds_barrier();  // both waves' halves of block e are in LDS
     if (i < 0 || i >= nb) continue;
     const uint32_t qs = lds0 + uint32_t(st) * kStage, dss = qs + kTile;
     const float* lds_ld = reinterpret_cast<const float*>(smem + size_t(st) * kStage + 2 * kTile);
