@@ -8,9 +8,12 @@
 // Five launches on the caller's stream:
 //   prep       per query row (LSE * log2(e), delta), fp32;
 //   transpose  per head, the query blocks that list each key block, ascending,
-//              and the split of long key columns and query rows into chunks;
-//   dkdv       one workgroup per chunk of a key block's query blocks;
-//   dq         one workgroup per chunk of a query block's CSR row;
+//              the split of long key columns and query rows into chunks, and
+//              the head's work items appended to its die's work lists;
+//   dkdv       persistent workgroups, one chunk of a key block's query blocks
+//              per item;
+//   dq         persistent workgroups, one chunk of a query block's CSR row per
+//              item;
 //   reduce     per split block, the chunks' fp32 partials summed in chunk order.
 // A column or row longer than the chunk length (twice the mean row length, at
 // least 16) is cut into near-equal chunks so that a few long ones (text blocks,
@@ -34,6 +37,17 @@ constexpr int kBB = 64;     // block (query block = key block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDqStages = 2;  // K/V ring depth of the dQ kernel
 
+// Work lists of the gradient kernels: one per die (XCD) when there are at least
+// as many heads as dies, else one.  Head bh's items go to list bh % n_lists.
+constexpr int kLists = 8;
+constexpr int kClaimStride = 32;  // ints between two claim counters (own cache lines)
+// Counter area (ints): [0], [1] partial-slot counters (dK/dV, dQ); kLenKv + l and
+// kLenKv + kLists + l the chunk and whole-block items in dK/dV list l, kLenQ + l
+// and kLenQ + kLists + l those of dQ list l; the claim counters of list l at
+// kClaimKv + l kClaimStride and kClaimQ + l kClaimStride.  prep_kernel clears it.
+constexpr int kLenKv = 16, kLenQ = 32, kClaimKv = 64, kClaimQ = kClaimKv + kLists * kClaimStride;
+constexpr int kCtrInts = kClaimQ + kLists * kClaimStride;
+
 __device__ __forceinline__ void lds_write16(uint32_t addr, v4u x) {
   *reinterpret_cast<BSA_LDS v4u*>(static_cast<uintptr_t>(addr)) = x;
 }
@@ -55,14 +69,15 @@ __device__ __forceinline__ float dot8(v4u a, v4u b) {
 
 // Per query row t: (LSE_t * log2(e), delta_t); rows with LSE = -inf (no active key)
 // get +inf so that every probability of the row is exp2(-inf) = 0.  HD / 8 lanes
-// per row, 16 bytes each.  Also clears the two partial-slot counters.
+// per row, 16 bytes each.  Also clears the counter area of the later launches.
 template <int HD>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ O,
                                                    const uint16_t* __restrict__ dO,
                                                    const float* __restrict__ LSE, int64_t rows,
                                                    float2* __restrict__ out,
                                                    int32_t* __restrict__ slot_ctr) {
-  if (blockIdx.x == 0 && threadIdx.x < 2) slot_ctr[threadIdx.x] = 0;  // read by transpose
+  if (blockIdx.x == 0)
+    for (int x = threadIdx.x; x < kCtrInts; x += 256) slot_ctr[x] = 0;
   constexpr int LPR = HD / 8;  // lanes per row
   const int64_t t = (int64_t(blockIdx.x) * 256 + threadIdx.x) / LPR;
   const int c = threadIdx.x & (LPR - 1);
@@ -199,6 +214,13 @@ __device__ int block_scan(int32_t* a, int n, int32_t* tmp) {
 // slots from the counters (cleared by prep_kernel).  If the slots run out (they
 // cannot when the capacity is the bound the host sizes), the head is left
 // unsplit, which is slower but exact.
+// Work items: a record {bh nb + j, first entry, end entry, partial slot or -1}
+// for every chunk of key column j (dK/dV list, entries of row_idx) and of CSR
+// row j (dQ list, entries of col_idx), appended to list bh % n_lists at ranges
+// the head reserves there.  A list has two parts of list_cap records: the
+// chunks of split blocks (the longest items, claimed first), each head's in
+// block order, and the whole blocks, each head's longest first (a counting
+// sort by length; equal lengths in any order).
 __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restrict__ row_ptr,
                                                         const int32_t* __restrict__ col_idx,
                                                         int32_t nb, int32_t n_heads,
@@ -208,12 +230,16 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ slot_ctr,
                                                         int32_t cap_kv, int32_t cap_q,
                                                         int2* __restrict__ col_split,
-                                                        int2* __restrict__ row_split) {
+                                                        int2* __restrict__ row_split,
+                                                        int32_t n_lists, int32_t list_cap,
+                                                        int4* __restrict__ items_kv,
+                                                        int4* __restrict__ items_q) {
   extern __shared__ uint32_t bits[];
   __shared__ int32_t rp[kMaxBlocks + 1];
   __shared__ int32_t start[kMaxBlocks], nch_c[kMaxBlocks], nch_r[kMaxBlocks];
   __shared__ int32_t pre_c[kMaxBlocks], pre_r[kMaxBlocks], tmp[256];
-  __shared__ int32_t base_sh[2];
+  __shared__ int32_t hist[kMaxBlocks];  // length histogram of the whole blocks
+  __shared__ int32_t base_sh[4];
   const int tid = threadIdx.x;
   const int W = (nb + 31) >> 5;
   const int bh = blockIdx.x;
@@ -274,6 +300,56 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
     row_split[r0 + j] = (nch_r[j] > 1 && bq >= 0) ? make_int2(bq + pre_r[j], nch_r[j])
                                                   : make_int2(-1, 1);
   }
+  __syncthreads();
+  for (int j = tid; j < nb; j += 256) {  // 1 for the blocks left whole
+    nch_c[j] = (nch_c[j] > 1 && bk >= 0) ? 0 : 1;
+    nch_r[j] = (nch_r[j] > 1 && bq >= 0) ? 0 : 1;
+  }
+  __syncthreads();
+  const int n_wk = block_scan(nch_c, nb, tmp);  // whole blocks before block j
+  const int n_wq = block_scan(nch_r, nb, tmp);
+  const int l = bh % n_lists;
+  if (tid == 0) {
+    // chunks: one per partial slot, at the slot's offset in the head's range
+    base_sh[0] = atomicAdd(slot_ctr + kLenKv + l, bk >= 0 ? tot_kv : 0);
+    base_sh[1] = atomicAdd(slot_ctr + kLenKv + kLists + l, n_wk);
+    base_sh[2] = atomicAdd(slot_ctr + kLenQ + l, bq >= 0 ? tot_q : 0);
+    base_sh[3] = atomicAdd(slot_ctr + kLenQ + kLists + l, n_wq);
+  }
+  __syncthreads();
+  int4* const ck = items_kv + size_t(2 * l) * list_cap + base_sh[0];
+  int4* const wk = items_kv + size_t(2 * l + 1) * list_cap + base_sh[1];
+  int4* const cq = items_q + size_t(2 * l) * list_cap + base_sh[2];
+  int4* const wq = items_q + size_t(2 * l + 1) * list_cap + base_sh[3];
+  // Bin of a whole block of `len` entries: longer blocks in lower bins.
+  auto bin = [](int len) { return kMaxBlocks - 1 - min(len, kMaxBlocks - 1); };
+  for (int kind = 0; kind < 2; ++kind) {  // key columns, then CSR rows
+    const int32_t* whole = kind ? nch_r : nch_c;
+    const int n_whole = kind ? n_wq : n_wk;
+    for (int b = tid; b < kMaxBlocks; b += 256) hist[b] = 0;
+    __syncthreads();
+    for (int j = tid; j < nb; j += 256) {
+      const int len = kind ? rp[j + 1] - rp[j]
+                           : (j + 1 < nb ? begin + start[j + 1] : end) - (begin + start[j]);
+      if ((j + 1 < nb ? whole[j + 1] : n_whole) > whole[j]) atomicAdd(&hist[bin(len)], 1);
+    }
+    __syncthreads();
+    block_scan(hist, kMaxBlocks, tmp);
+    for (int j = tid; j < nb; j += 256) {
+      const int a = kind ? rp[j] : begin + start[j];
+      const int len = (kind ? rp[j + 1] : (j + 1 < nb ? begin + start[j + 1] : end)) - a;
+      if ((j + 1 < nb ? whole[j + 1] : n_whole) > whole[j]) {
+        (kind ? wq : wk)[atomicAdd(&hist[bin(len)], 1)] = make_int4(r0 + j, a, a + len, -1);
+      } else {
+        const int n = n_chunks(len, chunk, max_ch), pre = kind ? pre_r[j] : pre_c[j];
+        const int base = kind ? bq : bk;
+        for (int c = 0; c < n; ++c)
+          (kind ? cq : ck)[pre + c] = make_int4(r0 + j, a + int(int64_t(len) * c / n),
+                                                a + int(int64_t(len) * (c + 1) / n), base + pre + c);
+      }
+    }
+    __syncthreads();
+  }
   for (int e = begin + listed + tid; e < end; e += 256) row_idx[e] = -1;
   for (int j = tid; j < nb; j += 256) {
     int pos = begin + start[j];
@@ -288,14 +364,61 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
   }
 }
 
-// dK, dV of one chunk of key block j (workgroup (chunk, bh, j), two wavefronts;
+// Persistent gradient workgroups take their items from the work lists:
+// workgroup b starts at list b % n_lists (its own die's when there is one list
+// per die: workgroups are dealt to the dies round robin); once that list is
+// used up it reads every list's claim counter in one go and moves on to the
+// next list with items left, so dies that finish early help the others.  One
+// lane claims (vector atomics, agent scope); the claim for the next item is
+// issued when an item starts, and its record is loaded during the item's last
+// step.
+struct ListClaims {
+  const int4* items;
+  const int32_t* lens;
+  int32_t* claims;
+  int n_lists, cap, list, nc, nw;  // nc, nw: the current list's chunks and whole blocks
+
+  __device__ void load_lens() {
+    nc = lens[list];
+    nw = lens[kLists + list];
+  }
+  __device__ int claim() const {
+    return __hip_atomic_fetch_add(claims + list * kClaimStride, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Called by all lanes of one wave: the item of claim number s (lane 0's) on
+  // the current list (its chunks, then its whole blocks), else one claimed from a
+  // list with items left; a record with block -1 once no list has any.
+  __device__ int4 item(int s, int lane) {
+    s = __builtin_amdgcn_readfirstlane(s);
+    for (;;) {
+      if (s < nc) return items[size_t(2 * list) * cap + s];
+      if (s < nc + nw) return items[size_t(2 * list + 1) * cap + (s - nc)];
+      int left = 0;
+      if (lane < n_lists)
+        left = lens[lane] + lens[kLists + lane] -
+               __hip_atomic_load(claims + lane * kClaimStride, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t m = __ballot(left > 0);
+      if (m == 0) return make_int4(-1, 0, 0, -1);
+      const uint64_t hi = m >> list;  // lists at or after the current one first
+      list = hi ? list + __builtin_ctzll(hi) : __builtin_ctzll(m);
+      load_lens();
+      int t = 0;
+      if (lane == 0) t = claim();
+      s = __builtin_amdgcn_readfirstlane(t);
+    }
+  }
+};
+
+// dK, dV of one chunk of key block j (item (bh, j, chunk), two wavefronts;
 // wave w owns keys 32w .. 32w+31, which are the columns of its tiles).  For
 // every query block i of the chunk: the 64 Q and dO rows are staged in LDS (swizzled), then per
 // 32-query tile S = Q K^T and dP = dO V^T on MFMA (K, V rows of the wave's keys
 // are the B operands, held in registers), P = exp2(S scale log2e - LSE log2e),
 // dS = P (dP - delta), and dV^T += dO^T P, dK^T += Q^T dS with dO^T, Q^T read
 // transposed from LDS.  An unsplit column writes bf16 dK, dV; a chunk of a
-// split one writes its fp32 sums (dK unscaled) to partial slot `slot + chunk`.
+// split one writes its fp32 sums (dK unscaled) to the item's partial slot.
 // At HD = 128 the two stages take 65 KiB of LDS: two workgroups per CU, one
 // wave per SIMD, which may then use the whole register file.
 template <int HD>
@@ -303,16 +426,18 @@ struct DkdvCfg {
   static constexpr int RB = HD * 2, NDC = HD / 16, NDT = HD / 32;
   static constexpr uint32_t kTile = kBB * RB, kHalf = kTile / 2, kLd = kBB * 8;
   static constexpr uint32_t kStage = 2 * kTile + kLd;
-  static constexpr size_t LDS_BYTES = 2 * size_t(kStage);
+  static constexpr size_t kClaimAt = 2 * size_t(kStage);  // two records: the claimed items
+  static constexpr size_t LDS_BYTES = kClaimAt + 32;
 };
 
 template <int HD>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 2 : 1))) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ ld,
-    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
-    const int2* __restrict__ col_split, int32_t n_cols, int32_t N, int32_t nb, float c2,
-    float scale, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part) {
+    const int32_t* __restrict__ row_idx,
+    const int4* __restrict__ items, int32_t* __restrict__ ctr, int32_t n_lists, int32_t list_cap,
+    int32_t N, int32_t nb, float c2, float scale, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, float* __restrict__ part) {
   // Two stages of (Q tile, dO tile, per-row (LSE log2 e, delta)) of one query
   // block, each wave streaming its 32-row halves by LDS DMA one block ahead.
   using C = DkdvCfg<HD>;
@@ -323,12 +448,32 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hh = lane >> 5;
-  const int ch = blockIdx.x / n_cols;
-  const int r = blockIdx.x - ch * n_cols;
-  const int2 sp = col_split[r];
-  const int slot = __builtin_amdgcn_readfirstlane(sp.x);
-  const int nch = slot < 0 ? 1 : __builtin_amdgcn_readfirstlane(sp.y);
-  if (ch >= nch) return;
+  uint32_t hoff[RB / 32];
+  half_offsets<RB>(lane, 32 * w, hoff);
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  ListClaims lc{items, ctr + kLenKv, ctr + kClaimKv, n_lists, list_cap,
+                static_cast<int>(blockIdx.x % n_lists), 0, 0};
+  int4* const claimed = reinterpret_cast<int4*>(smem + C::kClaimAt);
+  int ticket = 0;
+  int4 nxt = make_int4(-1, 0, 0, -1);  // wave 0: the next item, loaded in the last step
+  if (tid < 64) {
+    lc.load_lens();
+    if (tid == 0) ticket = lc.claim();
+    const int4 c = lc.item(ticket, lane);
+    if (tid == 0) claimed[0] = c;
+  }
+  for (int par = 0;; par ^= 1) {
+  // The barrier publishes the item wave 0 resolved and keeps this item's first
+  // loads out of LDS the previous item may still be reading.
+  lds_barrier();
+  const int4 rec = claimed[par];
+  const int r = __builtin_amdgcn_readfirstlane(rec.x);
+  if (r < 0) break;
+  if (tid == 0) ticket = lc.claim();
+  const int e0 = __builtin_amdgcn_readfirstlane(rec.y);
+  const int e1 = __builtin_amdgcn_readfirstlane(rec.z);
+  const int pslot = __builtin_amdgcn_readfirstlane(rec.w);
   const int bh = r / nb, j = r - bh * nb;
   const size_t head = size_t(bh) * size_t(N) * HD;
   const uint32_t hbytes = static_cast<uint32_t>(N) * RB;
@@ -338,8 +483,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   // (LSE log2 e, delta) of the head's rows; rows past N read zeros, which is
   // harmless: their Q and dO rows are zeros too, so they add exactly nothing.
   const v4i ldd = uniform_desc(ld + size_t(bh) * N, static_cast<uint32_t>(N) * 8u);
-  uint32_t hoff[RB / 32];
-  half_offsets<RB>(lane, 32 * w, hoff);
   const int key = kBB * j + 32 * w + ql;
   const bool key_ok = key < N;
   bf16x8 kf[NDC], vf[NDC];
@@ -360,12 +503,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
       dk[u][x] = 0.f;
       dv[u][x] = 0.f;
     }
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int c0 = __builtin_amdgcn_readfirstlane(col_ptr[r]);
-  const int c1 = __builtin_amdgcn_readfirstlane(col_ptr[r + 1]);
-  const int e0 = c0 + int(int64_t(c1 - c0) * ch / nch);
-  const int e1 = c0 + int(int64_t(c1 - c0) * (ch + 1) / nch);
   IndexWindow rows;
   rows.init(row_idx, e0, e1, lane);
   // This wave's halves of query block i into stage st; a block
@@ -392,6 +529,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
     if (e + 1 < e1) {
       i_next = rows.at(e + 1, lane);
       issue(i_next, st ^ 1);
+    } else if (tid < 64) {
+      nxt = lc.item(ticket, lane);  // the claim returned by the wait above
     }
     if (i < 0 || i >= nb) continue;
     const uint32_t qs = lds0 + uint32_t(st) * kStage, dss = qs + kTile;
@@ -444,9 +583,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
     }
   }
   // register e of dv[u], dk[u]: dimension 32u + 8(e/4) + 4hh + e%4 of key `key`
-  if (nch > 1) {
+  if (pslot >= 0) {
     // [dK | dV] of the block's 64 keys, row-major, fp32; keys past N hold zeros
-    float* pk = part + size_t(slot + ch) * (2 * kBB * HD) + size_t(32 * w + ql) * HD;
+    float* pk = part + size_t(pslot) * (2 * kBB * HD) + size_t(32 * w + ql) * HD;
     float* pv = pk + kBB * HD;
 #pragma unroll
     for (int u = 0; u < NDT; ++u)
@@ -474,31 +613,37 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
                        pack_bf16x2(scale * dk[u][4 * g4 + 2], scale * dk[u][4 * g4 + 3]));
       }
   }
+  if (tid < 64) {
+    const int4 c = e1 > e0 ? nxt : lc.item(ticket, lane);
+    if (tid == 0) claimed[par ^ 1] = c;
+  }
+  }
 }
 
-// dQ of one chunk of query block i's row (workgroup (chunk, bh, i), two
+// dQ of one chunk of query block i's row (item (bh, i, chunk), two
 // wavefronts; wave kh owns keys 32kh .. 32kh+31 of every key block of the row).  The forward's orientation:
 // S^T = K Q^T and dP^T = V dO^T with the queries as columns (Q^T, dO^T B
 // operands held in registers, one LSE and delta per lane), dS^T = P^T (dP^T -
 // delta), and dQ^T += K^T dS^T with K^T read transposed from the wave's LDS
 // area.  The two key halves are summed through LDS at the end; an unsplit row
-// writes bf16 dQ, a chunk of a split one its fp32 sum (unscaled) to partial
-// slot `slot + chunk`.  At HD = 128 the rings take 64 KiB and the registers
+// writes bf16 dQ, a chunk of a split one its fp32 sum (unscaled) to the item's
+// partial slot.  At HD = 128 the rings take 64 KiB and the registers
 // exceed half the file: one wave per SIMD.
 template <int HD>
 struct DqCfg {
   static constexpr int RB = HD * 2;
   static constexpr uint32_t kHalf = 32 * RB, kStage = 2 * kHalf;
-  static constexpr size_t LDS_BYTES = 2 * size_t(kDqStages) * kStage;
+  static constexpr size_t kClaimAt = 2 * size_t(kDqStages) * kStage;  // two records: the claimed items
+  static constexpr size_t LDS_BYTES = kClaimAt + 32;
 };
 
 template <int HD>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 2 : 1))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ ld,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    const int2* __restrict__ row_split, int32_t n_rows, int32_t N, int32_t nb, float c2,
-    float scale, uint16_t* __restrict__ dQ, float* __restrict__ part) {
+    const int32_t* __restrict__ col_idx, const int4* __restrict__ items, int32_t* __restrict__ ctr, int32_t n_lists, int32_t list_cap,
+    int32_t N, int32_t nb, float c2, float scale, uint16_t* __restrict__ dQ,
+    float* __restrict__ part) {
   // Per wave: a ring of kDqStages stages of its 32 key rows of K and of V,
   // streamed by LDS DMA kDqStages - 1 key blocks ahead; no barrier in the loop.
   using C = DqCfg<HD>;
@@ -510,21 +655,39 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   const int lane = threadIdx.x & 63;
   const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 31, hh = lane >> 5;
-  const int ch = blockIdx.x / n_rows;
-  const int r = blockIdx.x - ch * n_rows;
-  const int2 sp = row_split[r];
-  const int slot = __builtin_amdgcn_readfirstlane(sp.x);
-  const int nch = slot < 0 ? 1 : __builtin_amdgcn_readfirstlane(sp.y);
-  if (ch >= nch) return;
+  const uint32_t ring = lds0 + uint32_t(kh) * (kDqStages * kStage);
+  uint32_t hoff[RB / 32];
+  half_offsets<RB>(lane, 32 * kh, hoff);
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  ListClaims lc{items, ctr + kLenQ, ctr + kClaimQ, n_lists, list_cap,
+                static_cast<int>(blockIdx.x % n_lists), 0, 0};
+  int4* const claimed = reinterpret_cast<int4*>(smem + C::kClaimAt);
+  int ticket = 0;
+  int4 nxt = make_int4(-1, 0, 0, -1);  // wave 0: the next item, loaded in the last step
+  if (threadIdx.x < 64) {
+    lc.load_lens();
+    if (threadIdx.x == 0) ticket = lc.claim();
+    const int4 c = lc.item(ticket, lane);
+    if (threadIdx.x == 0) claimed[0] = c;
+  }
+  for (int par = 0;; par ^= 1) {
+  // The barrier publishes the item wave 0 resolved and keeps this item's first
+  // loads out of the rings the previous item's key-half exchange may still read.
+  lds_barrier();
+  const int4 rec = claimed[par];
+  const int r = __builtin_amdgcn_readfirstlane(rec.x);
+  if (r < 0) break;
+  if (threadIdx.x == 0) ticket = lc.claim();
+  const int e0 = __builtin_amdgcn_readfirstlane(rec.y);
+  const int e1 = __builtin_amdgcn_readfirstlane(rec.z);
+  const int pslot = __builtin_amdgcn_readfirstlane(rec.w);
   const int bh = r / nb, i = r - bh * nb;
   const size_t head = size_t(bh) * size_t(N) * HD;
   const uint32_t hbytes = static_cast<uint32_t>(N) * RB;
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, hbytes);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(dO + head, hbytes);
   const v4i kd = uniform_desc(K + head, hbytes), vd = uniform_desc(V + head, hbytes);
-  const uint32_t ring = lds0 + uint32_t(kh) * (kDqStages * kStage);
-  uint32_t hoff[RB / 32];
-  half_offsets<RB>(lane, 32 * kh, hoff);
   bf16x8 qf[2][NDC], df[2][NDC];
   float L[2], Dl[2];
 #pragma unroll
@@ -555,12 +718,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
     for (int u = 0; u < NDT; ++u)
 #pragma unroll
       for (int x = 0; x < 16; ++x) acc[g][u][x] = 0.f;
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int b0 = __builtin_amdgcn_readfirstlane(row_ptr[r]);
-  const int b1 = __builtin_amdgcn_readfirstlane(row_ptr[r + 1]);
-  const int e0 = b0 + int(int64_t(b1 - b0) * ch / nch);
-  const int e1 = b0 + int(int64_t(b1 - b0) * (ch + 1) / nch);
   IndexWindow cols;
   cols.init(col_idx, e0, e1, lane);
   // This wave's half of key block j (K, then V) into ring stage st; a column
@@ -596,6 +753,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
       issue(ja, sa);
     }
     wait_vm_n(kLoads * (min(ahead, e1 - 1) - e));
+    if (e + 1 == e1 && threadIdx.x < 64) nxt = lc.item(ticket, lane);  // the claim has returned
     if (j < 0 || j >= nb) continue;
     const int kbase = kBB * j + 32 * kh;  // first key of this wave's half
     const uint32_t ks = ring + uint32_t(st) * kStage, vs = ks + kHalf;
@@ -653,9 +811,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   auto finish = [&](const f32x16 (&a)[NDT]) {
     const int t = kBB * i + 32 * kh + ql;
     const float* src = xo + size_t(1 - kh) * (kDqStages * kStage / 4);
-    if (nch > 1) {
+    if (pslot >= 0) {
       // dQ of the block's 64 queries, row-major, fp32 (queries past N too)
-      float* pq = part + size_t(slot + ch) * (kBB * HD) + size_t(32 * kh + ql) * HD;
+      float* pq = part + size_t(pslot) * (kBB * HD) + size_t(32 * kh + ql) * HD;
 #pragma unroll
       for (int u = 0; u < NDT; ++u)
 #pragma unroll
@@ -685,11 +843,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
     send(acc[1]);
   else
     send(acc[0]);
-  __syncthreads();
+  lds_barrier();
   if (kh == 0)
     finish(acc[0]);
   else
     finish(acc[1]);
+  if (threadIdx.x < 64) {
+    const int4 c = e1 > e0 ? nxt : lc.item(ticket, lane);
+    if (threadIdx.x == 0) claimed[par ^ 1] = c;
+  }
+  }
 }
 
 // The split blocks: the chunks' fp32 partials summed in chunk order, then bf16
@@ -757,22 +920,39 @@ int32_t chunk_len(int64_t nnz, int64_t n_rows) {
 // kind partition at most nnz entries.
 int64_t slot_cap(int64_t nnz, int32_t chunk) { return 2 * nnz / chunk + 1; }
 
+// Chunks a split column or row is cut into at most.
+int32_t max_chunks(int32_t nb, int32_t chunk) { return std::max(1, (nb + chunk - 1) / chunk); }
+
+// Work lists of the gradient kernels and the records each holds at most: every
+// head of a list contributes at most nb max_ch items.
+int32_t n_work_lists(int32_t n_heads) { return n_heads >= kLists ? kLists : 1; }
+int64_t list_cap(int32_t n_heads, int32_t nb, int32_t max_ch) {
+  const int32_t nl = n_work_lists(n_heads);
+  return int64_t((n_heads + nl - 1) / nl) * nb * max_ch;
+}
+
 struct BwdLayout {
-  size_t ld, col_ptr, row_idx, col_split, row_split, ctr, part_kv, part_q, total;
+  size_t ld, col_ptr, row_idx, col_split, row_split, ctr, items_kv, items_q, part_kv, part_q,
+      total;
 };
 
 BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, int64_t nnz) {
   BwdLayout L{};
   const size_t rows = size_t(B) * H * N;
-  const size_t nrow = size_t(B) * H * n_blocks(N, block);
-  const int64_t cap = slot_cap(nnz, chunk_len(nnz, int64_t(nrow)));
+  const int32_t nb = n_blocks(N, block);
+  const size_t nrow = size_t(B) * H * nb;
+  const int32_t chunk = chunk_len(nnz, int64_t(nrow));
+  const int64_t cap = slot_cap(nnz, chunk);
+  const size_t lists = 2 * size_t(n_work_lists(B * H)) * list_cap(B * H, nb, max_chunks(nb, chunk));
   size_t o = 0;
   L.ld = o;        o += round256(rows * sizeof(float2));
   L.col_ptr = o;   o += round256((nrow + 1) * sizeof(int32_t));
   L.row_idx = o;   o += round256(size_t(nnz) * sizeof(int32_t));
   L.col_split = o; o += round256(nrow * sizeof(int2));
   L.row_split = o; o += round256(nrow * sizeof(int2));
-  L.ctr = o;       o += 256;
+  L.ctr = o;       o += round256(kCtrInts * sizeof(int32_t));
+  L.items_kv = o;  o += round256(lists * sizeof(int4));
+  L.items_q = o;   o += round256(lists * sizeof(int4));
   L.part_kv = o;   o += round256(size_t(cap) * 2 * kBB * size_t(D) * sizeof(float));
   L.part_q = o;    o += round256(size_t(cap) * kBB * size_t(D) * sizeof(float));
   L.total = o;
@@ -812,6 +992,26 @@ __global__ __launch_bounds__(64) void refine_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Resident workgroups of the dK/dV (KV) or dQ kernel on the current device
+// (cached; the kernels' LDS attributes are set before the first call).
+template <int HD, bool KV>
+int resident_grad_workgroups() {
+  static std::once_flag once;
+  static int n = 0;
+  std::call_once(once, [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return;
+    const void* f = KV ? reinterpret_cast<const void*>(&dkdv_kernel<HD>)
+                       : reinterpret_cast<const void*>(&dq_kernel<HD>);
+    const size_t lds = KV ? DkdvCfg<HD>::LDS_BYTES : DqCfg<HD>::LDS_BYTES;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 128, lds) != hipSuccess) return;
+    n = cus * (per_cu > 0 ? per_cu : 1);
+  });
+  return n;
+}
+
 // The five launches for head dim HD (see the top of the file).
 template <int HD>
 bsa_status launch_backward(const void* q, const void* k, const void* v, const void* o,
@@ -824,9 +1024,12 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
   const int32_t n_heads = B * H;
   const int32_t n_rows = n_heads * nb;
   const int32_t chunk = chunk_len(nnz, n_rows);
-  const int32_t max_ch = std::max(1, (nb + chunk - 1) / chunk);
+  const int32_t max_ch = max_chunks(nb, chunk);
   const int64_t cap = slot_cap(nnz, chunk);
-  if (int64_t(n_rows) * max_ch > INT32_MAX || cap > INT32_MAX) return BSA_ERR_UNSUPPORTED;
+  const int32_t n_lists = n_work_lists(n_heads);
+  const int64_t lcap = list_cap(n_heads, nb, max_ch);
+  if (int64_t(n_rows) * max_ch > INT32_MAX || cap > INT32_MAX || 2 * lcap * n_lists > INT32_MAX)
+    return BSA_ERR_UNSUPPORTED;
   const BwdLayout lay = bwd_layout(B, H, N, HD, block, nnz);
   float2* ld = reinterpret_cast<float2*>(ws + lay.ld);
   int32_t* col_ptr = reinterpret_cast<int32_t*>(ws + lay.col_ptr);
@@ -834,6 +1037,8 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
   int2* col_split = reinterpret_cast<int2*>(ws + lay.col_split);
   int2* row_split = reinterpret_cast<int2*>(ws + lay.row_split);
   int32_t* ctr = reinterpret_cast<int32_t*>(ws + lay.ctr);
+  int4* items_kv = reinterpret_cast<int4*>(ws + lay.items_kv);
+  int4* items_q = reinterpret_cast<int4*>(ws + lay.items_q);
   float* part_kv = reinterpret_cast<float*>(ws + lay.part_kv);
   float* part_q = reinterpret_cast<float*>(ws + lay.part_q);
 
@@ -862,20 +1067,27 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
   const size_t bits_bytes = size_t(nb) * ((nb + 31) / 32) * 4;
   hipLaunchKernelGGL(transpose_kernel, dim3(n_heads), dim3(256), bits_bytes, s, row_ptr, col_idx,
                      nb, n_heads, col_ptr, row_idx, chunk, max_ch, ctr, static_cast<int32_t>(cap),
-                     static_cast<int32_t>(cap), col_split, row_split);
+                     static_cast<int32_t>(cap), col_split, row_split, n_lists,
+                     static_cast<int32_t>(lcap), items_kv, items_q);
   BSA_HIP_CHECK_LAUNCH();
   const float c2 = sc * kLog2e;
-  const dim3 grid(static_cast<uint32_t>(n_rows * max_ch));
-  hipLaunchKernelGGL(dkdv_kernel<HD>, grid, dim3(128), DkdvCfg<HD>::LDS_BYTES, s,
+  // Persistent grids: the resident workgroups, at most one per possible item.
+  const int res_kv = resident_grad_workgroups<HD, true>();
+  const int res_q = resident_grad_workgroups<HD, false>();
+  if (res_kv <= 0 || res_q <= 0) return BSA_ERR_HIP;
+  const int64_t slots = int64_t(n_rows) * max_ch;
+  const dim3 grid_kv(static_cast<uint32_t>(std::min<int64_t>(res_kv, slots)));
+  const dim3 grid_q(static_cast<uint32_t>(std::min<int64_t>(res_q, slots)));
+  hipLaunchKernelGGL(dkdv_kernel<HD>, grid_kv, dim3(128), DkdvCfg<HD>::LDS_BYTES, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
-                     col_ptr, row_idx, col_split, n_rows, N, nb, c2, sc,
+                     row_idx, items_kv, ctr, n_lists, static_cast<int32_t>(lcap), N, nb, c2, sc,
                      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), part_kv);
   BSA_HIP_CHECK_LAUNCH();
-  hipLaunchKernelGGL(dq_kernel<HD>, grid, dim3(128), DqCfg<HD>::LDS_BYTES, s,
+  hipLaunchKernelGGL(dq_kernel<HD>, grid_q, dim3(128), DqCfg<HD>::LDS_BYTES, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
-                     row_ptr, col_idx, row_split, n_rows, N, nb, c2, sc,
+                     col_idx, items_q, ctr, n_lists, static_cast<int32_t>(lcap), N, nb, c2, sc,
                      static_cast<uint16_t*>(dq), part_q);
   BSA_HIP_CHECK_LAUNCH();
   if (max_ch > 1) {

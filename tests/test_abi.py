@@ -223,18 +223,24 @@ def test_backward_workspace_bytes():
 
     def want(B, H, N, D, nnz):
         # (LSE log2 e, delta) per row, col_ptr [B*H*nb + 1], row_idx [nnz], the column
-        # and row splits (int2 [B*H*nb] each), the slot counters, then the partial
-        # slots: chunk = max(16, 2 * ceil(nnz / rows)), 2 nnz / chunk + 1 slots of
-        # fp32 [dK | dV] (2 x 64 x D x 4 bytes) and as many of dQ (64 x D x 4 bytes);
+        # and row splits (int2 [B*H*nb] each), the counter area (576 ints), the two
+        # work lists (n_lists = 8 if B*H >= 8 else 1, each ceil(B*H / n_lists) nb
+        # max_ch int4 records in each of two parts, max_ch = ceil(nb / chunk)), then
+        # the partial slots:
+        # chunk = max(16, 2 * ceil(nnz / rows)), 2 nnz / chunk + 1 slots of fp32
+        # [dK | dV] (2 x 64 x D x 4 bytes) and as many of dQ (64 x D x 4 bytes);
         # 256-byte rounding.
-        nrow = B * H * (-(-N // 64))
+        nb = -(-N // 64)
+        nrow = B * H * nb
         chunk = max(16, 2 * (-(-nnz // nrow)))
         cap = 2 * nnz // chunk + 1
+        nl = 8 if B * H >= 8 else 1
+        lists = nl * (-(-(B * H) // nl)) * nb * max(1, -(-nb // chunk))
         return (r256(8 * B * H * N) + r256(4 * (nrow + 1)) + r256(4 * nnz) + 2 * r256(8 * nrow)
-                + 256 + cap * 512 * D + cap * 256 * D)
+                + r256(4 * 576) + 2 * r256(32 * lists) + cap * 512 * D + cap * 256 * D)
 
     assert L.bsa_backward_workspace_bytes(1, 2, 512, 64, 64, 100) == want(1, 2, 512, 64, 100) \
-        == 648704
+        == 651776
     assert L.bsa_backward_workspace_bytes(2, 24, 4224, 64, 64, 31968) == \
         want(2, 24, 4224, 64, 31968)
     assert L.bsa_backward_workspace_bytes(1, 16, 8192, 128, 64, 26624) == \
