@@ -13,13 +13,15 @@
 //   dkdv       persistent workgroups, one chunk of a key block's query blocks
 //              per item;
 //   dq         persistent workgroups, one chunk of a query block's CSR row per
-//              item;
+//              item (at head dim 128 from the dS tiles dkdv stored);
 //   reduce     per split block, the chunks' fp32 partials summed in chunk order.
 // A column or row longer than the chunk length (twice the mean row length, at
 // least 16) is cut into near-equal chunks so that a few long ones (text blocks,
-// anchor columns) do not set the length of the launch.  The two gradient
-// kernels recompute S and P from the LSE; nothing uses atomics on the
-// gradients, so results are deterministic.  Block 64 and D = 64.
+// anchor columns) do not set the length of the launch.  The dK/dV kernel
+// recomputes S and P from the LSE; at head dim 64 so does the dQ kernel, at
+// head dim 128 it reads the dS tiles the dK/dV kernel stored.  Nothing uses
+// atomics on the gradients, so results are deterministic.  D = 64 or 128 over
+// 64-row blocks (a 128-row block CSR is refined to the 64-row CSR first).
 #include <math.h>
 
 #include <algorithm>
@@ -233,7 +235,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
                                                         int2* __restrict__ row_split,
                                                         int32_t n_lists, int32_t list_cap,
                                                         int4* __restrict__ items_kv,
-                                                        int4* __restrict__ items_q) {
+                                                        int4* __restrict__ items_q,
+                                                        int32_t* __restrict__ tpos) {
   extern __shared__ uint32_t bits[];
   __shared__ int32_t rp[kMaxBlocks + 1];
   __shared__ int32_t start[kMaxBlocks], nch_c[kMaxBlocks], nch_r[kMaxBlocks];
@@ -362,6 +365,27 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
       }
     }
   }
+  // Transposed position of every CSR entry (its pair's slot in row_idx: the
+  // column's start plus the rows before it that list the column), -1 for a
+  // column outside [0, nb); only when dS tiles are stored (tpos not null).
+  for (int e = begin + tid; tpos && e < end; e += 256) {
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (rp[mid] <= e)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int j = col_idx[e];
+    int t = -1;
+    if (j >= 0 && j < nb) {
+      const uint32_t* col = bits + j * W;
+      t = begin + start[j] + __popc(col[lo >> 5] & ((1u << (lo & 31)) - 1u));
+      for (int w = 0; w < (lo >> 5); ++w) t += __popc(col[w]);
+    }
+    tpos[e] = t;
+  }
 }
 
 // Persistent gradient workgroups take their items from the work lists:
@@ -417,8 +441,10 @@ struct ListClaims {
 // 32-query tile S = Q K^T and dP = dO V^T on MFMA (K, V rows of the wave's keys
 // are the B operands, held in registers), P = exp2(S scale log2e - LSE log2e),
 // dS = P (dP - delta), and dV^T += dO^T P, dK^T += Q^T dS with dO^T, Q^T read
-// transposed from LDS.  An unsplit column writes bf16 dK, dV; a chunk of a
-// split one writes its fp32 sums (dK unscaled) to the item's partial slot.
+// transposed from LDS.  With STORE, dS is also stored, bf16, as the pair's
+// 64 x 64 tile (slot = its position in row_idx), for dq_stored_kernel.  An unsplit column
+// writes bf16 dK, dV; a chunk of a split one writes its fp32 sums (dK
+// unscaled) to the item's partial slot.
 // At HD = 128 the two stages take 65 KiB of LDS: two workgroups per CU, one
 // wave per SIMD, which may then use the whole register file.
 template <int HD>
@@ -430,14 +456,14 @@ struct DkdvCfg {
   static constexpr size_t LDS_BYTES = kClaimAt + 32;
 };
 
-template <int HD>
+template <int HD, bool STORE>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 2 : 1))) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float2* __restrict__ ld,
     const int32_t* __restrict__ row_idx,
     const int4* __restrict__ items, int32_t* __restrict__ ctr, int32_t n_lists, int32_t list_cap,
     int32_t N, int32_t nb, float c2, float scale, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, float* __restrict__ part) {
+    uint16_t* __restrict__ dV, float* __restrict__ part, uint16_t* __restrict__ dst_tiles) {
   // Two stages of (Q tile, dO tile, per-row (LSE log2 e, delta)) of one query
   // block, each wave streaming its 32-row halves by LDS DMA one block ahead.
   using C = DkdvCfg<HD>;
@@ -519,12 +545,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   };
   int i_next = rows.at(e0, lane);
   if (e0 < e1) issue(i_next, 0);
+  int pend = 0;  // dS stores issued after the latest tile loads
   for (int e = e0, st = 0; e < e1; ++e, st ^= 1) {
     const int i = i_next;
-    // Only block e is in flight: this wave's halves of it have landed once
-    // the wait returns.  After the barrier both waves' halves are in LDS and
-    // both waves are done reading block e-1, whose stage then takes block e+1.
-    wait_vm(0);
+    // Only block e is in flight (and the dS stores of block e - 1, which are
+    // younger): this wave's halves of it have landed once the wait returns.
+    // After the barrier both waves' halves are in LDS and both waves are done
+    // reading block e-1, whose stage then takes block e+1.
+    wait_vm_n(pend);
+    pend = 0;
     lds_barrier();
     if (e + 1 < e1) {
       i_next = rows.at(e + 1, lane);
@@ -564,6 +593,24 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
           sb[ei >> 3][ei & 7] = static_cast<__bf16>(p * (dp[ei] - Dl[x]));
         }
       }
+      // With STORE: dS of this wave's keys for query group g into the pair's tile
+      // (slot e) for dq_stored_kernel.  Tile layout: four 2-KiB parts, one per 16 queries
+      // (part 2g + k2 holds queries 32g + 16k2 .. +15), each 64 keys x 16
+      // queries, key-major.  Elements 0..3 of sb[k2] are queries
+      // 32g + 16k2 + 4hh .. +3 and 4..7 those + 8; one swap with the other
+      // half-wave gives lane (key, hh) the 8 queries 32g + 16k2 + 8hh .. +7,
+      // so each store writes 1 KiB contiguous.
+      if constexpr (STORE) {
+        uint16_t* dtile = dst_tiles + size_t(e) * (kBB * kBB);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const uint4 x = __builtin_bit_cast(uint4, sb[k2]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, x.z, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, x.w, false, false);
+          uint16_t* dst = dtile + size_t((2 * g + k2) * kBB + 32 * w + ql) * 16 + 8 * hh;
+          *reinterpret_cast<uint4*>(dst) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        }
+      }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
@@ -581,6 +628,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
           dk[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[k2], dk[u], 0, 0, 0);
         }
     }
+    if constexpr (STORE) pend = 4;  // the dS stores above: 2 groups x 2 halves
   }
   // register e of dv[u], dk[u]: dimension 32u + 8(e/4) + 4hh + e%4 of key `key`
   if (pslot >= 0) {
@@ -855,6 +903,213 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   }
 }
 
+// dQ from stored dS (head dim 128): the items, key halves, ring and epilogue of
+// dq_kernel, but dQ^T += K^T dS^T reads the dS tiles the dK/dV kernel stored
+// instead of recomputing S, dP and the exponentials.  Each wave streams its 32
+// key rows of K and its 32 keys of the pair's dS tile (4 KiB: 1 KiB of each of
+// the tile's four 16-query parts) into its own two-stage LDS ring; K^T and dS^T
+// are both read transposed with the same lane pattern, so the keys of the A and
+// B operands come in the same order.  At head dim 128 this saves half of the
+// kernel's matrix work and all of its exponentials for 16 KiB of memory traffic
+// per block pair (measured: 4-8 % faster backward); at head dim 64 the dS
+// stream costs more than the recompute (t2i 237 -> 272 us), so dq_kernel stays.
+template <int HD>
+struct DqsCfg {
+  static constexpr int RB = HD * 2;
+  static constexpr uint32_t kHalf = 32 * RB;               // the wave's K rows
+  static constexpr uint32_t kDsHalf = 32 * kBB * 2;        // its keys of the dS tile
+  static constexpr uint32_t kStage = kHalf + kDsHalf;
+  static constexpr size_t kClaimAt = 2 * size_t(kDqStages) * kStage;  // two records: the claimed items
+  static constexpr size_t LDS_BYTES = kClaimAt + 32;
+};
+
+template <int HD>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void dq_stored_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ ds_tiles,
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ tpos,
+    const int4* __restrict__ items, int32_t* __restrict__ ctr, int32_t n_lists, int32_t list_cap,
+    int32_t N, int32_t nb, float scale, uint16_t* __restrict__ dQ, float* __restrict__ part) {
+  using C = DqsCfg<HD>;
+  constexpr int RB = C::RB, NDT = HD / 32;
+  constexpr uint32_t kHalf = C::kHalf, kStage = C::kStage;
+  constexpr int kLoads = RB / 32 + 4;  // tile loads one stage takes per wave
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
+  const int lane = threadIdx.x & 63;
+  const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ql = lane & 31, hh = lane >> 5;
+  const uint32_t ring = lds0 + uint32_t(kh) * (kDqStages * kStage);
+  uint32_t hoff[RB / 32];
+  half_offsets<RB>(lane, 32 * kh, hoff);
+  // dS: this wave's 1 KiB of part s sits at 2048 s + 1024 kh in the tile; the
+  // loads' immediate offsets add 1024 s to source and destination alike.
+  const uint32_t dsrc = uint32_t(1024 * kh + 16 * lane);
+  // Lane address of the transposing dS^T reads within a stage's dS area: part
+  // 2g + (lane / 16) % 2, key row 16k2 + tr_row, queries 4 (lane % 4) .. +3.
+  const uint32_t ds_lane = uint32_t(1024 * ((lane >> 4) & 1) + 32 * (4 * hh + ((lane & 15) >> 2)) +
+                                    8 * (lane & 3));
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  ListClaims lc{items, ctr + kLenQ, ctr + kClaimQ, n_lists, list_cap,
+                static_cast<int>(blockIdx.x % n_lists), 0, 0};
+  int4* const claimed = reinterpret_cast<int4*>(smem + C::kClaimAt);
+  int ticket = 0;
+  int4 nxt = make_int4(-1, 0, 0, -1);  // wave 0: the next item, loaded in the last step
+  if (threadIdx.x < 64) {
+    lc.load_lens();
+    if (threadIdx.x == 0) ticket = lc.claim();
+    const int4 c = lc.item(ticket, lane);
+    if (threadIdx.x == 0) claimed[0] = c;
+  }
+  for (int par = 0;; par ^= 1) {
+  // The barrier publishes the item wave 0 resolved and keeps this item's first
+  // loads out of the rings the previous item's key-half exchange may still read.
+  lds_barrier();
+  const int4 rec = claimed[par];
+  const int r = __builtin_amdgcn_readfirstlane(rec.x);
+  if (r < 0) break;
+  if (threadIdx.x == 0) ticket = lc.claim();
+  const int e0 = __builtin_amdgcn_readfirstlane(rec.y);
+  const int e1 = __builtin_amdgcn_readfirstlane(rec.z);
+  const int pslot = __builtin_amdgcn_readfirstlane(rec.w);
+  const int bh = r / nb, i = r - bh * nb;
+  const size_t head = size_t(bh) * size_t(N) * HD;
+  const uint32_t hbytes = static_cast<uint32_t>(N) * RB;
+  const v4i kd = uniform_desc(K + head, hbytes);
+  f32x16 acc[2][NDT];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < NDT; ++u)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[g][u][x] = 0.f;
+  IndexWindow cols, tiles;
+  cols.init(col_idx, e0, e1, lane);
+  tiles.init(tpos, e0, e1, lane);
+  // This wave's half of key block j's K rows and of the pair's dS^T tile (slot
+  // t) into ring stage st; a column outside [0, nb) reads zeros.
+  auto issue = [&](int j, int t, int st) {
+    const bool ok = j >= 0 && j < nb && t >= 0;
+    const uint32_t tb = ok ? uint32_t(j) * (kBB * RB) + uint32_t(kh) * kHalf : hbytes;
+    const uint32_t dst = ring + uint32_t(st) * kStage;
+    dma_half_tile<RB>(kd, hoff, tb, dst);
+    const v4i dd = uniform_desc(ds_tiles + size_t(ok ? t : 0) * (kBB * kBB), ok ? 8192u : 0u);
+    dma16x4(dd, dsrc, dsrc + 1024u, dsrc + 2048u, dsrc + 3072u, dst + kHalf);
+  };
+  // Blocks e0 .. e0 + kDqStages - 2 go first; at step e, block e + kDqStages - 1
+  // goes into the stage block e - 1 used (its reads are complete), then the
+  // wait leaves the younger blocks (kLoads loads each) in flight.
+  int jq[kDqStages];
+#pragma unroll
+  for (int x = 0; x < kDqStages - 1; ++x) {
+    jq[x] = cols.at(e0 + x, lane);
+    const int tq = tiles.at(e0 + x, lane);
+    if (e0 + x < e1) issue(jq[x], tq, x);
+  }
+  for (int e = e0, st = 0; e < e1; ++e, st = st + 1 == kDqStages ? 0 : st + 1) {
+    const int ahead = e + kDqStages - 1;
+    const int sa = st == 0 ? kDqStages - 1 : st - 1;
+    int j = -1;
+#pragma unroll
+    for (int x = 0; x < kDqStages; ++x)
+      if (x == st) j = jq[x];
+    if (ahead < e1) {
+      const int ja = cols.at(ahead, lane);
+      const int ta = tiles.at(ahead, lane);
+#pragma unroll
+      for (int x = 0; x < kDqStages; ++x)
+        if (x == sa) jq[x] = ja;
+      issue(ja, ta, sa);
+    }
+    wait_vm_n(kLoads * (min(ahead, e1 - 1) - e));
+    if (e + 1 == e1 && threadIdx.x < 64) nxt = lc.item(ticket, lane);  // the claim has returned
+    if (j < 0 || j >= nb) continue;
+    const uint32_t ks = ring + uint32_t(st) * kStage, dss = ks + kHalf;
+    // dS^T operands: lane (ql, hh) holds query 32g + ql and the keys of the K^T
+    // operands below (the same transposing read pattern over key rows).
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t at = dss + uint32_t(2048 * g + 512 * k2) + ds_lane;
+        const v4s lo = lds_read_tr(at);
+        const v4s hi = lds_read_tr(at + 256u);
+        sb[g][k2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int u = 0; u < NDT; ++u) {
+        const int col = 32 * u + tr_col;
+        const uint32_t clo = (col & 7) * 2;
+        const v4s lo = lds_read_tr(ks + swz<RB>(16 * k2 + tr_row, col >> 3) + clo);
+        const v4s hi = lds_read_tr(ks + swz<RB>(16 * k2 + 8 + tr_row, col >> 3) + clo);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[g][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[g][k2], acc[g][u], 0, 0, 0);
+      }
+  }
+  // Key-half sum: wave kh finishes query group kh and hands group 1 - kh over.
+  // Exchange through the rings (each wave's own is free once its loop ends).
+  float* xo = reinterpret_cast<float*>(smem);
+  auto send = [&](const f32x16 (&a)[NDT]) {
+    float* dst = xo + size_t(kh) * (kDqStages * kStage / 4);
+#pragma unroll
+    for (int u = 0; u < NDT; ++u)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(dst + ((u * 4 + g4) * 64 + lane) * 4) =
+            f32x4{a[u][4 * g4], a[u][4 * g4 + 1], a[u][4 * g4 + 2], a[u][4 * g4 + 3]};
+  };
+  auto finish = [&](const f32x16 (&a)[NDT]) {
+    const int t = kBB * i + 32 * kh + ql;
+    const float* src = xo + size_t(1 - kh) * (kDqStages * kStage / 4);
+    if (pslot >= 0) {
+      // dQ of the block's 64 queries, row-major, fp32 (queries past N too)
+      float* pq = part + size_t(pslot) * (kBB * HD) + size_t(32 * kh + ql) * HD;
+#pragma unroll
+      for (int u = 0; u < NDT; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + ((u * 4 + g4) * 64 + lane) * 4);
+          const int d = 32 * u + 8 * g4 + 4 * hh;
+          *reinterpret_cast<f32x4*>(pq + d) =
+              f32x4{a[u][4 * g4] + o1[0], a[u][4 * g4 + 1] + o1[1], a[u][4 * g4 + 2] + o1[2],
+                    a[u][4 * g4 + 3] + o1[3]};
+        }
+      return;
+    }
+    if (t >= N) return;
+    uint16_t* qrow = dQ + head + size_t(t) * HD;
+#pragma unroll
+    for (int u = 0; u < NDT; ++u)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + ((u * 4 + g4) * 64 + lane) * 4);
+        const int d = 32 * u + 8 * g4 + 4 * hh;
+        *reinterpret_cast<uint2*>(qrow + d) =
+            make_uint2(pack_bf16x2(scale * (a[u][4 * g4] + o1[0]), scale * (a[u][4 * g4 + 1] + o1[1])),
+                       pack_bf16x2(scale * (a[u][4 * g4 + 2] + o1[2]), scale * (a[u][4 * g4 + 3] + o1[3])));
+      }
+  };
+  if (kh == 0)
+    send(acc[1]);
+  else
+    send(acc[0]);
+  lds_barrier();
+  if (kh == 0)
+    finish(acc[0]);
+  else
+    finish(acc[1]);
+  if (threadIdx.x < 64) {
+    const int4 c = e1 > e0 ? nxt : lc.item(ticket, lane);
+    if (threadIdx.x == 0) claimed[par ^ 1] = c;
+  }
+  }
+}
+
 // The split blocks: the chunks' fp32 partials summed in chunk order, then bf16
 // dK (times scale) and dV of key column r, and dQ (times scale) of CSR row r
 // (r = bh nb + block).  Rows past N are not stored.  Unsplit blocks were
@@ -932,8 +1187,8 @@ int64_t list_cap(int32_t n_heads, int32_t nb, int32_t max_ch) {
 }
 
 struct BwdLayout {
-  size_t ld, col_ptr, row_idx, col_split, row_split, ctr, items_kv, items_q, part_kv, part_q,
-      total;
+  size_t ld, col_ptr, row_idx, col_split, row_split, ctr, items_kv, items_q, tpos, ds, part_kv,
+      part_q, total;
 };
 
 BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, int64_t nnz) {
@@ -953,6 +1208,9 @@ BwdLayout bwd_layout(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block, 
   L.ctr = o;       o += round256(kCtrInts * sizeof(int32_t));
   L.items_kv = o;  o += round256(lists * sizeof(int4));
   L.items_q = o;   o += round256(lists * sizeof(int4));
+  const size_t stored = D == 128 ? size_t(nnz) : 0;  // dS tiles kept at head dim 128
+  L.tpos = o;      o += round256(stored * sizeof(int32_t));
+  L.ds = o;        o += stored * kBB * kBB * sizeof(uint16_t);
   L.part_kv = o;   o += round256(size_t(cap) * 2 * kBB * size_t(D) * sizeof(float));
   L.part_q = o;    o += round256(size_t(cap) * kBB * size_t(D) * sizeof(float));
   L.total = o;
@@ -992,6 +1250,25 @@ __global__ __launch_bounds__(64) void refine_kernel(const int32_t* __restrict__ 
   }
 }
 
+// dS tiles are stored by the dK/dV kernel and read by dq_stored_kernel at head
+// dim 128; at head dim 64 dq_kernel recomputes them.
+template <int HD>
+constexpr bool kStoreDs = HD == 128;
+
+template <int HD>
+const void* dkdv_fn() {
+  return reinterpret_cast<const void*>(&dkdv_kernel<HD, kStoreDs<HD>>);
+}
+template <int HD>
+const void* dq_fn() {
+  if constexpr (kStoreDs<HD>) return reinterpret_cast<const void*>(&dq_stored_kernel<HD>);
+  return reinterpret_cast<const void*>(&dq_kernel<HD>);
+}
+template <int HD>
+constexpr size_t dq_lds() {
+  return kStoreDs<HD> ? DqsCfg<HD>::LDS_BYTES : DqCfg<HD>::LDS_BYTES;
+}
+
 // Resident workgroups of the dK/dV (KV) or dQ kernel on the current device
 // (cached; the kernels' LDS attributes are set before the first call).
 template <int HD, bool KV>
@@ -1003,9 +1280,8 @@ int resident_grad_workgroups() {
     if (hipGetDevice(&dev) != hipSuccess) return;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return;
-    const void* f = KV ? reinterpret_cast<const void*>(&dkdv_kernel<HD>)
-                       : reinterpret_cast<const void*>(&dq_kernel<HD>);
-    const size_t lds = KV ? DkdvCfg<HD>::LDS_BYTES : DqCfg<HD>::LDS_BYTES;
+    const void* f = KV ? dkdv_fn<HD>() : dq_fn<HD>();
+    const size_t lds = KV ? DkdvCfg<HD>::LDS_BYTES : dq_lds<HD>();
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 128, lds) != hipSuccess) return;
     n = cus * (per_cu > 0 ? per_cu : 1);
   });
@@ -1039,6 +1315,8 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
   int32_t* ctr = reinterpret_cast<int32_t*>(ws + lay.ctr);
   int4* items_kv = reinterpret_cast<int4*>(ws + lay.items_kv);
   int4* items_q = reinterpret_cast<int4*>(ws + lay.items_q);
+  int32_t* tpos = reinterpret_cast<int32_t*>(ws + lay.tpos);
+  uint16_t* ds = reinterpret_cast<uint16_t*>(ws + lay.ds);
   float* part_kv = reinterpret_cast<float*>(ws + lay.part_kv);
   float* part_q = reinterpret_cast<float*>(ws + lay.part_q);
 
@@ -1049,13 +1327,11 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                kMaxBlocks * (kMaxBlocks / 32) * 4);
     if (attr == hipSuccess)
-      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dkdv_kernel<HD>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+      attr = hipFuncSetAttribute(dkdv_fn<HD>(), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  static_cast<int>(DkdvCfg<HD>::LDS_BYTES));
     if (attr == hipSuccess)
-      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dq_kernel<HD>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 static_cast<int>(DqCfg<HD>::LDS_BYTES));
+      attr = hipFuncSetAttribute(dq_fn<HD>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(dq_lds<HD>()));
   });
   if (attr != hipSuccess) return BSA_ERR_HIP;
 
@@ -1068,7 +1344,8 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
   hipLaunchKernelGGL(transpose_kernel, dim3(n_heads), dim3(256), bits_bytes, s, row_ptr, col_idx,
                      nb, n_heads, col_ptr, row_idx, chunk, max_ch, ctr, static_cast<int32_t>(cap),
                      static_cast<int32_t>(cap), col_split, row_split, n_lists,
-                     static_cast<int32_t>(lcap), items_kv, items_q);
+                     static_cast<int32_t>(lcap), items_kv, items_q,
+                     kStoreDs<HD> ? tpos : nullptr);
   BSA_HIP_CHECK_LAUNCH();
   const float c2 = sc * kLog2e;
   // Persistent grids: the resident workgroups, at most one per possible item.
@@ -1078,17 +1355,23 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
   const int64_t slots = int64_t(n_rows) * max_ch;
   const dim3 grid_kv(static_cast<uint32_t>(std::min<int64_t>(res_kv, slots)));
   const dim3 grid_q(static_cast<uint32_t>(std::min<int64_t>(res_q, slots)));
-  hipLaunchKernelGGL(dkdv_kernel<HD>, grid_kv, dim3(128), DkdvCfg<HD>::LDS_BYTES, s,
+  hipLaunchKernelGGL((dkdv_kernel<HD, kStoreDs<HD>>), grid_kv, dim3(128), DkdvCfg<HD>::LDS_BYTES, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
                      row_idx, items_kv, ctr, n_lists, static_cast<int32_t>(lcap), N, nb, c2, sc,
-                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), part_kv);
+                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), part_kv, ds);
   BSA_HIP_CHECK_LAUNCH();
-  hipLaunchKernelGGL(dq_kernel<HD>, grid_q, dim3(128), DqCfg<HD>::LDS_BYTES, s,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
-                     col_idx, items_q, ctr, n_lists, static_cast<int32_t>(lcap), N, nb, c2, sc,
-                     static_cast<uint16_t*>(dq), part_q);
+  if constexpr (kStoreDs<HD>) {
+    hipLaunchKernelGGL(dq_stored_kernel<HD>, grid_q, dim3(128), DqsCfg<HD>::LDS_BYTES, s,
+                       static_cast<const uint16_t*>(k), ds, col_idx, tpos, items_q, ctr, n_lists,
+                       static_cast<int32_t>(lcap), N, nb, sc, static_cast<uint16_t*>(dq), part_q);
+  } else {
+    hipLaunchKernelGGL(dq_kernel<HD>, grid_q, dim3(128), DqCfg<HD>::LDS_BYTES, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(d_o), ld,
+                       col_idx, items_q, ctr, n_lists, static_cast<int32_t>(lcap), N, nb, c2, sc,
+                       static_cast<uint16_t*>(dq), part_q);
+  }
   BSA_HIP_CHECK_LAUNCH();
   if (max_ch > 1) {
     hipLaunchKernelGGL(reduce_kernel<HD>, dim3(static_cast<uint32_t>(n_rows)), dim3(256), 0, s,

@@ -458,9 +458,11 @@ BSA_API bsa_status bsa_gather_forward(const void* q, const void* k, const void* 
  * aligned; it holds (LSE log2 e, delta) per query row, the transposed CSR, the split
  * of key columns and CSR rows longer than the chunk length (twice the mean row
  * length, at least 16) into chunks, the work lists of the two gradient kernels (one
- * per die, 8, when B*H >= 8, else one; 16-byte records), and the chunks' fp32
- * partial gradients (bounded by 2 nnz / chunk + 1 slots of 768 D bytes); it needs
- * no initial contents.  Calls that share a workspace must not overlap.  With
+ * per die, 8, when B*H >= 8, else one; 16-byte records), at D = 128 the bf16 dS
+ * tile of every listed block pair (nnz x 8 KiB, written by the dK/dV pass and
+ * read by the dQ pass instead of recomputing it), and the chunks' fp32 partial
+ * gradients (bounded by 2 nnz / chunk + 1 slots of 768 D bytes); it needs no
+ * initial contents.  Calls that share a workspace must not overlap.  With
  * block = 128 the CSR is first refined to the 64-block CSR of the same mask (query
  * block i is query blocks 2i, 2i + 1 and key block j key blocks 2j, 2j + 1; at most
  * 4 nnz entries, held in the workspace), and the rest works on that.

@@ -225,8 +225,9 @@ def test_backward_workspace_bytes():
         # (LSE log2 e, delta) per row, col_ptr [B*H*nb + 1], row_idx [nnz], the column
         # and row splits (int2 [B*H*nb] each), the counter area (576 ints), the two
         # work lists (n_lists = 8 if B*H >= 8 else 1, each ceil(B*H / n_lists) nb
-        # max_ch int4 records in each of two parts, max_ch = ceil(nb / chunk)), then
-        # the partial slots:
+        # max_ch int4 records in each of two parts, max_ch = ceil(nb / chunk)), at
+        # D = 128 the transposed position of every entry (nnz ints) and the dS tiles
+        # (nnz x 64 x 64 bf16), then the partial slots:
         # chunk = max(16, 2 * ceil(nnz / rows)), 2 nnz / chunk + 1 slots of fp32
         # [dK | dV] (2 x 64 x D x 4 bytes) and as many of dQ (64 x D x 4 bytes);
         # 256-byte rounding.
@@ -236,8 +237,10 @@ def test_backward_workspace_bytes():
         cap = 2 * nnz // chunk + 1
         nl = 8 if B * H >= 8 else 1
         lists = nl * (-(-(B * H) // nl)) * nb * max(1, -(-nb // chunk))
+        stored = r256(4 * nnz) + 8192 * nnz if D == 128 else 0
         return (r256(8 * B * H * N) + r256(4 * (nrow + 1)) + r256(4 * nnz) + 2 * r256(8 * nrow)
-                + r256(4 * 576) + 2 * r256(32 * lists) + cap * 512 * D + cap * 256 * D)
+                + r256(4 * 576) + 2 * r256(32 * lists) + stored
+                + cap * 512 * D + cap * 256 * D)
 
     assert L.bsa_backward_workspace_bytes(1, 2, 512, 64, 64, 100) == want(1, 2, 512, 64, 100) \
         == 651776
