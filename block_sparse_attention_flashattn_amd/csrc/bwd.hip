@@ -5,11 +5,12 @@
 //   P = exp(scale q.k - LSE), dV = P^T dO, dP = dO V^T,
 //   delta_t = sum_d dO[t,d] O[t,d], dS = P (dP - delta), dQ = scale dS K,
 //   dK = scale dS^T Q.
-// Five launches on the caller's stream:
+// Five launches on the caller's stream (six at head dim 128):
 //   prep       per query row (LSE * log2(e), delta), fp32;
 //   transpose  per head, the query blocks that list each key block, ascending,
 //              the split of long key columns and query rows into chunks, and
 //              the head's work items appended to its die's work lists;
+//   tpos       (head dim 128) per CSR entry, its block pair's dS tile slot;
 //   dkdv       persistent workgroups, one chunk of a key block's query blocks
 //              per item;
 //   dq         persistent workgroups, one chunk of a query block's CSR row per
@@ -235,8 +236,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
                                                         int2* __restrict__ row_split,
                                                         int32_t n_lists, int32_t list_cap,
                                                         int4* __restrict__ items_kv,
-                                                        int4* __restrict__ items_q,
-                                                        int32_t* __restrict__ tpos) {
+                                                        int4* __restrict__ items_q) {
   extern __shared__ uint32_t bits[];
   __shared__ int32_t rp[kMaxBlocks + 1];
   __shared__ int32_t start[kMaxBlocks], nch_c[kMaxBlocks], nch_r[kMaxBlocks];
@@ -365,24 +365,36 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
       }
     }
   }
-  // Transposed position of every CSR entry (its pair's slot in row_idx: the
-  // column's start plus the rows before it that list the column), -1 for a
-  // column outside [0, nb); only when dS tiles are stored (tpos not null).
-  for (int e = begin + tid; tpos && e < end; e += 256) {
-    int lo = 0, hi = nb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (rp[mid] <= e)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
+}
+
+// Transposed position of every CSR entry of row r (its pair's slot in row_idx:
+// the column's first slot plus the rows before r that list the column; -1 for
+// a column outside [0, nb)), for dq_stored_kernel.  One wavefront per CSR row,
+// a lane per entry, each a binary search over its column's ascending rows (the
+// head's padding slots, -1, sit after the last column's rows and compare as
+// larger than every row).
+__global__ __launch_bounds__(64) void tpos_kernel(const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_idx,
+                                                  const int32_t* __restrict__ col_ptr,
+                                                  const int32_t* __restrict__ row_idx, int32_t nb,
+                                                  int32_t* __restrict__ tpos) {
+  const int r = blockIdx.x;
+  const int bh = r / nb, i = r - bh * nb;
+  const int b0 = row_ptr[r], b1 = row_ptr[r + 1];
+  for (int e = b0 + static_cast<int>(threadIdx.x); e < b1; e += 64) {
     const int j = col_idx[e];
     int t = -1;
     if (j >= 0 && j < nb) {
-      const uint32_t* col = bits + j * W;
-      t = begin + start[j] + __popc(col[lo >> 5] & ((1u << (lo & 31)) - 1u));
-      for (int w = 0; w < (lo >> 5); ++w) t += __popc(col[w]);
+      int lo = col_ptr[bh * nb + j], hi = col_ptr[bh * nb + j + 1];  // first slot holding >= i
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int v = row_idx[mid];
+        if (v >= 0 && v < i)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      t = lo;
     }
     tpos[e] = t;
   }
@@ -1344,9 +1356,13 @@ bsa_status launch_backward(const void* q, const void* k, const void* v, const vo
   hipLaunchKernelGGL(transpose_kernel, dim3(n_heads), dim3(256), bits_bytes, s, row_ptr, col_idx,
                      nb, n_heads, col_ptr, row_idx, chunk, max_ch, ctr, static_cast<int32_t>(cap),
                      static_cast<int32_t>(cap), col_split, row_split, n_lists,
-                     static_cast<int32_t>(lcap), items_kv, items_q,
-                     kStoreDs<HD> ? tpos : nullptr);
+                     static_cast<int32_t>(lcap), items_kv, items_q);
   BSA_HIP_CHECK_LAUNCH();
+  if constexpr (kStoreDs<HD>) {
+    hipLaunchKernelGGL(tpos_kernel, dim3(static_cast<uint32_t>(n_rows)), dim3(64), 0, s, row_ptr,
+                       col_idx, col_ptr, row_idx, nb, tpos);
+    BSA_HIP_CHECK_LAUNCH();
+  }
   const float c2 = sc * kLog2e;
   // Persistent grids: the resident workgroups, at most one per possible item.
   const int res_kv = resident_grad_workgroups<HD, true>();
