@@ -67,10 +67,12 @@ def test_backward_matches_oracle(N, p, seed, D):
         assert np.all(got[0][0, 0, 64:128] == 0.0)       # the empty row's dQ
 
 
-def test_backward_unlisted_block_and_out_of_range_columns():
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_unlisted_block_and_out_of_range_columns(D):
     """A key block no row lists gets dK = dV = 0; columns outside [0, nb) are ignored."""
     bsa = need_gpu()
-    B, H, N, D, block = 1, 1, 384, 64, 64
+    print(f"case D={D}", flush=True)
+    B, H, N, block = 1, 1, 384, 64
     nb = N // block
     q, k, v = W.gaussian_qkv(5, B, H, N, D)
     do = W.gaussian_qkv(6, B, H, N, D)[0]
@@ -78,7 +80,7 @@ def test_backward_unlisted_block_and_out_of_range_columns():
     clean = csr_from_cols(cols)
     noisy = csr_from_cols([c + [-1, nb + 2] for c in cols])
     got = run(bsa, q, k, v, do, *noisy)
-    want = OB.block_sparse_backward(q, k, v, *clean, block, 1 / 8.0, do)
+    want = OB.block_sparse_backward(q, k, v, *clean, block, 1 / np.sqrt(D), do)
     compare(got, want)
     assert np.all(got[1][0, 0, 192:256] == 0.0) and np.all(got[2][0, 0, 192:256] == 0.0)
 
@@ -114,6 +116,32 @@ def test_backward_split_rows_and_columns(N, H, D):
     do = W.gaussian_qkv(400 + N, B, H, N, D)[0]
     cols = [list(range(nb)) if r % nb == 0 else sorted({0, r % nb, min(r % nb + 1, nb - 1)})
             for r in range(B * H * nb)]
+    rp, ci = csr_from_cols(cols)
+    got = run(bsa, q, k, v, do, rp, ci)
+    want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / np.sqrt(D), do)
+    compare(got, want)
+    again = run(bsa, q, k, v, do, rp, ci)
+    assert all(np.array_equal(a, b) for a, b in zip(got, again))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_twelve_heads_work_lists(D):
+    """Twelve heads: one work list per die with one or two heads each, so workgroups
+    whose list runs out take items from other lists; long rows and columns are split;
+    ragged N.  Two calls give the same bits (an item's result does not depend on the
+    workgroup that claims it)."""
+    bsa = need_gpu()
+    print(f"case D={D}", flush=True)
+    B, H, N, block = 2, 6, 1500, 64
+    nb = -(-N // block)
+    q, k, v = W.gaussian_qkv(700 + D, B, H, N, D)
+    do = W.gaussian_qkv(800 + D, B, H, N, D)[0]
+    rng = np.random.default_rng(D)
+    cols = []
+    for r in range(B * H * nb):
+        h, i = divmod(r, nb)
+        dens = 0.9 if i < 2 else 0.15 * (1 + h % 3)
+        cols.append(sorted(set(np.flatnonzero(rng.random(nb) < dens).tolist()) | {i, 0}))
     rp, ci = csr_from_cols(cols)
     got = run(bsa, q, k, v, do, rp, ci)
     want = OB.block_sparse_backward(q, k, v, rp, ci, block, 1 / np.sqrt(D), do)
