@@ -105,9 +105,10 @@ def cpu_model():
     return None
 
 
-def graph_ms(fn, reps, stream):
-    """Mean time of one call among `reps` back-to-back calls captured in one HIP graph
-    (HIP events on `stream` around the replay; one untimed replay uploads the graph)."""
+def graph_ms(fn, reps, stream, repeats=5):
+    """Time of one call among `reps` back-to-back calls captured in one HIP graph: the
+    median over `repeats` replays, each between HIP events on `stream` (one untimed
+    replay uploads the graph first)."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -115,12 +116,15 @@ def graph_ms(fn, reps, stream):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    times = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    return float(np.median(times))
 
 
 def linear_fit(x, y):
@@ -501,6 +505,12 @@ def main():
                                                 work=pc, out=occ, lse=lcc), reps, stream)
             b_ms = graph_ms(lambda: bsa.build_mask(qcd, kcd, wc.block, plan=pc, col_idx=cic),
                             reps, stream)
+
+            def one_step():
+                bsa.build_mask(qcd, kcd, wc.block, plan=pc, col_idx=cic)
+                bsa.forward(qcd, kcd, vcd, pc.row_ptr, cic, wc.block, work=pc, out=occ, lse=lcc)
+
+            s_ms = graph_ms(one_step, reps, stream)
             # The backward on the same CSR (a block-128 CSR is refined to 64-row blocks
             # inside it), eagerly timed like the t2i one.
             gc = torch.Generator("cpu").manual_seed(1000 + wc.N)
@@ -520,6 +530,11 @@ def main():
                      "forward_ms": f_ms, "forward_tflops": fl / (f_ms * 1e-3) / 1e12,
                      "forward_frac_of_bf16_peak": fl / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "kernel": fwd_kernel_name(wc.block, wc.D), "build_mask_ms": b_ms,
+                     # The builder is a scan: Q and K read once, the column indices written.
+                     "build_mask_gbps": (2 * qcd.numel() * 2 + 4 * pc.nnz) / (b_ms * 1e-3) / 1e9,
+                     "build_mask_frac_of_hbm_peak":
+                         (2 * qcd.numel() * 2 + 4 * pc.nnz) / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "build_and_forward_ms": s_ms,
                      "backward_ms": bk_ms,
                      "backward_tflops": 2.5 * fl / (bk_ms * 1e-3) / 1e12,
                      "backward_frac_of_bf16_peak": 2.5 * fl / (bk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
@@ -529,6 +544,12 @@ def main():
                 entry["cpu_oracle"] = {"tflops": cfl / dt / 1e12, "seconds": dt,
                                        "heads": f"{heads} of {wc.B * wc.H}",
                                        "gpu_over_cpu": (fl / (f_ms * 1e-3)) / (cfl / dt)}
+                # The builder oracle (fp64 mean pool, scores, fill to budget) on every head.
+                from oracle import builder as OBLD
+                t0 = time.perf_counter()
+                OBLD.build_mask(qc, kc, wc.block, wc.density, wc.prior(), wc.budgets(),
+                                wc.force_diag)
+                entry["cpu_builder_oracle_ms"] = (time.perf_counter() - t0) * 1e3
             others[name] = entry
             del qcd, kcd, vcd, occ, lcc, cic, doc, bwsc
             torch.cuda.empty_cache()
