@@ -32,7 +32,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ K, int32_t N,
                                                    int32_t nb, int32_t block,
                                                    float* __restrict__ Pq,
-                                                   float* __restrict__ Pk) {
+                                                   float* __restrict__ Pk,
+                                                   int32_t* __restrict__ status) {
+  // The builder's status word (counted up by select_kernel, which runs after
+  // this launch) starts at zero.
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
   constexpr int CPR = HD / 8;     // 16-byte chunks per token row
   constexpr int RPP = 256 / CPR;  // token rows per pass
   __shared__ float red[RPP][HD + 1];
@@ -315,23 +319,25 @@ extern "C" BSA_API bsa_status bsa_build_mask(const void* q, const void* k, int32
   float* S = reinterpret_cast<float*>(ws + w.s);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  hipLaunchKernelGGL(zero_status_kernel, dim3(1), dim3(1), 0, s, status);
-  BSA_HIP_CHECK_LAUNCH();
   if (need_scores) {
+    // pool_kernel also clears the status word.
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     if (D == 64)
       hipLaunchKernelGGL(pool_kernel<64>, dim3(n_rows, 2), dim3(256), 0, s, qq, kk, N, nb, block,
-                         pq, pk);
+                         pq, pk, status);
     else
       hipLaunchKernelGGL(pool_kernel<128>, dim3(n_rows, 2), dim3(256), 0, s, qq, kk, N, nb,
-                         block, pq, pk);
+                         block, pq, pk, status);
     BSA_HIP_CHECK_LAUNCH();
     const dim3 g((nb + 31) / 32, (nb + 31) / 32, B * H);
     if (D == 64)
       hipLaunchKernelGGL(score_kernel<64>, g, dim3(256), 0, s, pq, pk, nb, S);
     else
       hipLaunchKernelGGL(score_kernel<128>, g, dim3(256), 0, s, pq, pk, nb, S);
+    BSA_HIP_CHECK_LAUNCH();
+  } else {
+    hipLaunchKernelGGL(zero_status_kernel, dim3(1), dim3(1), 0, s, status);
     BSA_HIP_CHECK_LAUNCH();
   }
   const float* Sp = need_scores ? S : nullptr;
