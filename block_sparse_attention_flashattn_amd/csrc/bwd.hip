@@ -28,6 +28,7 @@
 #include <algorithm>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "tile.h"
@@ -600,7 +601,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
         for (int x = 0; x < 4; ++x) {
           const int ei = 4 * m + x;
           float p = __builtin_amdgcn_exp2f(fmaf(s[ei], c2, -L[x]));
-          p = key_ok ? p : 0.f;
+          // Without STORE a key past N reaches only its own column of dK and dV,
+          // which is never written out; with STORE its dS enters the tile.
+          if constexpr (STORE) p = key_ok ? p : 0.f;
           pb[ei >> 3][ei & 7] = static_cast<__bf16>(p);
           sb[ei >> 3][ei & 7] = static_cast<__bf16>(p * (dp[ei] - Dl[x]));
         }
@@ -644,7 +647,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
   }
   // register e of dv[u], dk[u]: dimension 32u + 8(e/4) + 4hh + e%4 of key `key`
   if (pslot >= 0) {
-    // [dK | dV] of the block's 64 keys, row-major, fp32; keys past N hold zeros
+    // [dK | dV] of the block's 64 keys, row-major, fp32; rows of keys past N are never read
     float* pk = part + size_t(pslot) * (2 * kBB * HD) + size_t(32 * w + ql) * HD;
     float* pv = pk + kBB * HD;
 #pragma unroll
@@ -824,23 +827,35 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
       ka[c] = lds_read16(ks + swz<RB>(ql, 2 * c + hh));
     }
     bf16x8 sb[2][2];
+    // register x of this lane: key kbase + 8(x/4) + 4hh + x%4, query 32g + ql.
+    // Keys past N (only in the last block of a ragged head) get probability 0;
+    // the tile body is instantiated twice so that full tiles skip the mask.
+    auto tile = [&](auto masked) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const f32x16 zero = {};
-      f32x16 s, dp;
+      for (int g = 0; g < 2; ++g) {
+        const f32x16 zero = {};
+        f32x16 s, dp;
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], df[g][c], c == 0 ? zero : dp, 0, 0, 0);
+        for (int c = 0; c < NDC; ++c) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], df[g][c], c == 0 ? zero : dp, 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          float p = __builtin_amdgcn_exp2f(fmaf(s[x], c2, -L[g]));
+          if constexpr (decltype(masked)::value) {
+            const int kv = kbase + 8 * (x >> 2) + 4 * hh + (x & 3);
+            p = kv < N ? p : 0.f;
+          }
+          sb[g][x >> 3][x & 7] = static_cast<__bf16>(p * (dp[x] - Dl[g]));
+        }
       }
-      // register x of this lane: key kbase + 8(x/4) + 4hh + x%4, query 32g + ql
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int kv = kbase + 8 * (x >> 2) + 4 * hh + (x & 3);
-        float p = __builtin_amdgcn_exp2f(fmaf(s[x], c2, -L[g]));
-        p = kv < N ? p : 0.f;
-        sb[g][x >> 3][x & 7] = static_cast<__bf16>(p * (dp[x] - Dl[g]));
-      }
+    };
+    if (kbase + 32 <= N) {
+      tile(std::false_type{});
+    } else {
+      asm volatile("");  // a side effect keeps this a branch, not a select per element
+      tile(std::true_type{});
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
