@@ -179,31 +179,56 @@ __device__ __forceinline__ int n_chunks(int len, int chunk, int max_ch) {
   return len > chunk ? min((len + chunk - 1) / chunk, max_ch) : 1;
 }
 
-// Exclusive prefix sum of a[0, n) in place by a 256-thread workgroup (n <= 1024);
-// returns the total.  tmp: 256 ints of LDS.
-__device__ int block_scan(int32_t* a, int n, int32_t* tmp) {
-  const int tid = threadIdx.x;
+// Exclusive prefix sums of a[0, n) and, when b is not null, of b[0, n), in place,
+// by a 256-thread workgroup (n <= 1024); returns the totals.  Each thread takes
+// a run of consecutive entries, each wavefront scans its threads' sums with
+// lane shifts, and one barrier shares the four wavefront totals.  Entries must
+// be written before a barrier that precedes the call; the call ends with one.
+// tmp: 8 ints of LDS.
+__device__ int2 block_scan(int32_t* a, int32_t* b, int n, int32_t* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (n + 255) >> 8;
   const int lo = min(tid * per, n), hi = min(lo + per, n);
-  int sum = 0;
-  for (int x = lo; x < hi; ++x) sum += a[x];
-  tmp[tid] = sum;
-  __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    const int v = tid >= d ? tmp[tid - d] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
-  }
-  int off = tid ? tmp[tid - 1] : 0;
-  const int total = tmp[255];
+  int sa = 0, sb = 0;
   for (int x = lo; x < hi; ++x) {
-    const int v = a[x];
-    a[x] = off;
-    off += v;
+    sa += a[x];
+    if (b) sb += b[x];
+  }
+  int ia = sa, ib = sb;  // inclusive scans over the wavefront's threads
+  for (int d = 1; d < 64; d <<= 1) {
+    const int ta = __shfl_up(ia, d, 64), tb = __shfl_up(ib, d, 64);
+    if (lane >= d) {
+      ia += ta;
+      ib += tb;
+    }
+  }
+  if (lane == 63) {
+    tmp[w] = ia;
+    tmp[4 + w] = ib;
   }
   __syncthreads();
-  return total;
+  int oa = ia - sa, ob = ib - sb, ta = 0, tb = 0;
+  for (int v = 0; v < 4; ++v) {
+    const int xa = tmp[v], xb = tmp[4 + v];
+    if (v < w) {
+      oa += xa;
+      ob += xb;
+    }
+    ta += xa;
+    tb += xb;
+  }
+  for (int x = lo; x < hi; ++x) {
+    const int va = a[x];
+    a[x] = oa;
+    oa += va;
+    if (b) {
+      const int vb = b[x];
+      b[x] = ob;
+      ob += vb;
+    }
+  }
+  __syncthreads();
+  return make_int2(ta, tb);
 }
 
 // Transpose of one head's CSR: for key block j, the query blocks i whose row
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
   extern __shared__ uint32_t bits[];
   __shared__ int32_t rp[kMaxBlocks + 1];
   __shared__ int32_t start[kMaxBlocks], nch_c[kMaxBlocks], nch_r[kMaxBlocks];
-  __shared__ int32_t pre_c[kMaxBlocks], pre_r[kMaxBlocks], tmp[256];
+  __shared__ int32_t pre_c[kMaxBlocks], pre_r[kMaxBlocks], tmp[8];
   __shared__ int32_t hist[kMaxBlocks];  // length histogram of the whole blocks
   __shared__ int32_t base_sh[4];
   const int tid = threadIdx.x;
@@ -277,7 +302,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
     nch_c[j] = c;  // the column's length (the last one gains the padding below)
   }
   __syncthreads();
-  const int listed = block_scan(start, nb, tmp);
+  const int listed = block_scan(start, nullptr, nb, tmp).x;
   if (tid == 0) nch_c[nb - 1] += (end - begin) - listed;  // the head's -1 padding
   __syncthreads();
   for (int j = tid; j < nb; j += 256) {
@@ -286,8 +311,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
     pre_c[j] = n > 1 ? n : 0;
   }
   __syncthreads();
-  const int tot_kv = block_scan(pre_c, nb, tmp);
-  const int tot_q = block_scan(pre_r, nb, tmp);
+  const int2 tot = block_scan(pre_c, pre_r, nb, tmp);
+  const int tot_kv = tot.x, tot_q = tot.y;
   if (tid == 0) {
     int bk = tot_kv ? atomicAdd(slot_ctr, tot_kv) : 0;
     int bq = tot_q ? atomicAdd(slot_ctr + 1, tot_q) : 0;
@@ -310,8 +335,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
     nch_r[j] = (nch_r[j] > 1 && bq >= 0) ? 0 : 1;
   }
   __syncthreads();
-  const int n_wk = block_scan(nch_c, nb, tmp);  // whole blocks before block j
-  const int n_wq = block_scan(nch_r, nb, tmp);
+  const int2 n_w = block_scan(nch_c, nch_r, nb, tmp);  // whole blocks before block j
+  const int n_wk = n_w.x, n_wq = n_w.y;
   const int l = bh % n_lists;
   if (tid == 0) {
     // chunks: one per partial slot, at the slot's offset in the head's range
@@ -338,7 +363,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
       if ((j + 1 < nb ? whole[j + 1] : n_whole) > whole[j]) atomicAdd(&hist[bin(len)], 1);
     }
     __syncthreads();
-    block_scan(hist, kMaxBlocks, tmp);
+    block_scan(hist, nullptr, kMaxBlocks, tmp);
     for (int j = tid; j < nb; j += 256) {
       const int a = kind ? rp[j] : begin + start[j];
       const int len = (kind ? rp[j + 1] : (j + 1 < nb ? begin + start[j + 1] : end)) - a;
