@@ -237,7 +237,7 @@ __device__ int2 block_scan(int32_t* a, int32_t* b, int n, int32_t* tmp) {
 // A pair listed twice, or a column outside [0, nb), leaves a slot that is
 // filled with -1 at the end of the head's last column.  An LDS bitmap
 // (bit i of word j*W + i/32) orders each column without sorting; the entries
-// are read in parallel, each finding its row by binary search.
+// are read in parallel, in one run of consecutive entries per thread.
 // Splits: col_split[bh nb + j] = (first partial slot, chunks) of key column j,
 // row_split the same for the CSR rows; a head's split blocks take consecutive
 // slots from the counters (cleared by prep_kernel).  If the slots run out (they
@@ -282,17 +282,37 @@ __global__ __launch_bounds__(256) void transpose_kernel(const int32_t* __restric
     nch_r[i] = n;
     pre_r[i] = n > 1 ? n : 0;
   }
-  for (int e = begin + tid; e < end; e += 256) {
-    int lo = 0, hi = nb - 1;  // the row i with rp[i] <= e < rp[i + 1]
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (rp[mid] <= e)
-        lo = mid;
-      else
-        hi = mid - 1;
+  {
+    // Thread tid sets the bits of a run of consecutive entries: one binary
+    // search for the row of its first entry, then the row advances with the
+    // entries; column indices are loaded eight at a time.
+    const int per = (end - begin + 255) >> 8;
+    int e = begin + tid * per;
+    const int e_end = min(e + per, end);
+    int row = 0;
+    if (e < e_end) {
+      int lo = 0, hi = nb - 1;  // the row i with rp[i] <= e < rp[i + 1]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (rp[mid] <= e)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      row = lo;
     }
-    const int j = col_idx[e];
-    if (j >= 0 && j < nb) atomicOr(&bits[j * W + (lo >> 5)], 1u << (lo & 31));
+    for (; e < e_end; e += 8) {
+      int jv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) jv[t] = e + t < e_end ? col_idx[e + t] : -1;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (e + t >= e_end) break;
+        while (rp[row + 1] <= e + t) ++row;
+        const int j = jv[t];
+        if (j >= 0 && j < nb) atomicOr(&bits[j * W + (row >> 5)], 1u << (row & 31));
+      }
+    }
   }
   __syncthreads();
   for (int j = tid; j < nb; j += 256) {
