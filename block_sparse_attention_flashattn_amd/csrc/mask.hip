@@ -87,14 +87,27 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ Pq
   const int j0 = blockIdx.x * 32;
   const int i0 = blockIdx.y * 32;
   const size_t bh = blockIdx.z;
-  for (int x = tid; x < 32 * HD / 4; x += 256) {
+  // Every thread's loads are issued before any is stored, so the workgroup
+  // waits for one memory round trip, not one per load.
+  constexpr int kPer = 32 * HD / 4 / 256;  // 16-byte loads per thread and operand
+  static_assert(kPer * 256 == 32 * HD / 4, "the tile loads cover the threads evenly");
+  f32x4 qv[kPer], kv[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int x = tid + 256 * t;
     const int rr = x / (HD / 4);
     const int d = 4 * (x - rr * (HD / 4));
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(sq + rr * LD + d) =
-        (i0 + rr < nb) ? *reinterpret_cast<const f32x4*>(Pq + (bh * nb + i0 + rr) * HD + d) : z;
-    *reinterpret_cast<f32x4*>(sk + rr * LD + d) =
-        (j0 + rr < nb) ? *reinterpret_cast<const f32x4*>(Pk + (bh * nb + j0 + rr) * HD + d) : z;
+    qv[t] = (i0 + rr < nb) ? *reinterpret_cast<const f32x4*>(Pq + (bh * nb + i0 + rr) * HD + d) : z;
+    kv[t] = (j0 + rr < nb) ? *reinterpret_cast<const f32x4*>(Pk + (bh * nb + j0 + rr) * HD + d) : z;
+  }
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int x = tid + 256 * t;
+    const int rr = x / (HD / 4);
+    const int d = 4 * (x - rr * (HD / 4));
+    *reinterpret_cast<f32x4*>(sq + rr * LD + d) = qv[t];
+    *reinterpret_cast<f32x4*>(sk + rr * LD + d) = kv[t];
   }
   __syncthreads();
   const int ti = tid >> 4;
@@ -132,42 +145,7 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// A 64-bit value moved between lanes by a DPP pattern (both halves).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(v & 0xffffffffu), static_cast<int>(v & 0xffffffffu), CTRL, 0xf, 0xf, false));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(v >> 32), static_cast<int>(v >> 32), CTRL, 0xf, 0xf, false));
-  return (uint64_t(hi) << 32) | lo;
-}
-
-// Maximum of a 64-bit value over the wavefront, in every lane, without LDS:
-// DPP exchanges within each 16-lane row (lane ^ 1, lane ^ 2, mirror within 8,
-// mirror within 16), then v_permlane16_swap (the other row of a 32-lane half)
-// and v_permlane32_swap (the other half).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
-  v = mx(v, dpp_u64<0xb1>(v));   // quad_perm [1, 0, 3, 2]
-  v = mx(v, dpp_u64<0x4e>(v));   // quad_perm [2, 3, 0, 1]
-  v = mx(v, dpp_u64<0x141>(v));  // row_half_mirror
-  v = mx(v, dpp_u64<0x140>(v));  // row_mirror
-  const bool odd_row = (threadIdx.x & 16) != 0, upper = (threadIdx.x & 32) != 0;
-  {
-    const uint32_t lo = static_cast<uint32_t>(v & 0xffffffffu), hi = static_cast<uint32_t>(v >> 32);
-    const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    v = mx(v, (uint64_t(odd_row ? sh[0] : sh[1]) << 32) | (odd_row ? sl[0] : sl[1]));
-  }
-  {
-    const uint32_t lo = static_cast<uint32_t>(v & 0xffffffffu), hi = static_cast<uint32_t>(v >> 32);
-    const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    v = mx(v, (uint64_t(upper ? sh[0] : sh[1]) << 32) | (upper ? sl[0] : sl[1]));
-  }
-  return v;
-}
-
+// Set bits of a ballot mask below this lane.
 __device__ __forceinline__ int popc_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
@@ -231,18 +209,46 @@ __global__ __launch_bounds__(256) void select_kernel(
     if (lane == 0) atomicAdd(status, 1);
     return;
   }
-  for (int f = 0; f < fill; ++f) {
-    uint64_t best = 0;
+  // The `fill` largest keys (score, then lower column) among the candidates
+  // (key != 0): a bitwise search finds H, the fill-th largest score word;
+  // every candidate above H is taken, and of those equal to H the ones with
+  // the lowest columns (column order is c-major, then lane) until `fill` are
+  // taken.  Counts come from ballots, so the search costs the same for any fill.
+  if (fill > 0) {
+    uint32_t hi[CM];
+    bool cand[CM];
+    int n_cand = 0;
 #pragma unroll
-    for (int c = 0; c < CM; ++c) best = key[c] > best ? key[c] : best;
-    best = wave_max_u64(best);
-    if (best == 0) break;
+    for (int c = 0; c < CM; ++c) {
+      cand[c] = key[c] != 0;
+      hi[c] = static_cast<uint32_t>(key[c] >> 32);
+      n_cand += __popcll(__ballot(cand[c]));
+    }
+    if (n_cand <= fill) {
 #pragma unroll
-    for (int c = 0; c < CM; ++c)
-      if (key[c] == best) {
-        key[c] = 0;
-        chosen[c] = true;
+      for (int c = 0; c < CM; ++c) chosen[c] = cand[c];
+    } else {
+      uint32_t H = 0;  // largest value with at least `fill` candidates at or above it
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = H | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int c = 0; c < CM; ++c) n += __popcll(__ballot(cand[c] && hi[c] >= t));
+        if (n >= fill) H = t;
       }
+      int above = 0;
+#pragma unroll
+      for (int c = 0; c < CM; ++c) above += __popcll(__ballot(cand[c] && hi[c] > H));
+      const int need = fill - above;  // taken from the candidates equal to H
+      int before = 0;                 // equal candidates in lower column blocks
+#pragma unroll
+      for (int c = 0; c < CM; ++c) {
+        const bool eq = cand[c] && hi[c] == H;
+        const uint64_t m = __ballot(eq);
+        chosen[c] = (cand[c] && hi[c] > H) || (eq && before + popc_below(m) < need);
+        before += __popcll(m);
+      }
+    }
   }
   int base = 0;
 #pragma unroll
