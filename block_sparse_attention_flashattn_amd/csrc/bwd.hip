@@ -668,7 +668,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(HD == 64 ? 
           const auto s0 = __builtin_amdgcn_permlane32_swap(x.x, x.z, false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(x.y, x.w, false, false);
           uint16_t* dst = dtile + size_t((2 * g + k2) * kBB + 32 * w + ql) * 16 + 8 * hh;
-          *reinterpret_cast<uint4*>(dst) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          // Non-temporal: the tile is read once, by dq_stored_kernel.
+          __builtin_nontemporal_store(v4u{s0[0], s1[0], s0[1], s1[1]}, reinterpret_cast<v4u*>(dst));
         }
       }
 #pragma unroll
@@ -1066,7 +1067,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     const uint32_t dst = ring + uint32_t(st) * kStage;
     dma_half_tile<RB>(kd, hoff, tb, dst);
     const v4i dd = uniform_desc(ds_tiles + size_t(ok ? t : 0) * (kBB * kBB), ok ? 8192u : 0u);
-    dma16x4(dd, dsrc, dsrc + 1024u, dsrc + 2048u, dsrc + 3072u, dst + kHalf);
+    dma16x4<true>(dd, dsrc, dsrc + 1024u, dsrc + 2048u, dsrc + 3072u, dst + kHalf);  // read once
   };
   // Blocks e0 .. e0 + kDqStages - 2 go first; at step e, block e + kDqStages - 1
   // goes into the stage block e - 1 used (its reads are complete), then the

@@ -39,21 +39,39 @@ __device__ __forceinline__ void dma16(v4i desc, uint32_t voff, uint32_t lds) {
 // immediate offset 1024 i moves the source and the LDS destination together,
 // so load i takes the source offset v_i = (its source offset) - 1024 i, which
 // the caller keeps non-negative.  The immediate is range-checked with the offset.
+// NT: non-temporal loads, for data read once, so that the caches keep what is
+// reused.
+template <bool NT = false>
 __device__ __forceinline__ void dma16x4(v4i desc, uint32_t v0, uint32_t v1, uint32_t v2,
                                         uint32_t v3, uint32_t dst) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
-      "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
-      "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
-      "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(dst), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(desc)
-      : "memory");
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %6, 0 offen nt lds\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 nt lds\n\t"
+        "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 nt lds\n\t"
+        "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(dst), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(desc)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(dst), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(desc)
+        : "memory");
+  }
 }
 
 // s_waitcnt vmcnt(n): n vector-memory operations may still be outstanding.
