@@ -62,8 +62,8 @@ def compulsory_bytes(B, H, N, D, nnz, n_rows):
 
 def fwd_kernel_name(block, D):
     """The forward kernel that serves (block, D), as rocprofv3 names it."""
-    if block == 64 and D == 64:
-        return "bsa_forward (fwd_wide_kernel; cut rows combined inside it)"
+    if block == 64:
+        return f"bsa_forward (fwd_wide_kernel<{D}>; cut rows combined inside it)"
     return f"bsa_forward (fwd_kernel<{block}, {D}> + merge_kernel<{block}, {D}>)"
 
 

@@ -610,7 +610,7 @@ __global__ __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------------------
-// Wide wavefronts for 64-row blocks at head dim 64.
+// Wide wavefronts for 64-row blocks at head dim 64 or 128.
 //
 // Two wavefronts per workgroup.  Wave h owns keys 32h .. 32h+31 of every
 // 64-key tile for all 64 query rows of the block (two 32-row query groups),
@@ -621,27 +621,35 @@ __global__ __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2))) vo
 // tile loop has no barrier.  The next item's query tile is staged in LDS while
 // the current item runs; the two key halves meet once per item, in the
 // epilogue, through the stages the last tile freed.
+//
+// At head dim 128 everything doubles along d (40 -> 80 KB of LDS: two workgroups
+// per CU, one wavefront per SIMD, which may then use the whole register file).
+template <int HD_>
 struct Wide {
-  static constexpr int BLK = 64, HD = 64, ROWB = 128;
+  static constexpr int BLK = 64, HD = HD_, ROWB = 2 * HD;
   static constexpr int NT = 128;                     // two wavefronts
+  static constexpr int NDC = HD / 16;                // k-steps of the QK^T product
+  static constexpr int NDT = HD / 32;                // 32-wide d subtiles of the output
   static constexpr int HALFB = 32 * ROWB;            // one wave's half of a K or V tile
+  static constexpr int LPH = HALFB / 1024;           // 16-byte-per-lane loads per half tile
   static constexpr int STAGEB = 2 * HALFB;           // K half, then V half
   static constexpr int RINGB = 2 * STAGEB;           // two stages per wave
   static constexpr int QB = BLK * ROWB;              // staged query tile
-  static constexpr size_t LDS_BYTES = 2 * RINGB + QB;  // 40 KB: four workgroups per CU
-  static_assert(2 * 16 * 4 * 64 == STAGEB, "one query group's accumulator fills a stage");
+  static constexpr size_t LDS_BYTES = 2 * RINGB + QB;  // 40 KB (80 KB at head dim 128)
+  static_assert(NDT * 16 * 4 * 64 == STAGEB, "one query group's accumulator fills a stage");
+  static_assert(HD == 64 || HD == 128, "head dim 64 or 128");
 };
 
-template <bool RES>
-__global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) void fwd_wide_kernel(
+template <int HD_, bool RES>
+__global__ __launch_bounds__(Wide<HD_>::NT) __attribute__((amdgpu_waves_per_eu(HD_ == 64 ? 2 : 1))) void fwd_wide_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ work, int32_t n_items,
     int32_t n_merges, int32_t N, int32_t nb, int32_t n_rows, float sl2, uint16_t* __restrict__ O,
     float* __restrict__ LSE, float* __restrict__ part, int32_t* __restrict__ ctr, int32_t n_slots,
     int32_t* __restrict__ mctr, const uint16_t* __restrict__ R) {
-  using W = Wide;
-  constexpr int BLK = W::BLK, HD = W::HD;
+  using W = Wide<HD_>;
+  constexpr int BLK = W::BLK, HD = W::HD, NDC = W::NDC, NDT = W::NDT;
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((BSA_LDS uint8_t*)smem));
 
@@ -692,13 +700,30 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
   };
 
   // Source offsets of the chunks that land at this lane's swizzled LDS
-  // positions in segments 0 and 1 (relative to their segment).
-  uint32_t ve, vo;
-  {
+  // positions in segments 0 and 1 (relative to their segment); at head dim 128
+  // (4 rows per segment, a swizzle of period 16 rows) in segments 0 .. 3.
+  uint32_t ve = 0, vo = 0, vs[4] = {0, 0, 0, 0};
+  if constexpr (HD == 64) {
     const int r0 = lane >> 3, p = lane & 7;
     ve = uint32_t(r0) * W::ROWB + uint32_t((p ^ chunk_swizzle<W::ROWB>(r0)) << 4);
     vo = uint32_t(r0) * W::ROWB + uint32_t((p ^ chunk_swizzle<W::ROWB>(8 + r0)) << 4);
+  } else {
+    const int r0 = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vs[i] = uint32_t(r0) * W::ROWB + uint32_t((p ^ chunk_swizzle<W::ROWB>(4 * i + r0)) << 4);
   }
+  // One 32-row half tile (source offset tb) into LDS at dst: W::LPH loads.
+  auto dma_rows = [&](v4i desc, uint32_t tb, uint32_t dst) {
+    if constexpr (HD == 64) {
+      dma_half(desc, ve + tb, vo + tb, dst);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        dma16x4(desc, vs[0] + tb + 4096u * h, vs[1] + tb + 4096u * h, vs[2] + tb + 4096u * h,
+                vs[3] + tb + 4096u * h, dst + 4096u * h);
+    }
+  };
 
   // Buffer descriptor over head bh of tensor T (an empty range when row < 0).
   auto head_desc = [&](const uint16_t* T, int row, int bh) -> v4i {
@@ -720,17 +745,17 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
     if (row < 0) return;
     const int qb = row - bh * nb;
     const uint32_t tb = uint32_t(qb) * (BLK * W::ROWB) + uint32_t(kh) * W::HALFB;
-    dma_half(head_desc(Q, row, bh), ve + tb, vo + tb, qarea + uint32_t(kh) * W::HALFB);
-    seq += 4;
+    dma_rows(head_desc(Q, row, bh), tb, qarea + uint32_t(kh) * W::HALFB);
+    seq += W::LPH;
     q_stamp = seq;
   };
   // Query fragments (B operand of S^T = K Q^T) from the staging area: lane
   // holds d = 16c + 8hh .. +7 of query row 32g + ql.
-  auto read_q = [&](bf16x8 (&qf)[2][4]) {
+  auto read_q = [&](bf16x8 (&qf)[2][NDC]) {
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[g][c] = lds_read16(qarea + swz<W::ROWB>(32 * g + ql, 2 * c + hh));
+      for (int c = 0; c < NDC; ++c) qf[g][c] = lds_read16(qarea + swz<W::ROWB>(32 * g + ql, 2 * c + hh));
   };
 
   // ---- item source --------------------------------------------------------
@@ -782,9 +807,8 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
   auto issue = [&](v4i d, int j, int p, bool is_v) {
     const bool ok = j >= 0 && j < nb;
     const uint32_t tb = ok ? uint32_t(j) * (BLK * W::ROWB) + uint32_t(kh) * W::HALFB : head_bytes;
-    dma_half(d, ve + tb, vo + tb,
-             ring + uint32_t((ib + p) & 1) * W::STAGEB + (is_v ? uint32_t(W::HALFB) : 0u));
-    seq += 4;
+    dma_rows(d, tb, ring + uint32_t((ib + p) & 1) * W::STAGEB + (is_v ? uint32_t(W::HALFB) : 0u));
+    seq += W::LPH;
     if (is_v)
       v_last = seq;
     else
@@ -794,7 +818,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
   auto first_of_next = [&]() -> int { return nxt_cnt > 0 ? ld_uniform(col_idx, nxt_c0) : -1; };
 
   // Start-up: the first query tile and the first item's first K and V tiles.
-  bf16x8 qf[2][4];
+  bf16x8 qf[2][NDC];
   stage_q(cur_row, cur_bh);
   if (cur_cnt > 0) {
     const int j0 = ld_uniform(col_idx, cur_c0);
@@ -860,17 +884,18 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
     const __amdgpu_buffer_rsrc_t pr =
         make_rsrc(part + size_t(slot0) * kSlotFloats, uint32_t(nc) * kSlotFloats * 4u);
     const int q = 32 * kh + ql;
-    const uint32_t qoff = uint32_t(q * HD + 32 * hh) * 4u;
+    constexpr int NJ = HD / 8;  // 16-byte pieces of the lane's HD / 2 fp32 columns
+    const uint32_t qoff = uint32_t(q * HD + (HD / 2) * hh) * 4u;
     float M = -INFINITY, L = 0.f;
-    f32x4 o[8];
+    f32x4 o[NJ];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Chunks are read kMB at a time (their loads in flight together); the
     // batch is kept small so that the merge does not set the kernel's
     // register budget.
     constexpr int kMB = 2;
     for (int c0 = 0; c0 < nc; c0 += kMB) {
-      f32x4 a[kMB][8];
+      f32x4 a[kMB][NJ];
       float mc[kMB], lc[kMB];
 #pragma unroll
       for (int t = 0; t < kMB; ++t) {
@@ -881,7 +906,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
         lc[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             pr, cb + uint32_t(BLK * HD + BLK + q) * 4u, 0, kAgentScope));
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < NJ; ++j)
           a[t][j] = __builtin_bit_cast(
               f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, cb + qoff + 16u * j, 0, kAgentScope));
       }
@@ -893,7 +918,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
         const float wc = mc[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc[t] - mn);
         L = L * wo + lc[t] * wc;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = o[j] * wo + a[t][j] * wc;
+        for (int j = 0; j < NJ; ++j) o[j] = o[j] * wo + a[t][j] * wc;
         M = mn;
       }
     }
@@ -901,16 +926,16 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
     const int qrow = (r - bh * nb) * BLK + q;
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const __amdgpu_buffer_rsrc_t orsc = make_rsrc(O + size_t(bh) * size_t(N) * HD, head_bytes);
-    const uint32_t ob = uint32_t(qrow) * W::ROWB + uint32_t(32 * hh) * 2u;
+    const uint32_t ob = uint32_t(qrow) * W::ROWB + uint32_t((HD / 2) * hh) * 2u;
     // O = attention (+ R, summed in fp32), rounded once to bf16.
-    v4u rr[4];
+    v4u rr[NJ / 2];
     if (RES) {
       const __amdgpu_buffer_rsrc_t rrsc = make_rsrc(R + size_t(bh) * size_t(N) * HD, head_bytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rr[j] = __builtin_amdgcn_raw_buffer_load_b128(rrsc, ob + 16u * j, 0, 0);
+      for (int j = 0; j < NJ / 2; ++j) rr[j] = __builtin_amdgcn_raw_buffer_load_b128(rrsc, ob + 16u * j, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ / 2; ++j) {
       f32x4 x = o[2 * j] * inv, y = o[2 * j + 1] * inv;
       if (RES) {
         x += f32x4{bf16_lo(rr[j][0]), bf16_hi(rr[j][0]), bf16_lo(rr[j][1]), bf16_hi(rr[j][1])};
@@ -920,13 +945,13 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
                         pack_bf16x2(y[2], y[3])};
       __builtin_amdgcn_raw_buffer_store_b128(w, orsc, ob + 16u * j, 0, 0);
     }
-    if (LSE == nullptr) return 4;
+    if (LSE == nullptr) return NJ / 2;
     const __amdgpu_buffer_rsrc_t lrsc =
         make_rsrc(LSE + size_t(bh) * size_t(N), static_cast<uint32_t>(N) * 4u);
     const float lv = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f : -INFINITY;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lrsc,
                                           hh == 0 ? uint32_t(qrow) * 4u : uint32_t(N) * 4u, 0, 0);
-    return 5;
+    return NJ / 2 + 1;
   };
 
   // Lane position of the transposing V^T reads: for the 16-key step c2, V^T
@@ -938,36 +963,36 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
   // swizzle alike.
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  uint32_t koff[4], voff[4];  // lane offsets of the K and V^T reads within a stage
+  uint32_t koff[NDC], voff[2 * NDT];  // lane offsets of the K and V^T reads within a stage
 #pragma unroll
-  for (int c = 0; c < 4; ++c) koff[c] = swz<W::ROWB>(ql, 2 * c + hh);
+  for (int c = 0; c < NDC; ++c) koff[c] = swz<W::ROWB>(ql, 2 * c + hh);
 #pragma unroll
-  for (int u2 = 0; u2 < 2; ++u2)
+  for (int u2 = 0; u2 < NDT; ++u2)
 #pragma unroll
     for (int hl = 0; hl < 2; ++hl) {
       const int col = 32 * u2 + tr_col;
       voff[2 * u2 + hl] = W::HALFB + swz<W::ROWB>(8 * hl + tr_row, col >> 3) + (col & 7) * 2;
     }
   auto stage_at = [&](int p) -> uint32_t { return ring + uint32_t((ib + p) & 1) * W::STAGEB; };
-  auto read_k = [&](uint32_t st, bf16x8 (&ka)[4]) {
+  auto read_k = [&](uint32_t st, bf16x8 (&ka)[NDC]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ka[c] = lds_read16(st + koff[c]);
+    for (int c = 0; c < NDC; ++c) ka[c] = lds_read16(st + koff[c]);
   };
-  auto read_v = [&](uint32_t st, v4s (&vlo)[2][2], v4s (&vhi)[2][2]) {
+  auto read_v = [&](uint32_t st, v4s (&vlo)[2][NDT], v4s (&vhi)[2][NDT]) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int u2 = 0; u2 < 2; ++u2) {
-        vlo[c2][u2] = lds_read_tr(st + voff[2 * u2] + 2048u * c2);
-        vhi[c2][u2] = lds_read_tr(st + voff[2 * u2 + 1] + 2048u * c2);
+      for (int u2 = 0; u2 < NDT; ++u2) {
+        vlo[c2][u2] = lds_read_tr(st + voff[2 * u2] + uint32_t(16 * W::ROWB) * c2);
+        vhi[c2][u2] = lds_read_tr(st + voff[2 * u2 + 1] + uint32_t(16 * W::ROWB) * c2);
       }
   };
   // S^T of query group g: lane (ql, hh) holds keys 8(i/4) + 4hh + (i%4) (of
   // this half) of query 32g + ql.
-  auto scores_g = [&](int g, const bf16x8 (&ka)[4], f32x16& s) {
+  auto scores_g = [&](int g, const bf16x8 (&ka)[NDC], f32x16& s) {
     const f32x16 zero = {};
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NDC; ++c)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : s, 0, 0, 0);
   };
   // Keys at or past the tile's valid count score -inf (both groups).  Lane
@@ -1003,11 +1028,11 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
     // ---- one item ---------------------------------------------------------
     float m_run[2] = {kNoMax, kNoMax};  // running max of scale*log2(e)*s
     float l_run[2] = {0.f, 0.f};        // lane-partial running sums
-    f32x16 acc[2][2];                   // [query group][d half]
+    f32x16 acc[2][NDT];                 // [query group][32-wide d subtile]
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < NDT; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[g][u][i] = 0.f;
 
@@ -1026,7 +1051,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
           const float alpha = rescale[g] ? __builtin_amdgcn_exp2f(m_run[g] - mt[g]) : 1.f;
           l_run[g] *= alpha;
 #pragma unroll
-          for (int u2 = 0; u2 < 2; ++u2)
+          for (int u2 = 0; u2 < NDT; ++u2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[g][u2][i] *= alpha;
         }
@@ -1052,38 +1077,42 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
     // Query group g: the softmax numerators of tile u (scores sc) interleaved
     // with the four MFMAs of tile u + 1's scores (into sn), a quarter of the
     // vector work after each, so that both run at once.
-    auto phase = [&](int g, const bf16x8 (&ka)[4], const f32x16& sc, f32x16& sn, bf16x8 (&pb)[2]) {
+    auto phase = [&](int g, const bf16x8 (&ka)[NDC], const f32x16& sc, f32x16& sn, bf16x8 (&pb)[2]) {
+      constexpr int EPC = 16 / NDC;  // softmax elements per score MFMA
       const f32x16 zero = {};
       float p[16];
       float ls[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NDC; ++c) {
         sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[g][c], c == 0 ? zero : sn, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * c + e;
+        for (int e = 0; e < EPC; ++e) {
+          const int i = EPC * c + e;
           p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -m_run[g]));
-          if (c == 0)
-            ls[e] = p[i];
+          if (i < 4)
+            ls[i & 3] = p[i];
           else
-            ls[e] += p[i];
+            ls[i & 3] += p[i];
         }
-        if (c & 1) {
+        if ((EPC * (c + 1)) % 8 == 0) {
+          const int h8 = EPC * (c + 1) / 8 - 1;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pb[c >> 1][e] = static_cast<__bf16>(p[8 * (c >> 1) + e]);
+          for (int e = 0; e < 8; ++e) pb[h8][e] = static_cast<__bf16>(p[8 * h8 + e]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // its share of the softmax
+        if constexpr (HD == 64) {  // (at head dim 128 the compiler's order measured as fast)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // its share of the softmax
+        }
       }
       l_run[g] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
     // O^T += V^T P^T, one V^T operand per 16-key step and d half, shared by both
     // query groups.
-    auto pv = [&](const v4s (&vlo)[2][2], const v4s (&vhi)[2][2], const bf16x8 (&pb)[2][2]) {
+    auto pv = [&](const v4s (&vlo)[2][NDT], const v4s (&vhi)[2][NDT], const bf16x8 (&pb)[2][2]) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-        for (int u2 = 0; u2 < 2; ++u2) {
+        for (int u2 = 0; u2 < NDT; ++u2) {
           const bf16x8 a = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(vlo[c2][u2], vhi[c2][u2], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -1124,20 +1153,20 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
       if (queue && kh == 0 && claim_out && !nn_known && u + 2 == cnt) resolve_claim();
       settle(sc);
       issue(vd_cur, jv, u + 1, true);
-      int issued = 4;
+      int issued = W::LPH;
       if (u + 2 < cnt) {
         issue(kd_cur, jk, u + 2, false);
-        issued = 8;
+        issued = 2 * W::LPH;
       } else if (jk >= 0) {  // the next item's first tile
         issue(kd_nxt, jk, u + 2, false);
-        issued = 8;
+        issued = 2 * W::LPH;
       }
       vs = valid_of(jv);
       jv = jk;
       jk = u + 3 < cnt ? ld_uniform(col_idx, cur_c0 + u + 3) : j0n;
       wait_vm_n(issued);
-      bf16x8 ka[4];
-      v4s vlo[2][2], vhi[2][2];
+      bf16x8 ka[NDC];
+      v4s vlo[2][NDT], vhi[2][NDT];
       bf16x8 pb[2][2];
       read_k(stage_at(u + 1), ka);
       read_v(stage_at(u), vlo, vhi);
@@ -1148,10 +1177,12 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
       __builtin_amdgcn_sched_barrier(0);
       pv(vlo, vhi, pb);
       tile_max(sn, mt);
+      if constexpr (HD == 64) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one P V MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // row max of the next tile
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one P V MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // row max of the next tile
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -1173,7 +1204,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
       {
         vs = valid_of(ld_uniform(col_idx, cur_c0));
         wait_vm_n(seq - k0_stamp);
-        bf16x8 ka[4];
+        bf16x8 ka[NDC];
         read_k(stage_at(0), ka);
         scores_g(0, ka, sa[0]);
         scores_g(1, ka, sa[1]);
@@ -1200,7 +1231,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
       const int v_stamp = v_last;
       if (j0n >= 0) issue(vd_nxt, j0n, cnt, true);
       wait_vm_n(seq - v_stamp);
-      v4s vlo[2][2], vhi[2][2];
+      v4s vlo[2][NDT], vhi[2][NDT];
       bf16x8 pb[2][2];
       read_v(stage_at(cnt - 1), vlo, vhi);
       probs_g(0, sa[0], pb[0]);
@@ -1216,12 +1247,12 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
     // its lanes finalise; rows past N read as zeros) is loaded now and lands
     // during the exchange.  Chunks of cut rows add it when they are combined.
     const bool add_r = RES && cur_row >= 0 && cur_slot < 0;
-    v2u rres[2][4];
+    v2u rres[NDT][4];
     if (add_r) {
       const __amdgpu_buffer_rsrc_t rrsc = make_rsrc(R + size_t(cur_bh) * size_t(N) * HD, head_bytes);
       const uint32_t rrow = uint32_t((cur_row - cur_bh * nb) * BLK + kh * 32 + ql) * W::ROWB;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < NDT; ++u)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
           rres[u][g4] = __builtin_amdgcn_raw_buffer_load_b64(
@@ -1252,11 +1283,11 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
     // (Branches on kh keep every register array index a compile-time constant.)
     const int st_free = (ib + cur_cnt + 1) & 1;
     float* xml = reinterpret_cast<float*>(smem + 2 * size_t(W::RINGB));
-    auto send = [&](const f32x16 (&a)[2], float m, float l) {
+    auto send = [&](const f32x16 (&a)[NDT], float m, float l) {
       float* xo = reinterpret_cast<float*>(smem + size_t(kh) * W::RINGB +
                                            size_t(st_free) * W::STAGEB);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < NDT; ++u)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
           *reinterpret_cast<f32x4*>(xo + ((u * 4 + g4) * 64 + lane) * 4) =
@@ -1267,7 +1298,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     };
     int n_stores = 0;  // vector-memory stores this wave issues in the epilogue
-    auto finish = [&](const f32x16 (&a)[2], float m0, float l0) {
+    auto finish = [&](const f32x16 (&a)[NDT], float m0, float l0) {
       const int go = 1 - kh;
       const float* xi = reinterpret_cast<const float*>(smem + size_t(go) * W::RINGB +
                                                        size_t(st_free) * W::STAGEB);
@@ -1277,9 +1308,9 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
       const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
       const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
       const float l = l0 * a0 + l1 * a1;
-      f32x16 o[2];
+      f32x16 o[NDT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < NDT; ++u)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x4 o1 = *reinterpret_cast<const f32x4*>(xi + ((u * 4 + g4) * 64 + lane) * 4);
@@ -1298,7 +1329,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
         constexpr uint32_t kSlotBytes = BLK * (HD + 2) * 4;
         const __amdgpu_buffer_rsrc_t pr = make_rsrc(part + size_t(cur_slot) * BLK * (HD + 2), kSlotBytes);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < NDT; ++u)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4)
             __builtin_amdgcn_raw_buffer_store_b128(
@@ -1312,7 +1343,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), pr,
                                               hh == 0 ? uint32_t(BLK * HD + BLK + q) * 4u : kSlotBytes,
                                               0, kAgentScope);
-        n_stores = 10;
+        n_stores = 4 * NDT + 2;
       } else if (cur_row >= 0) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const __amdgpu_buffer_rsrc_t orsc =
@@ -1320,12 +1351,12 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
         const uint32_t orow = uint32_t(qrow) * W::ROWB;
         // O = attention (+ R, summed in fp32), rounded once to bf16.
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < NDT; ++u)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[u][i] *= inv;
         if (add_r) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < NDT; ++u)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
               o[u][4 * g4 + 0] += bf16_lo(rres[u][g4][0]);
@@ -1339,7 +1370,7 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
         // leaves every lane 8 contiguous columns (32u + 16p + 8hh .. +7), so four
         // 16-byte stores write the row.
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < NDT; ++u)
 #pragma unroll
           for (int pq = 0; pq < 2; ++pq) {
             const int ge = 2 * pq, go2 = 2 * pq + 1;
@@ -1361,14 +1392,14 @@ __global__ __launch_bounds__(Wide::NT) __attribute__((amdgpu_waves_per_eu(2))) v
             __builtin_amdgcn_raw_buffer_store_b128(w, orsc, orow + uint32_t(32 * u + 16 * pq + 8 * hh) * 2u,
                                                    0, 0);
           }
-        n_stores = 4;
+        n_stores = 2 * NDT;
         if (LSE != nullptr) {
           const __amdgpu_buffer_rsrc_t lrsc =
               make_rsrc(LSE + size_t(bh) * size_t(N), static_cast<uint32_t>(N) * 4u);
           const float lv = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lrsc,
                                                 hh == 0 ? uint32_t(qrow) * 4u : uint32_t(N) * 4u, 0, 0);
-          n_stores = 5;
+          n_stores = 2 * NDT + 1;
         }
       }
     };
@@ -2024,7 +2055,7 @@ int32_t launch_grid(int32_t items, int resident, bool queued) {
   return g;
 }
 
-template <bool RES>
+template <int HD, bool RES>
 int resident_wide_workgroups() {
   static std::once_flag once;
   static int n = 0;
@@ -2034,15 +2065,15 @@ int resident_wide_workgroups() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&fwd_wide_kernel<RES>), Wide::NT,
-            Wide::LDS_BYTES) != hipSuccess)
+            &per_cu, reinterpret_cast<const void*>(&fwd_wide_kernel<HD, RES>), Wide<HD>::NT,
+            Wide<HD>::LDS_BYTES) != hipSuccess)
       return;
     n = cus * (per_cu > 0 ? per_cu : 1);
   });
   return n;
 }
 
-template <bool RES>
+template <int HD, bool RES>
 bsa_status launch_wide(const void* q, const void* k, const void* v, int32_t N, int32_t nb,
                        int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
                        const int32_t* work, int32_t n_items, int32_t n_merges, int32_t n_slots,
@@ -2051,17 +2082,17 @@ bsa_status launch_wide(const void* q, const void* k, const void* v, int32_t N, i
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_wide_kernel<RES>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_wide_kernel<HD, RES>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(Wide::LDS_BYTES));
+                               static_cast<int>(Wide<HD>::LDS_BYTES));
   });
   if (attr != hipSuccess) return BSA_ERR_HIP;
   const int32_t items = work ? n_items : n_rows;
-  const int resident = resident_wide_workgroups<RES>();
+  const int resident = resident_wide_workgroups<HD, RES>();
   if (resident <= 0) return BSA_ERR_HIP;
   const int32_t grid = launch_grid(items, resident, work != nullptr);
   if (grid > 0) {
-    hipLaunchKernelGGL(fwd_wide_kernel<RES>, dim3(grid), dim3(Wide::NT), Wide::LDS_BYTES, stream,
+    hipLaunchKernelGGL((fwd_wide_kernel<HD, RES>), dim3(grid), dim3(Wide<HD>::NT), Wide<HD>::LDS_BYTES, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), row_ptr, col_idx, work, items, n_merges,
                        N, nb, n_rows, sl2, static_cast<uint16_t*>(o), lse, part, ctr,
@@ -2161,14 +2192,14 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, int32_t B, 
   q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items, n_merges, sl2, o, lse, \
       part, ctr, r, s
   const bool res = r != nullptr;
+#define BSA_WIDE_ARGS                                                                           \
+  q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev, n_items, n_merges, n_slots, sl2, o, \
+      lse, part, ctr, mctr, r, s
   if (block == 64 && D == 64)
-    return res ? launch_wide<true>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev,
-                                   n_items, n_merges, n_slots, sl2, o, lse, part, ctr, mctr, r, s)
-               : launch_wide<false>(q, k, v, N, nb, n_rows, row_ptr_dev, col_idx_dev, work_dev,
-                                    n_items, n_merges, n_slots, sl2, o, lse, part, ctr, mctr, r,
-                                    s);
+    return res ? launch_wide<64, true>(BSA_WIDE_ARGS) : launch_wide<64, false>(BSA_WIDE_ARGS);
   if (block == 64 && D == 128)
-    return res ? launch_fwd<64, 128, true>(BSA_FWD_ARGS) : launch_fwd<64, 128, false>(BSA_FWD_ARGS);
+    return res ? launch_wide<128, true>(BSA_WIDE_ARGS) : launch_wide<128, false>(BSA_WIDE_ARGS);
+#undef BSA_WIDE_ARGS
   if (block == 128 && D == 64)
     return res ? launch_fwd<128, 64, true>(BSA_FWD_ARGS) : launch_fwd<128, 64, false>(BSA_FWD_ARGS);
   return res ? launch_fwd<128, 128, true>(BSA_FWD_ARGS) : launch_fwd<128, 128, false>(BSA_FWD_ARGS);
