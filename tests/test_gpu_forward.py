@@ -177,7 +177,8 @@ def test_item_queue_matches_static_order_and_resets(block, D, n_groups):
 
 
 @pytest.mark.parametrize("block,D,max_tiles,n_groups", [(64, 64, 2, 8), (64, 64, 3, 1),
-                                                         (64, 64, 1, 8), (64, 128, 2, 8)])
+                                                         (64, 64, 1, 8), (64, 128, 2, 8),
+                                                         (64, 128, 1, 1)])
 def test_cut_rows_repeat_bitwise_and_counters_reset(block, D, max_tiles, n_groups):
     """Cut rows combined once their last chunk is stored: the oracle's values, the same
     bits call after call, and every item and merge counter back at zero after each call.
@@ -204,8 +205,9 @@ def test_cut_rows_repeat_bitwise_and_counters_reset(block, D, max_tiles, n_group
         assert int(work.workspace[:n_cnt].count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("block,D,max_tiles", [(64, 64, 1), (64, 64, 3), (64, 128, 2),
-                                               (128, 64, 4), (128, 128, 1)])
+@pytest.mark.parametrize("block,D,max_tiles", [(64, 64, 1), (64, 64, 3), (64, 128, 1),
+                                               (64, 128, 2), (64, 128, 3), (128, 64, 4),
+                                               (128, 128, 1)])
 def test_cut_rows_match_oracle(block, D, max_tiles):
     """Rows cut into chunks (partials in the workspace, then combined) against the oracle."""
     bsa = need_gpu()
